@@ -1,0 +1,244 @@
+"""Benchmark of the NVFP4 quantized-linear hot path on one MI355X.
+
+One step = forward + backward of the dense linear layer
+X [8192 x 4096] (BF16), W [14336 x 4096] (BF16), dY [8192 x 14336] (BF16):
+  1 quantize X   row-wise 1x16 RTN + column-wise 1x16 RHT SR   (one read of X)
+  2 quantize W   16x16 RTN
+  3 fprop        Y  = Xq Wq^T       NVFP4 GEMM, BF16 out
+  4 quantize dY  column-wise 1x16 RHT SR + row-wise MXFP8 SR  (one read of dY)
+  5 requantize   Wq -> MXFP8 of Wq^T, SR
+  6 dgrad        dX = dY W          MXFP8 GEMM, BF16 out
+  7 wgrad        dW = dY^T X        NVFP4 GEMM over the RHT'd copies, FP32 out
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Prints one JSON line (value = whole-step GEMM TFLOP/s including every
+quantize pass), with per-kernel times, a roofline entry for the fprop GEMM
+and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, K, N = 8192, 4096, 14336
+GEMM_FLOP = 2.0 * M * N * K                     # 962.07 GFLOP per GEMM
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0                      # MFMA class the NVFP4 GEMM issues
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP4_TFLOPS = 10100.0
+
+
+def nvfp4_bytes(r, c):
+    return r * c // 2 + r * c // 16
+
+
+def algorithmic_bytes():
+    """Bytes each memory-bound pass must move (one read of its input + its outputs)."""
+    x_in, w_in, dy_in = 2 * M * K, 2 * N * K, 2 * M * N
+    return {
+        "quant_x": x_in + nvfp4_bytes(M, K) + nvfp4_bytes(K, M),
+        "quant_w": w_in + (N * K // 2 + (N // 16) * (K // 16)),
+        "quant_dy": dy_in + nvfp4_bytes(N, M) + (M * N + M * N // 32),
+        "requant_w": (N * K // 2 + (N // 16) * (K // 16)) + (K * N + K * N // 32),
+    }
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded slice of the same step; each
+    component's time is scaled to the full size by the share of work sampled."""
+    import oracle as O
+    from workloads import synth
+    ms, ns = 512, 2048                    # sampled token rows / weight rows
+    x = synth.normal_with_outliers(ms, K, 301)
+    w = synth.normal(ns, K, 302, 0.02)
+    dy = synth.laplace(ms, N, 401, 1e-3)
+    s = synth.rht_signs(402)
+    t = {}
+    t0 = time.perf_counter()
+    xq = O.nvfp4_quantize(x)
+    xc = O.nvfp4_quantize(x, transpose=True, rht=True, signs=s, mode=O.SR, seed=405)
+    t["quant_x"] = (time.perf_counter() - t0) * (M / ms)
+    t0 = time.perf_counter()
+    wq = O.nvfp4_quantize(w, tile2d=True)
+    t["quant_w"] = (time.perf_counter() - t0) * (N / ns)
+    t0 = time.perf_counter()
+    gc = O.nvfp4_quantize(dy, transpose=True, rht=True, signs=s, mode=O.SR, seed=403)
+    gm = O.mxfp8_quantize(dy, mode=O.SR, seed=404)
+    t["quant_dy"] = (time.perf_counter() - t0) * (M / ms)
+    t0 = time.perf_counter()
+    wt = O.mxfp8_requantize_t(wq, mode=O.SR, seed=406)
+    t["requant_w"] = (time.perf_counter() - t0) * (N / ns)
+    # GEMMs: FP64 over dequantized operands, on ms x ns outputs
+    t0 = time.perf_counter()
+    O.gemm_f64(xq.dequant_f64(), wq.dequant_f64())
+    t["fprop"] = (time.perf_counter() - t0) * (M / ms) * (N / ns)
+    t0 = time.perf_counter()
+    # dX sample: ms x K outputs over an ns-wide slice of the contraction dim N
+    O.gemm_f64(np.ascontiguousarray(gm.dequant_f64()[:, :ns]), wt.dequant_f64())
+    t["dgrad"] = (time.perf_counter() - t0) * (M / ms) * (N / ns)
+    t0 = time.perf_counter()
+    O.gemm_f64(gc.dequant_f64()[:ns], xc.dequant_f64()[:ns])
+    t["wgrad"] = (time.perf_counter() - t0) * (N / ns) * (K / ns) * (M / ms)
+    total = sum(t.values())
+    return {
+        "value": round(3 * GEMM_FLOP / total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": (f"X/dY slices of {ms} token rows, W slice of {ns} rows; fprop on {ms}x{ns} "
+                   f"outputs, dgrad on {ms}x{K} outputs over {ns} of N, wgrad on {ns}x{ns} "
+                   f"outputs over {ms} tokens; each part's time scaled to the full step by "
+                   f"its work ratio"),
+        "extrapolated_step_s": round(total, 2),
+        "parts_s": {k: round(v, 2) for k, v in t.items()},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import bit_block_scaled_amd as bbs
+    from workloads import synth
+
+    dev = torch.device("cuda:0")
+    fw = synth.dense_forward(M, K, N)
+    bw = synth.backward(M, N)
+    signs, seeds = bw["rht_signs"], bw["seeds"]
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev)
+
+    x, w, dy = up(fw["x"]), up(fw["w"]), up(bw["dy"])
+    del fw, bw
+    T = bbs.NVFP4Tensor
+    xq, xc = T.empty(M, K, device=dev), T.empty(K, M, device=dev)
+    wq = T.empty(N, K, tile2d=True, device=dev)
+    gc = T.empty(N, M, device=dev)
+    gm = bbs.MXFP8Tensor.empty(M, N, device=dev)
+    wt = bbs.MXFP8Tensor.empty(K, N, device=dev)
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.int16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    ws = bbs.amax_workspace(dev)
+
+    ops = {
+        "quant_x": lambda: bbs.nvfp4_quantize(x, xq, xc, col_round=bbs.SR,
+                                              col_rng=(seeds["x_col"], 0), col_rht=True,
+                                              rht_signs=signs, amax_ws=ws),
+        "quant_w": lambda: bbs.nvfp4_quantize(w, wq, tile2d=True, amax_ws=ws),
+        "fprop": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, xq, wq, y, bbs.OUT_BF16),
+        "quant_dy": lambda: bbs.nvfp4_quantize(dy, None, gc, gm, col_round=bbs.SR,
+                                               col_rng=(seeds["dy_col"], 0), col_rht=True,
+                                               rht_signs=signs, mx8_round=bbs.SR,
+                                               mx8_rng=(seeds["dy_mx8"], 0), amax_ws=ws),
+        "requant_w": lambda: bbs.mxfp8_requantize_t(wq, wt, bbs.SR, (seeds["w_req"], 0)),
+        "dgrad": lambda: bbs.nvfp4_gemm(bbs.FMT_MXFP8, gm, wt, dx, bbs.OUT_BF16),
+        "wgrad": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, gc, xc, dw, bbs.OUT_F32),
+    }
+
+    def step():
+        for f in ops.values():
+            f()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} steps done", file=sys.stderr, flush=True)
+
+    # whole-step timing
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel timing: the same launches back to back on the same stream
+    per = {}
+    for name, f in ops.items():
+        f()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        per[name] = s0.elapsed_time(s1) / args.steps
+    ab = algorithmic_bytes()
+    kernels = {}
+    for name, t_ms in per.items():
+        e = {"ms": round(t_ms, 4)}
+        if name in ab:
+            gbps = ab[name] / (t_ms * 1e-3) / 1e9
+            e.update({"GB/s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                      "bytes": ab[name]})
+        else:
+            tf = GEMM_FLOP / (t_ms * 1e-3) / 1e12
+            peak = PEAK_FP8_TFLOPS if name == "dgrad" else PEAK_BF16_TFLOPS
+            e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / peak, 4),
+                      "fp4_peak_frac": round(tf / PEAK_FP4_TFLOPS, 4)})
+        kernels[name] = e
+    print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+
+    fprop_ms = per["fprop"]
+    fprop_tf = GEMM_FLOP / (fprop_ms * 1e-3) / 1e12
+    qbytes = ab["quant_x"] + ab["quant_w"]
+    q_gbps = qbytes / ((per["quant_x"] + per["quant_w"]) * 1e-3) / 1e9
+    value = 3 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "NVFP4 quantize GB/s + NVFP4 GEMM TFLOPS (8192x4096x14336), % of roofline",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4/mxfp8 operands, bf16+fp8 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "dense NVFP4 linear fwd+bwd, X 8192x4096, W 14336x4096, "
+                               "dY 8192x14336", "M": M, "K": K, "N": N,
+                   "step_gemm_flop": 3 * GEMM_FLOP},
+        "quantize_GBps": round(q_gbps, 1),
+        "gemm_TFLOPs": round(fprop_tf, 1),
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "achieved": round(fprop_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fprop_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "nvfp4_gemm_kernel (fprop)",
+                     "peak_fp4": PEAK_FP4_TFLOPS,
+                     "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
+        "wall_s_timed": round(wall_s, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

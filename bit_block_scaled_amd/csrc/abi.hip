@@ -1,0 +1,262 @@
+// C ABI of the library (declared in include/bbs.h): argument checks, then
+// kernel launches on the caller's stream.  Nothing here allocates device
+// memory or synchronises the host.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bbs.h"
+#include "bbs_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return BBS_OK;
+    return fail(BBS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape and pointer checks of one NVFP4 descriptor.
+int check_fp4(const bbs_fp4 *d, const char *name, bool need_sdec) {
+    if (!d) return fail(BBS_EINVAL, "%s: null descriptor", name);
+    if (!d->codes || !d->scales || (need_sdec && !d->s_dec))
+        return fail(BBS_EINVAL, "%s: null codes/scales/s_dec", name);
+    if (d->rows <= 0 || d->cols <= 0 || d->rows % 16 || d->cols % 16)
+        return fail(BBS_EINVAL, "%s: rows=%lld cols=%lld must be positive multiples of 16", name,
+                    (long long)d->rows, (long long)d->cols);
+    if (!aligned(d->codes, 16)) return fail(BBS_EINVAL, "%s: codes not 16-byte aligned", name);
+    if (d->tile2d != 0 && d->tile2d != 1) return fail(BBS_EINVAL, "%s: tile2d must be 0 or 1", name);
+    return BBS_OK;
+}
+
+int check_mx8(const bbs_mx8 *d, const char *name) {
+    if (!d) return fail(BBS_EINVAL, "%s: null descriptor", name);
+    if (!d->codes || !d->scales) return fail(BBS_EINVAL, "%s: null codes/scales", name);
+    if (d->rows <= 0 || d->cols <= 0 || d->cols % 32)
+        return fail(BBS_EINVAL, "%s: rows=%lld cols=%lld (cols must be a multiple of 32)", name,
+                    (long long)d->rows, (long long)d->cols);
+    if (!aligned(d->codes, 16)) return fail(BBS_EINVAL, "%s: codes not 16-byte aligned", name);
+    return BBS_OK;
+}
+
+bool round_ok(int32_t r) { return r == BBS_RTN || r == BBS_SR; }
+
+}  // namespace
+
+extern "C" {
+
+const char *bbs_strerror(int status) {
+    switch (status) {
+        case BBS_OK: return "ok";
+        case BBS_EINVAL: return "invalid argument";
+        case BBS_ENOTSUP: return "unsupported combination";
+        case BBS_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *bbs_last_error(void) { return g_err; }
+
+int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
+    g_err[0] = 0;
+    if (!a) return fail(BBS_EINVAL, "null args");
+    if (!a->x) return fail(BBS_EINVAL, "null x");
+    if (!a->row && !a->col && !a->row_mx8) return fail(BBS_EINVAL, "no output copy requested");
+    if (a->rows <= 0 || a->cols <= 0 || a->rows % 16 || a->cols % 16)
+        return fail(BBS_EINVAL, "rows=%lld cols=%lld must be positive multiples of 16",
+                    (long long)a->rows, (long long)a->cols);
+    if (a->ld < a->cols || a->ld % 8) return fail(BBS_EINVAL, "ld must be >= cols and a multiple of 8");
+    if (!aligned(a->x, 16)) return fail(BBS_EINVAL, "x not 16-byte aligned");
+    if (a->tile2d != 0 && a->tile2d != 1) return fail(BBS_EINVAL, "tile2d must be 0 or 1");
+    const bool need_amax = a->row || a->col;
+    if (need_amax && !a->amax_ws) return fail(BBS_EINVAL, "null amax workspace");
+    int st;
+    if (a->row) {
+        if ((st = check_fp4(a->row, "row", true))) return st;
+        if (a->row->rows != a->rows || a->row->cols != a->cols)
+            return fail(BBS_EINVAL, "row copy must be rows x cols");
+        if (a->row->tile2d != a->tile2d) return fail(BBS_EINVAL, "row copy tile2d mismatch");
+        if (!round_ok(a->row_round)) return fail(BBS_EINVAL, "bad row_round");
+    }
+    if (a->col) {
+        if ((st = check_fp4(a->col, "col", true))) return st;
+        if (a->col->rows != a->cols || a->col->cols != a->rows)
+            return fail(BBS_EINVAL, "col copy must be cols x rows");
+        if (a->col->tile2d != a->tile2d) return fail(BBS_EINVAL, "col copy tile2d mismatch");
+        if (!round_ok(a->col_round)) return fail(BBS_EINVAL, "bad col_round");
+        if (a->col_rht != 0 && a->col_rht != 1) return fail(BBS_EINVAL, "col_rht must be 0 or 1");
+        if (a->col_rht && a->tile2d) return fail(BBS_ENOTSUP, "RHT on a 16x16-tiled copy");
+        if (a->rht_signs > 0xFFFFu) return fail(BBS_EINVAL, "rht_signs has more than 16 bits");
+    }
+    if (a->row_mx8) {
+        if ((st = check_mx8(a->row_mx8, "row_mx8"))) return st;
+        if (a->row_mx8->rows != a->rows || a->row_mx8->cols != a->cols)
+            return fail(BBS_EINVAL, "row_mx8 copy must be rows x cols");
+        if (!round_ok(a->mx8_round)) return fail(BBS_EINVAL, "bad mx8_round");
+    }
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    bbs::QuantParams p{};
+    p.x = a->x;
+    p.R = a->rows;
+    p.C = a->cols;
+    p.ld = a->ld;
+    const bool rht = a->col && a->col_rht;
+    const bool plain = a->row || (a->col && !rht);
+    if (plain) {
+        hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, a->amax_ws, &p.n_part, s);
+        if ((st = hip_status(e, "amax launch"))) return st;
+        p.part = a->amax_ws;
+    }
+    if (rht) {
+        float *ws = a->amax_ws + bbs::kAmaxPartials;
+        hipError_t e = bbs::launch_amax_rht(a->x, a->rows, a->cols, a->ld, a->rht_signs, ws,
+                                            &p.n_part_rht, s);
+        if ((st = hip_status(e, "amax_rht launch"))) return st;
+        p.part_rht = ws;
+    }
+    if (a->row) {
+        p.row_codes = a->row->codes;
+        p.row_scales = a->row->scales;
+        p.row_sdec = a->row->s_dec;
+        p.row_round = a->row_round;
+        p.row_seed = a->row_rng.seed;
+        p.row_stream = a->row_rng.stream;
+    }
+    if (a->col) {
+        p.col_codes = a->col->codes;
+        p.col_scales = a->col->scales;
+        p.col_sdec = a->col->s_dec;
+        p.col_round = a->col_round;
+        p.col_seed = a->col_rng.seed;
+        p.col_stream = a->col_rng.stream;
+        p.rht_signs = a->rht_signs;
+    }
+    if (a->row_mx8) {
+        p.mx_codes = a->row_mx8->codes;
+        p.mx_scales = a->row_mx8->scales;
+        p.mx_round = a->mx8_round;
+        p.mx_seed = a->mx8_rng.seed;
+        p.mx_stream = a->mx8_rng.stream;
+    }
+    hipError_t e = bbs::launch_quant_tile(p, a->row != nullptr, a->col != nullptr,
+                                          a->row_mx8 != nullptr, a->tile2d != 0, rht, s);
+    return hip_status(e, "quantize launch");
+}
+
+int mxfp8_requantize_t(const bbs_fp4 *src, const bbs_mx8 *dst, int32_t round, bbs_rng rng,
+                       void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_fp4(src, "src", true))) return st;
+    if ((st = check_mx8(dst, "dst"))) return st;
+    if (dst->rows != src->cols || dst->cols != src->rows)
+        return fail(BBS_EINVAL, "dst must be src.cols x src.rows");
+    if (src->rows % 32) return fail(BBS_EINVAL, "src.rows must be a multiple of 32");
+    if (!round_ok(round)) return fail(BBS_EINVAL, "bad round");
+    if (!aligned(src->codes, 8)) return fail(BBS_EINVAL, "src codes not 8-byte aligned");
+    bbs::RequantParams p{};
+    p.codes = src->codes;
+    p.scales = src->scales;
+    p.s_dec = src->s_dec;
+    p.R = src->rows;
+    p.C = src->cols;
+    p.tile2d = src->tile2d;
+    p.out_codes = dst->codes;
+    p.out_scales = dst->scales;
+    p.seed = rng.seed;
+    p.stream = rng.stream;
+    return hip_status(bbs::launch_requant(p, round == BBS_SR, reinterpret_cast<hipStream_t>(stream)),
+                      "requantize launch");
+}
+
+int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dtype, int64_t ldc,
+               void *stream) {
+    g_err[0] = 0;
+    if (!C) return fail(BBS_EINVAL, "null C");
+    if (c_dtype != BBS_OUT_F32 && c_dtype != BBS_OUT_BF16) return fail(BBS_EINVAL, "bad c_dtype");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int st;
+    if (fmt == BBS_FMT_NVFP4) {
+        const bbs_fp4 *a = static_cast<const bbs_fp4 *>(A), *b = static_cast<const bbs_fp4 *>(B);
+        if ((st = check_fp4(a, "A", true))) return st;
+        if ((st = check_fp4(b, "B", true))) return st;
+        if (a->cols != b->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+        if (ldc < b->rows) return fail(BBS_EINVAL, "ldc < N");
+        bbs::GemmParams p{};
+        p.a = {a->codes, a->scales, a->s_dec, a->rows, a->tile2d};
+        p.b = {b->codes, b->scales, b->s_dec, b->rows, b->tile2d};
+        p.M = a->rows;
+        p.N = b->rows;
+        p.K = a->cols;
+        p.c = C;
+        p.ldc = ldc;
+        return hip_status(bbs::launch_nvfp4_gemm(p, c_dtype == BBS_OUT_BF16, s), "gemm launch");
+    }
+    if (fmt == BBS_FMT_MXFP8) {
+        const bbs_mx8 *a = static_cast<const bbs_mx8 *>(A), *b = static_cast<const bbs_mx8 *>(B);
+        if ((st = check_mx8(a, "A"))) return st;
+        if ((st = check_mx8(b, "B"))) return st;
+        if (a->cols != b->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+        if (ldc < b->rows) return fail(BBS_EINVAL, "ldc < N");
+        bbs::Mx8GemmParams p{};
+        p.a_codes = a->codes;
+        p.a_scales = a->scales;
+        p.b_codes = b->codes;
+        p.b_scales = b->scales;
+        p.M = a->rows;
+        p.N = b->rows;
+        p.K = a->cols;
+        p.c = C;
+        p.ldc = ldc;
+        return hip_status(bbs::launch_mxfp8_gemm(p, c_dtype == BBS_OUT_BF16, s), "mxfp8 gemm launch");
+    }
+    return fail(BBS_EINVAL, "unknown fmt %d", fmt);
+}
+
+int grouped_nvfp4_gemm(const bbs_fp4 *A, const int32_t *row_index, const int64_t *group_offsets,
+                       int32_t G, int64_t max_rows, const bbs_fp4 *B, int64_t N, void *C,
+                       int32_t c_dtype, int64_t ldc, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_fp4(A, "A", true))) return st;
+    if ((st = check_fp4(B, "B", true))) return st;
+    if (!group_offsets) return fail(BBS_EINVAL, "null group_offsets");
+    if (!C) return fail(BBS_EINVAL, "null C");
+    if (G <= 0 || G > 1024) return fail(BBS_EINVAL, "G must be in [1, 1024]");
+    if (N <= 0 || N % 16 || B->rows != (int64_t)G * N)
+        return fail(BBS_EINVAL, "B.rows must equal G * N with N %% 16 == 0");
+    if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+    if (max_rows < 0) return fail(BBS_EINVAL, "max_rows < 0");
+    if (ldc < N) return fail(BBS_EINVAL, "ldc < N");
+    if (c_dtype != BBS_OUT_F32 && c_dtype != BBS_OUT_BF16) return fail(BBS_EINVAL, "bad c_dtype");
+    bbs::GemmParams p{};
+    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d};
+    p.b = {B->codes, B->scales, B->s_dec, N, B->tile2d};
+    p.M = max_rows;
+    p.N = N;
+    p.K = A->cols;
+    p.c = C;
+    p.ldc = ldc;
+    p.row_index = row_index;
+    p.group_offsets = group_offsets;
+    p.G = G;
+    p.max_rows = max_rows;
+    p.a_src_rows = A->rows;
+    return hip_status(bbs::launch_grouped_nvfp4_gemm(p, c_dtype == BBS_OUT_BF16,
+                                                     reinterpret_cast<hipStream_t>(stream)),
+                      "grouped gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Kernel parameter blocks and host-side launchers shared by the C ABI layer
+// and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bbs {
+
+// Upper bound on the workgroups of an amax pass (= partial maxima written).
+constexpr int kAmaxPartials = 2048;
+
+struct QuantParams {
+    const uint16_t *x;
+    int64_t R, C, ld;
+    // row-wise NVFP4 copy
+    uint8_t *row_codes, *row_scales;
+    float *row_sdec;
+    int row_round;
+    uint32_t row_stream;
+    uint64_t row_seed;
+    // column-wise NVFP4 copy (of x^T)
+    uint8_t *col_codes, *col_scales;
+    float *col_sdec;
+    int col_round;
+    uint32_t col_stream;
+    uint64_t col_seed;
+    uint32_t rht_signs;
+    // row-wise MXFP8 copy
+    uint8_t *mx_codes, *mx_scales;
+    int mx_round;
+    uint32_t mx_stream;
+    uint64_t mx_seed;
+    // amax partials
+    const float *part;
+    const float *part_rht;
+    int n_part, n_part_rht;
+};
+
+struct RequantParams {
+    const uint8_t *codes, *scales;
+    const float *s_dec;
+    int64_t R, C;
+    int tile2d;
+    uint8_t *out_codes, *out_scales;
+    uint64_t seed;
+    uint32_t stream;
+};
+
+// NVFP4 GEMM operand view: rows x K, codes rows x K/2, scales per tile2d.
+struct Fp4View {
+    const uint8_t *codes, *scales;
+    const float *s_dec;
+    int64_t rows;
+    int tile2d;
+};
+
+struct GemmParams {
+    Fp4View a, b;
+    int64_t M, N, K;
+    void *c;
+    int64_t ldc;
+    // grouped mode
+    const int32_t *row_index;      // A row gather (nullptr = identity)
+    const int64_t *group_offsets;  // G + 1 entries
+    int G;
+    int64_t max_rows;
+    int64_t a_src_rows;            // rows of A addressable through row_index
+};
+
+struct Mx8GemmParams {
+    const uint8_t *a_codes, *a_scales, *b_codes, *b_scales;
+    int64_t M, N, K;
+    void *c;
+    int64_t ldc;
+};
+
+hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, float *part,
+                       int *n_part, hipStream_t s);
+hipError_t launch_amax_rht(const uint16_t *x, int64_t R, int64_t C, int64_t ld, uint32_t signs,
+                           float *part, int *n_part, hipStream_t s);
+hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
+                             bool tile2d, bool rht, hipStream_t s);
+hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s);
+hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
+hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
+hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);
+
+}  // namespace bbs

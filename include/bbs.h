@@ -1,0 +1,171 @@
+/*
+ * bbs.h - C ABI of the MI355X (gfx950) NVFP4 quantized-linear library.
+ *
+ * The library implements the data-parallel hot path of an NVFP4 quantized
+ * linear layer: the fused NVFP4 quantizer, the dequantize-transpose-
+ * requantize to MXFP8 of a saved NVFP4 tensor, and the block-scaled GEMMs.
+ * Every arithmetic step runs in HIP kernels on the GPU.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *    caller.  The library never allocates, frees or retains them.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *    enqueued; no call synchronises the host.
+ *  - Matrices are row-major.  BF16 values are passed as their 16-bit
+ *    patterns.  An NVFP4 matrix of shape rows x cols stores its E2M1 codes
+ *    as rows x cols/2 bytes: element 2j of a row is the low nibble of byte j,
+ *    element 2j+1 the high nibble.  Its E4M3 block scales are row-major,
+ *    rows x cols/16 (1x16 blocks) or rows/16 x cols/16 (16x16 tiles).  An
+ *    MXFP8 matrix stores rows x cols E4M3 bytes and rows x cols/32 E8M0
+ *    bytes (scale 2^(byte-127)).
+ *  - Return value: BBS_OK (0) or a negative status.  Arguments are checked
+ *    before anything is enqueued; on error nothing is launched.  Faults of
+ *    a running kernel surface at the caller's next synchronisation.
+ *  - Calls are thread-safe.  Calls on one stream run in order.
+ *  - Precondition of the quantizers: finite inputs, and a tensor amax that
+ *    is either 0 or at least 2^-100 (smaller non-zero maxima overflow the
+ *    FP32 encode scales; the result is then unspecified).
+ */
+#ifndef BBS_H
+#define BBS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BBS_OK 0
+#define BBS_EINVAL (-1)  /* null pointer, bad shape, misalignment, short workspace */
+#define BBS_ENOTSUP (-2) /* a valid but unsupported combination of options        */
+#define BBS_EHIP (-3)    /* the HIP runtime rejected a launch; see bbs_last_error  */
+
+enum bbs_round { BBS_RTN = 0, BBS_SR = 1 };
+enum bbs_out_dtype { BBS_OUT_F32 = 0, BBS_OUT_BF16 = 1 };
+enum bbs_fmt { BBS_FMT_NVFP4 = 0, BBS_FMT_MXFP8 = 1 };
+
+/* Words of device workspace nvfp4_quantize needs for its amax partials. */
+#define BBS_AMAX_WS_FLOATS 4096
+
+/* One NVFP4 tensor: value = E2M1(code) x E4M3(block scale) x s_dec
+ * ("value = FP4 code x FP8 block scale x FP32 outer scale"; Pretraining LLMs
+ * with NVFP4, "NVFP4 Format and Quantization Procedure", steps 1-5).
+ * Blocks run along cols, the GEMM contraction dimension.  s_dec points to one
+ * FP32 decode scale (G scales for the stacked weights of grouped_nvfp4_gemm).
+ * codes must be 16-byte aligned; rows and cols must be multiples of 16. */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    float *s_dec;
+    int64_t rows, cols;
+    int32_t tile2d; /* 0: 1x16 blocks, 1: 16x16 tiles */
+} bbs_fp4;
+
+/* One MXFP8 tensor: value = E4M3(code) x 2^(scale-127), one scale per 32
+ * consecutive values of a row.  codes 16-byte aligned; cols % 32 == 0. */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    int64_t rows, cols;
+} bbs_mx8;
+
+/* Key of the stochastic-rounding draws: element idx of an output copy
+ * (its row-major index in that copy's own layout) uses 16-bit lane idx % 8
+ * of Philox4x32-10(counter = (idx/8 low, idx/8 high, stream, 0), key = seed),
+ * as u = (lane + 1/2) / 65536, and rounds to floor(t + u) grid steps, t being
+ * the magnitude in units of the local grid step (4bit.vizuara.ai, section 6:
+ * "floor(t + rand)").  The same (seed, stream) reproduces the same bits for
+ * any launch geometry. */
+typedef struct {
+    uint64_t seed;
+    uint32_t stream;
+} bbs_rng;
+
+/* Arguments of nvfp4_quantize.  Any of row / col / row_mx8 may be NULL
+ * (that copy is skipped); at least one must be given. */
+typedef struct {
+    const uint16_t *x; /* BF16 source, rows x cols, row stride ld elements   */
+    int64_t rows, cols, ld; /* rows, cols % 16 == 0; ld % 8 == 0; x 16B aligned */
+
+    bbs_fp4 *row;      /* NVFP4 copy of x (blocks along cols), shape rows x cols */
+    int32_t row_round; /* BBS_RTN or BBS_SR */
+    bbs_rng row_rng;
+
+    bbs_fp4 *col;      /* NVFP4 copy of x^T (blocks along rows), shape cols x rows */
+    int32_t col_round;
+    bbs_rng col_rng;
+    int32_t col_rht;    /* 1: 16-point random Hadamard transform of each 16-chunk
+                           of the copy's rows before the amax and the encode */
+    uint32_t rht_signs; /* bit i set: flip the sign of chunk element i first */
+
+    bbs_mx8 *row_mx8;  /* MXFP8 copy of x (blocks of 32 along cols); cols % 32 == 0 */
+    int32_t mx8_round;
+    bbs_rng mx8_rng;
+
+    int32_t tile2d; /* 1: 16x16 tile scales for row and col copies (col is then
+                       the bit-identical transpose of row when both round RTN) */
+    float *amax_ws; /* device workspace, >= BBS_AMAX_WS_FLOATS floats, not kept */
+} bbs_quant_args;
+
+/* NVFP4 quantizer (Pretraining LLMs with NVFP4, "NVFP4 Format and
+ * Quantization Procedure", steps 1-4; 4bit.vizuara.ai, sections 5-6 and 13).
+ * For each requested copy: tensor amax a (over the RHT'd values for an RHT
+ * copy), s_enc = 2688 / a (1 if a == 0), s_dec = 1 / s_enc written to
+ * copy->s_dec[0]; per block: E4M3 code of (amax_b / 6) * s_enc, round to
+ * nearest even, saturating, never below code 1; s_enc_b = 1 / (E4M3 * s_dec);
+ * elements x * s_enc_b rounded to E2M1 (nearest even, or stochastic).
+ * The MXFP8 copy uses, per 32-block, the smallest power of two 2^k with
+ * amax_b <= 448 * 2^k and rounds x * 2^-k to E4M3.
+ * Errors: BBS_EINVAL (null x / workspace, no copy, bad shape or alignment,
+ * output shapes not matching x), BBS_ENOTSUP (RHT on a tile2d copy). */
+int nvfp4_quantize(const bbs_quant_args *a, void *stream);
+
+/* Dequantize -> transpose -> requantize to MXFP8 (4bit.vizuara.ai, sections
+ * 9-10; End-to-End 4-Bit Training, "requantization with stochastic
+ * rounding").  src is an NVFP4 matrix R x C; dst receives the MXFP8 matrix of
+ * src^T, shape C x R, blocks of 32 along R (R % 32 == 0).  Each value is
+ * dequantized in FP32 as (E2M1 x E4M3) x s_dec, then encoded as in the MXFP8
+ * copy of nvfp4_quantize with the given rounding and key.
+ * Errors: BBS_EINVAL on null pointers or mismatched / unaligned shapes. */
+int mxfp8_requantize_t(const bbs_fp4 *src, const bbs_mx8 *dst, int32_t round, bbs_rng rng,
+                       void *stream);
+
+/* Block-scaled GEMM C = A * B^T with FP32 accumulation (Pretraining LLMs
+ * with NVFP4, "NVFP4 Format and Quantization Procedure", step 5;
+ * 4bit.vizuara.ai, section 7).  Both operands carry their blocks along the
+ * shared contraction dimension K = A.cols = B.cols; M = A.rows, N = B.rows.
+ *   fmt == BBS_FMT_NVFP4: A, B are const bbs_fp4 *; C = s_dec,A * s_dec,B *
+ *      sum over blocks of (E4M3_A * E4M3_B * sum of E2M1 products).
+ *   fmt == BBS_FMT_MXFP8: A, B are const bbs_mx8 *; K % 32 == 0.
+ * C is M x N with row stride ldc (>= N) elements of c_dtype (BBS_OUT_F32 or
+ * BBS_OUT_BF16, round to nearest even).  Errors: BBS_EINVAL. */
+int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dtype,
+               int64_t ldc, void *stream);
+
+/* Grouped NVFP4 GEMM for mixture-of-experts layers (4bit.vizuara.ai,
+ * section 11; End-to-End 4-Bit Training, "quantized communication"): for each
+ * expert g, rows [group_offsets[g], group_offsets[g+1]) of the routed
+ * activations times expert g's weights:
+ *   C[i, :] = A_row(i) * B_g^T,   B_g = rows [g*N, (g+1)*N) of B, s_dec = B.s_dec[g]
+ * A_row(i) is row row_index[i] of A, or row i when row_index is NULL.
+ * group_offsets: device array of G+1 non-decreasing int64 (offsets[0] = 0);
+ * empty groups are allowed.  max_rows bounds the routed rows C can hold
+ * (rows beyond it are not computed).  B.rows == G * N, N % 16 == 0.
+ * Tiles are scheduled on the device from group_offsets; the host never
+ * reads them.  Errors: BBS_EINVAL. */
+int grouped_nvfp4_gemm(const bbs_fp4 *A, const int32_t *row_index,
+                       const int64_t *group_offsets, int32_t G, int64_t max_rows,
+                       const bbs_fp4 *B, int64_t N, void *C, int32_t c_dtype, int64_t ldc,
+                       void *stream);
+
+/* Name of a status code. */
+const char *bbs_strerror(int status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *bbs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BBS_H */

@@ -1,0 +1,108 @@
+"""CPU-only checks of the C ABI library: it loads, it exports every entry
+point the header declares, and argument errors come back as status codes
+before any GPU work is attempted."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "bit_block_scaled_amd", "libbbs.so")
+HDR = os.path.join(ROOT, "include", "bbs.h")
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_lists_the_entry_points():
+    names = _declared()
+    for n in ["nvfp4_quantize", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm",
+              "bbs_strerror", "bbs_last_error"]:
+        assert n in names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libbbs.so is not built (run __graft_entry__.build())")
+    return C.CDLL(LIB)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_error_paths_return_status(lib):
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    # null argument block / null x / no copy requested
+    assert L.nvfp4_quantize(None, None) == bbs.BBS_EINVAL
+    a = bbs.QuantArgs()
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"null x" in L.bbs_last_error()
+    a.x = 0x1000
+    a.rows, a.cols, a.ld = 32, 32, 32
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"no output copy" in L.bbs_last_error()
+    # shapes that are not multiples of 16
+    d = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 30, 32, 0)
+    a.row = C.pointer(d)
+    a.rows = 30
+    a.amax_ws = 0x4000
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    # misaligned x
+    a.rows, d.rows = 32, 32
+    a.x = 0x1002
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"aligned" in L.bbs_last_error()
+    # RHT on a 16x16-tiled copy is not supported
+    a.x = 0x1000
+    a.row = None
+    cd = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 32, 1)
+    a.col = C.pointer(cd)
+    a.tile2d = 1
+    a.col_rht = 1
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_ENOTSUP
+    # bad rounding mode
+    a.col_rht = 0
+    a.col_round = 7
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    # GEMM: mismatched K, null C, bad dtype, bad fmt
+    A = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 64, 0)
+    B = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 48, 32, 0)
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 48, None) == bbs.BBS_EINVAL
+    B.cols = 64
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), None, 0, 48, None) == bbs.BBS_EINVAL
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 9, 48, None) == bbs.BBS_EINVAL
+    assert L.nvfp4_gemm(5, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 48, None) == bbs.BBS_EINVAL
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 40, None) == bbs.BBS_EINVAL
+    # MXFP8 operands need cols % 32 == 0
+    MA = bbs.Mx8Desc(0x1000, 0x2000, 32, 48)
+    MB = bbs.Mx8Desc(0x1000, 0x2000, 32, 48)
+    assert L.nvfp4_gemm(1, C.byref(MA), C.byref(MB), C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_EINVAL
+    # requantize: source rows must be a multiple of 32, dst the transpose
+    src = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 48, 32, 0)
+    dst = bbs.Mx8Desc(0x1000, 0x2000, 32, 48)
+    assert L.mxfp8_requantize_t(C.byref(src), C.byref(dst), 1, bbs.Rng(0, 0), None) == bbs.BBS_EINVAL
+    # grouped: B rows must be G * N, G in range
+    gA = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 64, 64, 0)
+    gB = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 96, 64, 1)
+    assert L.grouped_nvfp4_gemm(C.byref(gA), None, C.c_void_p(0x6000), 4, 64, C.byref(gB), 32,
+                                C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_EINVAL
+    assert L.grouped_nvfp4_gemm(C.byref(gA), None, C.c_void_p(0x6000), 0, 64, C.byref(gB), 32,
+                                C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_EINVAL
+    assert L.grouped_nvfp4_gemm(C.byref(gA), None, None, 3, 64, C.byref(gB), 32,
+                                C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_EINVAL
+    assert L.bbs_strerror(bbs.BBS_EINVAL) == b"invalid argument"
+
+
+def test_binding_has_no_cpu_fallback():
+    import bit_block_scaled_amd as bbs
+    src = open(bbs.__file__).read()
+    assert "oracle" not in src.replace("no CPU fallback", "")

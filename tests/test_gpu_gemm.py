@@ -1,0 +1,209 @@
+"""GPU parity of the block-scaled GEMMs against the oracle's FP64 accumulation.
+
+Operands are produced by the oracle (or drawn at random), uploaded byte for
+byte, and multiplied on the GPU; the reference is the FP64 sum over the same
+dequantized operands.  Bar: relative Frobenius error <= 1e-3 (FP32 output
+against the raw FP64 sum; BF16 output against the FP64 sum rounded to BF16).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_util import announce, bf16_bits_to_f64, dev, host, to_dev, upload_mxfp8, upload_nvfp4
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def bbs():
+    import bit_block_scaled_amd as b
+    return b
+
+
+def _run_gemm(bbs, fmt, a, b, M, N, bf16):
+    c = torch.empty((M, N), dtype=torch.int16 if bf16 else torch.float32, device=dev())
+    bbs.nvfp4_gemm(fmt, a, b, c, bbs.OUT_BF16 if bf16 else bbs.OUT_F32)
+    torch.cuda.synchronize()
+    y = host(c)
+    return bf16_bits_to_f64(y.view(np.uint16)) if bf16 else y.astype(np.float64)
+
+
+def _check(y, ref, bf16, what):
+    r = O.bf16_rne(ref) if bf16 else ref
+    err = O.rel_fro(y, r)
+    print(f"  {what}: rel err {err:.3e}", flush=True)
+    assert err <= TOL, f"{what}: relative error {err}"
+    return err
+
+
+def _random_nvfp4(R, C, seed, tile2d=False, s_dec=0.5):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
+    shape = (R // 16, C // 16) if tile2d else (R, C // 16)
+    scales = rng.integers(1, 0x7F, size=shape, dtype=np.uint8)
+    return O.NVFP4(codes, scales, np.float32(s_dec), R, C, tile2d)
+
+
+def test_tiny_linear(bbs):
+    announce("tiny linear 256^3, 1x16 X, 16x16 W, FP32 out")
+    d = synth.tiny_linear()
+    ox = O.nvfp4_quantize(d["x"])
+    ow = O.nvfp4_quantize(d["w"], tile2d=True)
+    y = _run_gemm(bbs, bbs.FMT_NVFP4, upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs), 256, 256,
+                  False)
+    err = _check(y, O.gemm_f64(ox.dequant_f64(), ow.dequant_f64()), False, "tiny")
+    assert err < 1e-5
+
+
+def test_integer_case_bit_exact(bbs):
+    # all block scales 1.0 (0x38) and s_dec = 1: every partial sum is a
+    # multiple of 1/4 below 2^22, so FP32 accumulation is exact.
+    announce("integer special case, exact")
+    rng = np.random.default_rng(11)
+    M, N, K = 64, 96, 256
+    a = O.NVFP4(rng.integers(0, 256, (M, K // 2), dtype=np.uint8),
+                np.full((M, K // 16), 0x38, np.uint8), np.float32(1), M, K, False)
+    b = O.NVFP4(rng.integers(0, 256, (N, K // 2), dtype=np.uint8),
+                np.full((N // 16, K // 16), 0x38, np.uint8), np.float32(1), N, K, True)
+    y = _run_gemm(bbs, bbs.FMT_NVFP4, upload_nvfp4(a, bbs), upload_nvfp4(b, bbs), M, N, False)
+    assert np.array_equal(y, O.gemm_f64(a.dequant_f64(), b.dequant_f64()))
+
+
+@pytest.mark.parametrize("M,N,K,ta,tb,bf16", [
+    (16, 16, 16, False, False, False),       # one block
+    (144, 80, 80, False, True, False),       # ragged M/N, K not a multiple of the K slab
+    (272, 272, 528, True, True, True),       # tile2d on both sides, BF16 out
+    (272, 400, 1040, False, True, True),
+    (48, 528, 4096, False, False, False),
+])
+def test_random_operands(bbs, M, N, K, ta, tb, bf16):
+    announce(f"random NVFP4 operands M={M} N={N} K={K} tile2d=({ta},{tb}) bf16={bf16}")
+    a = _random_nvfp4(M, K, M + K, ta, 0.25)
+    b = _random_nvfp4(N, K, N + 3 * K, tb, 0.125)
+    y = _run_gemm(bbs, bbs.FMT_NVFP4, upload_nvfp4(a, bbs), upload_nvfp4(b, bbs), M, N, bf16)
+    _check(y, O.gemm_f64(a.dequant_f64(), b.dequant_f64()), bf16, "random")
+
+
+def _sampled_check(y_full, A64, B64, bf16, what, n=4096, seed=0):
+    M, N = y_full.shape
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([rng.integers(0, M, n), np.full(N, M - 1), np.arange(N) * 0])
+    cols = np.concatenate([rng.integers(0, N, n), np.arange(N), np.arange(N)])
+    ref = O.gemm_f64_sampled(A64, B64, rows, cols)
+    return _check(y_full[rows, cols], ref, bf16, what)
+
+
+def test_full_dense_forward(bbs):
+    announce("dense forward 8192x14336x4096, BF16 out (sampled outputs)")
+    d = synth.dense_forward()
+    ox = O.nvfp4_quantize(d["x"])
+    ow = O.nvfp4_quantize(d["w"], tile2d=True)
+    y = _run_gemm(bbs, bbs.FMT_NVFP4, upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs), 8192, 14336,
+                  True)
+    _sampled_check(y, ox.dequant_f64(), ow.dequant_f64(), True, "fprop")
+
+
+def test_full_wgrad(bbs):
+    announce("wgrad 14336x4096x8192 (RHT'd column copies), FP32 out (sampled)")
+    fw, bw = synth.dense_forward(), synth.backward()
+    s, seeds = bw["rht_signs"], bw["seeds"]
+    og = O.nvfp4_quantize(bw["dy"], transpose=True, rht=True, signs=s, mode=O.SR,
+                          seed=seeds["dy_col"])
+    ox = O.nvfp4_quantize(fw["x"], transpose=True, rht=True, signs=s, mode=O.SR,
+                          seed=seeds["x_col"])
+    y = _run_gemm(bbs, bbs.FMT_NVFP4, upload_nvfp4(og, bbs), upload_nvfp4(ox, bbs), 14336, 4096,
+                  False)
+    _sampled_check(y, og.dequant_f64(), ox.dequant_f64(), False, "wgrad")
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (dgrad)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(32, 32, 32), (144, 80, 96), (256, 256, 512), (80, 272, 1056)])
+def test_mxfp8_small(bbs, M, N, K):
+    announce(f"MXFP8 GEMM M={M} N={N} K={K}")
+    a = O.mxfp8_quantize(synth.laplace(M, K, M + K, 1e-3), mode=O.SR, seed=1)
+    w = O.nvfp4_quantize(synth.normal(K, N, N + K, 0.02), tile2d=True)
+    b = O.mxfp8_requantize_t(w, mode=O.SR, seed=2)            # N x K
+    for bf16 in (False, True):
+        y = _run_gemm(bbs, bbs.FMT_MXFP8, upload_mxfp8(a, bbs), upload_mxfp8(b, bbs), M, N, bf16)
+        _check(y, O.gemm_f64(a.dequant_f64(), b.dequant_f64()), bf16, "mxfp8")
+
+
+def test_full_dgrad(bbs):
+    announce("dgrad 8192x4096x14336 MXFP8, BF16 out (sampled)")
+    fw, bw = synth.dense_forward(), synth.backward()
+    seeds = bw["seeds"]
+    og = O.mxfp8_quantize(bw["dy"], mode=O.SR, seed=seeds["dy_mx8"])
+    ow = O.mxfp8_requantize_t(O.nvfp4_quantize(fw["w"], tile2d=True), mode=O.SR,
+                              seed=seeds["w_req"])
+    y = _run_gemm(bbs, bbs.FMT_MXFP8, upload_mxfp8(og, bbs), upload_mxfp8(ow, bbs), 8192, 4096,
+                  True)
+    _sampled_check(y, og.dequant_f64(), ow.dequant_f64(), True, "dgrad")
+
+
+# ---------------------------------------------------------------------------
+# Grouped (MoE)
+# ---------------------------------------------------------------------------
+
+def _grouped_case(bbs, tokens, hidden, ffn, experts, sizes, gather, bf16, seed, row_index=None):
+    rng = np.random.default_rng(seed)
+    offsets = np.zeros(experts + 1, np.int64)
+    offsets[1:] = np.cumsum(sizes)
+    total = int(offsets[-1])
+    if not gather:                       # A holds the routed rows themselves
+        tokens = max(16, (total + 15) // 16 * 16)
+    x = synth.normal_with_outliers(tokens, hidden, seed)
+    ox = O.nvfp4_quantize(x)
+    if gather and row_index is None:
+        row_index = rng.integers(0, tokens, total).astype(np.int32)
+    ws = [O.nvfp4_quantize(w, tile2d=True) for w in synth.moe_weights(experts, ffn, hidden, seed + 1)]
+    codes = np.concatenate([w.codes for w in ws])
+    scales = np.concatenate([w.scales for w in ws])
+    sdec = np.array([w.s_dec for w in ws], np.float32)
+    B = O.NVFP4(codes, scales, np.float32(0), experts * ffn, hidden, True)
+    bd = upload_nvfp4(B, bbs, n_scales=sdec)
+    ad = upload_nvfp4(ox, bbs)
+    c = torch.full((max(total, 1), ffn), -1, dtype=torch.int16 if bf16 else torch.float32,
+                   device=dev())
+    bbs.grouped_nvfp4_gemm(ad, to_dev(row_index) if gather else None, to_dev(offsets), experts,
+                           total, bd, ffn, c, bbs.OUT_BF16 if bf16 else bbs.OUT_F32)
+    torch.cuda.synchronize()
+    y = host(c)
+    y = bf16_bits_to_f64(y.view(np.uint16)) if bf16 else y.astype(np.float64)
+    A64 = ox.dequant_f64()
+    src = row_index if gather else np.arange(total)
+    ref = np.zeros((total, ffn))
+    for g in range(experts):
+        r0, r1 = offsets[g], offsets[g + 1]
+        if r1 > r0:
+            ref[r0:r1] = O.gemm_f64(A64[src[r0:r1]], ws[g].dequant_f64())
+    return y[:total], ref
+
+
+@pytest.mark.parametrize("sizes,gather,bf16", [
+    ([0, 5, 1, 0, 200, 131, 0, 64], True, False),
+    ([128, 0, 0, 1, 257, 3], False, True),
+    ([300], True, True),
+])
+def test_grouped_small(bbs, sizes, gather, bf16):
+    experts = len(sizes)
+    announce(f"grouped sizes={sizes} gather={gather} bf16={bf16}")
+    y, ref = _grouped_case(bbs, 512, 256, 144, experts, np.array(sizes), gather, bf16,
+                           8000 + experts)
+    _check(y, ref, bf16, "grouped")
+
+
+def test_grouped_routed_medium(bbs):
+    announce("grouped, Zipf top-8 routing, 2048 tokens, 64 experts, 512 -> 192")
+    row_index, offsets = synth.moe_routing(2048, 64, 8, 77)
+    sizes = np.diff(offsets)
+    assert (sizes == 0).sum() >= 4
+    y, ref = _grouped_case(bbs, 2048, 512, 192, 64, sizes, True, True, 8100, row_index)
+    _check(y, ref, True, "grouped-routed")
