@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbbs.so")
-SOURCES = ["abi.hip", "quantize.hip", "gemm.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "gemm_nvfp4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -41,6 +41,15 @@ def build() -> str:
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB
+
+
+def build_probe() -> str:
+    """Compile the instruction probes used by tests/test_gpu_isa.py."""
+    src = os.path.join(os.path.dirname(HERE), "tests", "hip", "probe.hip")
+    out = os.path.join(os.path.dirname(src), "libprobe.so")
+    subprocess.check_call([HIPCC, *FLAGS, "-shared", src, "-o", out + ".tmp"])
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

@@ -227,8 +227,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_nvfp4_gemm_kernel(GemmPa
 // ---------------------------------------------------------------------------
 // MXFP8 x MXFP8 with v_mfma_scale_f32_16x16x128_f8f6f4.
 // Tile 128 x 128, K-slab 128 (one MFMA deep); wave tile 64 x 64 = 4 x 4 MFMAs.
-// A lane of a 16x16x128 MFMA holds row lane%16 and the 32 K-values of block
-// lane/16, with that block's E8M0 scale in byte 0 of its scale operand.
+// Operand layout of the 16x16x128 MFMA with 8-bit elements (measured on
+// gfx950): lane l holds row l%16; its bytes 0-15 are K = 16g .. 16g+15 and its
+// bytes 16-31 are K = 64 + 16g .. 64 + 16g + 15, g = l/16.  The E8M0 scale of
+// the 32-block b (K = 32b .. 32b+31) is byte 0 of the scale operand of lane
+// group b.  So lane group g loads slab bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) and supplies the scale of the slab's block g.
 // ---------------------------------------------------------------------------
 constexpr int kMxBK = 128;
 constexpr int kMxStride = kMxBK + 16;
@@ -289,8 +293,9 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp8_gemm_kernel(Mx8GemmParams 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = wm * 64 + i * 16 + (lane & 15);
-            const uint4 *s = reinterpret_cast<const uint4 *>(sm.a + r * kMxStride + kg * 32);
-            const uint4 x0 = s[0], x1 = s[1];
+            const uint8_t *row = sm.a + r * kMxStride;
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(row + 16 * kg);
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * kg);
             af[i] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                           (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
             as_[i] = sm.as[r * 4 + kg];
@@ -298,8 +303,9 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp8_gemm_kernel(Mx8GemmParams 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = wn * 64 + j * 16 + (lane & 15);
-            const uint4 *s = reinterpret_cast<const uint4 *>(sm.b + r * kMxStride + kg * 32);
-            const uint4 x0 = s[0], x1 = s[1];
+            const uint8_t *row = sm.b + r * kMxStride;
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(row + 16 * kg);
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(row + 64 + 16 * kg);
             bfr[j] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                            (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
             bs_[j] = sm.bs[r * 4 + kg];
@@ -337,7 +343,18 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp8_gemm_kernel(Mx8GemmParams 
 // Launchers
 // ---------------------------------------------------------------------------
 
+hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s);
+hipError_t launch_grouped_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s);
+
+// The large-tile kernel needs K % 128 == 0 and 8-byte aligned scale rows.
+static bool big_ok(const GemmParams &p) {
+    auto al = [](const void *q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
+    return p.K % 128 == 0 && al(p.a.codes, 16) && al(p.b.codes, 16) && al(p.a.scales, 8) &&
+           al(p.b.scales, 8);
+}
+
 hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s) {
+    if (big_ok(p)) return launch_nvfp4_gemm_big(p, bf16_out, s);
     const dim3 grid((unsigned)((p.N + kBN - 1) / kBN), (unsigned)((p.M + kBM - 1) / kBM));
     if (bf16_out) hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, p);
     else hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, grid, dim3(kGemmThreads), 0, s, p);
@@ -346,6 +363,7 @@ hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s) 
 
 hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s) {
     if (p.G > kMaxGroups) return hipErrorInvalidValue;
+    if (big_ok(p)) return launch_grouped_nvfp4_gemm_big(p, bf16_out, s);
     const dim3 grid(1024);
     if (bf16_out)
         hipLaunchKernelGGL(grouped_nvfp4_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, p);

@@ -1,0 +1,95 @@
+// Probes of gfx950 instruction behaviour that the library's kernels rely on
+// or may rely on: the per-lane data / scale layout of the block-scaled FP8
+// MFMA, and the rounding and scaling of the FP4 / FP8 conversion
+// instructions.  Every probe only reads and writes the buffers it is given,
+// with grids sized by the host wrapper.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// One wave per (hot lane L, hot byte J): the operand `which` (0 = A, 1 = B)
+// holds E4M3 1.0 (0x38) only at byte J of lane L, the other operand is all
+// 1.0.  The one-hot operand's scale in lane l is 2^(l/16) (byte 127 + l/16);
+// the other operand's scales are 1.0.  out[wave][m][n] = the 16x16 result.
+__global__ void mfma_scale_layout_kernel(int which, const int *one, float *out) {
+    const int lane = threadIdx.x;
+    const int L = blockIdx.x / 32, J = blockIdx.x % 32;
+    uint8_t hot[32], ones[32];
+    for (int j = 0; j < 32; ++j) {
+        hot[j] = (lane == L && j == J) ? 0x38 : 0x00;
+        ones[j] = 0x38;
+    }
+    i32x8 h, o;
+    for (int v = 0; v < 8; ++v) {
+        h[v] = (int)(hot[4 * v] | (hot[4 * v + 1] << 8) | (hot[4 * v + 2] << 16) | ((uint32_t)hot[4 * v + 3] << 24));
+        o[v] = (int)(ones[4 * v] | (ones[4 * v + 1] << 8) | (ones[4 * v + 2] << 16) | ((uint32_t)ones[4 * v + 3] << 24));
+    }
+    const int s_var = 127 * one[0] + (lane >> 4);   // runtime values, not constants
+    const int s_one = 127 * one[0];
+    f32x4 acc = {0, 0, 0, 0};
+    if (which == 0)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(h, o, acc, 0, 0, 0, s_var, 0, s_one);
+    else
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o, h, acc, 0, 0, 0, s_one, 0, s_var);
+    // store raw accumulator registers: out[wave][lane][v]
+    for (int v = 0; v < 4; ++v) out[(blockIdx.x * 64 + lane) * 4 + v] = acc[v];
+}
+
+// cvt_scalef32_pk_bf16_fp4: for every scale s and source byte b, the two
+// BF16 results for byte select 0..3 of a word holding b in every byte.
+__global__ void cvt_bf16_fp4_kernel(const float *scales, int ns, uint32_t *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ns * 256) return;
+    const int si = i / 256, b = i % 256;
+    const uint32_t src = (uint32_t)b * 0x01010101u;
+    const float s = scales[si];
+    bf16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, s, 0);
+    bf16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, s, 1);
+    bf16x2 r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, s, 2);
+    bf16x2 r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, s, 3);
+    out[i * 4 + 0] = __builtin_bit_cast(uint32_t, r0);
+    out[i * 4 + 1] = __builtin_bit_cast(uint32_t, r1);
+    out[i * 4 + 2] = __builtin_bit_cast(uint32_t, r2);
+    out[i * 4 + 3] = __builtin_bit_cast(uint32_t, r3);
+}
+
+// cvt_scalef32_pk_fp4_f32 with scale 1.0: the packed byte for (x[i], -x[i]).
+__global__ void cvt_fp4_f32_kernel(const float *x, int n, const float *scale, uint8_t *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[i], -x[i], scale[0], 0);
+    out[i] = (uint8_t)(r & 0xFF);
+}
+
+// cvt_scalef32_pk_fp8_f32 (E4M3) with scale 1.0: bytes for (x[i], -x[i]).
+__global__ void cvt_fp8_f32_kernel(const float *x, int n, const float *scale, uint16_t *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    i16x2 old = {0, 0};
+    i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, x[i], -x[i], scale[0], false);
+    out[i] = (uint16_t)r[0];
+}
+
+extern "C" {
+int probe_mfma_scale_layout(int which, const int *one, float *out) {
+    hipLaunchKernelGGL(mfma_scale_layout_kernel, dim3(64 * 32), dim3(64), 0, 0, which, one, out);
+    return (int)hipDeviceSynchronize();
+}
+int probe_cvt_bf16_fp4(const float *scales, int ns, uint32_t *out) {
+    const int n = ns * 256;
+    hipLaunchKernelGGL(cvt_bf16_fp4_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, scales, ns, out);
+    return (int)hipDeviceSynchronize();
+}
+int probe_cvt_fp4_f32(const float *x, int n, const float *scale, uint8_t *out) {
+    hipLaunchKernelGGL(cvt_fp4_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, x, n, scale, out);
+    return (int)hipDeviceSynchronize();
+}
+int probe_cvt_fp8_f32(const float *x, int n, const float *scale, uint16_t *out) {
+    hipLaunchKernelGGL(cvt_fp8_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, x, n, scale, out);
+    return (int)hipDeviceSynchronize();
+}
+}

@@ -80,6 +80,9 @@ def test_integer_case_bit_exact(bbs):
     (272, 272, 528, True, True, True),       # tile2d on both sides, BF16 out
     (272, 400, 1040, False, True, True),
     (48, 528, 4096, False, False, False),
+    (272, 400, 1024, True, True, True),      # large-tile path, ragged M and N
+    (528, 272, 512, False, False, False),
+    (16, 4112, 128, False, True, True),
 ])
 def test_random_operands(bbs, M, N, K, ta, tb, bf16):
     announce(f"random NVFP4 operands M={M} N={N} K={K} tile2d=({ta},{tb}) bf16={bf16}")

@@ -1,0 +1,85 @@
+"""Checks of the gfx950 instruction behaviour the kernels are built on:
+the operand / scale layout of v_mfma_scale_f32_16x16x128_f8f6f4 with 8-bit
+operands, and the exactness of v_cvt_scalef32_pk_f16_fp4 at scale 1.0 (the
+NVFP4 GEMM's expansion).  Also records that v_cvt_scalef32_pk_fp4_f32 rounds
+like the oracle's round-to-nearest-even (not used by the kernels yet)."""
+import ctypes as C
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_util import announce, dev
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hip", "libprobe.so")
+
+
+@pytest.fixture(scope="module")
+def probe():
+    if not os.path.exists(LIB):
+        pytest.fail("tests/hip/libprobe.so is not built (run __graft_entry__.build())")
+    return C.CDLL(LIB)
+
+
+def test_scaled_fp8_mfma_layout(probe):
+    announce("v_mfma_scale_f32_16x16x128_f8f6f4 lane layout")
+    one = torch.ones(1, dtype=torch.int32, device=dev())
+    for which in (0, 1):
+        out = torch.zeros(2048 * 64 * 4, dtype=torch.float32, device=dev())
+        assert probe.probe_mfma_scale_layout(which, C.c_void_p(one.data_ptr()),
+                                             C.c_void_p(out.data_ptr())) == 0
+        acc = out.cpu().numpy().reshape(64, 32, 64, 4)     # [hot lane][hot byte][lane][v]
+        for L in range(64):
+            for J in range(32):
+                D = np.zeros((16, 16))
+                a = acc[L, J]
+                for lane in range(64):
+                    D[4 * (lane // 16):4 * (lane // 16) + 4, lane % 16] = a[lane]
+                # hot element: row / column L % 16, K index 16*(L//16) + J (+48 for J >= 16)
+                g = L // 16
+                k = 16 * g + J if J < 16 else 64 + 16 * g + (J - 16)
+                block = k // 32
+                want = np.zeros((16, 16))
+                if which == 0:
+                    want[L % 16, :] = 2.0 ** block
+                else:
+                    want[:, L % 16] = 2.0 ** block
+                assert np.array_equal(D, want), (which, L, J)
+
+
+def test_fp4_to_f16_conversion_exact(probe):
+    announce("v_cvt_scalef32_pk_bf16_fp4 scale handling")
+    scales = np.array([1.0, 2.0, 0.25], np.float32)
+    sd = torch.from_numpy(scales).to(dev())
+    out = torch.zeros(len(scales) * 256 * 4, dtype=torch.int32, device=dev())
+    assert probe.probe_cvt_bf16_fp4(C.c_void_p(sd.data_ptr()), len(scales),
+                                    C.c_void_p(out.data_ptr())) == 0
+    r = out.cpu().numpy().view(np.uint32).reshape(len(scales), 256, 4)
+    dec = np.array([O.e2m1_value(c) for c in range(16)])
+    for si, s in enumerate(scales):
+        for b in range(256):
+            w = r[si, b, 0]
+            lo = np.array([w << 16], np.uint32).view(np.float32)[0]
+            hi = np.array([w & 0xFFFF0000], np.uint32).view(np.float32)[0]
+            assert (lo, hi) == (dec[b & 15] * s, dec[b >> 4] * s)
+
+
+def test_fp4_rtn_conversion_matches_oracle(probe):
+    announce("v_cvt_scalef32_pk_fp4_f32 rounding")
+    grid = np.array([O.e2m1_value(c) for c in range(8)], np.float32)
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([np.linspace(0, 8, 200001, dtype=np.float32), mids,
+                        np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(9)),
+                        np.float32([1e-40, 0.0, 100.0])]).astype(np.float32)
+    xd = torch.from_numpy(x).to(dev())
+    s1 = torch.ones(1, dtype=torch.float32, device=dev())
+    o = torch.zeros(len(x), dtype=torch.uint8, device=dev())
+    assert probe.probe_cvt_fp4_f32(C.c_void_p(xd.data_ptr()), len(x), C.c_void_p(s1.data_ptr()),
+                                   C.c_void_p(o.data_ptr())) == 0
+    o = o.cpu().numpy()
+    assert np.array_equal(o & 0xF, O.e2m1_code(O.round_to(x, O.E2M1)))
+    assert np.array_equal(o >> 4, O.e2m1_code(O.round_to(-x, O.E2M1)))
