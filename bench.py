@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="time one op of the step in isolation (quant_x, quant_w, fprop, "
+                         "quant_dy, requant_w, dgrad, wgrad); used for counter runs")
     return ap.parse_args()
 
 
@@ -157,6 +160,22 @@ def main():
     def step():
         for f in ops.values():
             f()
+
+    if args.only:
+        # inputs of the op come from one untimed step
+        step()
+        torch.cuda.synchronize()
+        f = ops[args.only]
+        for _ in range(args.warmup):
+            f()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "ms": s0.elapsed_time(s1) / args.steps}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()

@@ -6,22 +6,25 @@
 //
 // Tiling: a workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of C; each wave
 // owns 128 x 128 = 4 x 4 v_mfma_f32_32x32x16_f16 accumulators (256 FP32 per
-// lane).  K advances in slabs of 128 (8 NVFP4 blocks), double-buffered in LDS:
-// while a slab is consumed, the next one is fetched from global memory into
-// registers and stored to the other buffer.  LDS holds the packed 4-bit codes
-// as they are in HBM (64 bytes per row and slab) and the block scales already
-// converted to FP16 pairs.
+// lane).  K advances in slabs of 128 (8 NVFP4 blocks).  Each slab is copied
+// global -> LDS with global_load_lds (asynchronous, no staging registers) into
+// one of three LDS stages (two slabs in flight ahead of the one consumed): the packed 4-bit codes exactly as stored in HBM (64
+// bytes per row) and the raw E4M3 scale bytes (8 per row).
 //
 // Exact expansion: v_cvt_scalef32_pk_f16_fp4 (scale 1.0) turns two E2M1 codes
-// into two FP16 values and one v_pk_mul_f16 applies the FP16 copy of the E4M3
-// block scale.  code x scale has at most 6 significant bits and lies in
-// [2^-10, 2688], so both steps are exact in FP16; the MFMA products are exact
-// in FP32 and only the accumulation rounds.
+// into two FP16 values and one v_pk_mul_f16 applies the block scale, decoded
+// to FP16 by v_cvt_scalef32_pk_f16_fp8 (two blocks per instruction).  code x scale
+// has at most 6 significant bits and lies in [2^-10, 2688], so both steps are
+// exact in FP16; the MFMA products are exact in FP32 and only the
+// accumulation rounds.  The expansion of MFMA step s + 1 is interleaved with
+// the MFMAs of step s.
 //
 // K order inside a slab: lane half h of an MFMA step takes 8 codes from the
-// 16-byte group [16h, 16h+16) of the current 32-byte chunk (4 steps per
-// chunk), so one ds_read_b128 feeds four MFMA steps.  A and B use the same
-// order, so the sum is unchanged; each lane's 8 codes always lie in one block.
+// 16-byte group 2c + h of the row (c = 32-byte chunk, 4 steps per chunk), so
+// one ds_read_b128 feeds four MFMA steps.  A and B use the same order, so the
+// sum is unchanged; each lane's 8 codes always lie in one block.  In LDS the
+// 16-byte group p of row r sits at position p ^ ((r >> 2) & 3), which puts the
+// 16 rows of one fragment read on 16 distinct bank groups.
 //
 // Tile order is XCD-aware: workgroup i runs on XCD i % 8, so each XCD is given
 // a contiguous range of tile ids, and ids walk 8 M-tiles down before moving
@@ -34,42 +37,32 @@ namespace bbs {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
 
 namespace big {
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int NT = 256;
-constexpr int CS = 80;            // LDS row stride of the codes: 64 bytes + 16 pad
-constexpr int SB = BK / 16;       // scale blocks per row and slab (8)
+constexpr int RB = BK / 2;        // code bytes per row and slab (64)
+constexpr int SB = BK / 16;       // scale bytes per row and slab (8)
 constexpr int GROUP_M = 8;
 
 struct Stage {
-    uint8_t a[BM * CS];
-    uint8_t b[BN * CS];
-    uint32_t as[BM * SB];         // FP16 pair (scale, scale) per row and block
-    uint32_t bs[BN * SB];
+    uint8_t a[BM * RB];
+    uint8_t b[BN * RB];
+    uint8_t as[BM * SB];
+    uint8_t bs[BN * SB];
 };
 struct Smem {
-    Stage st[2];
+    Stage st[3];
 };
 
-// E4M3 byte (positive) -> FP16 bits of the same value.  Normal codes map by
-// a shift and an exponent rebias; the subnormal codes m * 2^-9 (m = 1..7) go
-// through an integer-to-FP16 conversion and a 9-binade shift.
-__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
-    const uint32_t normal = (b << 7) + 0x2000u;
-    const uint32_t sub = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(float)b) - 0x2400u;
-    return b >= 8u ? normal : (b ? sub : 0u);
-}
+__device__ __forceinline__ int swz(int row, int pos) { return pos ^ ((row >> 2) & 3); }
 
-__device__ __forceinline__ uint32_t f16_pair(uint32_t b) {
-    const uint32_t h = e4m3_to_f16_bits(b);
-    return h | (h << 16);
-}
-
-// Eight E2M1 codes of one 32-bit word times an FP16 scale pair -> 8 FP16.
-__device__ __forceinline__ f16x8 expand8_f16(uint32_t w, uint32_t scale_pair) {
-    const f16x2 s = __builtin_bit_cast(f16x2, scale_pair);
+// Eight E2M1 codes of one 32-bit word times one FP16 scale -> 8 FP16.
+__device__ __forceinline__ f16x8 expand8_f16(uint32_t w, _Float16 scale) {
+    const f16x2 s = {scale, scale};
     const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
     const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
     const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
@@ -77,18 +70,12 @@ __device__ __forceinline__ f16x8 expand8_f16(uint32_t w, uint32_t scale_pair) {
     return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
-// Per-thread staging registers of one slab.
-struct Regs {
-    uint4 a[4], b[4];
-    uint2 sa, sb;
-};
-
-// Source offsets this thread stages each slab (fixed for the whole tile).
+// Per-lane global sources of the copies of one slab (K offset added later).
+// Rows past the operand's end are clamped to a valid row: they only feed
+// outputs that are never written.
 struct Plan {
-    const uint8_t *a_row[4];      // code row of A for chunk q (nullptr = zero row)
-    const uint8_t *b_row[4];
-    const uint8_t *sa_row;        // scale row (nullptr = none)
-    const uint8_t *sb_row;
+    const uint8_t *a[4], *b[4];   // code copies: 16 rows x 64 bytes per instruction
+    const uint8_t *sa[2], *sb[2]; // scale copies: 32 rows x 8 bytes per instruction
 };
 
 template <typename RowMap>
@@ -96,119 +83,165 @@ __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, in
                                           int64_t m0, int64_t m_end, int64_t n0, int64_t n_end,
                                           RowMap a_row) {
     Plan pl;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int64_t kb = K / 2, ks = K / 16;
+    auto arow = [&](int r) -> int64_t {
+        const int64_t m = min(m0 + r, m_end - 1);
+        const int64_t s = a_row(m);
+        return s < 0 ? 0 : s;
+    };
+    auto brow = [&](int r) -> int64_t { return min(n0 + r, n_end - 1); };
+    const int pos = swz(lane >> 2, lane & 3);     // (row >> 2) & 3 == (lane >> 4) & 3 here
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int row = (q * NT + t) >> 2;
-        const int64_t m = m0 + row;
-        const int64_t src = (m < m_end) ? a_row(m) : -1;
-        pl.a_row[q] = src >= 0 ? A.codes + src * kb + (t & 3) * 16 : nullptr;
-        const int64_t n = n0 + row;
-        pl.b_row[q] = n < n_end ? B.codes + n * kb + (t & 3) * 16 : nullptr;
+        const int r = (w * 4 + q) * 16 + (lane >> 2);
+        pl.a[q] = A.codes + arow(r) * kb + 16 * pos;
+        pl.b[q] = B.codes + brow(r) * kb + 16 * pos;
     }
-    {
-        const int64_t m = m0 + t;
-        const int64_t src = (m < m_end) ? a_row(m) : -1;
-        pl.sa_row = src >= 0 ? A.scales + (A.tile2d ? src / 16 : src) * ks : nullptr;
-        // B: 1x16 -> one scale row per tile row; 16x16 -> 16 tile rows per tile
-        const int brows = B.tile2d ? BN / 16 : BN;
-        const int64_t n = B.tile2d ? n0 / 16 + t : n0 + t;
-        const int64_t lim = B.tile2d ? (n_end + 15) / 16 : n_end;
-        pl.sb_row = (t < brows && n < lim) ? B.scales + n * ks : nullptr;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = (w * 2 + q) * 32 + (lane >> 1);
+        const int64_t sa_row = A.tile2d ? arow(r) / 16 : arow(r);
+        pl.sa[q] = A.scales + sa_row * ks + 4 * (lane & 1);
+        if (B.tile2d) {
+            // 16 tile rows: lanes 0..31 (the upper lanes repeat them)
+            const int tr = (lane >> 1) & 15;
+            const int64_t n = min(n0 / 16 + tr, (n_end - 1) / 16);
+            pl.sb[q] = B.scales + n * ks + 4 * (lane & 1);
+        } else {
+            pl.sb[q] = B.scales + brow(r) * ks + 4 * (lane & 1);
+        }
     }
     return pl;
 }
 
-__device__ __forceinline__ void fetch(Regs &r, const Plan &pl, int64_t k0) {
-    const int64_t cb = k0 / 2, sbk = k0 / 16;
+template <bool BT>
+__device__ __forceinline__ void issue(Stage &st, const Plan &pl, int64_t k0) {
+    const int w = threadIdx.x >> 6;
+    const int64_t cb = k0 / 2, sk = k0 / 16;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        r.a[q] = pl.a_row[q] ? *reinterpret_cast<const uint4 *>(pl.a_row[q] + cb) : make_uint4(0, 0, 0, 0);
-        r.b[q] = pl.b_row[q] ? *reinterpret_cast<const uint4 *>(pl.b_row[q] + cb) : make_uint4(0, 0, 0, 0);
+        const int seg = (w * 4 + q) * 1024;
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.a[q] + cb), (lds_void_t *)(st.a + seg), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.b[q] + cb), (lds_void_t *)(st.b + seg), 16, 0, 0);
     }
-    r.sa = pl.sa_row ? *reinterpret_cast<const uint2 *>(pl.sa_row + sbk) : make_uint2(0, 0);
-    r.sb = pl.sb_row ? *reinterpret_cast<const uint2 *>(pl.sb_row + sbk) : make_uint2(0, 0);
-}
-
-__device__ __forceinline__ void store(Stage &st, const Regs &r, bool b_tile2d) {
-    const int t = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = q * NT + t, row = c >> 2, seg = c & 3;
-        *reinterpret_cast<uint4 *>(st.a + row * CS + seg * 16) = r.a[q];
-        *reinterpret_cast<uint4 *>(st.b + row * CS + seg * 16) = r.b[q];
+    for (int q = 0; q < 2; ++q) {
+        const int seg = (w * 2 + q) * 256;
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sa[q] + sk), (lds_void_t *)(st.as + seg), 4, 0, 0);
     }
-    uint32_t s[8];
+    if (!BT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        s[j] = f16_pair((r.sa.x >> (8 * j)) & 0xFFu);
-        s[4 + j] = f16_pair((r.sa.y >> (8 * j)) & 0xFFu);
-    }
-    *reinterpret_cast<uint4 *>(st.as + t * SB) = make_uint4(s[0], s[1], s[2], s[3]);
-    *reinterpret_cast<uint4 *>(st.as + t * SB + 4) = make_uint4(s[4], s[5], s[6], s[7]);
-    if (!b_tile2d || t < BN / 16) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            s[j] = f16_pair((r.sb.x >> (8 * j)) & 0xFFu);
-            s[4 + j] = f16_pair((r.sb.y >> (8 * j)) & 0xFFu);
+        for (int q = 0; q < 2; ++q) {
+            const int seg = (w * 2 + q) * 256;
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sb[q] + sk), (lds_void_t *)(st.bs + seg), 4, 0, 0);
         }
-        *reinterpret_cast<uint4 *>(st.bs + t * SB) = make_uint4(s[0], s[1], s[2], s[3]);
-        *reinterpret_cast<uint4 *>(st.bs + t * SB + 4) = make_uint4(s[4], s[5], s[6], s[7]);
+    } else {
+        // the 16 tile rows (128 bytes); every wave writes the same bytes
+        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sb[0] + sk), (lds_void_t *)(st.bs), 4, 0, 0);
     }
 }
 
-// One slab: 2 chunks x 4 MFMA steps x (4 x 4) MFMAs per wave.
-__device__ __forceinline__ void compute(const Stage &st, f32x16 (&acc)[4][4], bool b_tile2d,
-                                        int wm, int wn, int lane) {
+// Code words of one 32-byte chunk of a slab for the wave's 4 + 4 fragment
+// rows (16 bytes per lane each: four MFMA steps).
+struct Chunk {
+    uint4 ca[4], cb[4];
+};
+
+// FP16 block scales of one chunk: the two blocks of each fragment row that
+// the lane's 16 code bytes span (steps 0-1 use the first, steps 2-3 the
+// second).  v_cvt_scalef32_pk_f16_fp8 (scale 1.0) decodes two E4M3 bytes at
+// once, exactly (every E4M3 value is a normal FP16 number).
+struct Pairs {
+    f16x2 pa[4], pb[4];
+};
+
+__device__ __forceinline__ void load_chunk(Chunk &c, const Stage &st, int chunk, int wm, int wn,
+                                           int lane) {
     const int h = lane >> 5, rl = lane & 31;
 #pragma unroll
-    for (int chunk = 0; chunk < 2; ++chunk) {
-        uint4 ca[4], cb[4];
-        uint2 sa[4], sb[4];
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + rl;
+        c.ca[i] = *reinterpret_cast<const uint4 *>(st.a + r * RB + 16 * swz(r, 2 * chunk + h));
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 128 + i * 32 + rl;
-            ca[i] = *reinterpret_cast<const uint4 *>(st.a + r * CS + chunk * 32 + h * 16);
-            sa[i] = *reinterpret_cast<const uint2 *>(st.as + r * SB + chunk * 4 + 2 * h);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wn * 128 + j * 32 + rl;
-            const int sr = b_tile2d ? (r >> 4) : r;
-            cb[j] = *reinterpret_cast<const uint4 *>(st.b + r * CS + chunk * 32 + h * 16);
-            sb[j] = *reinterpret_cast<const uint2 *>(st.bs + sr * SB + chunk * 4 + 2 * h);
-        }
-#pragma unroll
-        for (int step = 0; step < 4; ++step) {
-            f16x8 af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t w = step == 0 ? ca[i].x : step == 1 ? ca[i].y : step == 2 ? ca[i].z : ca[i].w;
-                af[i] = expand8_f16(w, (step >> 1) ? sa[i].y : sa[i].x);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t w = step == 0 ? cb[j].x : step == 1 ? cb[j].y : step == 2 ? cb[j].z : cb[j].w;
-                bf[j] = expand8_f16(w, (step >> 1) ? sb[j].y : sb[j].x);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + j * 32 + rl;
+        c.cb[j] = *reinterpret_cast<const uint4 *>(st.b + r * RB + 16 * swz(r, 2 * chunk + h));
     }
 }
 
-template <bool BF16_OUT, typename RowMap>
+template <bool BT>
+__device__ __forceinline__ void load_scales(uint2 (&sca)[4], uint2 (&scb)[4], const Stage &st,
+                                            int wm, int wn, int lane) {
+    const int rl = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sca[i] = *reinterpret_cast<const uint2 *>(st.as + (wm * 128 + i * 32 + rl) * SB);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + j * 32 + rl;
+        scb[j] = *reinterpret_cast<const uint2 *>(st.bs + (BT ? (r >> 4) : r) * SB);
+    }
+}
+
+__device__ __forceinline__ void load_pairs(Pairs &p, const uint2 (&sca)[4], const uint2 (&scb)[4],
+                                           int chunk, int lane) {
+    const int sh = 16 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        p.pa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((chunk ? sca[i].y : sca[i].x) >> sh, 1.0f, false);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        p.pb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((chunk ? scb[j].y : scb[j].x) >> sh, 1.0f, false);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4 &v, int s) {
+    return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
+// Expanded operands of MFMA step s (0..3) of a chunk.
+__device__ __forceinline__ void expand_step(f16x8 (&af)[4], f16x8 (&bf)[4], const Chunk &c,
+                                            const Pairs &p, int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = expand8_f16(word(c.ca[i], s), p.pa[i][s >> 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = expand8_f16(word(c.cb[j], s), p.pb[j][s >> 1]);
+}
+
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const f16x8 (&af)[4],
+                                          const f16x8 (&bf)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// Interleave: one MFMA, then four VALU, sixteen times.
+__device__ __forceinline__ void interleave_1_4() {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+}
+
+// s_waitcnt vmcnt(n), other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | (((N >> 4) & 3) << 14));
+}
+
+template <bool BF16_OUT, bool BT, typename RowMap>
 __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &B, int64_t K,
                                      int64_t m0, int64_t m_end, int64_t n0, int64_t n_end,
                                      RowMap a_row, float out_scale, void *C, int64_t ldc) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const bool bt = B.tile2d != 0;
     const Plan pl = make_plan(A, B, K, m0, m_end, n0, n_end, a_row);
+    // global_load_lds instructions one wave issues per slab
+    constexpr int kIssued = 4 + 4 + 2 + (BT ? 1 : 2);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -216,40 +249,89 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
 
-    Regs r;
-    fetch(r, pl, 0);
-    store(sm.st[0], r, bt);
-    __syncthreads();
     const int64_t nslab = K / BK;
-    for (int64_t s = 0; s < nslab; ++s) {
-        const bool more = s + 1 < nslab;
-        if (more) fetch(r, pl, (s + 1) * BK);
-        compute(sm.st[s & 1], acc, bt, wm, wn, lane);
-        if (more) store(sm.st[(s + 1) & 1], r, bt);
-        __syncthreads();
+    // Three LDS stages: slab s lives in stage s % 3.  Slabs 0 and 1 are in
+    // flight before the loop; slab s + 2 is issued at the top of iteration s.
+    issue<BT>(sm.st[0], pl, 0);
+    if (nslab > 1) {
+        issue<BT>(sm.st[1], pl, BK);
+        wait_vmcnt<kIssued>();
+    } else {
+        wait_vmcnt<0>();
     }
+    __syncthreads();
+
+    uint2 sca[4], scb[4];
+    Chunk c0, c1;
+    Pairs p0, p1;
+    f16x8 af[4], bf[4], an[4], bn[4];
+    int cs = 0;                                   // stage holding slab s
+    load_scales<BT>(sca, scb, sm.st[0], wm, wn, lane);
+    load_chunk(c0, sm.st[0], 0, wm, wn, lane);
+    load_pairs(p0, sca, scb, 0, lane);
+    expand_step(af, bf, c0, p0, 0);
+
+    // The 8 MFMA steps of one slab except the last; the expansion of step
+    // k + 1 runs under the MFMAs of step k.
+    auto slab_body = [&](const Stage &st) {
+        load_chunk(c1, st, 1, wm, wn, lane);
+        load_pairs(p1, sca, scb, 1, lane);
+        expand_step(an, bn, c0, p0, 1); mfma_step(acc, af, bf); interleave_1_4();
+        expand_step(af, bf, c0, p0, 2); mfma_step(acc, an, bn); interleave_1_4();
+        expand_step(an, bn, c0, p0, 3); mfma_step(acc, af, bf); interleave_1_4();
+        expand_step(af, bf, c1, p1, 0); mfma_step(acc, an, bn); interleave_1_4();
+        expand_step(an, bn, c1, p1, 1); mfma_step(acc, af, bf); interleave_1_4();
+        expand_step(af, bf, c1, p1, 2); mfma_step(acc, an, bn); interleave_1_4();
+        expand_step(an, bn, c1, p1, 3); mfma_step(acc, af, bf); interleave_1_4();
+    };
+
+    for (int64_t s = 0; s + 1 < nslab; ++s) {
+        const int ns = cs == 2 ? 0 : cs + 1;      // stage of slab s + 1
+        const int n2 = ns == 2 ? 0 : ns + 1;      // stage of slab s + 2
+        if (s + 2 < nslab) issue<BT>(sm.st[n2], pl, (s + 2) * BK);
+        slab_body(sm.st[cs]);
+        // every read of stage cs is done: wait for slab s + 1 (slab s + 2 may
+        // stay in flight), then start slab s + 1 under the last 16 MFMAs
+        if (s + 2 < nslab) wait_vmcnt<kIssued>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        load_scales<BT>(sca, scb, sm.st[ns], wm, wn, lane);
+        load_chunk(c0, sm.st[ns], 0, wm, wn, lane);
+        load_pairs(p0, sca, scb, 0, lane);
+        expand_step(af, bf, c0, p0, 0);
+        mfma_step(acc, an, bn);
+        interleave_1_4();
+        cs = ns;
+    }
+    slab_body(sm.st[cs]);
+    mfma_step(acc, an, bn);
 
     // Epilogue.  32x32 accumulator layout: lane holds column lane % 32 and rows
-    // 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+    // 8 * (v / 4) + 4 * (lane / 32) + v % 4.  One row address per (i, v); the
+    // four column blocks j are immediate offsets from it.
+    const int64_t nb = n0 + wn * 128 + (lane & 31);
+    const bool full_n = n0 + BN <= n_end;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
-            if (n >= n_end) continue;
+        for (int v = 0; v < 16; ++v) {
+            const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (m >= m_end) continue;
+            if (BF16_OUT) {
+                uint16_t *row = reinterpret_cast<uint16_t *>(C) + m * ldc + nb;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (m < m_end) {
-                    const float y = acc[i][j][v] * out_scale;
-                    if (BF16_OUT)
-                        reinterpret_cast<uint16_t *>(C)[m * ldc + n] = (uint16_t)f32_to_bf16(y);
-                    else
-                        reinterpret_cast<float *>(C)[m * ldc + n] = y;
-                }
+                for (int j = 0; j < 4; ++j)
+                    if (full_n || nb + 32 * j < n_end)
+                        row[32 * j] = (uint16_t)f32_to_bf16(acc[i][j][v] * out_scale);
+            } else {
+                float *row = reinterpret_cast<float *>(C) + m * ldc + nb;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (full_n || nb + 32 * j < n_end) row[32 * j] = acc[i][j][v] * out_scale;
             }
         }
 }
+
 
 }  // namespace big
 
@@ -269,8 +351,13 @@ __global__ __launch_bounds__(big::NT) void nvfp4_gemm_big_kernel(GemmParams p) {
     const int64_t gm = (tm - g * big::GROUP_M) < big::GROUP_M ? (tm - g * big::GROUP_M) : big::GROUP_M;
     const int64_t mt = g * big::GROUP_M + in % gm, nt = in / gm;
     const float out_scale = p.a.s_dec[0] * p.b.s_dec[0];
-    big::tile<BF16_OUT>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
-                        [](int64_t r) { return r; }, out_scale, p.c, p.ldc);
+    auto ident = [](int64_t r) { return r; };
+    if (p.b.tile2d)
+        big::tile<BF16_OUT, true>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N, ident,
+                                  out_scale, p.c, p.ldc);
+    else
+        big::tile<BF16_OUT, false>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N, ident,
+                                   out_scale, p.c, p.ldc);
 }
 
 constexpr int kMaxGroupsBig = 1024;
@@ -309,13 +396,14 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_big_kernel(GemmPar
         const float out_scale = p.a.s_dec[0] * p.b.s_dec[g];
         const int32_t *ri = p.row_index;
         const int64_t src_rows = p.a_src_rows;
-        big::tile<BF16_OUT>(
-            sm, p.a, B, p.K, m0, re, n0, p.N,
-            [ri, src_rows](int64_t r) -> int64_t {
-                const int64_t s = ri ? (int64_t)ri[r] : r;
-                return (s >= 0 && s < src_rows) ? s : -1;
-            },
-            out_scale, p.c, p.ldc);
+        auto gather = [ri, src_rows](int64_t r) -> int64_t {
+            const int64_t s = ri ? (int64_t)ri[r] : r;
+            return (s >= 0 && s < src_rows) ? s : -1;
+        };
+        if (B.tile2d)
+            big::tile<BF16_OUT, true>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, out_scale, p.c, p.ldc);
+        else
+            big::tile<BF16_OUT, false>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, out_scale, p.c, p.ldc);
         __syncthreads();
     }
 }
