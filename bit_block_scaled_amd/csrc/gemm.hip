@@ -346,15 +346,17 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp8_gemm_kernel(Mx8GemmParams 
 hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s);
 
-// The large-tile kernel needs K % 128 == 0 and 8-byte aligned scale rows.
-static bool big_ok(const GemmParams &p) {
+// The large-tile kernel needs K % 128 == 0, 8-byte aligned scale rows and
+// 16-byte aligned output rows (its epilogue stores 16-byte row segments).
+static bool big_ok(const GemmParams &p, bool bf16_out) {
     auto al = [](const void *q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
+    const int64_t es = bf16_out ? 2 : 4;
     return p.K % 128 == 0 && al(p.a.codes, 16) && al(p.b.codes, 16) && al(p.a.scales, 8) &&
-           al(p.b.scales, 8);
+           al(p.b.scales, 8) && al(p.c, 16) && (p.ldc * es) % 16 == 0;
 }
 
 hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s) {
-    if (big_ok(p)) return launch_nvfp4_gemm_big(p, bf16_out, s);
+    if (big_ok(p, bf16_out)) return launch_nvfp4_gemm_big(p, bf16_out, s);
     const dim3 grid((unsigned)((p.N + kBN - 1) / kBN), (unsigned)((p.M + kBM - 1) / kBM));
     if (bf16_out) hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, p);
     else hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, grid, dim3(kGemmThreads), 0, s, p);
@@ -363,7 +365,7 @@ hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s) 
 
 hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s) {
     if (p.G > kMaxGroups) return hipErrorInvalidValue;
-    if (big_ok(p)) return launch_grouped_nvfp4_gemm_big(p, bf16_out, s);
+    if (big_ok(p, bf16_out)) return launch_grouped_nvfp4_gemm_big(p, bf16_out, s);
     const dim3 grid(1024);
     if (bf16_out)
         hipLaunchKernelGGL(grouped_nvfp4_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, p);

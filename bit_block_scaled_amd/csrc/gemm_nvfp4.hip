@@ -227,10 +227,73 @@ __device__ __forceinline__ void interleave_1_4() {
     }
 }
 
+// After a slab barrier the next slab's operands are still in flight from
+// LDS: issue 8 MFMAs first, then interleave the rest 1:8 with the expansion.
+__device__ __forceinline__ void interleave_8_then_1_8() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+}
+
 // s_waitcnt vmcnt(n), other counters unconstrained.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | (((N >> 4) & 3) << 14));
+}
+
+// Epilogue.  The 32x32 accumulator layout gives lane l column l % 32 and rows
+// 8 * (v / 4) + 4 * (l / 32) + v % 4 of each 32 x 32 block.  Each wave writes
+// its scaled, converted 128 x 128 tile through LDS in pieces (64 rows of BF16
+// or 32 rows of FP32, 16 KB each) and stores it back to C as whole 16-byte
+// row segments per lane.  Row m < m_end and column n < n_end are written;
+// N being a multiple of 16 keeps every 16-byte segment wholly in or out.
+template <bool BF16_OUT>
+__device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], int64_t m0,
+                                         int64_t m_end, int64_t n0, int64_t n_end,
+                                         float out_scale, void *C, int64_t ldc, int wm, int wn,
+                                         int lane) {
+    constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
+    constexpr int RS = 128 * ES + 16;                 // LDS row stride (padded)
+    constexpr int ROWS = BF16_OUT ? 64 : 32;          // rows per piece
+    constexpr int I_PER = ROWS / 32;                  // accumulator row blocks per piece
+    __syncthreads();                                  // the slab ring is free now
+    uint8_t *buf = reinterpret_cast<uint8_t *>(&sm) + (threadIdx.x >> 6) * (ROWS * RS);
+    const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
+#pragma unroll
+    for (int piece = 0; piece < 4 / I_PER; ++piece) {
+#pragma unroll
+        for (int ii = 0; ii < I_PER; ++ii) {
+            const int i = piece * I_PER + ii;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = ii * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    const int c = j * 32 + (lane & 31);
+                    const float y = acc[i][j][v] * out_scale;
+                    if (BF16_OUT)
+                        *reinterpret_cast<uint16_t *>(buf + r * RS + c * 2) = (uint16_t)f32_to_bf16(y);
+                    else
+                        *reinterpret_cast<float *>(buf + r * RS + c * 4) = y;
+                }
+        }
+        // read back whole rows: 16 bytes per lane, 1 KB per instruction
+        constexpr int LPR = 128 * ES / 16;            // lanes per row
+        constexpr int RPI = 64 / LPR;                 // rows per instruction
+#pragma unroll
+        for (int q = 0; q < ROWS / RPI; ++q) {
+            const int r = q * RPI + lane / LPR;
+            const int cb = (lane % LPR) * 16;         // byte offset in the row
+            const uint4 val = *reinterpret_cast<const uint4 *>(buf + r * RS + cb);
+            const int64_t m = mw + piece * ROWS + r;
+            const int64_t n = nw + cb / ES;
+            if (m < m_end && n < n_end)
+                *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
+        }
+    }
 }
 
 template <bool BF16_OUT, bool BT, typename RowMap>
@@ -300,38 +363,14 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
         load_pairs(p0, sca, scb, 0, lane);
         expand_step(af, bf, c0, p0, 0);
         mfma_step(acc, an, bn);
-        interleave_1_4();
+        interleave_8_then_1_8();
         cs = ns;
     }
     slab_body(sm.st[cs]);
     mfma_step(acc, an, bn);
 
-    // Epilogue.  32x32 accumulator layout: lane holds column lane % 32 and rows
-    // 8 * (v / 4) + 4 * (lane / 32) + v % 4.  One row address per (i, v); the
-    // four column blocks j are immediate offsets from it.
-    const int64_t nb = n0 + wn * 128 + (lane & 31);
-    const bool full_n = n0 + BN <= n_end;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t m = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (m >= m_end) continue;
-            if (BF16_OUT) {
-                uint16_t *row = reinterpret_cast<uint16_t *>(C) + m * ldc + nb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (full_n || nb + 32 * j < n_end)
-                        row[32 * j] = (uint16_t)f32_to_bf16(acc[i][j][v] * out_scale);
-            } else {
-                float *row = reinterpret_cast<float *>(C) + m * ldc + nb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (full_n || nb + 32 * j < n_end) row[32 * j] = acc[i][j][v] * out_scale;
-            }
-        }
+    epilogue<BF16_OUT>(sm, acc, m0, m_end, n0, n_end, out_scale, C, ldc, wm, wn, lane);
 }
-
 
 }  // namespace big
 
