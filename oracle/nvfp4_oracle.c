@@ -83,7 +83,9 @@ double orc_e8m0_value(uint32_t byte) { return ldexp(1.0, (int)byte - 127); }
  *   a = |v|; frexp gives a = m*2^ex with m in [0.5,1); the binade is
  *   e = clamp(ex-1, emin, emax); step = 2^(e-mbits); t = a/step;
  *   RTN: q = round-half-even(t)   (torch.round is half-to-even)
- *   SR : q = floor(t + u)         (u uniform in (0,1); FP32 add then floor)
+ *   SR : q = floor(t + u)         (u uniform in (0,1); the sum is exact:
+ *                                  t and u are summed in FP64, where both
+ *                                  are exact and so is their sum)
  *   result = copysign(min(q*step, vmax), v).
  * t = a/step is a power-of-two scaling, done with ldexpf (exact). */
 float orc_round(float v, int fmt_id, int mode, float u)
@@ -100,8 +102,9 @@ float orc_round(float v, int fmt_id, int mode, float u)
     if (mode == ORC_RTN) {
         q = rintf(t);                  /* default rounding mode: half to even */
     } else {
-        volatile float s = t + u;      /* one FP32 add, round to nearest even */
-        q = floorf(s);
+        /* t has 24 significant bits and u 17 fractional bits, so the FP64
+         * sum is exact: the decision is floor of the true t + u. */
+        q = (float)floor((double)t + (double)u);
     }
     float r = ldexpf(q, e - f.mbits);
     if (r > f.vmax) r = f.vmax;

@@ -101,3 +101,22 @@ def test_sr_on_grid_is_deterministic():
         u = O.sr_uniform(9, 9, np.arange(grid.size))
         assert np.array_equal(O.round_to(grid, fmt, O.SR, u), grid)
         assert np.array_equal(O.round_to(-grid, fmt, O.SR, u), -grid)
+
+
+def test_sr_decision_is_exact():
+    """floor(t + u) is decided on the exact sum (the pages define SR by its
+    probability of rounding up; no intermediate rounding may move t + u
+    across a grid point).  t + u = 1 - 2^-25 must round down although the
+    nearest FP32 number to it is 1.0; t + u = 1 exactly rounds up."""
+    u = np.float32([1.0 - 2.0 ** -17])               # the largest uniform, h = 65535
+    # E2M1 bottom binade: step 1/2, t = 2|x|
+    below = np.float32([2.0 ** -18 - 2.0 ** -26])     # t = 2^-17 - 2^-25
+    at = np.float32([2.0 ** -18])                     # t = 2^-17
+    assert O.round_to(below, O.E2M1, O.SR, u)[0] == 0.0
+    assert O.round_to(at, O.E2M1, O.SR, u)[0] == 0.5
+    assert O.round_to(-below, O.E2M1, O.SR, u)[0] == 0.0
+    # E4M3 subnormal binade: step 2^-9, t = |x| * 2^9
+    below8 = np.float32([(2.0 ** -17 - 2.0 ** -25) * 2.0 ** -9])
+    at8 = np.float32([2.0 ** -26])
+    assert O.round_to(below8, O.E4M3, O.SR, u)[0] == 0.0
+    assert O.round_to(at8, O.E4M3, O.SR, u)[0] == 2.0 ** -9
