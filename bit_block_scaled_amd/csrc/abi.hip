@@ -114,17 +114,14 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     p.ld = a->ld;
     const bool rht = a->col && a->col_rht;
     const bool plain = a->row || (a->col && !rht);
-    if (plain) {
-        hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, a->amax_ws, &p.n_part, s);
+    if (plain || rht) {
+        float *ws = a->amax_ws;
+        hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, plain, rht, a->rht_signs,
+                                        ws, ws + bbs::kAmaxPartials, &p.n_part, s);
         if ((st = hip_status(e, "amax launch"))) return st;
-        p.part = a->amax_ws;
-    }
-    if (rht) {
-        float *ws = a->amax_ws + bbs::kAmaxPartials;
-        hipError_t e = bbs::launch_amax_rht(a->x, a->rows, a->cols, a->ld, a->rht_signs, ws,
-                                            &p.n_part_rht, s);
-        if ((st = hip_status(e, "amax_rht launch"))) return st;
-        p.part_rht = ws;
+        p.part = ws;
+        p.part_rht = ws + bbs::kAmaxPartials;
+        p.n_part_rht = p.n_part;
     }
     if (a->row) {
         p.row_codes = a->row->codes;

@@ -5,8 +5,9 @@
 //   E2M1  s|ee|m, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
 //   E4M3  s|eeee|mmm, bias 7, max 448, min 2^-9, 0x7F is NaN (never written)
 //   E8M0  2^(byte - 127)
-// Every FP32 step that decides a code is a single IEEE operation rounded to
-// nearest even; the library is built with FP contraction off.
+// Every FP32 step before a rounding decision is a single IEEE operation
+// rounded to nearest even (the library is built with FP contraction off);
+// the decisions themselves are made by the gfx950 conversion instructions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,7 +33,7 @@ __device__ __forceinline__ int binade(float a) {
 __device__ __forceinline__ float pow2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
 
 // ---------------------------------------------------------------------------
-// E4M3
+// Decoders
 // ---------------------------------------------------------------------------
 
 // Positive E4M3 code -> value.
@@ -41,55 +42,100 @@ __device__ __forceinline__ float e4m3_pos_value(uint32_t c) {
     return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// Magnitude code of |v| on the E4M3 grid.  Rounding happens on t, the
-// magnitude in units of the local grid step 2^(e-3), e = clamp(floor(log2|v|),
-// -6, 8): q = rne(t) or floor(t + u).  The code is then ((e+7) << 3) + q - 8,
-// which also covers the subnormal binade (e = -6 gives code q) and a carry
-// into the next binade (q = 16); codes past 0x7E saturate at 448.
-template <bool SR>
-__device__ __forceinline__ uint32_t e4m3_mag_code(float a, float u) {
-    int e = binade(a);
-    e = e < -6 ? -6 : (e > 8 ? 8 : e);
-    float t = a * pow2i(3 - e);                  // exact power-of-two scaling
-    float q = SR ? floorf(t + u) : __builtin_rintf(t);
-    q = fminf(q, 16.0f);
-    int code = ((e + 7) << 3) + (int)q - 8;
-    return (uint32_t)(code > 0x7E ? 0x7E : code);
-}
-
-template <bool SR>
-__device__ __forceinline__ uint32_t e4m3_code(float v, float u) {
-    return e4m3_mag_code<SR>(fabsf(v), u) | ((__float_as_uint(v) >> 24) & 0x80u);
-}
-
-// ---------------------------------------------------------------------------
-// E2M1
-// ---------------------------------------------------------------------------
-
-// E2M1 magnitude code of |v|: e = clamp(floor(log2|v|), 0, 2), t = |v| / 2^(e-1),
-// q = rne(t) or floor(t + u); code = min(q + 2e, 7) (q = 2..4 in the normal
-// binades, 0..4 in the first; everything past 6 saturates at code 7).
-template <bool SR>
-__device__ __forceinline__ uint32_t e2m1_mag_code(float a, float u) {
-    int e = binade(a);
-    e = e < 0 ? 0 : (e > 2 ? 2 : e);
-    float t = a * pow2i(1 - e);
-    float q = SR ? floorf(t + u) : __builtin_rintf(t);
-    q = fminf(q, 8.0f);
-    int code = (int)q + 2 * e;
-    return (uint32_t)(code > 7 ? 7 : code);
-}
-
-template <bool SR>
-__device__ __forceinline__ uint32_t e2m1_code(float v, float u) {
-    return e2m1_mag_code<SR>(fabsf(v), u) | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // E2M1 nibble -> FP32 value.
 __device__ __forceinline__ float e2m1_value(uint32_t n) {
     uint32_t e = (n >> 1) & 3u, m = n & 1u;
     uint32_t bits = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
     return __uint_as_float(bits | ((n & 8u) << 28));
+}
+
+// ---------------------------------------------------------------------------
+// Rounding onto the E2M1 / E4M3 grids with the gfx950 conversion
+// instructions, always at conversion scale 1.0 (the value is scaled before).
+// Measured behaviour these helpers rely on (checked on the device by the
+// instruction tests):
+//  * round to nearest: ties to the even code, -0 kept, E2M1 saturates at 6;
+//    E4M3 is exact up to 448 (inputs above 448 are clamped first here);
+//  * stochastic: with r the 32-bit random operand, the first (or only)
+//    element rounds as floor(t + (r >> (32 - d)) / 2^d) on the exact t (the
+//    magnitude in units of the grid step), d = 22 for E2M1 and 20 for E4M3.
+//    With r = (h << 16) | 0x8000 that is floor(t + (h + 1/2) / 2^16): the
+//    16-bit uniform h of the stochastic-rounding rule.  The pair form's second
+//    element draws from bits overlapping the first one's, so one element is
+//    converted per instruction (the other slot gets +0, code 0).
+// ---------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+
+// Bytes 0 of four words -> one word (b0 in bits 7:0).
+__device__ __forceinline__ uint32_t pack_bytes4(uint32_t b0, uint32_t b1, uint32_t b2,
+                                                uint32_t b3) {
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// E2M1 round-to-nearest-even of (a, b): byte with a in bits 3:0 (upper bits
+// of the returned word are unspecified).
+__device__ __forceinline__ uint32_t e2m1_rne_pair(float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+}
+
+// Eight values times s, rounded to nearest, packed little-endian.
+__device__ __forceinline__ uint32_t e2m1_rne8(const float *f, float s) {
+    return pack_bytes4(e2m1_rne_pair(f[0] * s, f[1] * s), e2m1_rne_pair(f[2] * s, f[3] * s),
+                       e2m1_rne_pair(f[4] * s, f[5] * s), e2m1_rne_pair(f[6] * s, f[7] * s));
+}
+
+// Random operand for a 16-bit uniform held in the low / high half of w.
+__device__ __forceinline__ uint32_t sr_word_lo(uint32_t w) { return (w << 16) | 0x8000u; }
+__device__ __forceinline__ uint32_t sr_word_hi(uint32_t w) { return (w & 0xFFFF0000u) | 0x8000u; }
+
+// Stochastic E2M1 code of one value (nibble in bits 3:0, bits 7:4 zero).
+__device__ __forceinline__ uint32_t e2m1_sr1(float v, uint32_t r) {
+    f32x2_t p = {v, 0.0f};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r, 1.0f, 0);
+}
+
+// Eight values times s, stochastically rounded with the eight 16-bit
+// uniforms of one Philox block (value j uses half j & 1 of word j >> 1).
+__device__ __forceinline__ uint32_t e2m1_sr8(const float *f, float s, const uint32_t w[4]) {
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = e2m1_sr1(f[2 * i] * s, sr_word_lo(w[i]));
+        const uint32_t hi = e2m1_sr1(f[2 * i + 1] * s, sr_word_hi(w[i]));
+        b[i] = (hi << 4) | lo;
+    }
+    return pack_bytes4(b[0], b[1], b[2], b[3]);
+}
+
+// E4M3 round-to-nearest-even code of t >= 0 (saturating at 448).
+__device__ __forceinline__ uint32_t e4m3_rne_code(float t) {
+    t = fminf(t, 448.0f);
+    i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, t, t, 1.0f, false);
+    return (uint32_t)r[0] & 0xFFu;
+}
+
+// Four values (|y| <= 448) rounded to nearest E4M3, bytes little-endian.
+__device__ __forceinline__ uint32_t e4m3_rne4(float y0, float y1, float y2, float y3) {
+    i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, y0, y1, 1.0f, false);
+    i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, y2, y3, 1.0f, false);
+    return __builtin_amdgcn_perm((uint32_t)(uint16_t)hi[0], (uint32_t)(uint16_t)lo[0],
+                                 0x05040100u);
+}
+
+// Four values (|y| <= 448) stochastically rounded to E4M3 with random
+// operands r0..r3, bytes little-endian.
+__device__ __forceinline__ uint32_t e4m3_sr4(float y0, float y1, float y2, float y3,
+                                             uint32_t r0, uint32_t r1, uint32_t r2,
+                                             uint32_t r3) {
+    int w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y0, r0, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y1, r1, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y2, r2, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y3, r3, 1.0f, 3);
+    return (uint32_t)w;
 }
 
 // ---------------------------------------------------------------------------
@@ -105,14 +151,13 @@ __device__ __forceinline__ float tensor_s_enc(float amax) {
 
 // Block scale code: E4M3(rne((amax_b / 6) * s_enc)), never below code 1.
 __device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_enc) {
-    float t = (amax_b / 6.0f) * s_enc;
-    uint32_t c = e4m3_mag_code<false>(t, 0.0f);
+    const uint32_t c = e4m3_rne_code((amax_b / 6.0f) * s_enc);
     return c ? c : 1u;
 }
 
 // s_enc_b = 1 / (E4M3(code) * s_dec).
 __device__ __forceinline__ float block_enc_scale(uint32_t code, float s_dec) {
-    return 1.0f / (e4m3_pos_value(code) * s_dec);
+    return 1.0f / (__builtin_amdgcn_cvt_scalef32_f32_fp8((int)code, 1.0f, 0) * s_dec);
 }
 
 // MXFP8 block exponent: the smallest k with amax <= 448 * 2^k.  With
@@ -127,7 +172,8 @@ __device__ __forceinline__ int e8m0_k(float amax) {
 }
 
 // ---------------------------------------------------------------------------
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) and the SR uniforms
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): one 128-bit block per
+// counter; a block feeds eight elements with 16 bits each.
 // ---------------------------------------------------------------------------
 
 struct u32x4 {
@@ -153,28 +199,27 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     return {c0, c1, c2, c3};
 }
 
-// The eight uniforms of elements 8n .. 8n+7 of one output copy:
-// u_j = (16-bit lane j + 1/2) / 65536, lane j = word j/2, low half first.
-__device__ __forceinline__ void sr_uniforms8(uint64_t seed, uint32_t stream, uint64_t n,
-                                             float u[8]) {
-    u32x4 w = philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), stream, 0u, (uint32_t)seed,
-                            (uint32_t)(seed >> 32));
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u[2 * j] = ((float)(ws[j] & 0xFFFFu) + 0.5f) * (1.0f / 65536.0f);
-        u[2 * j + 1] = ((float)(ws[j] >> 16) + 0.5f) * (1.0f / 65536.0f);
-    }
+// The Philox block of elements 8n .. 8n+7 of one output copy: counter
+// (n lo, n hi, stream, 0), key = seed.
+__device__ __forceinline__ void sr_block(uint64_t seed, uint32_t stream, uint64_t n,
+                                         uint32_t w[4]) {
+    const u32x4 o = philox4x32_10((uint32_t)n, (uint32_t)(n >> 32), stream, 0u, (uint32_t)seed,
+                                  (uint32_t)(seed >> 32));
+    w[0] = o.x;
+    w[1] = o.y;
+    w[2] = o.z;
+    w[3] = o.w;
 }
 
 // ---------------------------------------------------------------------------
-// 16-point random Hadamard transform: sign flips, four sum/difference stages
-// with pair distance 1, 2, 4, 8, then one multiply by 1/4 (all FP32).
+// 16-point random Hadamard transform: sign flips (bit i of `signs` negates
+// y[i], as an exact flip of the sign bit), four sum/difference stages with
+// pair distance 1, 2, 4, 8, then one multiply by 1/4 (all FP32).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rht16(float y[16], uint32_t signs) {
+__device__ __forceinline__ void rht16_butterflies(float y[16], uint32_t signs) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-        if ((signs >> i) & 1u) y[i] = -y[i];
+        y[i] = __uint_as_float(__float_as_uint(y[i]) ^ (((signs >> i) & 1u) << 31));
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -186,6 +231,10 @@ __device__ __forceinline__ void rht16(float y[16], uint32_t signs) {
             }
         }
     }
+}
+
+__device__ __forceinline__ void rht16(float y[16], uint32_t signs) {
+    rht16_butterflies(y, signs);
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = y[i] * 0.25f;
 }

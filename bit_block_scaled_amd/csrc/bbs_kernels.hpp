@@ -75,10 +75,10 @@ struct Mx8GemmParams {
     int64_t ldc;
 };
 
-hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, float *part,
-                       int *n_part, hipStream_t s);
-hipError_t launch_amax_rht(const uint16_t *x, int64_t R, int64_t C, int64_t ld, uint32_t signs,
-                           float *part, int *n_part, hipStream_t s);
+// One read of x: partial maxima of |x| (plain) into part and of the RHT'd
+// column chunks (rht) into part_rht; *n_part partials each.
+hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
+                       uint32_t signs, float *part, float *part_rht, int *n_part, hipStream_t s);
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
                              bool tile2d, bool rht, hipStream_t s);
 hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s);

@@ -2,423 +2,505 @@
 //
 // Quantize (Pretraining LLMs with NVFP4, "NVFP4 Format and Quantization
 // Procedure", steps 1-4; 4bit.vizuara.ai sections 5-6, 13):
-//   pass 1  amax_kernel / amax_rht_kernel: partial maxima of |x| (or of the
-//           RHT'd column chunks) per workgroup, no atomics, no zeroing.
-//   pass 2  quant_tile_kernel: every workgroup folds the partials into the
-//           tensor amax (bit-identical everywhere), then each thread owns a
-//           16-row x 8-column tile of x loaded with 16-byte rows, and writes
-//           from that one read any of: the row-wise NVFP4 copy (block of 16 =
-//           two neighbouring lanes), the column-wise NVFP4 copy (x^T: eight
-//           full column blocks per thread, optional RHT), and the row-wise
-//           MXFP8 copy (block of 32 = four lanes).
+//   pass 1  amax_kernel: per-workgroup maxima of |x| and / or of the RHT'd
+//           16-row column chunks, from one read of x; no atomics, no zeroing.
+//   pass 2  quant_kernel: every wave folds the partials into the tensor amax
+//           (bit-identical everywhere).  A workgroup owns a 256-row x
+//           128-column tile of x; each thread a 16 x 8 piece of it, loaded as
+//           16 rows of 16 bytes.  From that one read it writes any of: the
+//           row-wise NVFP4 copy (a 1x16 block is two neighbouring lanes), the
+//           column-wise NVFP4 copy of x^T (eight full column blocks per
+//           thread, optional RHT), and the row-wise MXFP8 copy (a block of 32
+//           is four lanes).  With 256 tile rows, each transposed row's 128
+//           code bytes are written by one workgroup, so HBM sees whole lines.
+//           Block scales are gathered in LDS and written as contiguous runs.
 // Requantize (4bit.vizuara.ai sections 9-10): requant_kernel dequantizes a
-// 32-row x 16-column tile of an NVFP4 matrix in FP32, and writes the 16
+// 32-row x 8-column piece of an NVFP4 matrix in FP32 and writes its 8
 // transposed rows of 32 as MXFP8 (E8M0 per 32, E4M3 elements, RTN or SR).
+//
+// Workgroups are mapped to tiles so that each of the 8 XCDs works through a
+// contiguous run of tiles (neighbouring tiles share output lines in L2).
+#include <type_traits>
+
 #include "bbs_device.hpp"
 #include "bbs_kernels.hpp"
 
 namespace bbs {
 
-constexpr int kQuantThreads = 256;
+constexpr int kQT = 256;                       // threads per workgroup
+constexpr int kTileR = 256, kTileC = 128;      // quantizer tile of x
+constexpr int kAmaxGrid = 512;                 // workgroups (= partials) of pass 1
+constexpr int kReqR = 128, kReqC = 512;        // requantizer tile of the source
 
-// ---------------------------------------------------------------------------
-// Pass 1: partial amax.
-// ---------------------------------------------------------------------------
+static_assert(kAmaxGrid <= kAmaxPartials, "amax partials exceed the workspace");
 
-__device__ __forceinline__ float block_max_256(float v, float *red) {
-    // wave reduction through DPP-free shuffles, then across the 4 waves
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    float r = red[0];
-    for (int i = 1; i < kQuantThreads / 64; ++i) r = fmaxf(r, red[i]);
-    __syncthreads();
-    return r;
+// Tile t of T when workgroup b runs on XCD b % 8: XCD x takes a contiguous
+// run of tiles.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
+    const int64_t x = b % 8, j = b / 8, per = T / 8, rem = T % 8;
+    return x * per + (x < rem ? x : rem) + j;
 }
 
-// max |x| over rows x cols; each thread reads 8 BF16 (16 bytes) per step.
-__global__ __launch_bounds__(kQuantThreads) void amax_kernel(const uint16_t *__restrict__ x,
-                                                             int64_t rows, int64_t cols,
-                                                             int64_t ld, float *__restrict__ part) {
-    __shared__ float red[kQuantThreads / 64];
-    const int64_t groups_per_row = cols / 8;
-    const int64_t total = rows * groups_per_row;
-    float m = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * kQuantThreads) {
-        const int64_t r = i / groups_per_row, g = i - r * groups_per_row;
-        const uint4 v = *reinterpret_cast<const uint4 *>(x + r * ld + g * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// A thread's 16 x 8 piece of a quantizer tile.
+struct Piece {
+    int64_t R0, C0;   // the tile's first row / column
+    int64_t r0, c0;   // the piece's first row / column
+    int band, cg;     // 16-row band and 8-column group inside the tile
+    bool in;          // the piece lies inside x (R, C are multiples of 16)
+};
+
+__device__ __forceinline__ Piece piece_of(int64_t tile, int64_t R, int64_t C) {
+    const int64_t tiles_c = (C + kTileC - 1) / kTileC;
+    const int64_t tr = tile / tiles_c;
+    Piece q;
+    q.R0 = tr * kTileR;
+    q.C0 = (tile - tr * tiles_c) * kTileC;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    q.band = w * 4 + (lane >> 4);
+    q.cg = lane & 15;
+    q.r0 = q.R0 + q.band * 16;
+    q.c0 = q.C0 + q.cg * 8;
+    q.in = q.r0 < R && q.c0 < C;
+    return q;
+}
+
+// 16 rows of 16 bytes.  A piece outside x reads a valid piece instead (its
+// results are never stored), so the loads need no branches.
+__device__ __forceinline__ void load_piece(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
+                                           const Piece &q, uint4 v[16]) {
+    const int64_t r = q.r0 < R ? q.r0 : R - 16;
+    const int64_t c = q.c0 < C ? q.c0 : C - 8;
+    const uint16_t *src = x + r * ld + c;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m = fmaxf(m, fabsf(bf16_to_f32(w[j] & 0xFFFFu)));
-            m = fmaxf(m, fabsf(bf16_to_f32(w[j] >> 16)));
-        }
-    }
-    m = block_max_256(m, red);
-    if (threadIdx.x == 0) part[blockIdx.x] = m;
+    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + i * ld);
 }
 
-// max |RHT(column chunk)| over the column-wise copy: the chunks are 16
-// consecutive rows of one column.  Each thread takes a 16 x 8 tile.
-__global__ __launch_bounds__(kQuantThreads) void amax_rht_kernel(const uint16_t *__restrict__ x,
-                                                                 int64_t rows, int64_t cols,
-                                                                 int64_t ld, uint32_t signs,
-                                                                 float *__restrict__ part) {
-    __shared__ float red[kQuantThreads / 64];
-    const int64_t gpr = cols / 8;
-    const int64_t total = (rows / 16) * gpr;
-    float m = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * kQuantThreads) {
-        const int64_t band = i / gpr, g = i - band * gpr;
+// Element j (compile-time) of a row of 8 BF16 values, as FP32.
+__device__ __forceinline__ float elem(const uint4 &row, int j) {
+    const uint32_t w = j < 2 ? row.x : (j < 4 ? row.y : (j < 6 ? row.z : row.w));
+    return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: partial amax of |x| (PLAIN) and of |RHT(column chunks)| (RHT).
+// ---------------------------------------------------------------------------
+template <bool PLAIN, bool RHT>
+__global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ x, int64_t R,
+                                                   int64_t C, int64_t ld, uint32_t signs,
+                                                   float *__restrict__ part,
+                                                   float *__restrict__ part_rht) {
+    __shared__ float red[2][kQT / 64];
+    const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
+    float m = 0.0f, mr = 0.0f;
+    for (int64_t tile = blockIdx.x; tile < T; tile += gridDim.x) {
+        const Piece q = piece_of(tile, R, C);
         uint4 v[16];
+        load_piece(x, R, C, ld, q, v);
+        if (!q.in) continue;
+        if (PLAIN) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            v[r] = *reinterpret_cast<const uint4 *>(x + (band * 16 + r) * ld + g * 8);
+            for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float y[16];
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(v[r], j)));
+        }
+        if (RHT) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t w = (&v[r].x)[j >> 1];
-                y[r] = bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+            for (int j = 0; j < 8; ++j) {
+                float y[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
+                rht16_butterflies(y, signs);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mr = fmaxf(mr, fabsf(y[r]));
             }
-            rht16(y, signs);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(y[r]));
         }
     }
-    m = block_max_256(m, red);
-    if (threadIdx.x == 0) part[blockIdx.x] = m;
+    // The transform's final multiply by 1/4 is monotonic, so the maximum of
+    // the scaled values is the scaled maximum (bit for bit).
+    mr = mr * 0.25f;
+    m = wave_max(m);
+    mr = wave_max(mr);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][w] = m;
+        red[1][w] = mr;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float a = red[0][0], b = red[1][0];
+        for (int i = 1; i < kQT / 64; ++i) {
+            a = fmaxf(a, red[0][i]);
+            b = fmaxf(b, red[1][i]);
+        }
+        if (PLAIN) part[blockIdx.x] = a;
+        if (RHT) part_rht[blockIdx.x] = b;
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2: encode.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float fold_partials(const float *part, int n, float *red) {
+// The tensor amax: the maximum of n <= kAmaxPartials partials, in every lane.
+__device__ __forceinline__ float fold_partials(const float *part, int n) {
     float m = 0.0f;
-    for (int i = threadIdx.x; i < n; i += kQuantThreads) m = fmaxf(m, part[i]);
-    return block_max_256(m, red);
+    for (int i = threadIdx.x & 63; i < n; i += 64) m = fmaxf(m, part[i]);
+    return wave_max(m);
 }
 
-// Encode 8 values of one row segment with block encode scale s; returns the
-// 8 nibbles packed little-endian (element 0 in bits 3:0).
-template <bool SR>
-__device__ __forceinline__ uint32_t encode8_e2m1(const float v[8], float s, const float u[8]) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) packed |= e2m1_code<SR>(v[j] * s, SR ? u[j] : 0.0f) << (4 * j);
-    return packed;
+// Copy n bytes from LDS to global memory: one vector store when the run is
+// whole and aligned, else byte stores.
+template <int N>
+__device__ __forceinline__ void put_run(uint8_t *dst, const uint8_t *src, int64_t n) {
+    if (n == N && (reinterpret_cast<uintptr_t>(dst) % N) == 0) {
+        if constexpr (N == 16) *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+        if constexpr (N == 8) *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(src);
+        if constexpr (N == 4)
+            *reinterpret_cast<uint32_t *>(dst) = *reinterpret_cast<const uint32_t *>(src);
+    } else {
+        for (int64_t i = 0; i < n; ++i) dst[i] = src[i];
+    }
 }
 
 template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT>
-__global__ __launch_bounds__(kQuantThreads) void quant_tile_kernel(QuantParams p) {
-    __shared__ float red[kQuantThreads / 64];
-    // Tensor scales, identical in every workgroup.
-    float s_enc_plain = 1.0f, s_enc_col = 1.0f;
-    if (HAS_ROW || (HAS_COL && !RHT)) s_enc_plain = tensor_s_enc(fold_partials(p.part, p.n_part, red));
-    if (HAS_COL && RHT) s_enc_col = tensor_s_enc(fold_partials(p.part_rht, p.n_part_rht, red));
-    if (HAS_COL && !RHT) s_enc_col = s_enc_plain;
-    const float s_dec_row = 1.0f / s_enc_plain;
+__global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
+    __shared__ __align__(16) uint8_t s_row[kTileR * 8];    // row copy scales
+    __shared__ __align__(16) uint8_t s_col[kTileC * 16];   // column copy scales
+    __shared__ __align__(16) uint8_t s_mx[kTileR * 4];     // MXFP8 scales
+    const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
+    const Piece q = piece_of(xcd_tile(blockIdx.x, T), p.R, p.C);
+    uint4 v[16];
+    load_piece(p.x, p.R, p.C, p.ld, q, v);
+
+    // Tensor scales, identical in every wave.
+    float s_enc_row = 1.0f, s_enc_col = 1.0f;
+    if (HAS_ROW || (HAS_COL && !RHT)) s_enc_row = tensor_s_enc(fold_partials(p.part, p.n_part));
+    if (HAS_COL) s_enc_col = RHT ? tensor_s_enc(fold_partials(p.part_rht, p.n_part_rht)) : s_enc_row;
+    const float s_dec_row = 1.0f / s_enc_row;
     const float s_dec_col = 1.0f / s_enc_col;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (HAS_ROW) p.row_sdec[0] = s_dec_row;
         if (HAS_COL) p.col_sdec[0] = s_dec_col;
     }
-
     const int lane = threadIdx.x & 63;
-    const int64_t gpr = p.C / 8;                      // 8-column groups per row
-    const int64_t waves_per_band = (gpr + 63) / 64;
-    const int64_t wave = ((int64_t)blockIdx.x * kQuantThreads + threadIdx.x) >> 6;
-    const int64_t band = wave / waves_per_band;
-    const int64_t g = (wave - band * waves_per_band) * 64 + lane;
-    if (band >= p.R / 16) return;                    // whole wave leaves together
-    const bool active = g < gpr;                      // groups of 4 lanes agree (C % 32 == 0
-                                                     // whenever lane groups are combined)
-    const int64_t r0 = band * 16, c0 = g * 8;
 
-    uint4 v[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        v[r] = active ? *reinterpret_cast<const uint4 *>(p.x + (r0 + r) * p.ld + c0)
-                      : make_uint4(0, 0, 0, 0);
-    auto val = [&](int r, int j) -> float {
-        const uint32_t w = (&v[r].x)[j >> 1];
-        return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
-    };
-
-    // 16x16 tile amax (two lanes hold one tile).
+    // 16x16 tile amax (two lanes hold one tile; TILE2D excludes RHT).
     float tile_amax = 0.0f;
     if (TILE2D) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) tile_amax = fmaxf(tile_amax, fabsf(val(r, j)));
+            for (int j = 0; j < 8; ++j) tile_amax = fmaxf(tile_amax, fabsf(elem(v[r], j)));
         tile_amax = max_lane_pair(tile_amax);
     }
 
     // ---- row-wise NVFP4 copy -------------------------------------------------
     if (HAS_ROW) {
-        uint32_t tile_sc = 0;
-        float tile_s = 0.0f;
+        uint32_t tsc = 0;
+        float ts = 0.0f;
         if (TILE2D) {
-            tile_sc = block_scale_code(tile_amax, s_enc_plain);
-            tile_s = block_enc_scale(tile_sc, s_dec_row);
+            tsc = block_scale_code(tile_amax, s_enc_row);
+            ts = block_enc_scale(tsc, s_dec_row);
         }
+        uint8_t *codes = p.row_codes + q.r0 * (p.C / 2) + q.c0 / 2;
+        auto rows = [&](auto sr_tag) {
+            constexpr bool SR = decltype(sr_tag)::value;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x8[8];
-            float a = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                float f[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                x8[j] = val(r, j);
-                a = fmaxf(a, fabsf(x8[j]));
-            }
-            uint32_t sc;
-            float s;
-            if (TILE2D) {
-                sc = tile_sc;
-                s = tile_s;
-            } else {
-                a = max_lane_pair(a);
-                sc = block_scale_code(a, s_enc_plain);
-                s = block_enc_scale(sc, s_dec_row);
-            }
-            uint32_t packed;
-            if (p.row_round == 1) {
-                float u[8];
-                sr_uniforms8(p.row_seed, p.row_stream, (uint64_t)((r0 + r) * gpr + g), u);
-                packed = encode8_e2m1<true>(x8, s, u);
-            } else {
-                packed = encode8_e2m1<false>(x8, s, nullptr);
-            }
-            if (active) {
-                *reinterpret_cast<uint32_t *>(p.row_codes + (r0 + r) * (p.C / 2) + g * 4) = packed;
-                if ((lane & 1) == 0) {
-                    if (!TILE2D) p.row_scales[(r0 + r) * (p.C / 16) + g / 2] = (uint8_t)sc;
-                    else if (r == 0) p.row_scales[band * (p.C / 16) + g / 2] = (uint8_t)sc;
+                for (int j = 0; j < 8; ++j) f[j] = elem(v[r], j);
+                uint32_t sc = tsc;
+                float s = ts;
+                if (!TILE2D) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
+                    sc = block_scale_code(max_lane_pair(a), s_enc_row);
+                    s = block_enc_scale(sc, s_dec_row);
+                    if ((lane & 1) == 0) s_row[(q.band * 16 + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
                 }
+                uint32_t packed;
+                if (SR) {
+                    uint32_t w[4];
+                    sr_block(p.row_seed, p.row_stream,
+                             (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
+                    packed = e2m1_sr8(f, s, w);
+                } else {
+                    packed = e2m1_rne8(f, s);
+                }
+                if (q.in) *reinterpret_cast<uint32_t *>(codes + r * (p.C / 2)) = packed;
             }
-        }
+        };
+        if (p.row_round == 1) rows(std::true_type{});
+        else rows(std::false_type{});
+        if (TILE2D && (lane & 1) == 0) s_row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
     }
 
     // ---- row-wise MXFP8 copy -------------------------------------------------
     if (HAS_MX) {
+        uint8_t *codes = p.mx_codes + q.r0 * p.C + q.c0;
+        auto rows = [&](auto sr_tag) {
+            constexpr bool SR = decltype(sr_tag)::value;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x8[8];
-            float a = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                float y[8];
+                float a = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                x8[j] = val(r, j);
-                a = fmaxf(a, fabsf(x8[j]));
-            }
-            a = max_lane_quad(a);
-            const int k = e8m0_k(a);
-            float u[8];
-            const bool sr = p.mx_round == 1;
-            if (sr) sr_uniforms8(p.mx_seed, p.mx_stream, (uint64_t)((r0 + r) * gpr + g), u);
-            uint32_t lo = 0, hi = 0;
+                for (int j = 0; j < 8; ++j) {
+                    y[j] = elem(v[r], j);
+                    a = fmaxf(a, fabsf(y[j]));
+                }
+                const int k = e8m0_k(max_lane_quad(a));
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float y = ldexpf(x8[j], -k);
-                const uint32_t c = sr ? e4m3_code<true>(y, u[j]) : e4m3_code<false>(y, 0.0f);
-                if (j < 4) lo |= c << (8 * j);
-                else hi |= c << (8 * (j - 4));
+                for (int j = 0; j < 8; ++j) y[j] = ldexpf(y[j], -k);   // exact
+                uint32_t lo, hi;
+                if (SR) {
+                    uint32_t w[4];
+                    sr_block(p.mx_seed, p.mx_stream, (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
+                    lo = e4m3_sr4(y[0], y[1], y[2], y[3], sr_word_lo(w[0]), sr_word_hi(w[0]),
+                                  sr_word_lo(w[1]), sr_word_hi(w[1]));
+                    hi = e4m3_sr4(y[4], y[5], y[6], y[7], sr_word_lo(w[2]), sr_word_hi(w[2]),
+                                  sr_word_lo(w[3]), sr_word_hi(w[3]));
+                } else {
+                    lo = e4m3_rne4(y[0], y[1], y[2], y[3]);
+                    hi = e4m3_rne4(y[4], y[5], y[6], y[7]);
+                }
+                if (q.in) *reinterpret_cast<uint2 *>(codes + r * p.C) = make_uint2(lo, hi);
+                if ((lane & 3) == 0) s_mx[(q.band * 16 + r) * 4 + (q.cg >> 2)] = (uint8_t)(k + 127);
             }
-            if (active) {
-                *reinterpret_cast<uint2 *>(p.mx_codes + (r0 + r) * p.C + c0) = make_uint2(lo, hi);
-                if ((lane & 3) == 0) p.mx_scales[(r0 + r) * (p.C / 32) + g / 4] = (uint8_t)(k + 127);
-            }
-        }
+        };
+        if (p.mx_round == 1) rows(std::true_type{});
+        else rows(std::false_type{});
     }
 
     // ---- column-wise NVFP4 copy (of x^T) ---------------------------------------
     if (HAS_COL) {
-        uint32_t tile_sc = 0;
-        float tile_s = 0.0f;
+        uint32_t tsc = 0;
+        float ts = 0.0f;
         if (TILE2D) {
-            tile_sc = block_scale_code(tile_amax, s_enc_col);
-            tile_s = block_enc_scale(tile_sc, s_dec_col);
+            tsc = block_scale_code(tile_amax, s_enc_col);
+            ts = block_enc_scale(tsc, s_dec_col);
         }
+        auto cols = [&](auto sr_tag) {
+            constexpr bool SR = decltype(sr_tag)::value;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float y[16];
+            for (int j = 0; j < 8; ++j) {
+                float y[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) y[r] = val(r, j);
-            if (RHT) rht16(y, p.rht_signs);
-            uint32_t sc;
-            float s;
-            if (TILE2D) {
-                sc = tile_sc;
-                s = tile_s;
-            } else {
-                float a = 0.0f;
+                for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
+                if (RHT) rht16(y, p.rht_signs);
+                uint32_t sc = tsc;
+                float s = ts;
+                if (!TILE2D) {
+                    float a = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(y[r]));
-                sc = block_scale_code(a, s_enc_col);
-                s = block_enc_scale(sc, s_dec_col);
+                    for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(y[r]));
+                    sc = block_scale_code(a, s_enc_col);
+                    s = block_enc_scale(sc, s_dec_col);
+                    s_col[(q.cg * 8 + j) * 16 + q.band] = (uint8_t)sc;
+                }
+                const int64_t c = q.c0 + j;                 // row of the transposed copy
+                uint32_t w0, w1;
+                if (SR) {
+                    const uint64_t n0 = (uint64_t)(c * p.R + q.r0) / 8;
+                    uint32_t w[4];
+                    sr_block(p.col_seed, p.col_stream, n0, w);
+                    w0 = e2m1_sr8(y, s, w);
+                    sr_block(p.col_seed, p.col_stream, n0 + 1, w);
+                    w1 = e2m1_sr8(y + 8, s, w);
+                } else {
+                    w0 = e2m1_rne8(y, s);
+                    w1 = e2m1_rne8(y + 8, s);
+                }
+                if (q.in)
+                    *reinterpret_cast<uint2 *>(p.col_codes + c * (p.R / 2) + q.r0 / 2) =
+                        make_uint2(w0, w1);
             }
-            const int64_t c = c0 + j;                 // row of the transposed copy
-            uint32_t w0, w1;
-            if (p.col_round == 1) {
-                const uint64_t n0 = (uint64_t)(c * p.R + r0) / 8;
-                float u[8];
-                sr_uniforms8(p.col_seed, p.col_stream, n0, u);
-                w0 = encode8_e2m1<true>(y, s, u);
-                sr_uniforms8(p.col_seed, p.col_stream, n0 + 1, u);
-                w1 = encode8_e2m1<true>(y + 8, s, u);
-            } else {
-                w0 = encode8_e2m1<false>(y, s, nullptr);
-                w1 = encode8_e2m1<false>(y + 8, s, nullptr);
-            }
-            if (active) {
-                *reinterpret_cast<uint2 *>(p.col_codes + c * (p.R / 2) + r0 / 2) = make_uint2(w0, w1);
-                if (!TILE2D) p.col_scales[c * (p.R / 16) + band] = (uint8_t)sc;
-                else if (j == 0 && (lane & 1) == 0)
-                    p.col_scales[(c / 16) * (p.R / 16) + band] = (uint8_t)sc;
-            }
+        };
+        if (p.col_round == 1) cols(std::true_type{});
+        else cols(std::false_type{});
+        if (TILE2D && (lane & 1) == 0) s_col[(q.cg >> 1) * 16 + q.band] = (uint8_t)tsc;
+    }
+
+    // ---- block scales, as contiguous runs ------------------------------------
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int64_t nb_row = (p.C - q.C0) / 16, nb_col = (p.R - q.R0) / 16;
+    if (HAS_ROW) {
+        if (!TILE2D) {
+            if (q.R0 + t < p.R)
+                put_run<8>(p.row_scales + (q.R0 + t) * (p.C / 16) + q.C0 / 16, s_row + t * 8,
+                           nb_row < 8 ? nb_row : 8);
+        } else if (t < 16 && q.R0 / 16 + t < p.R / 16) {
+            put_run<8>(p.row_scales + (q.R0 / 16 + t) * (p.C / 16) + q.C0 / 16, s_row + t * 8,
+                       nb_row < 8 ? nb_row : 8);
+        }
+    }
+    if (HAS_MX && q.R0 + t < p.R) {
+        const int64_t nb = (p.C - q.C0) / 32;
+        put_run<4>(p.mx_scales + (q.R0 + t) * (p.C / 32) + q.C0 / 32, s_mx + t * 4,
+                   nb < 4 ? nb : 4);
+    }
+    if (HAS_COL) {
+        if (!TILE2D) {
+            if (t < kTileC && q.C0 + t < p.C)
+                put_run<16>(p.col_scales + (q.C0 + t) * (p.R / 16) + q.R0 / 16, s_col + t * 16,
+                            nb_col < 16 ? nb_col : 16);
+        } else if (t < kTileC / 16 && q.C0 / 16 + t < p.C / 16) {
+            put_run<16>(p.col_scales + (q.C0 / 16 + t) * (p.R / 16) + q.R0 / 16, s_col + t * 16,
+                        nb_col < 16 ? nb_col : 16);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Requantize: NVFP4 [R x C] -> MXFP8 of the transpose [C x R].
-// Each thread: 32 source rows x 16 source columns (8 code bytes per row).
+// A workgroup takes 128 source rows (a 32-row band per wave) x 512 source
+// columns (8 per lane), so each destination row's 128 bytes come from one
+// workgroup.  Each lane: 32 rows x 8 columns -> 8 destination rows of 32.
 // ---------------------------------------------------------------------------
-template <bool SR>
-__global__ __launch_bounds__(kQuantThreads) void requant_kernel(RequantParams p) {
-    const int lane = threadIdx.x & 63;
-    const int64_t gpr = p.C / 16;                    // 16-column groups per source row
-    const int64_t waves_per_band = (gpr + 63) / 64;
-    const int64_t wave = ((int64_t)blockIdx.x * kQuantThreads + threadIdx.x) >> 6;
-    const int64_t band = wave / waves_per_band;      // 32-row band of the source
-    const int64_t g = (wave - band * waves_per_band) * 64 + lane;
-    if (band >= p.R / 32 || g >= gpr) return;        // no cross-lane traffic here
-    const int64_t r0 = band * 32, c0 = g * 16;
+template <bool SR, bool TILE2D>
+__global__ __launch_bounds__(kQT) void requant_kernel(RequantParams p) {
+    const int64_t tiles_c = (p.C + kReqC - 1) / kReqC;
+    const int64_t T = ((p.R + kReqR - 1) / kReqR) * tiles_c;
+    const int64_t tile = xcd_tile(blockIdx.x, T);
+    const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = tr * kReqR + w * 32, c0 = tc * kReqC + lane * 8;
+    if (r0 >= p.R || c0 >= p.C) return;              // no barriers or lane exchange below
     const float s_dec = p.s_dec[0];
+    const int64_t nsb = p.C / 16;                    // scale bytes per scale row
 
-    uint2 cw[32];
-    uint32_t sc[32];
+    uint32_t cw[32];                                 // 8 nibbles of each source row
+    float bs[TILE2D ? 2 : 32];                       // E4M3 block scales, decoded
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        cw[r] = *reinterpret_cast<const uint2 *>(p.codes + (r0 + r) * (p.C / 2) + c0 / 2);
-        const int64_t srow = p.tile2d ? (r0 + r) / 16 : (r0 + r);
-        sc[r] = p.scales[srow * (p.C / 16) + g];
+    for (int r = 0; r < 32; ++r)
+        cw[r] = *reinterpret_cast<const uint32_t *>(p.codes + (r0 + r) * (p.C / 2) + c0 / 2);
+#pragma unroll
+    for (int i = 0; i < (TILE2D ? 2 : 32); ++i) {
+        const int64_t srow = TILE2D ? r0 / 16 + i : r0 + i;
+        bs[i] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)p.scales[srow * nsb + c0 / 16], 1.0f, 0);
     }
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll 1
-    for (int jj = 0; jj < 8; ++jj) {
-        const int j = half * 8 + jj;
-        float x[32];
+
+    auto emit = [&](const float (&x)[32], int64_t c) {
         float a = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const uint32_t w = half ? cw[r].y : cw[r].x;
-            const uint32_t nib = (w >> (4 * jj)) & 0xFu;
-            // (E2M1 x E4M3) is exact; the multiply by s_dec is one FP32 rounding.
-            x[r] = (e2m1_value(nib) * e4m3_pos_value(sc[r])) * s_dec;
-            a = fmaxf(a, fabsf(x[r]));
-        }
+        for (int r = 0; r < 32; ++r) a = fmaxf(a, fabsf(x[r]));
         const int k = e8m0_k(a);
-        const int64_t c = c0 + j;                    // destination row
         uint32_t out[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float u[8];
-            if (SR) sr_uniforms8(p.seed, p.stream, (uint64_t)(c * p.R + r0) / 8 + q, u);
+        for (int g = 0; g < 4; ++g) {
+            float y[8];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t word = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int e = q * 8 + h * 4 + b;
-                    const float y = ldexpf(x[e], -k);
-                    word |= e4m3_code<SR>(y, SR ? u[h * 4 + b] : 0.0f) << (8 * b);
-                }
-                out[q * 2 + h] = word;
+            for (int i = 0; i < 8; ++i) y[i] = ldexpf(x[8 * g + i], -k);   // exact
+            if (SR) {
+                uint32_t wd[4];
+                sr_block(p.seed, p.stream, (uint64_t)(c * p.R + r0) / 8 + g, wd);
+                out[2 * g] = e4m3_sr4(y[0], y[1], y[2], y[3], sr_word_lo(wd[0]), sr_word_hi(wd[0]),
+                                      sr_word_lo(wd[1]), sr_word_hi(wd[1]));
+                out[2 * g + 1] = e4m3_sr4(y[4], y[5], y[6], y[7], sr_word_lo(wd[2]),
+                                          sr_word_hi(wd[2]), sr_word_lo(wd[3]), sr_word_hi(wd[3]));
+            } else {
+                out[2 * g] = e4m3_rne4(y[0], y[1], y[2], y[3]);
+                out[2 * g + 1] = e4m3_rne4(y[4], y[5], y[6], y[7]);
             }
         }
         uint4 *dst = reinterpret_cast<uint4 *>(p.out_codes + c * p.R + r0);
         dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
         dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-        p.out_scales[c * (p.R / 32) + band] = (uint8_t)(k + 127);
-    }
+        p.out_scales[c * (p.R / 32) + r0 / 32] = (uint8_t)(k + 127);
+    };
+
+    auto pair = [&](auto jp_tag) {                   // source columns 2jp, 2jp + 1
+        constexpr int jp = decltype(jp_tag)::value;
+        float xe[32], xo[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[r], 1.0f, jp);
+            const float b = bs[TILE2D ? r / 16 : r];
+            // (E2M1 x E4M3) is exact; the multiply by s_dec is one FP32 rounding.
+            xe[r] = (e[0] * b) * s_dec;
+            xo[r] = (e[1] * b) * s_dec;
+        }
+        emit(xe, c0 + 2 * jp);
+        emit(xo, c0 + 2 * jp + 1);
+    };
+    pair(std::integral_constant<int, 0>{});
+    pair(std::integral_constant<int, 1>{});
+    pair(std::integral_constant<int, 2>{});
+    pair(std::integral_constant<int, 3>{});
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after argument checks).
 // ---------------------------------------------------------------------------
 
-int amax_grid(int64_t work_items) {
-    int64_t g = (work_items + kQuantThreads * 8 - 1) / (kQuantThreads * 8);
-    if (g < 1) g = 1;
-    if (g > kAmaxPartials) g = kAmaxPartials;
-    return (int)g;
-}
-
-hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, float *part,
-                       int *n_part, hipStream_t s) {
-    const int grid = amax_grid(R * (C / 8));
+hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
+                       uint32_t signs, float *part, float *part_rht, int *n_part,
+                       hipStream_t s) {
+    const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
+    const int grid = (int)(T < kAmaxGrid ? T : kAmaxGrid);
     *n_part = grid;
-    hipLaunchKernelGGL(amax_kernel, dim3(grid), dim3(kQuantThreads), 0, s, x, R, C, ld, part);
-    return hipGetLastError();
-}
-
-hipError_t launch_amax_rht(const uint16_t *x, int64_t R, int64_t C, int64_t ld, uint32_t signs,
-                           float *part, int *n_part, hipStream_t s) {
-    const int grid = amax_grid((R / 16) * (C / 8) * 16);
-    *n_part = grid;
-    hipLaunchKernelGGL(amax_rht_kernel, dim3(grid), dim3(kQuantThreads), 0, s, x, R, C, ld,
-                       signs, part);
+    if (plain && rht)
+        hipLaunchKernelGGL((amax_kernel<true, true>), dim3(grid), dim3(kQT), 0, s, x, R, C, ld,
+                           signs, part, part_rht);
+    else if (plain)
+        hipLaunchKernelGGL((amax_kernel<true, false>), dim3(grid), dim3(kQT), 0, s, x, R, C, ld,
+                           signs, part, part_rht);
+    else if (rht)
+        hipLaunchKernelGGL((amax_kernel<false, true>), dim3(grid), dim3(kQT), 0, s, x, R, C, ld,
+                           signs, part, part_rht);
     return hipGetLastError();
 }
 
 template <bool R_, bool C_, bool M_, bool T_, bool H_>
-static void launch_tile(const QuantParams &p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((quant_tile_kernel<R_, C_, M_, T_, H_>), grid, dim3(kQuantThreads), 0, s, p);
+static void launch_q(const QuantParams &p, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((quant_kernel<R_, C_, M_, T_, H_>), grid, dim3(kQT), 0, s, p);
 }
 
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
                              bool tile2d, bool rht, hipStream_t s) {
-    const int64_t gpr = p.C / 8;
-    const int64_t waves = (p.R / 16) * ((gpr + 63) / 64);
-    const dim3 grid((unsigned)((waves + 3) / 4));
+    const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
+    const dim3 grid((unsigned)T);
     // The combinations the quantizer supports (RHT only on a 1x16 column copy).
     const int key = (has_row << 4) | (has_col << 3) | (has_mx << 2) | (tile2d << 1) | rht;
     switch (key) {
-        case 0b10000: launch_tile<1, 0, 0, 0, 0>(p, grid, s); break;
-        case 0b10010: launch_tile<1, 0, 0, 1, 0>(p, grid, s); break;
-        case 0b11000: launch_tile<1, 1, 0, 0, 0>(p, grid, s); break;
-        case 0b11010: launch_tile<1, 1, 0, 1, 0>(p, grid, s); break;
-        case 0b11001: launch_tile<1, 1, 0, 0, 1>(p, grid, s); break;
-        case 0b01000: launch_tile<0, 1, 0, 0, 0>(p, grid, s); break;
-        case 0b01010: launch_tile<0, 1, 0, 1, 0>(p, grid, s); break;
-        case 0b01001: launch_tile<0, 1, 0, 0, 1>(p, grid, s); break;
-        case 0b00100: launch_tile<0, 0, 1, 0, 0>(p, grid, s); break;
-        case 0b10100: launch_tile<1, 0, 1, 0, 0>(p, grid, s); break;
-        case 0b10110: launch_tile<1, 0, 1, 1, 0>(p, grid, s); break;
-        case 0b01100: launch_tile<0, 1, 1, 0, 0>(p, grid, s); break;
-        case 0b01101: launch_tile<0, 1, 1, 0, 1>(p, grid, s); break;
-        case 0b11100: launch_tile<1, 1, 1, 0, 0>(p, grid, s); break;
-        case 0b11101: launch_tile<1, 1, 1, 0, 1>(p, grid, s); break;
-        case 0b01110: launch_tile<0, 1, 1, 1, 0>(p, grid, s); break;
-        case 0b11110: launch_tile<1, 1, 1, 1, 0>(p, grid, s); break;
+        case 0b10000: launch_q<1, 0, 0, 0, 0>(p, grid, s); break;
+        case 0b10010: launch_q<1, 0, 0, 1, 0>(p, grid, s); break;
+        case 0b11000: launch_q<1, 1, 0, 0, 0>(p, grid, s); break;
+        case 0b11010: launch_q<1, 1, 0, 1, 0>(p, grid, s); break;
+        case 0b11001: launch_q<1, 1, 0, 0, 1>(p, grid, s); break;
+        case 0b01000: launch_q<0, 1, 0, 0, 0>(p, grid, s); break;
+        case 0b01010: launch_q<0, 1, 0, 1, 0>(p, grid, s); break;
+        case 0b01001: launch_q<0, 1, 0, 0, 1>(p, grid, s); break;
+        case 0b00100: launch_q<0, 0, 1, 0, 0>(p, grid, s); break;
+        case 0b10100: launch_q<1, 0, 1, 0, 0>(p, grid, s); break;
+        case 0b10110: launch_q<1, 0, 1, 1, 0>(p, grid, s); break;
+        case 0b01100: launch_q<0, 1, 1, 0, 0>(p, grid, s); break;
+        case 0b01101: launch_q<0, 1, 1, 0, 1>(p, grid, s); break;
+        case 0b11100: launch_q<1, 1, 1, 0, 0>(p, grid, s); break;
+        case 0b11101: launch_q<1, 1, 1, 0, 1>(p, grid, s); break;
+        case 0b01110: launch_q<0, 1, 1, 1, 0>(p, grid, s); break;
+        case 0b11110: launch_q<1, 1, 1, 1, 0>(p, grid, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s) {
-    const int64_t gpr = p.C / 16;
-    const int64_t waves = (p.R / 32) * ((gpr + 63) / 64);
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    if (sr) hipLaunchKernelGGL(requant_kernel<true>, grid, dim3(kQuantThreads), 0, s, p);
-    else hipLaunchKernelGGL(requant_kernel<false>, grid, dim3(kQuantThreads), 0, s, p);
+    const int64_t T = ((p.R + kReqR - 1) / kReqR) * ((p.C + kReqC - 1) / kReqC);
+    const dim3 grid((unsigned)T);
+    if (sr && p.tile2d) hipLaunchKernelGGL((requant_kernel<true, true>), grid, dim3(kQT), 0, s, p);
+    else if (sr) hipLaunchKernelGGL((requant_kernel<true, false>), grid, dim3(kQT), 0, s, p);
+    else if (p.tile2d) hipLaunchKernelGGL((requant_kernel<false, true>), grid, dim3(kQT), 0, s, p);
+    else hipLaunchKernelGGL((requant_kernel<false, false>), grid, dim3(kQT), 0, s, p);
     return hipGetLastError();
 }
 

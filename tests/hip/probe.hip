@@ -93,3 +93,24 @@ int probe_cvt_fp8_f32(const float *x, int n, const float *scale, uint16_t *out) 
     return (int)hipDeviceSynchronize();
 }
 }
+
+// Stochastic conversions as the quantizers issue them: one value per
+// instruction (+0 in the second slot of the FP4 pair), random operand
+// (h << 16) | 0x8000 for a 16-bit uniform h, scale 1.0.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__global__ void cvt_sr_kernel(const float *x, const uint32_t *h, int n, const float *scale,
+                              uint8_t *fp4, uint8_t *fp8) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t r = (h[i] << 16) | 0x8000u;
+    f32x2 p = {x[i], 0.0f};
+    fp4[i] = (uint8_t)(__builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r, scale[0], 0) & 0xFF);
+    fp8[i] = (uint8_t)(__builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, x[i], r, scale[0], 0) & 0xFF);
+}
+
+extern "C" int probe_cvt_sr(const float *x, const uint32_t *h, int n, const float *scale,
+                            uint8_t *fp4, uint8_t *fp8) {
+    hipLaunchKernelGGL(cvt_sr_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, x, h, n, scale, fp4,
+                       fp8);
+    return (int)hipDeviceSynchronize();
+}

@@ -1,8 +1,9 @@
 """Checks of the gfx950 instruction behaviour the kernels are built on:
 the operand / scale layout of v_mfma_scale_f32_16x16x128_f8f6f4 with 8-bit
-operands, and the exactness of v_cvt_scalef32_pk_f16_fp4 at scale 1.0 (the
-NVFP4 GEMM's expansion).  Also records that v_cvt_scalef32_pk_fp4_f32 rounds
-like the oracle's round-to-nearest-even (not used by the kernels yet)."""
+operands, the exactness of v_cvt_scalef32_pk_f16_fp4 at scale 1.0 (the NVFP4
+GEMM's expansion), and the rounding of the FP4 / FP8 conversions the
+quantizers use: v_cvt_scalef32_pk_fp4_f32 (round to nearest even) and the
+stochastic v_cvt_scalef32_sr_pk_fp4_f32 / v_cvt_scalef32_sr_fp8_f32."""
 import ctypes as C
 import os
 
@@ -83,3 +84,32 @@ def test_fp4_rtn_conversion_matches_oracle(probe):
     o = o.cpu().numpy()
     assert np.array_equal(o & 0xF, O.e2m1_code(O.round_to(x, O.E2M1)))
     assert np.array_equal(o >> 4, O.e2m1_code(O.round_to(-x, O.E2M1)))
+
+
+def test_sr_conversions_match_oracle(probe):
+    """The stochastic E2M1 / E4M3 conversions, issued as the quantizers issue
+    them (random operand (h << 16) | 0x8000, one value per instruction),
+    round exactly like the oracle's floor(t + (h + 1/2) / 2^16)."""
+    announce("v_cvt_scalef32_sr_pk_fp4_f32 / v_cvt_scalef32_sr_fp8_f32 rounding")
+    rng = np.random.default_rng(5)
+    n = 1 << 20
+    x = (2.0 ** rng.uniform(-14, 9, n) * (rng.integers(0, 2, n) * 2 - 1)).astype(np.float32)
+    x[:64] = 0.0
+    x[64:128] = -0.0
+    h = rng.integers(0, 1 << 16, n).astype(np.uint32)
+    h[:4096] = np.arange(4096) % 2 * 65535                # both ends of the uniform range
+    xd, hd = torch.from_numpy(x).to(dev()), torch.from_numpy(h.view(np.int32)).to(dev())
+    s1 = torch.ones(1, dtype=torch.float32, device=dev())
+    o4 = torch.zeros(n, dtype=torch.uint8, device=dev())
+    o8 = torch.zeros(n, dtype=torch.uint8, device=dev())
+    assert probe.probe_cvt_sr(C.c_void_p(xd.data_ptr()), C.c_void_p(hd.data_ptr()), n,
+                              C.c_void_p(s1.data_ptr()), C.c_void_p(o4.data_ptr()),
+                              C.c_void_p(o8.data_ptr())) == 0
+    u = ((h.astype(np.float64) + 0.5) / 65536.0).astype(np.float32)
+    want4 = O.e2m1_code(O.round_to(x, O.E2M1, O.SR, u))   # saturates at 6 like the oracle
+    got4 = o4.cpu().numpy()
+    assert np.array_equal(got4 & 0xF, want4), np.nonzero((got4 & 0xF) != want4)[0][:5]
+    assert np.all(got4 >> 4 == 0)
+    in8 = np.abs(x) <= 448                                # MXFP8 inputs never exceed 448
+    want8 = O.e4m3_code(O.round_to(x[in8], O.E4M3, O.SR, u[in8]))
+    assert np.array_equal(o8.cpu().numpy()[in8], want8)
