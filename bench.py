@@ -31,6 +31,7 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0                      # MFMA class the NVFP4 GEMM issues
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
+COPY_BYTES = 1 << 29                            # counter calibration copy (512 MiB)
 
 
 def nvfp4_bytes(r, c):
@@ -56,7 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="time one op of the step in isolation (quant_x, quant_w, fprop, "
-                         "quant_dy, requant_w, dgrad, wgrad); used for counter runs")
+                         "quant_dy, requant_w, dgrad, wgrad), or 'copy' (a plain 512 MiB "
+                         "device copy); used for counter runs")
     return ap.parse_args()
 
 
@@ -118,10 +120,19 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
+    dev = torch.device("cuda:0")
+    if args.only == "copy":
+        # a plain copy of known size: calibrates the HBM byte counters
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes": COPY_BYTES}), flush=True)
+        return
     import bit_block_scaled_amd as bbs
     from workloads import synth
 
-    dev = torch.device("cuda:0")
     fw = synth.dense_forward(M, K, N)
     bw = synth.backward(M, N)
     signs, seeds = bw["rht_signs"], bw["seeds"]

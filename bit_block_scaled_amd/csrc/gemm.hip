@@ -378,8 +378,9 @@ hipError_t launch_mxfp8_gemm_big(const Mx8GemmParams &p, bool bf16_out, hipStrea
 
 hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s) {
     auto al = [](const void *q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
+    // the large-tile kernel stores groups of four output columns at once
     if (p.K % 128 == 0 && al(p.a_codes, 16) && al(p.b_codes, 16) && al(p.a_scales, 4) &&
-        al(p.b_scales, 4))
+        al(p.b_scales, 4) && p.N % 4 == 0 && al(p.c, 16) && p.ldc % 4 == 0)
         return launch_mxfp8_gemm_big(p, bf16_out, s);
     const dim3 grid((unsigned)((p.N + kBN - 1) / kBN), (unsigned)((p.M + kBM - 1) / kBM));
     if (bf16_out) hipLaunchKernelGGL(mxfp8_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, p);

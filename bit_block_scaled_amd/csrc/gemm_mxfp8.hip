@@ -132,8 +132,8 @@ __device__ __forceinline__ void compute(const Stage &st, f32x4 (&acc)[8][8], int
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
-                                                                         asc, 0, bsc[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
+                                                                         bsc[j], 0, asc);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -175,23 +175,25 @@ __global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p)
         __syncthreads();
     }
 
-    // 16x16 accumulator layout: lane holds column lane % 16, rows 4 * (lane / 16) + v.
+    // The MFMAs take the B fragment first, so block (i, jj) holds the
+    // transposed 16 x 16 product: lane l has output row l % 16 and columns
+    // 4 * (l / 16) + v, four consecutive columns stored at once.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        const int64_t m = m0 + wm * 128 + i * 16 + (lane & 15);
+        if (m >= p.M) continue;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t m = m0 + wm * 128 + i * 16 + 4 * (lane >> 4) + v;
-            if (m >= p.M) continue;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int64_t n = n0 + wn * 128 + jj * 16 + (lane & 15);
-                if (n < p.N) {
-                    const float y = acc[i][jj][v];
-                    if (BF16_OUT)
-                        reinterpret_cast<uint16_t *>(p.c)[m * p.ldc + n] = (uint16_t)f32_to_bf16(y);
-                    else
-                        reinterpret_cast<float *>(p.c)[m * p.ldc + n] = y;
-                }
+        for (int jj = 0; jj < 8; ++jj) {
+            const int64_t n = n0 + wn * 128 + jj * 16 + 4 * (lane >> 4);
+            if (n >= p.N) continue;
+            const f32x4 y = acc[i][jj];
+            if (BF16_OUT) {
+                const uint2 w = make_uint2(f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16),
+                                           f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16));
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = w;
+            } else {
+                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
+                    make_float4(y[0], y[1], y[2], y[3]);
             }
         }
     }
