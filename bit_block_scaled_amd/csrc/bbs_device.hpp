@@ -240,6 +240,26 @@ __device__ __forceinline__ void rht16(float y[16], uint32_t signs) {
 }
 
 // ---------------------------------------------------------------------------
+// Slab copies (global -> LDS, asynchronous) are issued through inline
+// assembly.  Issued through the compiler builtin, a copy counts as an LDS
+// store to an unknown address, and the compiler then waits for every copy in
+// flight before any later LDS read, which serialises the ring.  The loop
+// orders copies and reads itself (s_waitcnt vmcnt, then a workgroup barrier).
+// M0 holds the wave's LDS destination; a wait state separates its write from
+// the copy that reads it.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void copy_lds16(const void *g, const void *lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr(lds))
+                 : "memory");
+}
+__device__ __forceinline__ void copy_lds4(const void *g, const void *lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_addr(lds))
+                 : "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane maxima inside aligned groups of 2 and 4 lanes (DPP quad_perm).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float max_lane_pair(float v) {

@@ -85,15 +85,11 @@ __device__ __forceinline__ void issue(Stage &st, const Plan &pl, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int seg = (w * 8 + q) * 1024;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.a_base + k0 + pl.a_off[q]),
-                                         (lds_void_t *)(st.a + seg), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.b_base + k0 + pl.b_off[q]),
-                                         (lds_void_t *)(st.b + seg), 16, 0, 0);
+        copy_lds16(pl.a_base + k0 + pl.a_off[q], st.a + seg);
+        copy_lds16(pl.b_base + k0 + pl.b_off[q], st.b + seg);
     }
-    __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sa_base + k0 / 32 + pl.sa_off),
-                                     (lds_void_t *)(st.as + w * 64), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sb_base + k0 / 32 + pl.sb_off),
-                                     (lds_void_t *)(st.bs + w * 64), 4, 0, 0);
+    copy_lds4(pl.sa_base + k0 / 32 + pl.sa_off, st.as + w * 64);
+    copy_lds4(pl.sb_base + k0 / 32 + pl.sb_off, st.bs + w * 64);
 }
 
 __device__ __forceinline__ i32x8 frag(const uint8_t *tile, int r, int g) {

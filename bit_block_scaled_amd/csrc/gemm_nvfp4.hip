@@ -115,31 +115,41 @@ __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, in
     return pl;
 }
 
-template <bool BT>
-__device__ __forceinline__ void issue(Stage &st, const Plan &pl, int64_t k0) {
+// The copies of one slab, in three parts that the main loop spreads over
+// MFMA steps: 0 = A codes (4 instructions per wave), 1 = B codes (4),
+// 2 = scales (2 + 2, or 2 + 1 when B has 16x16 tiles).
+template <int PART, bool BT>
+__device__ __forceinline__ void issue_part(Stage &st, const Plan &pl, int64_t k0) {
     const int w = threadIdx.x >> 6;
     const int64_t cb = k0 / 2, sk = k0 / 16;
+    if (PART == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int seg = (w * 4 + q) * 1024;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.a[q] + cb), (lds_void_t *)(st.a + seg), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.b[q] + cb), (lds_void_t *)(st.b + seg), 16, 0, 0);
-    }
+        for (int q = 0; q < 4; ++q)
+            copy_lds16(pl.a[q] + cb, st.a + (w * 4 + q) * 1024);
+    } else if (PART == 1) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int seg = (w * 2 + q) * 256;
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sa[q] + sk), (lds_void_t *)(st.as + seg), 4, 0, 0);
-    }
-    if (!BT) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int seg = (w * 2 + q) * 256;
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sb[q] + sk), (lds_void_t *)(st.bs + seg), 4, 0, 0);
-        }
+        for (int q = 0; q < 4; ++q)
+            copy_lds16(pl.b[q] + cb, st.b + (w * 4 + q) * 1024);
     } else {
-        // the 16 tile rows (128 bytes); every wave writes the same bytes
-        __builtin_amdgcn_global_load_lds((gbl_void_t *)(pl.sb[0] + sk), (lds_void_t *)(st.bs), 4, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            copy_lds4(pl.sa[q] + sk, st.as + (w * 2 + q) * 256);
+        if (!BT) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                copy_lds4(pl.sb[q] + sk, st.bs + (w * 2 + q) * 256);
+        } else {
+            // the 16 tile rows (128 bytes); every wave writes the same bytes
+            copy_lds4(pl.sb[0] + sk, st.bs);
+        }
     }
+}
+
+template <bool BT>
+__device__ __forceinline__ void issue(Stage &st, const Plan &pl, int64_t k0) {
+    issue_part<0, BT>(st, pl, k0);
+    issue_part<1, BT>(st, pl, k0);
+    issue_part<2, BT>(st, pl, k0);
 }
 
 // Code words of one 32-byte chunk of a slab for the wave's 4 + 4 fragment
@@ -215,7 +225,7 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const f16x8 (&af)
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
 // Interleave: one MFMA, then four VALU, sixteen times.
@@ -227,14 +237,26 @@ __device__ __forceinline__ void interleave_1_4() {
     }
 }
 
-// After a slab barrier the next slab's operands are still in flight from
-// LDS: issue 8 MFMAs first, then interleave the rest 1:8 with the expansion.
-__device__ __forceinline__ void interleave_8_then_1_8() {
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+// One MFMA, then one vector-memory instruction (the first N times), then
+// four VALU, sixteen times: the slab copies issue under the MFMAs.
+template <int N>
+__device__ __forceinline__ void interleave_1_vmem_4() {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 16; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        if (k < N) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+}
+
+// One MFMA, one LDS read, four VALU: the next slab's fragment reads issue
+// early, under the MFMAs.
+__device__ __forceinline__ void interleave_1_ds_4() {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
 }
 
@@ -244,54 +266,62 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | (((N >> 4) & 3) << 14));
 }
 
-// Epilogue.  The 32x32 accumulator layout gives lane l column l % 32 and rows
-// 8 * (v / 4) + 4 * (l / 32) + v % 4 of each 32 x 32 block.  Each wave writes
-// its scaled, converted 128 x 128 tile through LDS in pieces (64 rows of BF16
-// or 32 rows of FP32, 16 KB each) and stores it back to C as whole 16-byte
-// row segments per lane.  Row m < m_end and column n < n_end are written;
-// N being a multiple of 16 keeps every 16-byte segment wholly in or out.
+// Epilogue.  The MFMAs take the B fragment as their first operand, so block
+// (i, j) of the accumulators holds the transposed 32 x 32 product: lane l has
+// output row l % 32 and columns 8 * (v / 4) + 4 * (l / 32) + v % 4, i.e. each
+// group of four registers is four consecutive columns of one row.  Each wave
+// writes those groups (8 bytes of BF16, 16 of FP32) into its own staging rows
+// in the (now idle) slab ring, then stores whole rows, 16 bytes per lane, so
+// every store instruction writes complete 256- or 512-byte row segments.
+// Rows m < m_end and columns n < n_end are written; N being a multiple of 16
+// keeps every 16-byte segment wholly in or out.
 template <bool BF16_OUT>
 __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], int64_t m0,
                                          int64_t m_end, int64_t n0, int64_t n_end,
                                          float out_scale, void *C, int64_t ldc, int wm, int wn,
                                          int lane) {
     constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
-    constexpr int RS = 128 * ES + 16;                 // LDS row stride (padded)
-    constexpr int ROWS = BF16_OUT ? 64 : 32;          // rows per piece
-    constexpr int I_PER = ROWS / 32;                  // accumulator row blocks per piece
-    __syncthreads();                                  // the slab ring is free now
-    uint8_t *buf = reinterpret_cast<uint8_t *>(&sm) + (threadIdx.x >> 6) * (ROWS * RS);
+    constexpr int RS = 128 * ES + 16;                 // staging row stride
+    constexpr int PR = BF16_OUT ? 32 : 16;            // rows per piece
+    constexpr int LPR = 128 * ES / 16;                // lanes per row on read-back
+    constexpr int RPI = 64 / LPR;                     // rows per read-back instruction
+    uint8_t *buf = reinterpret_cast<uint8_t *>(&sm) + (threadIdx.x >> 6) * (PR * RS);
     const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
+    const int lr = lane & 31;                          // the lane's row in a 32-row block
 #pragma unroll
-    for (int piece = 0; piece < 4 / I_PER; ++piece) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int ii = 0; ii < I_PER; ++ii) {
-            const int i = piece * I_PER + ii;
+        for (int piece = 0; piece < 32 / PR; ++piece) {
+            if (lr / PR == piece) {
+                uint8_t *row = buf + (lr - piece * PR) * RS;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = ii * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    const int c = j * 32 + (lane & 31);
-                    const float y = acc[i][j][v] * out_scale;
-                    if (BF16_OUT)
-                        *reinterpret_cast<uint16_t *>(buf + r * RS + c * 2) = (uint16_t)f32_to_bf16(y);
-                    else
-                        *reinterpret_cast<float *>(buf + r * RS + c * 4) = y;
-                }
-        }
-        // read back whole rows: 16 bytes per lane, 1 KB per instruction
-        constexpr int LPR = 128 * ES / 16;            // lanes per row
-        constexpr int RPI = 64 / LPR;                 // rows per instruction
+                    for (int g = 0; g < 4; ++g) {
+                        const int c = j * 32 + 8 * g + 4 * (lane >> 5);
+                        const float y0 = acc[i][j][4 * g] * out_scale;
+                        const float y1 = acc[i][j][4 * g + 1] * out_scale;
+                        const float y2 = acc[i][j][4 * g + 2] * out_scale;
+                        const float y3 = acc[i][j][4 * g + 3] * out_scale;
+                        if (BF16_OUT)
+                            *reinterpret_cast<uint2 *>(row + c * 2) =
+                                make_uint2(f32_to_bf16(y0) | (f32_to_bf16(y1) << 16),
+                                           f32_to_bf16(y2) | (f32_to_bf16(y3) << 16));
+                        else
+                            *reinterpret_cast<float4 *>(row + c * 4) = make_float4(y0, y1, y2, y3);
+                    }
+            }
+            // a wave reads back only its own rows: LDS order suffices
 #pragma unroll
-        for (int q = 0; q < ROWS / RPI; ++q) {
-            const int r = q * RPI + lane / LPR;
-            const int cb = (lane % LPR) * 16;         // byte offset in the row
-            const uint4 val = *reinterpret_cast<const uint4 *>(buf + r * RS + cb);
-            const int64_t m = mw + piece * ROWS + r;
-            const int64_t n = nw + cb / ES;
-            if (m < m_end && n < n_end)
-                *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
+            for (int q = 0; q < PR / RPI; ++q) {
+                const int r = q * RPI + lane / LPR;
+                const int cb = (lane % LPR) * 16;
+                const uint4 val = *reinterpret_cast<const uint4 *>(buf + r * RS + cb);
+                const int64_t m = mw + i * 32 + piece * PR + r;
+                const int64_t n = nw + cb / ES;
+                if (m < m_end && n < n_end)
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
+            }
         }
     }
 }
@@ -314,7 +344,9 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
 
     const int64_t nslab = K / BK;
     // Three LDS stages: slab s lives in stage s % 3.  Slabs 0 and 1 are in
-    // flight before the loop; slab s + 2 is issued at the top of iteration s.
+    // flight before the loop; iteration s copies slab s + 2 during its first
+    // MFMA steps (past the end it repeats the last slab into a free stage,
+    // which keeps the loop body free of branches).
     issue<BT>(sm.st[0], pl, 0);
     if (nslab > 1) {
         issue<BT>(sm.st[1], pl, BK);
@@ -334,40 +366,49 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
     load_pairs(p0, sca, scb, 0, lane);
     expand_step(af, bf, c0, p0, 0);
 
-    // The 8 MFMA steps of one slab except the last; the expansion of step
-    // k + 1 runs under the MFMAs of step k.
-    auto slab_body = [&](const Stage &st) {
-        load_chunk(c1, st, 1, wm, wn, lane);
-        load_pairs(p1, sca, scb, 1, lane);
-        expand_step(an, bn, c0, p0, 1); mfma_step(acc, af, bf); interleave_1_4();
-        expand_step(af, bf, c0, p0, 2); mfma_step(acc, an, bn); interleave_1_4();
-        expand_step(an, bn, c0, p0, 3); mfma_step(acc, af, bf); interleave_1_4();
-        expand_step(af, bf, c1, p1, 0); mfma_step(acc, an, bn); interleave_1_4();
-        expand_step(an, bn, c1, p1, 1); mfma_step(acc, af, bf); interleave_1_4();
-        expand_step(af, bf, c1, p1, 2); mfma_step(acc, an, bn); interleave_1_4();
-        expand_step(an, bn, c1, p1, 3); mfma_step(acc, af, bf); interleave_1_4();
-    };
-
+    // Each iteration: the 8 MFMA steps of slab s, with the expansion of step
+    // k + 1 under the MFMAs of step k.  Stage cs is read only by the chunk and
+    // scale loads at its start, so the slab barrier can come after step 4:
+    // the last three steps then cover the next slab's LDS reads.
     for (int64_t s = 0; s + 1 < nslab; ++s) {
         const int ns = cs == 2 ? 0 : cs + 1;      // stage of slab s + 1
         const int n2 = ns == 2 ? 0 : ns + 1;      // stage of slab s + 2
-        if (s + 2 < nslab) issue<BT>(sm.st[n2], pl, (s + 2) * BK);
-        slab_body(sm.st[cs]);
-        // every read of stage cs is done: wait for slab s + 1 (slab s + 2 may
-        // stay in flight), then start slab s + 1 under the last 16 MFMAs
-        if (s + 2 < nslab) wait_vmcnt<kIssued>();
-        else wait_vmcnt<0>();
+        const int64_t kn = (s + 2 < nslab ? s + 2 : nslab - 1) * BK;
+        load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
+        load_pairs(p1, sca, scb, 1, lane);
+        expand_step(an, bn, c0, p0, 1); mfma_step(acc, af, bf);
+        issue_part<0, BT>(sm.st[n2], pl, kn); interleave_1_vmem_4<4>();
+        expand_step(af, bf, c0, p0, 2); mfma_step(acc, an, bn);
+        issue_part<1, BT>(sm.st[n2], pl, kn); interleave_1_vmem_4<4>();
+        expand_step(an, bn, c0, p0, 3); mfma_step(acc, af, bf);
+        issue_part<2, BT>(sm.st[n2], pl, kn); interleave_1_vmem_4<4>();
+        expand_step(af, bf, c1, p1, 0); mfma_step(acc, an, bn); interleave_1_4();
+        expand_step(an, bn, c1, p1, 1); mfma_step(acc, af, bf); interleave_1_4();
+        // slab s + 1 is complete once every wave has seen its own copies land
+        wait_vmcnt<kIssued>();
         __syncthreads();
         load_scales<BT>(sca, scb, sm.st[ns], wm, wn, lane);
         load_chunk(c0, sm.st[ns], 0, wm, wn, lane);
+        expand_step(af, bf, c1, p1, 2); mfma_step(acc, an, bn); interleave_1_ds_4();
+        expand_step(an, bn, c1, p1, 3); mfma_step(acc, af, bf); interleave_1_4();
         load_pairs(p0, sca, scb, 0, lane);
-        expand_step(af, bf, c0, p0, 0);
-        mfma_step(acc, an, bn);
-        interleave_8_then_1_8();
+        expand_step(af, bf, c0, p0, 0); mfma_step(acc, an, bn); interleave_1_4();
         cs = ns;
     }
-    slab_body(sm.st[cs]);
+    // the last slab
+    load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
+    load_pairs(p1, sca, scb, 1, lane);
+    expand_step(an, bn, c0, p0, 1); mfma_step(acc, af, bf); interleave_1_4();
+    expand_step(af, bf, c0, p0, 2); mfma_step(acc, an, bn); interleave_1_4();
+    expand_step(an, bn, c0, p0, 3); mfma_step(acc, af, bf); interleave_1_4();
+    expand_step(af, bf, c1, p1, 0); mfma_step(acc, an, bn); interleave_1_4();
+    expand_step(an, bn, c1, p1, 1); mfma_step(acc, af, bf); interleave_1_4();
+    expand_step(af, bf, c1, p1, 2); mfma_step(acc, an, bn); interleave_1_4();
+    expand_step(an, bn, c1, p1, 3); mfma_step(acc, af, bf); interleave_1_4();
     mfma_step(acc, an, bn);
+    // no copy in flight and every wave done with the ring: it becomes staging
+    wait_vmcnt<0>();
+    __syncthreads();
 
     epilogue<BF16_OUT>(sm, acc, m0, m_end, n0, n_end, out_scale, C, ldc, wm, wn, lane);
 }
