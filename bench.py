@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="skip the grouped-GEMM (MoE expert forward) measurement")
     ap.add_argument("--only", default=None,
                     help="time one op of the step in isolation (quant_x, quant_w, fprop, "
                          "quant_dy, requant_w, dgrad, wgrad), or 'copy' (a plain 512 MiB "
@@ -111,6 +113,66 @@ def cpu_baseline():
         "extrapolated_step_s": round(total, 2),
         "parts_s": {k: round(v, 2) for k, v in t.items()},
     }
+
+
+def moe_bench(torch, bbs, dev, reps):
+    """The MoE expert forward (grouped NVFP4 GEMMs) at its full shape: 65536
+    tokens x hidden 4096, 64 experts, top-8 Zipf(1.1) routing with 4 empty
+    experts; up-projection 4096 -> 1536 over the gathered routed rows, then
+    the up output is quantized (1x16, RTN) and projected 1536 -> 4096.  Each
+    expert's weight is its own NVFP4 tensor (16x16 scales, own s_dec)."""
+    from workloads import synth
+    T_, H_, F_, E_, K_ = 65536, 4096, 1536, 64, 8
+    d = synth.moe_forward(T_, H_, F_, E_, K_, with_weights=False)
+    rows = int(d["group_offsets"][-1])
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    ri = torch.from_numpy(d["row_index"]).to(dev)
+    off = torch.from_numpy(d["group_offsets"]).to(dev)
+    del d
+    ws = bbs.amax_workspace(dev)
+    N4 = bbs.NVFP4Tensor
+
+    def stacked(n, k, seed0):
+        st = N4.empty(E_ * n, k, tile2d=True, n_scales=E_, device=dev)
+        for g in range(E_):
+            w = torch.from_numpy(synth.normal(n, k, seed0 + g, 0.02).view(np.int16)).to(dev)
+            view = N4(st.codes[g * n:(g + 1) * n], st.scales[g * n // 16:(g + 1) * n // 16],
+                      st.s_dec[g:g + 1], n, k, True)
+            bbs.nvfp4_quantize(w, view, tile2d=True, amax_ws=ws)
+        return st
+
+    w_up = stacked(F_, H_, 503)
+    w_dn = stacked(H_, F_, 503 + E_)
+    xq = N4.empty(T_, H_, device=dev)
+    bbs.nvfp4_quantize(x, xq, amax_ws=ws)
+    h = torch.empty((rows, F_), dtype=torch.int16, device=dev)
+    hq = N4.empty(rows, F_, device=dev)
+    y = torch.empty((rows, H_), dtype=torch.int16, device=dev)
+    ops = {
+        "moe_up": lambda: bbs.grouped_nvfp4_gemm(xq, ri, off, E_, rows, w_up, F_, h, bbs.OUT_BF16),
+        "moe_quant_h": lambda: bbs.nvfp4_quantize(h, hq, amax_ws=ws),
+        "moe_down": lambda: bbs.grouped_nvfp4_gemm(hq, None, off, E_, rows, w_dn, H_, y,
+                                                   bbs.OUT_BF16),
+    }
+    out = {}
+    for name, f in ops.items():
+        f()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(reps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        ms = s0.elapsed_time(s1) / reps
+        e = {"ms": round(ms, 4)}
+        if name != "moe_quant_h":
+            tf = 2.0 * rows * F_ * H_ / (ms * 1e-3) / 1e12
+            e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        out[name] = e
+    out["routed_rows"] = rows
+    out["flop_per_projection"] = 2.0 * rows * F_ * H_
+    return out
 
 
 def main():
@@ -264,6 +326,13 @@ def main():
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
         "wall_s_timed": round(wall_s, 3),
     }
+    if not args.no_moe:
+        del x, w, dy, xq, xc, wq, gc, gm, wt, y, dx, dw
+        torch.cuda.empty_cache()
+        print("[bench] MoE grouped GEMMs (65536 tokens, 64 experts, top-8)", file=sys.stderr,
+              flush=True)
+        out["moe"] = moe_bench(torch, bbs, dev, max(3, args.steps // 4))
+        print(f"[bench] moe: {json.dumps(out['moe'])}", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

@@ -210,3 +210,76 @@ def test_grouped_routed_medium(bbs):
     assert (sizes == 0).sum() >= 4
     y, ref = _grouped_case(bbs, 2048, 512, 192, 64, sizes, True, True, 8100, row_index)
     _check(y, ref, True, "grouped-routed")
+
+
+def _moe_operands(n_rows, k, experts, seed0):
+    """Stacked per-expert NVFP4 weights (16x16 scales, own s_dec each)."""
+    ws = [O.nvfp4_quantize(synth.normal(n_rows, k, seed0 + g, 0.02), tile2d=True)
+          for g in range(experts)]
+    B = O.NVFP4(np.concatenate([w.codes for w in ws]), np.concatenate([w.scales for w in ws]),
+                np.float32(0), experts * n_rows, k, True)
+    return ws, B, np.array([w.s_dec for w in ws], np.float32)
+
+
+def _moe_sampled_ref(A, a_rows, ws, offsets, rows, cols):
+    """FP64 reference of sampled outputs (rows, cols) of a grouped GEMM whose
+    routed row i reads A row a_rows[i] and expert g = the group holding i."""
+    g_of = np.searchsorted(offsets, rows, side="right") - 1
+    toks = np.unique(a_rows[rows])
+    sub = O.NVFP4(np.ascontiguousarray(A.codes[toks]), np.ascontiguousarray(A.scales[toks]),
+                  A.s_dec, len(toks), A.cols, False).dequant_f64()
+    pos = {t: i for i, t in enumerate(toks)}
+    ref = np.zeros(rows.size)
+    for g in np.unique(g_of):
+        Bg = ws[g].dequant_f64()
+        sel = np.nonzero(g_of == g)[0]
+        arows = sub[[pos[t] for t in a_rows[rows[sel]]]]
+        ref[sel] = np.einsum("ij,ij->i", arows, Bg[cols[sel]])
+    assert np.abs(ref).max() > 0
+    return ref
+
+
+def _moe_samples(offsets, n_cols, seed, n=2048):
+    rng = np.random.default_rng(seed)
+    total = int(offsets[-1])
+    firsts = [offsets[g] for g in range(len(offsets) - 1) if offsets[g + 1] > offsets[g]]
+    lasts = [offsets[g + 1] - 1 for g in range(len(offsets) - 1) if offsets[g + 1] > offsets[g]]
+    rows = np.concatenate([rng.integers(0, total, n), firsts, lasts]).astype(np.int64)
+    cols = rng.integers(0, n_cols, rows.size).astype(np.int64)
+    return rows, cols
+
+
+def test_moe_full_size_sampled(bbs):
+    """The MoE expert forward at its full shape (65536 tokens x hidden 4096,
+    64 experts, top-8 Zipf(1.1) routing with 4 empty experts): the gathered
+    up-projection 4096 -> 1536 and the down-projection 1536 -> 4096, in the
+    launch configuration the benchmark times, checked on sampled outputs."""
+    announce("MoE full size: grouped up 524288x1536x4096 (gather) + down 524288x4096x1536")
+    T, H, F, E = 65536, 4096, 1536, 64
+    d = synth.moe_forward(T, H, F, E, 8, with_weights=False)
+    ri, off = d["row_index"], d["group_offsets"]
+    R = int(off[-1])
+    assert R == T * 8 and int((np.diff(off) == 0).sum()) == 4
+    ox = O.nvfp4_quantize(d["x"])
+    del d
+    ws, B, sdec = _moe_operands(F, H, E, 503)
+    c = torch.empty((R, F), dtype=torch.int16, device=dev())
+    bbs.grouped_nvfp4_gemm(upload_nvfp4(ox, bbs), to_dev(ri), to_dev(off), E, R,
+                           upload_nvfp4(B, bbs, n_scales=sdec), F, c, bbs.OUT_BF16)
+    torch.cuda.synchronize()
+    rows, cols = _moe_samples(off, F, 11)
+    y = bf16_bits_to_f64(host(c[to_dev(rows), to_dev(cols)]).view(np.uint16))
+    del c
+    _check(y, _moe_sampled_ref(ox, ri, ws, off, rows, cols), True, "moe-up")
+    del ws, B
+    # down-projection: synthetic stand-in for the routed hidden rows
+    oh = O.nvfp4_quantize(synth.normal(R, F, 600, 1.0))
+    ws, B, sdec = _moe_operands(H, F, E, 503 + E)
+    c = torch.empty((R, H), dtype=torch.int16, device=dev())
+    bbs.grouped_nvfp4_gemm(upload_nvfp4(oh, bbs), None, to_dev(off), E, R,
+                           upload_nvfp4(B, bbs, n_scales=sdec), H, c, bbs.OUT_BF16)
+    torch.cuda.synchronize()
+    rows, cols = _moe_samples(off, H, 12)
+    y = bf16_bits_to_f64(host(c[to_dev(rows), to_dev(cols)]).view(np.uint16))
+    del c
+    _check(y, _moe_sampled_ref(oh, np.arange(R), ws, off, rows, cols), True, "moe-down")
