@@ -100,8 +100,14 @@ __device__ __forceinline__ i32x8 frag(const uint8_t *tile, int r, int g) {
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
+// The MFMAs of one slab.  The copies of the next slab into stage nx are
+// issued along the way, four 1 KB copies after each of the first four row
+// blocks' MFMAs (and the scale copies after the fourth): the wave never
+// waits on one long burst of copy issues, and the copies still have half a
+// slab of MFMAs to land in.
 __device__ __forceinline__ void compute(const Stage &st, f32x4 (&acc)[8][8], int wm, int wn,
-                                        int lane) {
+                                        int lane, Stage &nx, const Plan &pl, int64_t kn) {
+    const int w = threadIdx.x >> 6;
     const int g = lane >> 4, rl = lane & 15;
     i32x8 bf[8];
     int bsc[8];
@@ -130,6 +136,17 @@ __device__ __forceinline__ void compute(const Stage &st, f32x4 (&acc)[8][8], int
         for (int j = 0; j < 8; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
                                                                          bsc[j], 0, asc);
+        if (i < 4) {
+#pragma unroll
+            for (int q = 2 * i; q < 2 * i + 2; ++q) {
+                copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
+                copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
+            }
+        }
+        if (i == 3) {
+            copy_lds4(pl.sa_base + kn / 32 + pl.sa_off, nx.as + w * 64);
+            copy_lds4(pl.sb_base + kn / 32 + pl.sb_off, nx.bs + w * 64);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -165,8 +182,10 @@ __global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p)
     __syncthreads();
     const int64_t nslab = p.K / mx::BK;
     for (int64_t s = 0; s < nslab; ++s) {
-        if (s + 1 < nslab) mx::issue(sm.st[(s + 1) & 1], pl, (s + 1) * mx::BK);
-        mx::compute(sm.st[s & 1], acc, wm, wn, lane);
+        // slab s + 1 goes to the other stage (past the end the last slab is
+        // copied again into the stage nobody reads any more: no branch)
+        const int64_t kn = (s + 1 < nslab ? s + 1 : s) * mx::BK;
+        mx::compute(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, kn);
         __builtin_amdgcn_s_waitcnt(0x3F70);           // the next slab's copies have landed
         __syncthreads();
     }

@@ -260,6 +260,32 @@ __device__ __forceinline__ void interleave_1_ds_4() {
     }
 }
 
+// One MFMA step in four quarters, fenced from each other: quarter q expands
+// operand pair q of the next step (16 VALU), issues the 4 MFMAs of row block
+// q of this step (interleaved 1:4 with that expansion) and then copy(q), a
+// slab copy or nothing.  The fences keep each copy between MFMAs instead of
+// letting the scheduler gather them into one burst that stalls the wave.
+template <typename Copy>
+__device__ __forceinline__ void step_q(f32x16 (&acc)[4][4], const f16x8 (&af)[4],
+                                       const f16x8 (&bf)[4], f16x8 (&an)[4], f16x8 (&bn)[4],
+                                       const Chunk &c, const Pairs &p, int s, Copy copy) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        an[q] = expand8_f16(word(c.ca[q], s), p.pa[q][s >> 1]);
+        bn[q] = expand8_f16(word(c.cb[q], s), p.pb[q][s >> 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[q], acc[q][j], 0, 0, 0);
+        copy(q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // s_waitcnt vmcnt(n), other counters unconstrained.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -374,38 +400,52 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
         const int ns = cs == 2 ? 0 : cs + 1;      // stage of slab s + 1
         const int n2 = ns == 2 ? 0 : ns + 1;      // stage of slab s + 2
         const int64_t kn = (s + 2 < nslab ? s + 2 : nslab - 1) * BK;
-        load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
+        const Stage &cur = sm.st[cs];
+        Stage &dst = sm.st[n2];
+        auto none = [](int) {};
+        auto copy_a = [&](int q) {
+            copy_lds16(pl.a[q] + kn / 2, dst.a + (wave * 4 + q) * 1024);
+        };
+        auto copy_b = [&](int q) {
+            copy_lds16(pl.b[q] + kn / 2, dst.b + (wave * 4 + q) * 1024);
+        };
+        auto copy_s = [&](int q) {
+            if (q < 2) copy_lds4(pl.sa[q] + kn / 16, dst.as + (wave * 2 + q) * 256);
+            else if (!BT) copy_lds4(pl.sb[q - 2] + kn / 16, dst.bs + (wave * 2 + q - 2) * 256);
+            else if (q == 2) copy_lds4(pl.sb[0] + kn / 16, dst.bs);
+        };
+        load_chunk(c1, cur, 1, wm, wn, lane);
         load_pairs(p1, sca, scb, 1, lane);
-        expand_step(an, bn, c0, p0, 1); mfma_step(acc, af, bf);
-        issue_part<0, BT>(sm.st[n2], pl, kn); interleave_1_vmem_4<4>();
-        expand_step(af, bf, c0, p0, 2); mfma_step(acc, an, bn);
-        issue_part<1, BT>(sm.st[n2], pl, kn); interleave_1_vmem_4<4>();
-        expand_step(an, bn, c0, p0, 3); mfma_step(acc, af, bf);
-        issue_part<2, BT>(sm.st[n2], pl, kn); interleave_1_vmem_4<4>();
-        expand_step(af, bf, c1, p1, 0); mfma_step(acc, an, bn); interleave_1_4();
-        expand_step(an, bn, c1, p1, 1); mfma_step(acc, af, bf); interleave_1_4();
+        step_q(acc, af, bf, an, bn, c0, p0, 1, copy_a);
+        step_q(acc, an, bn, af, bf, c0, p0, 2, copy_b);
+        step_q(acc, af, bf, an, bn, c0, p0, 3, copy_s);
+        step_q(acc, an, bn, af, bf, c1, p1, 0, none);
+        step_q(acc, af, bf, an, bn, c1, p1, 1, none);
         // slab s + 1 is complete once every wave has seen its own copies land
         wait_vmcnt<kIssued>();
         __syncthreads();
         load_scales<BT>(sca, scb, sm.st[ns], wm, wn, lane);
         load_chunk(c0, sm.st[ns], 0, wm, wn, lane);
-        expand_step(af, bf, c1, p1, 2); mfma_step(acc, an, bn); interleave_1_ds_4();
-        expand_step(an, bn, c1, p1, 3); mfma_step(acc, af, bf); interleave_1_4();
+        step_q(acc, an, bn, af, bf, c1, p1, 2, none);
+        step_q(acc, af, bf, an, bn, c1, p1, 3, none);
         load_pairs(p0, sca, scb, 0, lane);
-        expand_step(af, bf, c0, p0, 0); mfma_step(acc, an, bn); interleave_1_4();
+        step_q(acc, an, bn, af, bf, c0, p0, 0, none);
         cs = ns;
     }
     // the last slab
-    load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
-    load_pairs(p1, sca, scb, 1, lane);
-    expand_step(an, bn, c0, p0, 1); mfma_step(acc, af, bf); interleave_1_4();
-    expand_step(af, bf, c0, p0, 2); mfma_step(acc, an, bn); interleave_1_4();
-    expand_step(an, bn, c0, p0, 3); mfma_step(acc, af, bf); interleave_1_4();
-    expand_step(af, bf, c1, p1, 0); mfma_step(acc, an, bn); interleave_1_4();
-    expand_step(an, bn, c1, p1, 1); mfma_step(acc, af, bf); interleave_1_4();
-    expand_step(af, bf, c1, p1, 2); mfma_step(acc, an, bn); interleave_1_4();
-    expand_step(an, bn, c1, p1, 3); mfma_step(acc, af, bf); interleave_1_4();
-    mfma_step(acc, an, bn);
+    {
+        auto none = [](int) {};
+        load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
+        load_pairs(p1, sca, scb, 1, lane);
+        step_q(acc, af, bf, an, bn, c0, p0, 1, none);
+        step_q(acc, an, bn, af, bf, c0, p0, 2, none);
+        step_q(acc, af, bf, an, bn, c0, p0, 3, none);
+        step_q(acc, an, bn, af, bf, c1, p1, 0, none);
+        step_q(acc, af, bf, an, bn, c1, p1, 1, none);
+        step_q(acc, an, bn, af, bf, c1, p1, 2, none);
+        step_q(acc, af, bf, an, bn, c1, p1, 3, none);
+        mfma_step(acc, an, bn);
+    }
     // no copy in flight and every wave done with the ring: it becomes staging
     wait_vmcnt<0>();
     __syncthreads();
