@@ -59,8 +59,9 @@ def parse():
                     help="skip the grouped-GEMM (MoE expert forward) measurement")
     ap.add_argument("--only", default=None,
                     help="time one op of the step in isolation (quant_x, quant_w, fprop, "
-                         "quant_dy, requant_w, dgrad, wgrad), or 'copy' (a plain 512 MiB "
-                         "device copy); used for counter runs")
+                         "quant_dy, requant_w, dgrad, wgrad), 'moe' (the grouped-GEMM "
+                         "expert forward alone) or 'copy' (a plain 512 MiB device copy); used "
+                         "for counter and trace runs")
     return ap.parse_args()
 
 
@@ -194,6 +195,10 @@ def main():
         return
     import bit_block_scaled_amd as bbs
     from workloads import synth
+    if args.only == "moe":
+        res = moe_bench(torch, bbs, dev, max(3, args.steps // 4))
+        print(json.dumps({"only": "moe", **res}), flush=True)
+        return
 
     fw = synth.dense_forward(M, K, N)
     bw = synth.backward(M, N)

@@ -98,11 +98,17 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
     __shared__ float red[2][kQT / 64];
     const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
     float m = 0.0f, mr = 0.0f;
-    for (int64_t tile = blockIdx.x; tile < T; tile += gridDim.x) {
-        const Piece q = piece_of(tile, R, C);
-        uint4 v[16];
-        load_piece(x, R, C, ld, q, v);
-        if (!q.in) continue;
+    // The next tile's piece is loaded while this one is reduced.
+    int64_t tile = blockIdx.x;
+    Piece q = piece_of(tile, R, C);
+    uint4 v[16];
+    if (tile < T) load_piece(x, R, C, ld, q, v);
+    while (tile < T) {
+        const int64_t next = tile + gridDim.x;
+        const Piece qn = piece_of(next < T ? next : tile, R, C);
+        uint4 vn[16];
+        if (next < T) load_piece(x, R, C, ld, qn, vn);
+        if (q.in) {
         if (PLAIN) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -120,6 +126,11 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
                 for (int r = 0; r < 16; ++r) mr = fmaxf(mr, fabsf(y[r]));
             }
         }
+        }
+        tile = next;
+        q = qn;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = vn[i];
     }
     // The transform's final multiply by 1/4 is monotonic, so the maximum of
     // the scaled values is the scaled maximum (bit for bit).
