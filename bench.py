@@ -33,6 +33,23 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
 COPY_BYTES = 1 << 29                            # counter calibration copy (512 MiB)
 
+# HBM bytes per launch of the fprop GEMM, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
+# (profiles/fprop_gemm_8192x14336x4096_counters.md), valid only for the kernel
+# sources they were taken on: reported as null once those sources change.
+FPROP_TRAFFIC = {"bytes": 673631599, "sources_sha256_16": "21248190218e484e"}
+FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
+                 "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
+
+
+def fprop_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FPROP_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return FPROP_TRAFFIC["bytes"] if h.hexdigest()[:16] == FPROP_TRAFFIC["sources_sha256_16"] else None
+
 
 def nvfp4_bytes(r, c):
     return r * c // 2 + r * c // 16
@@ -326,7 +343,8 @@ def main():
         "kernels": kernels,
         "roofline": {"bound": "mfma", "achieved": round(fprop_tf, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fprop_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "nvfp4_gemm_kernel (fprop)",
+                     "traffic": fprop_traffic(), "traffic_unit": "bytes per launch",
+                     "kernel": "nvfp4_gemm_big_kernel<true> (fprop, 8192x14336x4096, BF16 out)",
                      "peak_fp4": PEAK_FP4_TFLOPS,
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
         "wall_s_timed": round(wall_s, 3),
