@@ -355,6 +355,106 @@ void orc_nvfp4_dequant_f32(const uint8_t *codes, const uint8_t *scales, float s_
 }
 
 /* The same values in FP64 (code x scale x s_dec is exact in FP64). */
+/* ------------------------------------------------------------------------ */
+/* Activation copy with a per-token outer scale and Four Over Six            */
+/* ([VZ] sec 11, the article's smaller choices; [TML] recipe details)        */
+/* ------------------------------------------------------------------------ */
+
+/* Block scale that puts the block's largest magnitude on `top` (6 is the
+ * standard choice, 4 the alternative of Four Over Six): E4M3 of
+ * (amax_b / top) * s_enc, round half to even, saturating at 448, never
+ * below code 1 (as orc_block_scale_code). */
+static uint32_t orc_block_scale_code_top(float amax_b, float s_enc, float top)
+{
+    float t = (amax_b / top) * s_enc;
+    float g = orc_round(t, ORC_E4M3, ORC_RTN, 0.0f);
+    uint32_t code = orc_e4m3_code(g);
+    if (code == 0u) code = 1u;
+    return code;
+}
+
+/* Encode one block of 16 with block scale code sc (round to nearest):
+ * nibbles to q[16]; returns the block's squared error against x, in FP32,
+ * with d = x - (g * S) * s_dec, e = d * d, summed in order over elements
+ * 0..7 and over 8..15, then low + high (the order is part of the reading:
+ * the decision between two encodings is taken on this FP32 value). */
+static float orc_encode_block_err(const float *x, float s_dec, uint32_t sc, uint32_t q[16])
+{
+    const float S = (float)orc_e4m3_value(sc);
+    const float s_enc_b = 1.0f / (S * s_dec);
+    float half[2] = {0.0f, 0.0f};
+    for (int i = 0; i < 16; ++i) {
+        float g = orc_round(x[i] * s_enc_b, ORC_E2M1, ORC_RTN, 0.0f);
+        q[i] = orc_e2m1_code(g);
+        volatile float deq = (g * S) * s_dec;     /* g * S is exact */
+        volatile float d = x[i] - deq;
+        volatile float e = d * d;
+        half[i / 8] = half[i / 8] + e;
+    }
+    return half[0] + half[1];
+}
+
+/* One row-wise NVFP4 copy of src[R][C] (1x16 blocks, round to nearest) with
+ *   per_token != 0: outer scale per row, s_enc_i = 2688 / amax(row i)
+ *                   (1 for an all-zero row), s_dec[i] = 1 / s_enc_i;
+ *   per_token == 0: one tensor scale, s_dec[0];
+ *   four_six != 0 : each block keeps whichever of its top-6 and top-4
+ *                   encodings has the smaller squared error (top-6 on ties);
+ *                   the chosen scale is the block's stored E4M3 scale.
+ * s_dec receives R values (per_token) or 1. */
+void orc_nvfp4_quantize_act(const uint16_t *src, int64_t R, int64_t C, int64_t ld,
+                            int per_token, int four_six, uint8_t *codes, uint8_t *scales,
+                            float *s_dec)
+{
+    float *x = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    orc_bf16_to_f32(src, R, C, ld, x);
+    float s_enc_t = orc_tensor_s_enc(orc_amax(x, R * C));
+    if (!per_token) s_dec[0] = 1.0f / s_enc_t;
+    const int64_t nb = C / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i) {
+        const float *xr = &x[i * C];
+        const float s_enc = per_token ? orc_tensor_s_enc(orc_amax(xr, C)) : s_enc_t;
+        const float sd = 1.0f / s_enc;
+        if (per_token) s_dec[i] = sd;
+        for (int64_t kb = 0; kb < nb; ++kb) {
+            const float *xb = &xr[kb * 16];
+            const float amax_b = orc_amax(xb, 16);
+            uint32_t q6[16], q4[16];
+            const uint32_t sc6 = orc_block_scale_code_top(amax_b, s_enc, 6.0f);
+            const float e6 = orc_encode_block_err(xb, sd, sc6, q6);
+            uint32_t sc = sc6, *q = q6;
+            if (four_six) {
+                const uint32_t sc4 = orc_block_scale_code_top(amax_b, s_enc, 4.0f);
+                const float e4 = orc_encode_block_err(xb, sd, sc4, q4);
+                if (e4 < e6) {
+                    sc = sc4;
+                    q = q4;
+                }
+            }
+            scales[i * nb + kb] = (uint8_t)sc;
+            for (int j = 0; j < 16; j += 2)
+                codes[i * (C / 2) + kb * 8 + j / 2] = (uint8_t)(q[j] | (q[j + 1] << 4));
+        }
+    }
+    free(x);
+}
+
+/* Exact dequantization of a 1x16 NVFP4 copy whose rows carry their own
+ * decode scale s_dec[i]: (code * scale) * s_dec[i] in FP64. */
+void orc_nvfp4_dequant_rows_f64(const uint8_t *codes, const uint8_t *scales, const float *s_dec,
+                                int64_t R, int64_t C, double *out)
+{
+    const int64_t nb = C / 16;
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j) {
+            uint32_t byte = codes[i * (C / 2) + j / 2];
+            uint32_t c = (j & 1) ? (byte >> 4) : (byte & 0xFu);
+            out[i * C + j] = orc_e2m1_value(c) * orc_e4m3_value(scales[i * nb + j / 16]) *
+                             (double)s_dec[i];
+        }
+}
+
 void orc_nvfp4_dequant_f64(const uint8_t *codes, const uint8_t *scales, float s_dec,
                            int64_t R, int64_t C, int tile2d, double *out)
 {

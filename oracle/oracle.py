@@ -68,6 +68,8 @@ def lib():
             "orc_rht16_n": (None, [f32p, i64, u32]),
             "orc_e8m0_k_n": (None, [f32p, i64, i32p]),
             "orc_amax": (f32, [f32p, i64]),
+            "orc_nvfp4_quantize_act": (None, [u16p, i64, i64, i64, i32, i32, u8p, u8p, f32p]),
+            "orc_nvfp4_dequant_rows_f64": (None, [u8p, u8p, f32p, i64, i64, f64p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -189,6 +191,24 @@ class NVFP4:
         return out
 
 
+class NVFP4Rows(NVFP4):
+    """A 1x16 NVFP4 copy whose rows carry their own decode scale s_dec[i]
+    (per-token outer scale)."""
+
+    def __init__(self, codes, scales, s_dec_rows, rows, cols):
+        super().__init__(codes, scales, 0.0, rows, cols, False)
+        self.s_dec = np.ascontiguousarray(s_dec_rows, np.float32)
+
+    def dequant_f64(self) -> np.ndarray:
+        out = np.empty((self.rows, self.cols), np.float64)
+        lib().orc_nvfp4_dequant_rows_f64(self.codes, self.scales, self.s_dec, self.rows,
+                                         self.cols, out)
+        return out
+
+    def dequant_f32(self) -> np.ndarray:
+        raise NotImplementedError("per-row copies dequantize in FP64 only")
+
+
 class MXFP8:
     """One MXFP8 copy: E4M3 codes [r][c], E8M0 scales [r][c/32]."""
 
@@ -219,6 +239,22 @@ def nvfp4_quantize(x_bf16: np.ndarray, transpose=False, tile2d=False, rht=False,
     s_dec = lib().orc_nvfp4_quantize(x, R, Cc, Cc, int(transpose), int(tile2d), int(rht),
                                      signs, mode, seed, stream, codes, scales)
     return NVFP4(codes, scales, s_dec, r, c, tile2d)
+
+
+def nvfp4_quantize_act(x_bf16: np.ndarray, per_token=True, four_six=True):
+    """Row-wise 1x16 NVFP4 copy of an activation matrix, round to nearest,
+    with a per-token outer scale (per_token) and / or Four Over Six block
+    scales (four_six).  Returns NVFP4Rows when per_token, else NVFP4."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    R, Cc = x.shape
+    codes = np.zeros((R, Cc // 2), np.uint8)
+    scales = np.zeros((R, Cc // 16), np.uint8)
+    s_dec = np.zeros(R if per_token else 1, np.float32)
+    lib().orc_nvfp4_quantize_act(x, R, Cc, Cc, int(per_token), int(four_six), codes, scales,
+                                 s_dec)
+    if per_token:
+        return NVFP4Rows(codes, scales, s_dec, R, Cc)
+    return NVFP4(codes, scales, s_dec[0], R, Cc, False)
 
 
 def nvfp4_encode_f32(x: np.ndarray, s_enc: float, tile2d=False, mode=RTN, seed=0,
