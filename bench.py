@@ -317,6 +317,32 @@ def main():
         kernels[name] = e
     print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
+    # Activation copy of X with a per-token outer scale and Four Over Six
+    # (the first NEXT row; not part of the step) and the fprop GEMM over it.
+    xa = T.empty(M, K, device=dev, sdec_per_row=True)
+    extra = {
+        "quant_x_act": lambda: bbs.nvfp4_quantize(x, xa, row_per_token=True, row_four_six=True),
+        "fprop_act": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, xa, wq, y, bbs.OUT_BF16),
+    }
+    act = {}
+    for name, f in extra.items():
+        f()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        t_ms = s0.elapsed_time(s1) / args.steps
+        e = {"ms": round(t_ms, 4)}
+        if name == "quant_x_act":
+            b = 2 * M * K + nvfp4_bytes(M, K) + 4 * M
+            e.update({"GB/s": round(b / (t_ms * 1e-3) / 1e9, 1), "bytes": b})
+        else:
+            e["TFLOP/s"] = round(GEMM_FLOP / (t_ms * 1e-3) / 1e12, 1)
+        act[name] = e
+    print(f"[bench] per-token + 4/6 activation path: {json.dumps(act)}", file=sys.stderr, flush=True)
+
     fprop_ms = per["fprop"]
     fprop_tf = GEMM_FLOP / (fprop_ms * 1e-3) / 1e12
     qbytes = ab["quant_x"] + ab["quant_w"]
@@ -347,6 +373,7 @@ def main():
                      "kernel": "nvfp4_gemm_big_kernel<true> (fprop, 8192x14336x4096, BF16 out)",
                      "peak_fp4": PEAK_FP4_TFLOPS,
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
+        "activation_per_token_4over6": act,
         "wall_s_timed": round(wall_s, 3),
     }
     if not args.no_moe:

@@ -23,7 +23,8 @@ AMAX_WS_FLOATS = 4096
 
 class Fp4Desc(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("s_dec", C.c_void_p),
-                ("rows", C.c_int64), ("cols", C.c_int64), ("tile2d", C.c_int32)]
+                ("rows", C.c_int64), ("cols", C.c_int64), ("tile2d", C.c_int32),
+                ("sdec_per_row", C.c_int32)]
 
 
 class Mx8Desc(C.Structure):
@@ -41,7 +42,8 @@ class QuantArgs(C.Structure):
                 ("col", C.POINTER(Fp4Desc)), ("col_round", C.c_int32), ("col_rng", Rng),
                 ("col_rht", C.c_int32), ("rht_signs", C.c_uint32),
                 ("row_mx8", C.POINTER(Mx8Desc)), ("mx8_round", C.c_int32), ("mx8_rng", Rng),
-                ("tile2d", C.c_int32), ("amax_ws", C.c_void_p)]
+                ("tile2d", C.c_int32), ("amax_ws", C.c_void_p),
+                ("row_per_token", C.c_int32), ("row_four_six", C.c_int32)]
 
 
 class BbsError(RuntimeError):
@@ -92,23 +94,26 @@ def _stream(stream):
 # ---------------------------------------------------------------------------
 
 class NVFP4Tensor:
-    """codes [rows, cols/2] u8, scales [rows(/16), cols/16] u8, s_dec [n] f32."""
+    """codes [rows, cols/2] u8, scales [rows(/16), cols/16] u8, s_dec [n] f32
+    (n = 1, G stacked experts, or rows when sdec_per_row)."""
 
-    def __init__(self, codes, scales, s_dec, rows, cols, tile2d):
+    def __init__(self, codes, scales, s_dec, rows, cols, tile2d, sdec_per_row=False):
         self.codes, self.scales, self.s_dec = codes, scales, s_dec
         self.rows, self.cols, self.tile2d = rows, cols, int(tile2d)
+        self.sdec_per_row = int(sdec_per_row)
 
     @staticmethod
-    def empty(rows, cols, tile2d=False, n_scales=1, device="cuda"):
+    def empty(rows, cols, tile2d=False, n_scales=1, device="cuda", sdec_per_row=False):
         srows = rows // 16 if tile2d else rows
+        n = rows if sdec_per_row else n_scales
         return NVFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
                            torch.empty((srows, cols // 16), dtype=torch.uint8, device=device),
-                           torch.empty((n_scales,), dtype=torch.float32, device=device),
-                           rows, cols, tile2d)
+                           torch.empty((n,), dtype=torch.float32, device=device),
+                           rows, cols, tile2d, sdec_per_row)
 
     def desc(self):
         return Fp4Desc(_ptr(self.codes), _ptr(self.scales), _ptr(self.s_dec), self.rows,
-                       self.cols, self.tile2d)
+                       self.cols, self.tile2d, self.sdec_per_row)
 
 
 class MXFP8Tensor:
@@ -137,9 +142,12 @@ def amax_workspace(device="cuda"):
 
 def nvfp4_quantize(x, row=None, col=None, row_mx8=None, *, row_round=RTN, row_rng=(0, 0),
                    col_round=RTN, col_rng=(0, 0), col_rht=False, rht_signs=0, mx8_round=RTN,
-                   mx8_rng=(0, 0), tile2d=False, amax_ws=None, stream=None):
+                   mx8_rng=(0, 0), tile2d=False, amax_ws=None, row_per_token=False,
+                   row_four_six=False, stream=None):
     """x: BF16 bit patterns as a [rows, cols] int16/uint16/bfloat16 device tensor
-    (row stride x.stride(0)).  row / col: NVFP4Tensor outputs; row_mx8: MXFP8Tensor."""
+    (row stride x.stride(0)).  row / col: NVFP4Tensor outputs; row_mx8: MXFP8Tensor.
+    row_per_token / row_four_six: activation options of the row copy (a
+    per-token row copy needs NVFP4Tensor.empty(..., sdec_per_row=True))."""
     rd = row.desc() if row is not None else None
     cd = col.desc() if col is not None else None
     md = row_mx8.desc() if row_mx8 is not None else None
@@ -150,7 +158,7 @@ def nvfp4_quantize(x, row=None, col=None, row_mx8=None, *, row_round=RTN, row_rn
                   C.pointer(cd) if cd else None, col_round, Rng(*col_rng),
                   int(col_rht), rht_signs,
                   C.pointer(md) if md else None, mx8_round, Rng(*mx8_rng),
-                  int(tile2d), _ptr(amax_ws))
+                  int(tile2d), _ptr(amax_ws), int(row_per_token), int(row_four_six))
     _check(lib.nvfp4_quantize(C.byref(a), _stream(stream)))
 
 

@@ -37,6 +37,10 @@ int check_fp4(const bbs_fp4 *d, const char *name, bool need_sdec) {
                     (long long)d->rows, (long long)d->cols);
     if (!aligned(d->codes, 16)) return fail(BBS_EINVAL, "%s: codes not 16-byte aligned", name);
     if (d->tile2d != 0 && d->tile2d != 1) return fail(BBS_EINVAL, "%s: tile2d must be 0 or 1", name);
+    if (d->sdec_per_row != 0 && d->sdec_per_row != 1)
+        return fail(BBS_EINVAL, "%s: sdec_per_row must be 0 or 1", name);
+    if (d->sdec_per_row && d->tile2d)
+        return fail(BBS_EINVAL, "%s: a per-row decode scale needs 1x16 blocks", name);
     return BBS_OK;
 }
 
@@ -79,7 +83,13 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     if (a->ld < a->cols || a->ld % 8) return fail(BBS_EINVAL, "ld must be >= cols and a multiple of 8");
     if (!aligned(a->x, 16)) return fail(BBS_EINVAL, "x not 16-byte aligned");
     if (a->tile2d != 0 && a->tile2d != 1) return fail(BBS_EINVAL, "tile2d must be 0 or 1");
-    const bool need_amax = a->row || a->col;
+    if ((a->row_per_token != 0 && a->row_per_token != 1) ||
+        (a->row_four_six != 0 && a->row_four_six != 1))
+        return fail(BBS_EINVAL, "row_per_token / row_four_six must be 0 or 1");
+    const bool act = a->row_per_token || a->row_four_six;
+    if (act && (!a->row || a->col || a->row_mx8 || a->tile2d || a->row_round != BBS_RTN))
+        return fail(BBS_ENOTSUP, "per-token / Four Over Six apply to a lone 1x16 RTN row copy");
+    const bool need_amax = (a->row && !a->row_per_token) || a->col;
     if (need_amax && !a->amax_ws) return fail(BBS_EINVAL, "null amax workspace");
     int st;
     if (a->row) {
@@ -87,6 +97,8 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
         if (a->row->rows != a->rows || a->row->cols != a->cols)
             return fail(BBS_EINVAL, "row copy must be rows x cols");
         if (a->row->tile2d != a->tile2d) return fail(BBS_EINVAL, "row copy tile2d mismatch");
+        if (a->row->sdec_per_row != a->row_per_token)
+            return fail(BBS_EINVAL, "row copy sdec_per_row must equal row_per_token");
         if (!round_ok(a->row_round)) return fail(BBS_EINVAL, "bad row_round");
     }
     if (a->col) {
@@ -94,6 +106,7 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
         if (a->col->rows != a->cols || a->col->cols != a->rows)
             return fail(BBS_EINVAL, "col copy must be cols x rows");
         if (a->col->tile2d != a->tile2d) return fail(BBS_EINVAL, "col copy tile2d mismatch");
+        if (a->col->sdec_per_row) return fail(BBS_ENOTSUP, "col copy with a per-row decode scale");
         if (!round_ok(a->col_round)) return fail(BBS_EINVAL, "bad col_round");
         if (a->col_rht != 0 && a->col_rht != 1) return fail(BBS_EINVAL, "col_rht must be 0 or 1");
         if (a->col_rht && a->tile2d) return fail(BBS_ENOTSUP, "RHT on a 16x16-tiled copy");
@@ -112,6 +125,20 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     p.R = a->rows;
     p.C = a->cols;
     p.ld = a->ld;
+    if (act) {
+        if (!a->row_per_token) {
+            hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, true, false, 0,
+                                            a->amax_ws, a->amax_ws + bbs::kAmaxPartials,
+                                            &p.n_part, s);
+            if ((st = hip_status(e, "amax launch"))) return st;
+            p.part = a->amax_ws;
+        }
+        p.row_codes = a->row->codes;
+        p.row_scales = a->row->scales;
+        p.row_sdec = a->row->s_dec;
+        return hip_status(bbs::launch_quant_act(p, a->row_per_token != 0, a->row_four_six != 0, s),
+                          "activation quantize launch");
+    }
     const bool rht = a->col && a->col_rht;
     const bool plain = a->row || (a->col && !rht);
     if (plain || rht) {
@@ -161,6 +188,7 @@ int mxfp8_requantize_t(const bbs_fp4 *src, const bbs_mx8 *dst, int32_t round, bb
     if (dst->rows != src->cols || dst->cols != src->rows)
         return fail(BBS_EINVAL, "dst must be src.cols x src.rows");
     if (src->rows % 32) return fail(BBS_EINVAL, "src.rows must be a multiple of 32");
+    if (src->sdec_per_row) return fail(BBS_ENOTSUP, "requantize of a per-row-scaled copy");
     if (!round_ok(round)) return fail(BBS_EINVAL, "bad round");
     if (!aligned(src->codes, 8)) return fail(BBS_EINVAL, "src codes not 8-byte aligned");
     bbs::RequantParams p{};
@@ -192,13 +220,16 @@ int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dty
         if (a->cols != b->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
         if (ldc < b->rows) return fail(BBS_EINVAL, "ldc < N");
         bbs::GemmParams p{};
-        p.a = {a->codes, a->scales, a->s_dec, a->rows, a->tile2d};
-        p.b = {b->codes, b->scales, b->s_dec, b->rows, b->tile2d};
+        if (b->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
+        p.a = {a->codes, a->scales, a->s_dec, a->rows, a->tile2d, a->sdec_per_row};
+        p.b = {b->codes, b->scales, b->s_dec, b->rows, b->tile2d, 0};
         p.M = a->rows;
         p.N = b->rows;
         p.K = a->cols;
         p.c = C;
         p.ldc = ldc;
+        if (a->sdec_per_row && !bbs::big_ok(p, c_dtype == BBS_OUT_BF16))
+            return fail(BBS_ENOTSUP, "per-row A scale needs K %% 128 == 0 and aligned operands / C");
         return hip_status(bbs::launch_nvfp4_gemm(p, c_dtype == BBS_OUT_BF16, s), "gemm launch");
     }
     if (fmt == BBS_FMT_MXFP8) {
@@ -239,8 +270,9 @@ int grouped_nvfp4_gemm(const bbs_fp4 *A, const int32_t *row_index, const int64_t
     if (ldc < N) return fail(BBS_EINVAL, "ldc < N");
     if (c_dtype != BBS_OUT_F32 && c_dtype != BBS_OUT_BF16) return fail(BBS_EINVAL, "bad c_dtype");
     bbs::GemmParams p{};
-    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d};
-    p.b = {B->codes, B->scales, B->s_dec, N, B->tile2d};
+    if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
+    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
+    p.b = {B->codes, B->scales, B->s_dec, N, B->tile2d, 0};
     p.M = max_rows;
     p.N = N;
     p.K = A->cols;
@@ -251,6 +283,8 @@ int grouped_nvfp4_gemm(const bbs_fp4 *A, const int32_t *row_index, const int64_t
     p.G = G;
     p.max_rows = max_rows;
     p.a_src_rows = A->rows;
+    if (A->sdec_per_row && !bbs::big_ok(p, c_dtype == BBS_OUT_BF16))
+        return fail(BBS_ENOTSUP, "per-row A scale needs K %% 128 == 0 and aligned operands / C");
     return hip_status(bbs::launch_grouped_nvfp4_gemm(p, c_dtype == BBS_OUT_BF16,
                                                      reinterpret_cast<hipStream_t>(stream)),
                       "grouped gemm launch");

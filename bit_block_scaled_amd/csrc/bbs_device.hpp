@@ -149,9 +149,12 @@ __device__ __forceinline__ float tensor_s_enc(float amax) {
     return (s > 3.40282347e38f) ? 3.40282347e38f : s;
 }
 
-// Block scale code: E4M3(rne((amax_b / 6) * s_enc)), never below code 1.
-__device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_enc) {
-    const uint32_t c = e4m3_rne_code((amax_b / 6.0f) * s_enc);
+// Block scale code: E4M3(rne((amax_b / top) * s_enc)), never below code 1.
+// top = 6 puts the block's largest magnitude on the top of the E2M1 grid;
+// Four Over Six also tries top = 4.
+__device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_enc,
+                                                     float top = 6.0f) {
+    const uint32_t c = e4m3_rne_code((amax_b / top) * s_enc);
     return c ? c : 1u;
 }
 

@@ -53,6 +53,7 @@ struct Fp4View {
     const float *s_dec;
     int64_t rows;
     int tile2d;
+    int sdec_rows;      // s_dec holds one decode scale per row
 };
 
 struct GemmParams {
@@ -82,6 +83,12 @@ hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
                              bool tile2d, bool rht, hipStream_t s);
 hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s);
+// Row copy of an activation with a per-token outer scale and / or Four Over
+// Six (RTN, 1x16); without per_token, p.part holds the tensor amax partials.
+hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six, hipStream_t s);
+// The large-tile NVFP4 kernels apply (K % 128 == 0, aligned operands and C);
+// they are the ones that support a per-row A decode scale.
+bool big_ok(const GemmParams &p, bool bf16_out);
 hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);

@@ -348,7 +348,7 @@ hipError_t launch_grouped_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hip
 
 // The large-tile kernel needs K % 128 == 0, 8-byte aligned scale rows and
 // 16-byte aligned output rows (its epilogue stores 16-byte row segments).
-static bool big_ok(const GemmParams &p, bool bf16_out) {
+bool big_ok(const GemmParams &p, bool bf16_out) {
     auto al = [](const void *q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
     const int64_t es = bf16_out ? 2 : 4;
     return p.K % 128 == 0 && al(p.a.codes, 16) && al(p.b.codes, 16) && al(p.a.scales, 8) &&

@@ -301,10 +301,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every store instruction writes complete 256- or 512-byte row segments.
 // Rows m < m_end and columns n < n_end are written; N being a multiple of 16
 // keeps every 16-byte segment wholly in or out.
-template <bool BF16_OUT>
+template <bool BF16_OUT, typename ScaleFn>
 __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], int64_t m0,
                                          int64_t m_end, int64_t n0, int64_t n_end,
-                                         float out_scale, void *C, int64_t ldc, int wm, int wn,
+                                         ScaleFn scale_of, void *C, int64_t ldc, int wm, int wn,
                                          int lane) {
     constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
     constexpr int RS = 128 * ES + 16;                 // staging row stride
@@ -316,6 +316,9 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     const int lr = lane & 31;                          // the lane's row in a 32-row block
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        // output scale of the lane's row: s_dec,A (of that row) * s_dec,B
+        const int64_t mr = mw + i * 32 + lr;
+        const float out_scale = scale_of(mr < m_end ? mr : m_end - 1);
 #pragma unroll
         for (int piece = 0; piece < 32 / PR; ++piece) {
             if (lr / PR == piece) {
@@ -352,10 +355,10 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     }
 }
 
-template <bool BF16_OUT, bool BT, typename RowMap>
+template <bool BF16_OUT, bool BT, typename RowMap, typename ScaleFn>
 __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &B, int64_t K,
                                      int64_t m0, int64_t m_end, int64_t n0, int64_t n_end,
-                                     RowMap a_row, float out_scale, void *C, int64_t ldc) {
+                                     RowMap a_row, ScaleFn scale_of, void *C, int64_t ldc) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const Plan pl = make_plan(A, B, K, m0, m_end, n0, n_end, a_row);
@@ -450,7 +453,7 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
     wait_vmcnt<0>();
     __syncthreads();
 
-    epilogue<BF16_OUT>(sm, acc, m0, m_end, n0, n_end, out_scale, C, ldc, wm, wn, lane);
+    epilogue<BF16_OUT>(sm, acc, m0, m_end, n0, n_end, scale_of, C, ldc, wm, wn, lane);
 }
 
 }  // namespace big
@@ -470,14 +473,23 @@ __global__ __launch_bounds__(big::NT) void nvfp4_gemm_big_kernel(GemmParams p) {
     const int64_t g = tid / gsize, in = tid - g * gsize;
     const int64_t gm = (tm - g * big::GROUP_M) < big::GROUP_M ? (tm - g * big::GROUP_M) : big::GROUP_M;
     const int64_t mt = g * big::GROUP_M + in % gm, nt = in / gm;
-    const float out_scale = p.a.s_dec[0] * p.b.s_dec[0];
     auto ident = [](int64_t r) { return r; };
-    if (p.b.tile2d)
-        big::tile<BF16_OUT, true>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N, ident,
-                                  out_scale, p.c, p.ldc);
-    else
-        big::tile<BF16_OUT, false>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N, ident,
-                                   out_scale, p.c, p.ldc);
+    const float sb = p.b.s_dec[0];
+    auto run = [&](auto scale_of) {
+        if (p.b.tile2d)
+            big::tile<BF16_OUT, true>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
+                                      ident, scale_of, p.c, p.ldc);
+        else
+            big::tile<BF16_OUT, false>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
+                                       ident, scale_of, p.c, p.ldc);
+    };
+    if (p.a.sdec_rows) {
+        const float *sa = p.a.s_dec;
+        run([sa, sb](int64_t m) { return sa[m] * sb; });
+    } else {
+        const float out_scale = p.a.s_dec[0] * sb;
+        run([out_scale](int64_t) { return out_scale; });
+    }
 }
 
 constexpr int kMaxGroupsBig = 1024;
@@ -513,17 +525,32 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_big_kernel(GemmPar
         Fp4View B = p.b;
         B.codes = p.b.codes + (int64_t)g * p.N * (p.K / 2);
         B.scales = p.b.scales + (int64_t)g * (B.tile2d ? (p.N / 16) : p.N) * (p.K / 16);
-        const float out_scale = p.a.s_dec[0] * p.b.s_dec[g];
         const int32_t *ri = p.row_index;
         const int64_t src_rows = p.a_src_rows;
         auto gather = [ri, src_rows](int64_t r) -> int64_t {
             const int64_t s = ri ? (int64_t)ri[r] : r;
             return (s >= 0 && s < src_rows) ? s : -1;
         };
-        if (B.tile2d)
-            big::tile<BF16_OUT, true>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, out_scale, p.c, p.ldc);
-        else
-            big::tile<BF16_OUT, false>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, out_scale, p.c, p.ldc);
+        const float sb = p.b.s_dec[g];
+        auto run = [&](auto scale_of) {
+            if (B.tile2d)
+                big::tile<BF16_OUT, true>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
+                                          p.ldc);
+            else
+                big::tile<BF16_OUT, false>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
+                                           p.ldc);
+        };
+        if (p.a.sdec_rows) {
+            const float *sa = p.a.s_dec;
+            // the decode scale of the A row the output row was computed from
+            run([sa, sb, gather](int64_t m) {
+                const int64_t s = gather(m);
+                return sa[s < 0 ? 0 : s] * sb;
+            });
+        } else {
+            const float out_scale = p.a.s_dec[0] * sb;
+            run([out_scale](int64_t) { return out_scale; });
+        }
         __syncthreads();
     }
 }

@@ -372,6 +372,129 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Activation copy: per-token outer scale and / or Four Over Six
+// (4bit.vizuara.ai, section 11; End-to-End 4-Bit Training, recipe details).
+// One wave per row; in chunk k of 512 columns lane l holds columns
+// 512k + 8l .. 512k + 8l + 7, so a 1x16 block is two neighbouring lanes.
+// With a per-token scale the row amax comes first (the first 8 chunks stay
+// in registers; longer rows are read again).  Four Over Six encodes every
+// block with its top-6 and its top-4 scale and keeps the encoding with the
+// smaller squared error, computed in FP32 as the sum over the block's first
+// eight values (the even lane) plus the sum over its last eight (the odd
+// lane), each in element order; the top-6 encoding is kept on ties.
+// ---------------------------------------------------------------------------
+constexpr int kActChunks = 8;
+
+__device__ __forceinline__ void load_chunk8(const uint16_t *row, int64_t C, int64_t k, int lane,
+                                            uint4 &v) {
+    const int64_t c = k * 512 + lane * 8;
+    v = c < C ? *reinterpret_cast<const uint4 *>(row + c) : make_uint4(0, 0, 0, 0);
+}
+
+// Squared error of 8 values f against their E2M1 codes (packed nibbles)
+// dequantized as (code * S) * s_dec, summed in element order.
+__device__ __forceinline__ float half_err(const float f[8], uint32_t packed, float S,
+                                          float s_dec) {
+    const f32x2_t g[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 3)};
+    float e = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float d = f[j] - (g[j >> 1][j & 1] * S) * s_dec;    // code * S is exact
+        e = e + d * d;
+    }
+    return e;
+}
+
+template <bool FOUR_SIX>
+__device__ __forceinline__ void act_encode_chunk(const uint4 &v, float s_enc, float s_dec,
+                                                 int lane, uint32_t &packed, uint32_t &sc) {
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = elem(v, j);
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
+    a = max_lane_pair(a);
+    const uint32_t sc6 = block_scale_code(a, s_enc, 6.0f);
+    packed = e2m1_rne8(f, block_enc_scale(sc6, s_dec));
+    sc = sc6;
+    if (FOUR_SIX) {
+        const uint32_t sc4 = block_scale_code(a, s_enc, 4.0f);
+        const uint32_t p4 = e2m1_rne8(f, block_enc_scale(sc4, s_dec));
+        const float S6 = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sc6, 1.0f, 0);
+        const float S4 = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sc4, 1.0f, 0);
+        const float h6 = half_err(f, packed, S6, s_dec), h4 = half_err(f, p4, S4, s_dec);
+        // the partner lane's half (quad_perm [1,0,3,2]); low half + high half
+        const float o6 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(h6), 0xB1, 0xF, 0xF, false));
+        const float o4 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(h4), 0xB1, 0xF, 0xF, false));
+        const bool lo = (lane & 1) == 0;
+        const float e6 = lo ? h6 + o6 : o6 + h6;
+        const float e4 = lo ? h4 + o4 : o4 + h4;
+        if (e4 < e6) {
+            packed = p4;
+            sc = sc4;
+        }
+    }
+}
+
+template <bool PER_TOKEN, bool FOUR_SIX>
+__global__ __launch_bounds__(kQT) void quant_act_kernel(QuantParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = ((int64_t)blockIdx.x * kQT + threadIdx.x) >> 6;
+    float s_enc;
+    if (!PER_TOKEN) {
+        s_enc = tensor_s_enc(fold_partials(p.part, p.n_part));
+        if (blockIdx.x == 0 && threadIdx.x == 0) p.row_sdec[0] = 1.0f / s_enc;
+    }
+    if (r >= p.R) return;                             // whole waves leave together
+    const uint16_t *row = p.x + r * p.ld;
+    const int64_t nch = (p.C + 511) / 512;
+    uint4 v[kActChunks];
+#pragma unroll
+    for (int k = 0; k < kActChunks; ++k)
+        if (k < nch) load_chunk8(row, p.C, k, lane, v[k]);
+    if (PER_TOKEN) {
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kActChunks; ++k)
+            if (k < nch)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(v[k], j)));
+        for (int64_t k = kActChunks; k < nch; ++k) {
+            uint4 w;
+            load_chunk8(row, p.C, k, lane, w);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(w, j)));
+        }
+        s_enc = tensor_s_enc(wave_max(m));
+        if (lane == 0) p.row_sdec[r] = 1.0f / s_enc;
+    }
+    const float s_dec = 1.0f / s_enc;
+    uint8_t *codes = p.row_codes + r * (p.C / 2);
+    uint8_t *scales = p.row_scales + r * (p.C / 16);
+    auto emit = [&](const uint4 &w, int64_t k) {
+        uint32_t packed, sc;
+        act_encode_chunk<FOUR_SIX>(w, s_enc, s_dec, lane, packed, sc);
+        const int64_t c = k * 512 + lane * 8;
+        if (c < p.C) {
+            *reinterpret_cast<uint32_t *>(codes + c / 2) = packed;
+            if ((lane & 1) == 0) scales[c / 16] = (uint8_t)sc;
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kActChunks; ++k)
+        if (k < nch) emit(v[k], k);
+    for (int64_t k = kActChunks; k < nch; ++k) {
+        uint4 w;
+        load_chunk8(row, p.C, k, lane, w);
+        emit(w, k);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Requantize: NVFP4 [R x C] -> MXFP8 of the transpose [C x R].
 // A workgroup takes 128 source rows (a 32-row band per wave) x 512 source
 // columns (8 per lane), so each destination row's 128 bytes come from one
@@ -502,6 +625,19 @@ hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, b
         case 0b11110: launch_q<1, 1, 1, 1, 0>(p, grid, s); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six, hipStream_t s) {
+    const dim3 grid((unsigned)((p.R + kQT / 64 - 1) / (kQT / 64)));
+    if (per_token && four_six)
+        hipLaunchKernelGGL((quant_act_kernel<true, true>), grid, dim3(kQT), 0, s, p);
+    else if (per_token)
+        hipLaunchKernelGGL((quant_act_kernel<true, false>), grid, dim3(kQT), 0, s, p);
+    else if (four_six)
+        hipLaunchKernelGGL((quant_act_kernel<false, true>), grid, dim3(kQT), 0, s, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

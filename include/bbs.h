@@ -51,14 +51,17 @@ enum bbs_fmt { BBS_FMT_NVFP4 = 0, BBS_FMT_MXFP8 = 1 };
  * ("value = FP4 code x FP8 block scale x FP32 outer scale"; Pretraining LLMs
  * with NVFP4, "NVFP4 Format and Quantization Procedure", steps 1-5).
  * Blocks run along cols, the GEMM contraction dimension.  s_dec points to one
- * FP32 decode scale (G scales for the stacked weights of grouped_nvfp4_gemm).
+ * FP32 decode scale (G scales for the stacked weights of grouped_nvfp4_gemm),
+ * or, with sdec_per_row = 1, to one per row (an activation copy with a
+ * per-token outer scale, 4bit.vizuara.ai section 11; 1x16 blocks only).
  * codes must be 16-byte aligned; rows and cols must be multiples of 16. */
 typedef struct {
     uint8_t *codes;
     uint8_t *scales;
     float *s_dec;
     int64_t rows, cols;
-    int32_t tile2d; /* 0: 1x16 blocks, 1: 16x16 tiles */
+    int32_t tile2d;       /* 0: 1x16 blocks, 1: 16x16 tiles */
+    int32_t sdec_per_row; /* 0: s_dec per tensor (per expert), 1: s_dec[row] */
 } bbs_fp4;
 
 /* One MXFP8 tensor: value = E4M3(code) x 2^(scale-127), one scale per 32
@@ -72,10 +75,10 @@ typedef struct {
 /* Key of the stochastic-rounding draws: element idx of an output copy
  * (its row-major index in that copy's own layout) uses 16-bit lane idx % 8
  * of Philox4x32-10(counter = (idx/8 low, idx/8 high, stream, 0), key = seed),
- * as u = (lane + 1/2) / 65536, and rounds to floor(t + u) grid steps, t being
- * the magnitude in units of the local grid step (4bit.vizuara.ai, section 6:
- * "floor(t + rand)").  The same (seed, stream) reproduces the same bits for
- * any launch geometry. */
+ * as u = (lane + 1/2) / 65536, and rounds to floor(t + u) grid steps on the
+ * exact sum, t being the magnitude in units of the local grid step
+ * (4bit.vizuara.ai, section 6).  The same (seed, stream) reproduces the same
+ * bits for any launch geometry. */
 typedef struct {
     uint64_t seed;
     uint32_t stream;
@@ -105,6 +108,20 @@ typedef struct {
     int32_t tile2d; /* 1: 16x16 tile scales for row and col copies (col is then
                        the bit-identical transpose of row when both round RTN) */
     float *amax_ws; /* device workspace, >= BBS_AMAX_WS_FLOATS floats, not kept */
+
+    /* Activation options of the row copy (4bit.vizuara.ai, section 11;
+     * End-to-End 4-Bit Training, recipe details); both need row_round ==
+     * BBS_RTN, tile2d == 0 and no col / row_mx8 copy in the same call.
+     * row_per_token = 1: each row gets its own outer scale, s_enc_i = 2688 /
+     *   amax(row i), and row->s_dec receives rows values (row->sdec_per_row
+     *   must be 1); no tensor amax pass and no workspace are needed.
+     * row_four_six = 1: each block is encoded with the scale that puts its
+     *   largest magnitude on 6 and with the one that puts it on 4, and keeps
+     *   the encoding with the smaller squared error (FP32: first eight
+     *   values' sum plus last eight values' sum, each in element order; ties
+     *   keep the first). */
+    int32_t row_per_token;
+    int32_t row_four_six;
 } bbs_quant_args;
 
 /* NVFP4 quantizer (Pretraining LLMs with NVFP4, "NVFP4 Format and
@@ -138,7 +155,11 @@ int mxfp8_requantize_t(const bbs_fp4 *src, const bbs_mx8 *dst, int32_t round, bb
  *      sum over blocks of (E4M3_A * E4M3_B * sum of E2M1 products).
  *   fmt == BBS_FMT_MXFP8: A, B are const bbs_mx8 *; K % 32 == 0.
  * C is M x N with row stride ldc (>= N) elements of c_dtype (BBS_OUT_F32 or
- * BBS_OUT_BF16, round to nearest even).  Errors: BBS_EINVAL. */
+ * BBS_OUT_BF16, round to nearest even).  Output row i is scaled by
+ * s_dec,A[i] * s_dec,B when A has a decode scale per row (then K % 128 == 0
+ * and 16-byte aligned C, ldc * size % 16 == 0).
+ * Errors: BBS_EINVAL; BBS_ENOTSUP for a per-row B scale or a per-row A
+ * scale outside those conditions. */
 int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dtype,
                int64_t ldc, void *stream);
 
@@ -152,7 +173,8 @@ int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dty
  * empty groups are allowed.  max_rows bounds the routed rows C can hold
  * (rows beyond it are not computed).  B.rows == G * N, N % 16 == 0.
  * Tiles are scheduled on the device from group_offsets; the host never
- * reads them.  Errors: BBS_EINVAL. */
+ * reads them.  A per-row A decode scale is taken at A_row(i) (same
+ * conditions as nvfp4_gemm).  Errors: BBS_EINVAL, BBS_ENOTSUP. */
 int grouped_nvfp4_gemm(const bbs_fp4 *A, const int32_t *row_index,
                        const int64_t *group_offsets, int32_t G, int64_t max_rows,
                        const bbs_fp4 *B, int64_t N, void *C, int32_t c_dtype, int64_t ldc,

@@ -102,6 +102,47 @@ def test_error_paths_return_status(lib):
     assert L.bbs_strerror(bbs.BBS_EINVAL) == b"invalid argument"
 
 
+def test_activation_option_errors(lib):
+    """Per-token / Four Over Six: only on a lone 1x16 RTN row copy whose
+    descriptor carries per-row decode scales exactly when per-token."""
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    a = bbs.QuantArgs()
+    a.x, a.rows, a.cols, a.ld = 0x1000, 32, 64, 64
+    row = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 64, 0, 1)
+    a.row = C.pointer(row)
+    a.row_per_token = 2
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    a.row_per_token = 1
+    a.row_round = bbs.SR
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_ENOTSUP
+    a.row_round = bbs.RTN
+    col = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 64, 32, 0, 0)
+    a.col = C.pointer(col)
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_ENOTSUP
+    a.col = None
+    row.sdec_per_row = 0                      # per-token output needs per-row s_dec
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    row.sdec_per_row, row.tile2d = 1, 1       # per-row decode scales need 1x16 blocks
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    # Four Over Six with a tensor scale still needs the amax workspace
+    row.sdec_per_row, row.tile2d = 0, 0
+    a.row_per_token, a.row_four_six = 0, 1
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"workspace" in L.bbs_last_error()
+    # GEMM: a per-row B scale is not supported; a per-row A scale needs K % 128
+    A = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 64, 0, 1)
+    B = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 64, 0, 1)
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_ENOTSUP
+    B.sdec_per_row = 0
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_ENOTSUP
+    assert b"128" in L.bbs_last_error()
+    # requantize of a per-row-scaled copy is not supported
+    src = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 64, 32, 0, 1)
+    dst = bbs.Mx8Desc(0x1000, 0x2000, 32, 64)
+    assert L.mxfp8_requantize_t(C.byref(src), C.byref(dst), 1, bbs.Rng(0, 0), None) == bbs.BBS_ENOTSUP
+
+
 def test_binding_has_no_cpu_fallback():
     import bit_block_scaled_amd as bbs
     src = open(bbs.__file__).read()

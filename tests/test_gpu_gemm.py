@@ -283,3 +283,62 @@ def test_moe_full_size_sampled(bbs):
     y = bf16_bits_to_f64(host(c[to_dev(rows), to_dev(cols)]).view(np.uint16))
     del c
     _check(y, _moe_sampled_ref(oh, np.arange(R), ws, off, rows, cols), True, "moe-down")
+
+
+# ---------------------------------------------------------------------------
+# GEMMs over an activation copy with per-row (per-token) decode scales
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K,bf16", [(272, 400, 1024, True), (96, 144, 512, False)])
+def test_gemm_per_token_A(bbs, M, N, K, bf16):
+    announce(f"gemm per-token A {M}x{N}x{K} bf16={bf16}")
+    oa = O.nvfp4_quantize_act(synth.normal_with_outliers(M, K, 810), True, True)
+    ob = O.nvfp4_quantize(synth.normal(N, K, 811, 0.02), tile2d=True)
+    A = bbs.NVFP4Tensor(to_dev(oa.codes), to_dev(oa.scales), to_dev(oa.s_dec), M, K, False, True)
+    c = torch.empty((M, N), dtype=torch.int16 if bf16 else torch.float32, device=dev())
+    bbs.nvfp4_gemm(bbs.FMT_NVFP4, A, upload_nvfp4(ob, bbs), c, bbs.OUT_BF16 if bf16 else bbs.OUT_F32)
+    torch.cuda.synchronize()
+    y = host(c)
+    y = bf16_bits_to_f64(y.view(np.uint16)) if bf16 else y.astype(np.float64)
+    _check(y, O.gemm_f64(oa.dequant_f64(), ob.dequant_f64()), bf16, "per-token A")
+
+
+def test_full_dense_forward_per_token(bbs):
+    announce("dense forward 8192x14336x4096 with a per-token 4/6 X copy (sampled outputs)")
+    d = synth.dense_forward()
+    oa = O.nvfp4_quantize_act(d["x"], True, True)
+    ow = O.nvfp4_quantize(d["w"], tile2d=True)
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    A = bbs.NVFP4Tensor(to_dev(oa.codes), to_dev(oa.scales), to_dev(oa.s_dec), M, K, False, True)
+    c = torch.empty((M, N), dtype=torch.int16, device=dev())
+    bbs.nvfp4_gemm(bbs.FMT_NVFP4, A, upload_nvfp4(ow, bbs), c, bbs.OUT_BF16)
+    torch.cuda.synchronize()
+    y = bf16_bits_to_f64(host(c).view(np.uint16))
+    _sampled_check(y, oa.dequant_f64(), ow.dequant_f64(), True, "fprop per-token")
+
+
+def test_grouped_per_token_A(bbs):
+    """Gathered grouped GEMM whose A rows carry per-token decode scales: each
+    output row takes the scale of the token it was gathered from."""
+    announce("grouped, per-token A, gather, 6 experts")
+    rng = np.random.default_rng(820)
+    sizes = np.array([40, 0, 300, 7, 0, 129])
+    E, H, F, T = len(sizes), 512, 144, 256
+    off = np.zeros(E + 1, np.int64)
+    off[1:] = np.cumsum(sizes)
+    total = int(off[-1])
+    ri = rng.integers(0, T, total).astype(np.int32)
+    ox = O.nvfp4_quantize_act(synth.normal_with_outliers(T, H, 821), True, True)
+    ws, B, sdec = _moe_operands(F, H, E, 822)
+    A = bbs.NVFP4Tensor(to_dev(ox.codes), to_dev(ox.scales), to_dev(ox.s_dec), T, H, False, True)
+    c = torch.empty((total, F), dtype=torch.float32, device=dev())
+    bbs.grouped_nvfp4_gemm(A, to_dev(ri), to_dev(off), E, total,
+                           upload_nvfp4(B, bbs, n_scales=sdec), F, c, bbs.OUT_F32)
+    torch.cuda.synchronize()
+    A64 = ox.dequant_f64()
+    ref = np.zeros((total, F))
+    for g in range(E):
+        if off[g + 1] > off[g]:
+            ref[off[g]:off[g + 1]] = O.gemm_f64(A64[ri[off[g]:off[g + 1]]], ws[g].dequant_f64())
+    _check(host(c).astype(np.float64), ref, False, "grouped per-token")

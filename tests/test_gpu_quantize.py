@@ -244,3 +244,65 @@ def test_full_backward_quantize(bbs):
     bbs.mxfp8_requantize_t(src, dst, bbs.SR, (seeds["w_req"], 0))
     torch.cuda.synchronize()
     _same_mx8(dst, O.mxfp8_requantize_t(ow, mode=O.SR, seed=seeds["w_req"]), "W requant")
+
+
+# ---------------------------------------------------------------------------
+# Activation copy: per-token outer scale and / or Four Over Six
+# ---------------------------------------------------------------------------
+
+ACT_SHAPES = [(16, 16), (48, 80), (64, 1040), (256, 4096), (32, 8192 + 528)]
+
+
+def _gpu_quantize_act(bbs, x, per_token, four_six):
+    R, C = x.shape
+    q = bbs.NVFP4Tensor.empty(R, C, device=dev(), sdec_per_row=per_token)
+    bbs.nvfp4_quantize(to_dev(x), q, row_per_token=per_token, row_four_six=four_six)
+    torch.cuda.synchronize()
+    return q
+
+
+@pytest.mark.parametrize("shape", ACT_SHAPES)
+@pytest.mark.parametrize("per_token,four_six", [(True, True), (True, False), (False, True)])
+def test_activation_copy(bbs, shape, per_token, four_six):
+    R, C = shape
+    announce(f"activation copy {R}x{C} per_token={per_token} four_six={four_six}")
+    x = synth.normal_with_outliers(R, C, 700 + R + C)
+    g = _gpu_quantize_act(bbs, x, per_token, four_six)
+    o = O.nvfp4_quantize_act(x, per_token, four_six)
+    assert np.array_equal(host(g.scales), o.scales), "scales differ"
+    gc = host(g.codes)
+    if not np.array_equal(gc, o.codes):
+        bad = np.argwhere(gc != o.codes)
+        raise AssertionError(f"{len(bad)} code bytes differ, first at {bad[0].tolist()}")
+    sd = host(g.s_dec)
+    assert np.array_equal(sd, np.atleast_1d(o.s_dec)), "decode scales differ"
+
+
+def test_activation_copy_degenerate_rows(bbs):
+    """All-zero rows (s_dec 1), a row of one repeated value (the top-4 scale
+    saturates: ties keep the top-6 encoding) and a tiny-valued row."""
+    announce("activation copy with zero / constant / tiny rows")
+    x = synth.normal_with_outliers(32, 512, 91)
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    xf[3] = 0.0
+    xf[7] = 3.0
+    xf[11] *= np.float32(2.0 ** -60)
+    xb = synth.bf16_bits(xf)
+    for pt, fs in [(True, True), (False, True)]:
+        g = _gpu_quantize_act(bbs, xb, pt, fs)
+        o = O.nvfp4_quantize_act(xb, pt, fs)
+        assert np.array_equal(host(g.codes), o.codes)
+        assert np.array_equal(host(g.scales), o.scales)
+        assert np.array_equal(host(g.s_dec), np.atleast_1d(o.s_dec))
+
+
+def test_full_activation_copy(bbs):
+    """X of the dense forward (8192 x 4096) as the activation copy: per-token
+    outer scale + Four Over Six, in the configuration bench.py times."""
+    announce("full activation copy 8192x4096 per-token + 4/6")
+    x = synth.dense_forward()["x"]
+    g = _gpu_quantize_act(bbs, x, True, True)
+    o = O.nvfp4_quantize_act(x, True, True)
+    assert np.array_equal(host(g.scales), o.scales)
+    assert np.array_equal(host(g.codes), o.codes)
+    assert np.array_equal(host(g.s_dec), o.s_dec)
