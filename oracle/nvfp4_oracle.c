@@ -25,6 +25,10 @@
  *  Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
  *        Easy as 1, 2, 3", SC'11 (the generator is not on the pages; it is
  *        the counter-based generator both sides implement independently).
+ *  GELU: Hendrycks and Gimpel, "Gaussian Error Linear Units", tanh form; exp
+ *        by Cody-Waite range reduction and a Taylor polynomial (neither is on
+ *        the pages; both sides implement the same FP32 steps independently so
+ *        that the fused GELU + quantize of [VZ] section 13 is reproducible).
  *
  * Readings where the pages are silent or disagree are listed in the
  * design notes; the ones that change arithmetic are repeated inline below.
@@ -394,20 +398,87 @@ static float orc_encode_block_err(const float *x, float s_dec, uint32_t sc, uint
     return half[0] + half[1];
 }
 
+/* exp in FP32 by Cody-Waite range reduction and a Taylor polynomial
+ * (W. J. Cody and W. Waite, Software Manual for the Elementary Functions,
+ * 1980): k = rint(v * log2 e); r = (v - k * ln2_hi) - k * ln2_lo, with ln2
+ * split so that k * ln2_hi is exact; exp(v) = 2^k * P(r), P the degree-7
+ * Taylor polynomial of exp evaluated by Horner's rule.  Every step is one
+ * FP32 operation in this order; v >= 88.5 gives +inf and v <= -87 gives 0
+ * (so no result is subnormal). */
+float orc_exp_f32(float v)
+{
+    if (v >= 88.5f) return INFINITY;
+    if (v <= -87.0f) return 0.0f;
+    const float log2e = 1.44269502162933349609375f;
+    const float ln2_hi = 0.693145751953125f;           /* 0x3F317200 */
+    const float ln2_lo = 1.428606765330187045e-06f;    /* 0x35BFBE8E */
+    volatile float t = v * log2e;
+    const float k = rintf(t);
+    volatile float a = k * ln2_hi;
+    volatile float r = v - a;
+    volatile float b = k * ln2_lo;
+    r = r - b;
+    const float c[8] = {1.0f, 1.0f, 0.5f, 1.0f / 6.0f, 1.0f / 24.0f, 1.0f / 120.0f,
+                        1.0f / 720.0f, 1.0f / 5040.0f};
+    volatile float p = c[7];
+    for (int i = 6; i >= 0; --i) {
+        volatile float q = p * r;
+        p = q + c[i];
+    }
+    return ldexpf(p, (int)k);
+}
+
+/* GELU in its tanh form (Hendrycks and Gimpel, "Gaussian Error Linear Units",
+ * 2016): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
+ * tanh(u) = 1 - 2 / (exp(2u) + 1) and exp as orc_exp_f32; FP32 steps in the
+ * order written, no fused operations.  The fused GELU + quantize of the
+ * pages' kernel (4bit.vizuara.ai, section 13) leaves the GELU output in FP32
+ * and quantizes it directly. */
+float orc_gelu_f32(float x)
+{
+    const float c0 = 0.797884583473205566f;            /* sqrt(2/pi) in FP32 */
+    const float c1 = 0.044715f;
+    volatile float x2 = x * x;
+    volatile float x3 = x2 * x;
+    volatile float w = c1 * x3;
+    volatile float z = x + w;
+    volatile float u = c0 * z;
+    volatile float e = orc_exp_f32(2.0f * u);
+    volatile float den = e + 1.0f;
+    volatile float q = 2.0f / den;
+    volatile float th = 1.0f - q;
+    volatile float h = 0.5f * x;
+    volatile float g = 1.0f + th;
+    return h * g;
+}
+
+void orc_gelu_n(const float *x, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_gelu_f32(x[i]);
+}
+
+void orc_exp_n(const float *x, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_exp_f32(x[i]);
+}
+
 /* One row-wise NVFP4 copy of src[R][C] (1x16 blocks, round to nearest) with
  *   per_token != 0: outer scale per row, s_enc_i = 2688 / amax(row i)
  *                   (1 for an all-zero row), s_dec[i] = 1 / s_enc_i;
  *   per_token == 0: one tensor scale, s_dec[0];
  *   four_six != 0 : each block keeps whichever of its top-6 and top-4
  *                   encodings has the smaller squared error (top-6 on ties);
- *                   the chosen scale is the block's stored E4M3 scale.
+ *                   the chosen scale is the block's stored E4M3 scale;
+ *   gelu != 0     : the quantized values are orc_gelu_f32 of the inputs.
  * s_dec receives R values (per_token) or 1. */
 void orc_nvfp4_quantize_act(const uint16_t *src, int64_t R, int64_t C, int64_t ld,
-                            int per_token, int four_six, uint8_t *codes, uint8_t *scales,
-                            float *s_dec)
+                            int per_token, int four_six, int gelu, uint8_t *codes,
+                            uint8_t *scales, float *s_dec)
 {
     float *x = (float *)malloc(sizeof(float) * (size_t)(R * C));
     orc_bf16_to_f32(src, R, C, ld, x);
+    if (gelu)
+        for (int64_t i = 0; i < R * C; ++i) x[i] = orc_gelu_f32(x[i]);
     float s_enc_t = orc_tensor_s_enc(orc_amax(x, R * C));
     if (!per_token) s_dec[0] = 1.0f / s_enc_t;
     const int64_t nb = C / 16;

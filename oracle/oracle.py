@@ -68,7 +68,10 @@ def lib():
             "orc_rht16_n": (None, [f32p, i64, u32]),
             "orc_e8m0_k_n": (None, [f32p, i64, i32p]),
             "orc_amax": (f32, [f32p, i64]),
-            "orc_nvfp4_quantize_act": (None, [u16p, i64, i64, i64, i32, i32, u8p, u8p, f32p]),
+            "orc_nvfp4_quantize_act": (None, [u16p, i64, i64, i64, i32, i32, i32, u8p, u8p,
+                                              f32p]),
+            "orc_exp_n": (None, [f32p, i64, f32p]),
+            "orc_gelu_n": (None, [f32p, i64, f32p]),
             "orc_nvfp4_dequant_rows_f64": (None, [u8p, u8p, f32p, i64, i64, f64p]),
         }
         for name, (res, args) in sig.items():
@@ -241,20 +244,53 @@ def nvfp4_quantize(x_bf16: np.ndarray, transpose=False, tile2d=False, rht=False,
     return NVFP4(codes, scales, s_dec, r, c, tile2d)
 
 
-def nvfp4_quantize_act(x_bf16: np.ndarray, per_token=True, four_six=True):
+def exp_f32(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty_like(x)
+    lib().orc_exp_n(x.reshape(-1), x.size, out.reshape(-1))
+    return out
+
+
+def gelu_f32(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty_like(x)
+    lib().orc_gelu_n(x.reshape(-1), x.size, out.reshape(-1))
+    return out
+
+
+def nvfp4_quantize_act(x_bf16: np.ndarray, per_token=True, four_six=True, gelu=False):
     """Row-wise 1x16 NVFP4 copy of an activation matrix, round to nearest,
     with a per-token outer scale (per_token) and / or Four Over Six block
-    scales (four_six).  Returns NVFP4Rows when per_token, else NVFP4."""
+    scales (four_six), optionally of GELU(x) (gelu).  Returns NVFP4Rows when
+    per_token, else NVFP4."""
     x = np.ascontiguousarray(x_bf16, np.uint16)
     R, Cc = x.shape
     codes = np.zeros((R, Cc // 2), np.uint8)
     scales = np.zeros((R, Cc // 16), np.uint8)
     s_dec = np.zeros(R if per_token else 1, np.float32)
-    lib().orc_nvfp4_quantize_act(x, R, Cc, Cc, int(per_token), int(four_six), codes, scales,
-                                 s_dec)
+    lib().orc_nvfp4_quantize_act(x, R, Cc, Cc, int(per_token), int(four_six), int(gelu), codes,
+                                 scales, s_dec)
     if per_token:
         return NVFP4Rows(codes, scales, s_dec, R, Cc)
     return NVFP4(codes, scales, s_dec[0], R, Cc, False)
+
+
+def bf16_to_f32(x_bf16: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns (uint16) to FP32 values (exact)."""
+    return (np.asarray(x_bf16, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def gelu_quantize(x_bf16: np.ndarray, mode=RTN, seed=0, stream=0, mx_mode=None, mx_seed=0,
+                  mx_stream=0):
+    """GELU(x) in FP32, then its row-wise 1x16 NVFP4 copy with the per-tensor
+    outer scale of GELU(x), and (mx_mode not None) its row-wise MXFP8 copy
+    (4bit.vizuara.ai, section 13: the activation is applied in the quantizer
+    and its FP32 result is quantized).  Returns (NVFP4, MXFP8 or None)."""
+    g = gelu_f32(bf16_to_f32(x_bf16))
+    q = nvfp4_encode_f32(g, tensor_s_enc(float(np.abs(g).max())), mode=mode, seed=seed,
+                         stream=stream)
+    m = None if mx_mode is None else mxfp8_encode_f32(g, mx_mode, mx_seed, mx_stream)
+    return q, m
 
 
 def nvfp4_encode_f32(x: np.ndarray, s_enc: float, tile2d=False, mode=RTN, seed=0,
