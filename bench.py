@@ -343,6 +343,41 @@ def main():
         act[name] = e
     print(f"[bench] per-token + 4/6 activation path: {json.dumps(act)}", file=sys.stderr, flush=True)
 
+    # Fused GELU + quantize of the MLP hidden tensor H [M x N] (between the
+    # layer's two projections): the NVFP4 copy of GELU(H) alone, with its
+    # MXFP8 SR copy for the backward pass, and as the per-token + 4/6
+    # activation copy.  Each op is the amax pass plus the encode pass.
+    h = up(synth.mlp_hidden(M, N)["h"])
+    hq = T.empty(M, N, device=dev)
+    hm = bbs.MXFP8Tensor.empty(M, N, device=dev)
+    ha = T.empty(M, N, device=dev, sdec_per_row=True)
+    gelu_ops = {
+        "gelu_quant_row": (lambda: bbs.nvfp4_quantize(h, hq, gelu=True, amax_ws=ws),
+                           2 * M * N + nvfp4_bytes(M, N)),
+        "gelu_quant_row_mx8": (lambda: bbs.nvfp4_quantize(h, hq, None, hm, mx8_round=bbs.SR,
+                                                          mx8_rng=(synth.MLP_SEEDS["mx8"], 0),
+                                                          gelu=True, amax_ws=ws),
+                               2 * M * N + nvfp4_bytes(M, N) + M * N + M * N // 32),
+        "gelu_quant_act": (lambda: bbs.nvfp4_quantize(h, ha, row_per_token=True,
+                                                      row_four_six=True, gelu=True, amax_ws=ws),
+                           2 * M * N + nvfp4_bytes(M, N) + 4 * M),
+    }
+    gelu = {}
+    for name, (f, b) in gelu_ops.items():
+        f()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        t_ms = s0.elapsed_time(s1) / args.steps
+        gelu[name] = {"ms": round(t_ms, 4), "GB/s": round(b / (t_ms * 1e-3) / 1e9, 1),
+                      "bytes": b, "Gelem/s": round(M * N / (t_ms * 1e-3) / 1e9, 1)}
+    del h, hq, hm, ha
+    print(f"[bench] fused GELU + quantize of H {M}x{N}: {json.dumps(gelu)}", file=sys.stderr,
+          flush=True)
+
     fprop_ms = per["fprop"]
     fprop_tf = GEMM_FLOP / (fprop_ms * 1e-3) / 1e12
     qbytes = ab["quant_x"] + ab["quant_w"]
@@ -374,6 +409,7 @@ def main():
                      "peak_fp4": PEAK_FP4_TFLOPS,
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
         "activation_per_token_4over6": act,
+        "gelu_quantize_mlp_hidden_8192x14336": gelu,
         "wall_s_timed": round(wall_s, 3),
     }
     if not args.no_moe:

@@ -18,7 +18,7 @@ BBS_OK, BBS_EINVAL, BBS_ENOTSUP, BBS_EHIP = 0, -1, -2, -3
 RTN, SR = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 FMT_NVFP4, FMT_MXFP8 = 0, 1
-AMAX_WS_FLOATS = 4096
+AMAX_WS_FLOATS = 11264
 
 
 class Fp4Desc(C.Structure):
@@ -43,7 +43,8 @@ class QuantArgs(C.Structure):
                 ("col_rht", C.c_int32), ("rht_signs", C.c_uint32),
                 ("row_mx8", C.POINTER(Mx8Desc)), ("mx8_round", C.c_int32), ("mx8_rng", Rng),
                 ("tile2d", C.c_int32), ("amax_ws", C.c_void_p),
-                ("row_per_token", C.c_int32), ("row_four_six", C.c_int32)]
+                ("row_per_token", C.c_int32), ("row_four_six", C.c_int32),
+                ("gelu", C.c_int32)]
 
 
 class BbsError(RuntimeError):
@@ -143,11 +144,12 @@ def amax_workspace(device="cuda"):
 def nvfp4_quantize(x, row=None, col=None, row_mx8=None, *, row_round=RTN, row_rng=(0, 0),
                    col_round=RTN, col_rng=(0, 0), col_rht=False, rht_signs=0, mx8_round=RTN,
                    mx8_rng=(0, 0), tile2d=False, amax_ws=None, row_per_token=False,
-                   row_four_six=False, stream=None):
+                   row_four_six=False, gelu=False, stream=None):
     """x: BF16 bit patterns as a [rows, cols] int16/uint16/bfloat16 device tensor
     (row stride x.stride(0)).  row / col: NVFP4Tensor outputs; row_mx8: MXFP8Tensor.
     row_per_token / row_four_six: activation options of the row copy (a
-    per-token row copy needs NVFP4Tensor.empty(..., sdec_per_row=True))."""
+    per-token row copy needs NVFP4Tensor.empty(..., sdec_per_row=True)).
+    gelu: the row / row_mx8 copies are of GELU(x) (tanh form, FP32)."""
     rd = row.desc() if row is not None else None
     cd = col.desc() if col is not None else None
     md = row_mx8.desc() if row_mx8 is not None else None
@@ -158,7 +160,8 @@ def nvfp4_quantize(x, row=None, col=None, row_mx8=None, *, row_round=RTN, row_rn
                   C.pointer(cd) if cd else None, col_round, Rng(*col_rng),
                   int(col_rht), rht_signs,
                   C.pointer(md) if md else None, mx8_round, Rng(*mx8_rng),
-                  int(tile2d), _ptr(amax_ws), int(row_per_token), int(row_four_six))
+                  int(tile2d), _ptr(amax_ws), int(row_per_token), int(row_four_six),
+                  int(gelu))
     _check(lib.nvfp4_quantize(C.byref(a), _stream(stream)))
 
 

@@ -8,6 +8,8 @@
 #include "../../include/bbs.h"
 #include "bbs_kernels.hpp"
 
+static_assert(bbs::kWorkspaceFloats == BBS_AMAX_WS_FLOATS, "workspace size mismatch");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -86,11 +88,18 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     if ((a->row_per_token != 0 && a->row_per_token != 1) ||
         (a->row_four_six != 0 && a->row_four_six != 1))
         return fail(BBS_EINVAL, "row_per_token / row_four_six must be 0 or 1");
+    if (a->gelu != 0 && a->gelu != 1) return fail(BBS_EINVAL, "gelu must be 0 or 1");
+    const bool gelu = a->gelu != 0;
+    if (gelu && (a->col || a->tile2d))
+        return fail(BBS_ENOTSUP, "gelu applies to the row-wise 1x16 and MXFP8 copies");
     const bool act = a->row_per_token || a->row_four_six;
     if (act && (!a->row || a->col || a->row_mx8 || a->tile2d || a->row_round != BBS_RTN))
         return fail(BBS_ENOTSUP, "per-token / Four Over Six apply to a lone 1x16 RTN row copy");
-    const bool need_amax = (a->row && !a->row_per_token) || a->col;
-    if (need_amax && !a->amax_ws) return fail(BBS_EINVAL, "null amax workspace");
+    const bool need_ws = (a->row && !a->row_per_token) || a->col || gelu;
+    if (need_ws && !a->amax_ws) return fail(BBS_EINVAL, "null amax workspace");
+    if (need_ws && !aligned(a->amax_ws, 16))
+        return fail(BBS_EINVAL, "amax workspace not 16-byte aligned");
+    float *gelu_tab = gelu ? a->amax_ws + bbs::kGeluTabOffset : nullptr;
     int st;
     if (a->row) {
         if ((st = check_fp4(a->row, "row", true))) return st;
@@ -125,18 +134,23 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     p.R = a->rows;
     p.C = a->cols;
     p.ld = a->ld;
+    p.gelu_tab = gelu_tab;
     if (act) {
         if (!a->row_per_token) {
             hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, true, false, 0,
                                             a->amax_ws, a->amax_ws + bbs::kAmaxPartials,
-                                            &p.n_part, s);
+                                            &p.n_part, s, gelu_tab);
             if ((st = hip_status(e, "amax launch"))) return st;
             p.part = a->amax_ws;
+        } else if (gelu) {
+            if ((st = hip_status(bbs::launch_gelu_table(gelu_tab, s), "GELU table launch")))
+                return st;
         }
         p.row_codes = a->row->codes;
         p.row_scales = a->row->scales;
         p.row_sdec = a->row->s_dec;
-        return hip_status(bbs::launch_quant_act(p, a->row_per_token != 0, a->row_four_six != 0, s),
+        return hip_status(bbs::launch_quant_act(p, a->row_per_token != 0, a->row_four_six != 0,
+                                                gelu, s),
                           "activation quantize launch");
     }
     const bool rht = a->col && a->col_rht;
@@ -144,11 +158,13 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     if (plain || rht) {
         float *ws = a->amax_ws;
         hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, plain, rht, a->rht_signs,
-                                        ws, ws + bbs::kAmaxPartials, &p.n_part, s);
+                                        ws, ws + bbs::kAmaxPartials, &p.n_part, s, gelu_tab);
         if ((st = hip_status(e, "amax launch"))) return st;
         p.part = ws;
         p.part_rht = ws + bbs::kAmaxPartials;
         p.n_part_rht = p.n_part;
+    } else if (gelu) {                  // an MXFP8 copy alone: no amax pass
+        if ((st = hip_status(bbs::launch_gelu_table(gelu_tab, s), "GELU table launch"))) return st;
     }
     if (a->row) {
         p.row_codes = a->row->codes;
@@ -175,7 +191,7 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
         p.mx_stream = a->mx8_rng.stream;
     }
     hipError_t e = bbs::launch_quant_tile(p, a->row != nullptr, a->col != nullptr,
-                                          a->row_mx8 != nullptr, a->tile2d != 0, rht, s);
+                                          a->row_mx8 != nullptr, a->tile2d != 0, rht, s, gelu);
     return hip_status(e, "quantize launch");
 }
 

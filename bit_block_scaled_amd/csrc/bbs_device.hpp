@@ -243,6 +243,82 @@ __device__ __forceinline__ void rht16(float y[16], uint32_t signs) {
 }
 
 // ---------------------------------------------------------------------------
+// GELU in its tanh form (Hendrycks and Gimpel, "Gaussian Error Linear
+// Units"): 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
+// tanh(u) = 1 - 2 / (exp(2u) + 1).  exp by Cody-Waite range reduction:
+// k = rint(v log2 e), r = (v - k ln2_hi) - k ln2_lo, where ln2_hi has 15
+// significant bits so that k ln2_hi is exact, then the degree-7 Taylor
+// polynomial of exp(r) by Horner's rule, times 2^k; v >= 88.5 gives +inf and
+// v <= -87 gives 0.  Every step is one FP32 operation rounded to nearest
+// even, in the order written, so the result is reproducible bit for bit
+// (finite inputs).  Over every finite BF16 input, GELU is non-decreasing for
+// x >= 0 and |GELU(x)| < kGeluNegBound for x < 0 (exhaustive tests).
+// ---------------------------------------------------------------------------
+constexpr float kGeluNegBound = 0.171875f;
+
+__device__ __forceinline__ float exp_cw(float v) {
+    const float w = fminf(fmaxf(v, -87.0f), 88.5f);      // keeps k in range
+    const float k = __builtin_rintf(w * 1.4426950408889634f);
+    float r = w - k * 0.693145751953125f;
+    r = r - k * 1.4286068202862268e-06f;
+    float p = 1.0f / 5040.0f;
+    p = p * r + 1.0f / 720.0f;
+    p = p * r + 1.0f / 120.0f;
+    p = p * r + 1.0f / 24.0f;
+    p = p * r + 1.0f / 6.0f;
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    const float e = __builtin_amdgcn_ldexpf(p, (int)k);
+    return v >= 88.5f ? __builtin_inff() : (v <= -87.0f ? 0.0f : e);
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float z = x + 0.044715f * ((x * x) * x);
+    const float u = 0.7978845608028654f * z;
+    const float th = 1.0f - 2.0f / (exp_cw(2.0f * u) + 1.0f);
+    return (0.5f * x) * (1.0f + th);
+}
+
+// GELU of a BF16 input by table.  Over the finite BF16 values, gelu_tanh(x)
+// is exactly 0.5 x below 2^-25 in magnitude (BF16 exponent field < 102),
+// exactly x for x >= 8 and -0 for x <= -8 (exponent field >= 130); the
+// 2 x 28 binades between are tabulated (entry = gelu_tanh of the value, so
+// the lookup equals gelu_tanh bit for bit; exhaustive tests).  The amax pass
+// writes the table to the workspace; each encode workgroup copies it to LDS.
+constexpr int kGeluTabE0 = 102, kGeluTabE1 = 130;
+constexpr int kGeluTabHalf = (kGeluTabE1 - kGeluTabE0) * 128;    // one sign
+constexpr int kGeluTabSize = 2 * kGeluTabHalf;
+
+// Entry i of the table (positive values first, then negative ones).
+__device__ __forceinline__ float gelu_table_entry(int i) {
+    const uint32_t h = (uint32_t)(i % kGeluTabHalf + (kGeluTabE0 << 7)) |
+                       (i >= kGeluTabHalf ? 0x8000u : 0u);
+    return gelu_tanh(__uint_as_float(h << 16));
+}
+
+// Workspace table -> LDS (every thread of the workgroup takes part; the
+// caller synchronises before the first lookup).
+__device__ __forceinline__ void gelu_table_load(float *lds, const float *tab) {
+    for (int i = threadIdx.x; i < kGeluTabSize / 4; i += blockDim.x)
+        reinterpret_cast<float4 *>(lds)[i] = reinterpret_cast<const float4 *>(tab)[i];
+}
+
+__device__ __forceinline__ float gelu_bf16(uint32_t h, const float *tab) {
+    const uint32_t a = h & 0x7FFFu;
+    const uint32_t d = a - (uint32_t)(kGeluTabE0 << 7);     // wraps below the table
+    const uint32_t i = min(d, (uint32_t)kGeluTabHalf - 1u) + (h >> 15) * (uint32_t)kGeluTabHalf;
+    float r = tab[i];
+    // outside the table (rare): skipped unless some lane of the wave needs it
+    if (__builtin_amdgcn_ballot_w64(d >= (uint32_t)kGeluTabHalf)) {
+        const float x = __uint_as_float(h << 16);
+        const float big = (h & 0x8000u) ? -0.0f : x;
+        if (d >= (uint32_t)kGeluTabHalf) r = a < (uint32_t)(kGeluTabE0 << 7) ? 0.5f * x : big;
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
 // Slab copies (global -> LDS, asynchronous) are issued through inline
 // assembly.  Issued through the compiler builtin, a copy counts as an LDS
 // store to an unknown address, and the compiler then waits for every copy in

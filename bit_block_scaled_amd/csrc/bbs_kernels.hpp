@@ -9,6 +9,9 @@ namespace bbs {
 
 // Upper bound on the workgroups of an amax pass (= partial maxima written).
 constexpr int kAmaxPartials = 2048;
+// Workspace layout (floats): plain partials, RHT partials, GELU table.
+constexpr int kGeluTabOffset = 2 * kAmaxPartials;
+constexpr int kWorkspaceFloats = kGeluTabOffset + 7168;
 
 struct QuantParams {
     const uint16_t *x;
@@ -35,6 +38,9 @@ struct QuantParams {
     const float *part;
     const float *part_rht;
     int n_part, n_part_rht;
+    // GELU table (kGeluTabSize floats, 16-byte aligned) when the copies are
+    // of GELU(x)
+    const float *gelu_tab;
 };
 
 struct RequantParams {
@@ -77,15 +83,24 @@ struct Mx8GemmParams {
 };
 
 // One read of x: partial maxima of |x| (plain) into part and of the RHT'd
-// column chunks (rht) into part_rht; *n_part partials each.
+// column chunks (rht) into part_rht; *n_part partials each.  With gelu (and
+// plain, without rht) the partials are maxima of |GELU(x)|, and the pass
+// also writes the GELU table.
 hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
-                       uint32_t signs, float *part, float *part_rht, int *n_part, hipStream_t s);
+                       uint32_t signs, float *part, float *part_rht, int *n_part, hipStream_t s,
+                       float *gelu_tab = nullptr);
+// The GELU table alone (for the activation copy with a per-token scale).
+hipError_t launch_gelu_table(float *gelu_tab, hipStream_t s);
+// gelu: the row-wise copies (NVFP4 and / or MXFP8, no column copy, 1x16) are
+// of GELU(x).
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
-                             bool tile2d, bool rht, hipStream_t s);
+                             bool tile2d, bool rht, hipStream_t s, bool gelu = false);
 hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s);
 // Row copy of an activation with a per-token outer scale and / or Four Over
-// Six (RTN, 1x16); without per_token, p.part holds the tensor amax partials.
-hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six, hipStream_t s);
+// Six (RTN, 1x16), optionally of GELU(x); without per_token, p.part holds
+// the tensor amax partials.
+hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six, bool gelu,
+                            hipStream_t s);
 // The large-tile NVFP4 kernels apply (K % 128 == 0, aligned operands and C);
 // they are the ones that support a per-row A decode scale.
 bool big_ok(const GemmParams &p, bool bf16_out);

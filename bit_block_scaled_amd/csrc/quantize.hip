@@ -33,6 +33,8 @@ constexpr int kAmaxGrid = 512;                 // workgroups (= partials) of pas
 constexpr int kReqR = 128, kReqC = 512;        // requantizer tile of the source
 
 static_assert(kAmaxGrid <= kAmaxPartials, "amax partials exceed the workspace");
+static_assert(kGeluTabOffset + kGeluTabSize <= kWorkspaceFloats, "GELU table exceeds the workspace");
+static_assert(kGeluTabOffset % 4 == 0, "GELU table must stay 16-byte aligned");
 
 // Tile t of T when workgroup b runs on XCD b % 8: XCD x takes a contiguous
 // run of tiles.
@@ -81,6 +83,12 @@ __device__ __forceinline__ float elem(const uint4 &row, int j) {
     return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
 }
 
+// Element j (compile-time) of a row of 8 BF16 values, as BF16 bits.
+__device__ __forceinline__ uint32_t elem_bits(const uint4 &row, int j) {
+    const uint32_t w = j < 2 ? row.x : (j < 4 ? row.y : (j < 6 ? row.z : row.w));
+    return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
 __device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -90,14 +98,26 @@ __device__ __forceinline__ float wave_max(float m) {
 // ---------------------------------------------------------------------------
 // Pass 1: partial amax of |x| (PLAIN) and of |RHT(column chunks)| (RHT).
 // ---------------------------------------------------------------------------
-template <bool PLAIN, bool RHT>
+// GELU: the partials are maxima of |GELU(x)|, found without evaluating GELU
+// on most elements.  GELU is non-decreasing for x >= 0, so the largest value
+// over the non-negative elements is GELU of their maximum; every negative
+// element has |GELU| < kGeluNegBound, so the negative elements of a wave's
+// pieces are evaluated only when GELU of the wave's largest element is below
+// that bound (wave-uniform branch).  The result is the exact maximum.
+template <bool PLAIN, bool RHT, bool GELU>
 __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ x, int64_t R,
                                                    int64_t C, int64_t ld, uint32_t signs,
                                                    float *__restrict__ part,
-                                                   float *__restrict__ part_rht) {
+                                                   float *__restrict__ part_rht,
+                                                   float *__restrict__ gelu_tab) {
+    static_assert(!GELU || (!PLAIN && !RHT), "GELU partials replace the plain ones");
+    if (GELU)
+        for (int i = blockIdx.x * kQT + threadIdx.x; i < kGeluTabSize; i += gridDim.x * kQT)
+            gelu_tab[i] = gelu_table_entry(i);
     __shared__ float red[2][kQT / 64];
     const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
     float m = 0.0f, mr = 0.0f;
+    float mx = 0.0f;     // GELU: largest element seen (0 if none is positive)
     // The next tile's piece is loaded while this one is reduced.
     int64_t tile = blockIdx.x;
     Piece q = piece_of(tile, R, C);
@@ -127,6 +147,22 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
             }
         }
         }
+        if (GELU) {
+            float pm = 0.0f;
+            if (q.in) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) pm = fmaxf(pm, elem(v[r], j));
+            }
+            mx = fmaxf(mx, pm);
+            if (gelu_tanh(wave_max(pm)) < kGeluNegBound && q.in) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(gelu_tanh(elem(v[r], j))));
+            }
+        }
         tile = next;
         q = qn;
 #pragma unroll
@@ -135,6 +171,7 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
     // The transform's final multiply by 1/4 is monotonic, so the maximum of
     // the scaled values is the scaled maximum (bit for bit).
     mr = mr * 0.25f;
+    if (GELU) m = fmaxf(m, gelu_tanh(mx));
     m = wave_max(m);
     mr = wave_max(mr);
     const int w = threadIdx.x >> 6;
@@ -149,7 +186,7 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
             a = fmaxf(a, red[0][i]);
             b = fmaxf(b, red[1][i]);
         }
-        if (PLAIN) part[blockIdx.x] = a;
+        if (PLAIN || GELU) part[blockIdx.x] = a;
         if (RHT) part_rht[blockIdx.x] = b;
     }
 }
@@ -179,11 +216,16 @@ __device__ __forceinline__ void put_run(uint8_t *dst, const uint8_t *src, int64_
     }
 }
 
-template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT>
+// GELU: the row-wise copies are of GELU(x), evaluated once per element in
+// FP32 (the pages' fused activation + quantize); the amax partials are those
+// of |GELU(x)|.
+template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT, bool GELU>
 __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
+    static_assert(!GELU || (!HAS_COL && !TILE2D && !RHT), "GELU feeds the row-wise copies");
     __shared__ __align__(16) uint8_t s_row[kTileR * 8];    // row copy scales
     __shared__ __align__(16) uint8_t s_col[kTileC * 16];   // column copy scales
     __shared__ __align__(16) uint8_t s_mx[kTileR * 4];     // MXFP8 scales
+    __shared__ __align__(16) float s_gelu[GELU ? kGeluTabSize : 1];
     const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
     const Piece q = piece_of(xcd_tile(blockIdx.x, T), p.R, p.C);
     uint4 v[16];
@@ -200,6 +242,17 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
         if (HAS_COL) p.col_sdec[0] = s_dec_col;
     }
     const int lane = threadIdx.x & 63;
+    if constexpr (GELU) {
+        gelu_table_load(s_gelu, p.gelu_tab);        // while the piece is in flight
+        __syncthreads();
+    }
+    // Element j of row r of the piece, as the row-wise copies see it (GELU:
+    // looked up where it is used, so the piece stays in its BF16 registers).
+    auto val = [&](int r, int j) -> float __attribute__((always_inline)) {
+        if constexpr (GELU) return gelu_bf16(elem_bits(v[r], j), s_gelu);
+        else return elem(v[r], j);
+    };
+
 
     // 16x16 tile amax (two lanes hold one tile; TILE2D excludes RHT).
     float tile_amax = 0.0f;
@@ -211,85 +264,85 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
         tile_amax = max_lane_pair(tile_amax);
     }
 
-    // ---- row-wise NVFP4 copy -------------------------------------------------
-    if (HAS_ROW) {
-        uint32_t tsc = 0;
-        float ts = 0.0f;
-        if (TILE2D) {
-            tsc = block_scale_code(tile_amax, s_enc_row);
-            ts = block_enc_scale(tsc, s_dec_row);
+    // ---- row-wise copies (NVFP4 and MXFP8), one row of the piece at a time ----
+    uint32_t tsc = 0;
+    float ts = 0.0f;
+    if (HAS_ROW && TILE2D) {
+        tsc = block_scale_code(tile_amax, s_enc_row);
+        ts = block_enc_scale(tsc, s_dec_row);
+    }
+    // NVFP4 copy of row r of the piece (values f)
+    auto row_copy = [&](auto sr_tag, int r, const float f[8]) __attribute__((always_inline)) {
+        constexpr bool SR = decltype(sr_tag)::value;
+        uint32_t sc = tsc;
+        float s = ts;
+        if (!TILE2D) {
+            float a = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
+            sc = block_scale_code(max_lane_pair(a), s_enc_row);
+            s = block_enc_scale(sc, s_dec_row);
+            if ((lane & 1) == 0) s_row[(q.band * 16 + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
         }
-        uint8_t *codes = p.row_codes + q.r0 * (p.C / 2) + q.c0 / 2;
-        auto rows = [&](auto sr_tag) {
-            constexpr bool SR = decltype(sr_tag)::value;
+        uint32_t packed;
+        if (SR) {
+            uint32_t w[4];
+            sr_block(p.row_seed, p.row_stream, (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
+            packed = e2m1_sr8(f, s, w);
+        } else {
+            packed = e2m1_rne8(f, s);
+        }
+        if (q.in) *reinterpret_cast<uint32_t *>(p.row_codes + (q.r0 + r) * (p.C / 2) + q.c0 / 2) =
+            packed;
+    };
+    // MXFP8 copy of row r of the piece (values f)
+    auto mx_copy = [&](auto sr_tag, int r, const float f[8]) __attribute__((always_inline)) {
+        constexpr bool SR = decltype(sr_tag)::value;
+        float y[8];
+        float a = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float f[8];
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
+        const int k = e8m0_k(max_lane_quad(a));
 #pragma unroll
-                for (int j = 0; j < 8; ++j) f[j] = elem(v[r], j);
-                uint32_t sc = tsc;
-                float s = ts;
-                if (!TILE2D) {
-                    float a = 0.0f;
+        for (int j = 0; j < 8; ++j) y[j] = ldexpf(f[j], -k);   // exact
+        uint32_t lo, hi;
+        if (SR) {
+            uint32_t w[4];
+            sr_block(p.mx_seed, p.mx_stream, (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
+            lo = e4m3_sr4(y[0], y[1], y[2], y[3], sr_word_lo(w[0]), sr_word_hi(w[0]),
+                          sr_word_lo(w[1]), sr_word_hi(w[1]));
+            hi = e4m3_sr4(y[4], y[5], y[6], y[7], sr_word_lo(w[2]), sr_word_hi(w[2]),
+                          sr_word_lo(w[3]), sr_word_hi(w[3]));
+        } else {
+            lo = e4m3_rne4(y[0], y[1], y[2], y[3]);
+            hi = e4m3_rne4(y[4], y[5], y[6], y[7]);
+        }
+        if (q.in) *reinterpret_cast<uint2 *>(p.mx_codes + (q.r0 + r) * p.C + q.c0) = make_uint2(lo, hi);
+        if ((lane & 3) == 0) s_mx[(q.band * 16 + r) * 4 + (q.cg >> 2)] = (uint8_t)(k + 127);
+    };
+    // (two loops of 8 rows: each stays under the compiler's full-unroll
+    // limit, so the piece's registers are never indexed at run time)
+    auto rows = [&](auto row_sr, auto mx_sr) __attribute__((always_inline)) {
+        auto one = [&](int r) __attribute__((always_inline)) {
+            float f[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
-                    sc = block_scale_code(max_lane_pair(a), s_enc_row);
-                    s = block_enc_scale(sc, s_dec_row);
-                    if ((lane & 1) == 0) s_row[(q.band * 16 + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
-                }
-                uint32_t packed;
-                if (SR) {
-                    uint32_t w[4];
-                    sr_block(p.row_seed, p.row_stream,
-                             (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
-                    packed = e2m1_sr8(f, s, w);
-                } else {
-                    packed = e2m1_rne8(f, s);
-                }
-                if (q.in) *reinterpret_cast<uint32_t *>(codes + r * (p.C / 2)) = packed;
-            }
+            for (int j = 0; j < 8; ++j) f[j] = val(r, j);
+            if (HAS_ROW) row_copy(row_sr, r, f);
+            if (HAS_MX) mx_copy(mx_sr, r, f);
         };
-        if (p.row_round == 1) rows(std::true_type{});
-        else rows(std::false_type{});
-        if (TILE2D && (lane & 1) == 0) s_row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) one(r);
+#pragma unroll
+        for (int r = 8; r < 16; ++r) one(r);
+    };
+    if (HAS_ROW || HAS_MX) {
+        const bool row_sr = HAS_ROW && p.row_round == 1, mx_sr = HAS_MX && p.mx_round == 1;
+        if (row_sr && mx_sr) rows(std::true_type{}, std::true_type{});
+        else if (row_sr) rows(std::true_type{}, std::false_type{});
+        else if (mx_sr) rows(std::false_type{}, std::true_type{});
+        else rows(std::false_type{}, std::false_type{});
     }
-
-    // ---- row-wise MXFP8 copy -------------------------------------------------
-    if (HAS_MX) {
-        uint8_t *codes = p.mx_codes + q.r0 * p.C + q.c0;
-        auto rows = [&](auto sr_tag) {
-            constexpr bool SR = decltype(sr_tag)::value;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float y[8];
-                float a = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    y[j] = elem(v[r], j);
-                    a = fmaxf(a, fabsf(y[j]));
-                }
-                const int k = e8m0_k(max_lane_quad(a));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) y[j] = ldexpf(y[j], -k);   // exact
-                uint32_t lo, hi;
-                if (SR) {
-                    uint32_t w[4];
-                    sr_block(p.mx_seed, p.mx_stream, (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
-                    lo = e4m3_sr4(y[0], y[1], y[2], y[3], sr_word_lo(w[0]), sr_word_hi(w[0]),
-                                  sr_word_lo(w[1]), sr_word_hi(w[1]));
-                    hi = e4m3_sr4(y[4], y[5], y[6], y[7], sr_word_lo(w[2]), sr_word_hi(w[2]),
-                                  sr_word_lo(w[3]), sr_word_hi(w[3]));
-                } else {
-                    lo = e4m3_rne4(y[0], y[1], y[2], y[3]);
-                    hi = e4m3_rne4(y[4], y[5], y[6], y[7]);
-                }
-                if (q.in) *reinterpret_cast<uint2 *>(codes + r * p.C) = make_uint2(lo, hi);
-                if ((lane & 3) == 0) s_mx[(q.band * 16 + r) * 4 + (q.cg >> 2)] = (uint8_t)(k + 127);
-            }
-        };
-        if (p.mx_round == 1) rows(std::true_type{});
-        else rows(std::false_type{});
-    }
+    if (HAS_ROW && TILE2D && (lane & 1) == 0) s_row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
 
     // ---- column-wise NVFP4 copy (of x^T) ---------------------------------------
     if (HAS_COL) {
@@ -408,12 +461,16 @@ __device__ __forceinline__ float half_err(const float f[8], uint32_t packed, flo
     return e;
 }
 
-template <bool FOUR_SIX>
-__device__ __forceinline__ void act_encode_chunk(const uint4 &v, float s_enc, float s_dec,
-                                                 int lane, uint32_t &packed, uint32_t &sc) {
-    float f[8];
+// A lane's 8 values of a chunk: x, or GELU(x) (tab: the LDS GELU table).
+template <bool GELU>
+__device__ __forceinline__ void act_values(const uint4 &v, float f[8], const float *tab) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = elem(v, j);
+    for (int j = 0; j < 8; ++j) f[j] = GELU ? gelu_bf16(elem_bits(v, j), tab) : elem(v, j);
+}
+
+template <bool FOUR_SIX>
+__device__ __forceinline__ void act_encode_chunk(const float f[8], float s_enc, float s_dec,
+                                                 int lane, uint32_t &packed, uint32_t &sc) {
     float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
@@ -440,36 +497,72 @@ __device__ __forceinline__ void act_encode_chunk(const uint4 &v, float s_enc, fl
     }
 }
 
-template <bool PER_TOKEN, bool FOUR_SIX>
+// GELU: the copy is of GELU(x); the per-token amax uses the same shortcut as
+// the amax pass (GELU of the row's largest element, and the negative
+// elements only when that is below kGeluNegBound).
+template <bool PER_TOKEN, bool FOUR_SIX, bool GELU>
 __global__ __launch_bounds__(kQT) void quant_act_kernel(QuantParams p) {
+    __shared__ __align__(16) float s_gelu[GELU ? kGeluTabSize : 1];
     const int lane = threadIdx.x & 63;
-    const int64_t r = ((int64_t)blockIdx.x * kQT + threadIdx.x) >> 6;
-    float s_enc;
+    float s_enc_t = 1.0f;                             // the tensor's, without PER_TOKEN
     if (!PER_TOKEN) {
-        s_enc = tensor_s_enc(fold_partials(p.part, p.n_part));
-        if (blockIdx.x == 0 && threadIdx.x == 0) p.row_sdec[0] = 1.0f / s_enc;
+        s_enc_t = tensor_s_enc(fold_partials(p.part, p.n_part));
+        if (blockIdx.x == 0 && threadIdx.x == 0) p.row_sdec[0] = 1.0f / s_enc_t;
     }
-    if (r >= p.R) return;                             // whole waves leave together
-    const uint16_t *row = p.x + r * p.ld;
+    const int64_t r = ((int64_t)blockIdx.x * kQT + threadIdx.x) >> 6;
+    const bool live = r < p.R;
+    float s_enc = s_enc_t;
+    const uint16_t *row = p.x + (live ? r : 0) * p.ld;
     const int64_t nch = (p.C + 511) / 512;
     uint4 v[kActChunks];
 #pragma unroll
     for (int k = 0; k < kActChunks; ++k)
         if (k < nch) load_chunk8(row, p.C, k, lane, v[k]);
+    if constexpr (GELU) {
+        gelu_table_load(s_gelu, p.gelu_tab);        // while the row is in flight
+        __syncthreads();
+    }
+    if (!live) return;                                // whole waves leave together
     if (PER_TOKEN) {
+        // GELU: m is the largest element (at least 0), else the largest |x|
+        // (chunks past the row's end hold zeros)
+        auto fold = [&](float m, const uint4 &w) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, GELU ? elem(w, j) : fabsf(elem(w, j)));
+            return m;
+        };
         float m = 0.0f;
 #pragma unroll
         for (int k = 0; k < kActChunks; ++k)
-            if (k < nch)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(v[k], j)));
+            if (k < nch) m = fold(m, v[k]);
         for (int64_t k = kActChunks; k < nch; ++k) {
             uint4 w;
             load_chunk8(row, p.C, k, lane, w);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(w, j)));
+            m = fold(m, w);
         }
-        s_enc = tensor_s_enc(wave_max(m));
+        float amax = wave_max(m);
+        if (GELU) {
+            amax = gelu_tanh(amax);
+            if (amax < kGeluNegBound) {                 // wave-uniform
+                float mn = 0.0f;
+                auto fold_neg = [&](const uint4 &w) {
+                    float f[8];
+                    act_values<true>(w, f, s_gelu);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) mn = fmaxf(mn, fabsf(f[j]));
+                };
+#pragma unroll
+                for (int k = 0; k < kActChunks; ++k)
+                    if (k < nch) fold_neg(v[k]);
+                for (int64_t k = kActChunks; k < nch; ++k) {
+                    uint4 w;
+                    load_chunk8(row, p.C, k, lane, w);
+                    fold_neg(w);
+                }
+                amax = fmaxf(amax, wave_max(mn));
+            }
+        }
+        s_enc = tensor_s_enc(amax);
         if (lane == 0) p.row_sdec[r] = 1.0f / s_enc;
     }
     const float s_dec = 1.0f / s_enc;
@@ -477,7 +570,9 @@ __global__ __launch_bounds__(kQT) void quant_act_kernel(QuantParams p) {
     uint8_t *scales = p.row_scales + r * (p.C / 16);
     auto emit = [&](const uint4 &w, int64_t k) {
         uint32_t packed, sc;
-        act_encode_chunk<FOUR_SIX>(w, s_enc, s_dec, lane, packed, sc);
+        float f[8];
+        act_values<GELU>(w, f, s_gelu);
+        act_encode_chunk<FOUR_SIX>(f, s_enc, s_dec, lane, packed, sc);
         const int64_t c = k * 512 + lane * 8;
         if (c < p.C) {
             *reinterpret_cast<uint32_t *>(codes + c / 2) = packed;
@@ -578,31 +673,54 @@ __global__ __launch_bounds__(kQT) void requant_kernel(RequantParams p) {
 
 hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
                        uint32_t signs, float *part, float *part_rht, int *n_part,
-                       hipStream_t s) {
+                       hipStream_t s, float *gelu_tab) {
     const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
     const int grid = (int)(T < kAmaxGrid ? T : kAmaxGrid);
     *n_part = grid;
-    if (plain && rht)
-        hipLaunchKernelGGL((amax_kernel<true, true>), dim3(grid), dim3(kQT), 0, s, x, R, C, ld,
-                           signs, part, part_rht);
+    if (gelu_tab) {
+        if (rht || !plain) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((amax_kernel<false, false, true>), dim3(grid), dim3(kQT), 0, s, x, R, C,
+                           ld, signs, part, part_rht, gelu_tab);
+    } else if (plain && rht)
+        hipLaunchKernelGGL((amax_kernel<true, true, false>), dim3(grid), dim3(kQT), 0, s, x, R, C,
+                           ld, signs, part, part_rht, nullptr);
     else if (plain)
-        hipLaunchKernelGGL((amax_kernel<true, false>), dim3(grid), dim3(kQT), 0, s, x, R, C, ld,
-                           signs, part, part_rht);
+        hipLaunchKernelGGL((amax_kernel<true, false, false>), dim3(grid), dim3(kQT), 0, s, x, R, C,
+                           ld, signs, part, part_rht, nullptr);
     else if (rht)
-        hipLaunchKernelGGL((amax_kernel<false, true>), dim3(grid), dim3(kQT), 0, s, x, R, C, ld,
-                           signs, part, part_rht);
+        hipLaunchKernelGGL((amax_kernel<false, true, false>), dim3(grid), dim3(kQT), 0, s, x, R, C,
+                           ld, signs, part, part_rht, nullptr);
     return hipGetLastError();
 }
 
-template <bool R_, bool C_, bool M_, bool T_, bool H_>
+__global__ __launch_bounds__(kQT) void gelu_table_kernel(float *__restrict__ gelu_tab) {
+    const int i = blockIdx.x * kQT + threadIdx.x;
+    if (i < kGeluTabSize) gelu_tab[i] = gelu_table_entry(i);
+}
+
+hipError_t launch_gelu_table(float *gelu_tab, hipStream_t s) {
+    hipLaunchKernelGGL(gelu_table_kernel, dim3((kGeluTabSize + kQT - 1) / kQT), dim3(kQT), 0, s,
+                       gelu_tab);
+    return hipGetLastError();
+}
+
+template <bool R_, bool C_, bool M_, bool T_, bool H_, bool G_ = false>
 static void launch_q(const QuantParams &p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((quant_kernel<R_, C_, M_, T_, H_>), grid, dim3(kQT), 0, s, p);
+    hipLaunchKernelGGL((quant_kernel<R_, C_, M_, T_, H_, G_>), grid, dim3(kQT), 0, s, p);
 }
 
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
-                             bool tile2d, bool rht, hipStream_t s) {
+                             bool tile2d, bool rht, hipStream_t s, bool gelu) {
     const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
     const dim3 grid((unsigned)T);
+    if (gelu) {
+        if (has_col || tile2d || rht) return hipErrorInvalidValue;
+        if (has_row && has_mx) launch_q<1, 0, 1, 0, 0, 1>(p, grid, s);
+        else if (has_row) launch_q<1, 0, 0, 0, 0, 1>(p, grid, s);
+        else if (has_mx) launch_q<0, 0, 1, 0, 0, 1>(p, grid, s);
+        else return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     // The combinations the quantizer supports (RHT only on a 1x16 column copy).
     const int key = (has_row << 4) | (has_col << 3) | (has_mx << 2) | (tile2d << 1) | rht;
     switch (key) {
@@ -628,16 +746,23 @@ hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, b
     return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six, hipStream_t s) {
+template <bool P_, bool F_, bool G_>
+static void launch_act(const QuantParams &p, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((quant_act_kernel<P_, F_, G_>), grid, dim3(kQT), 0, s, p);
+}
+
+hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six, bool gelu,
+                            hipStream_t s) {
     const dim3 grid((unsigned)((p.R + kQT / 64 - 1) / (kQT / 64)));
-    if (per_token && four_six)
-        hipLaunchKernelGGL((quant_act_kernel<true, true>), grid, dim3(kQT), 0, s, p);
-    else if (per_token)
-        hipLaunchKernelGGL((quant_act_kernel<true, false>), grid, dim3(kQT), 0, s, p);
-    else if (four_six)
-        hipLaunchKernelGGL((quant_act_kernel<false, true>), grid, dim3(kQT), 0, s, p);
-    else
-        return hipErrorInvalidValue;
+    switch ((per_token << 2) | (four_six << 1) | gelu) {
+        case 0b110: launch_act<1, 1, 0>(p, grid, s); break;
+        case 0b100: launch_act<1, 0, 0>(p, grid, s); break;
+        case 0b010: launch_act<0, 1, 0>(p, grid, s); break;
+        case 0b111: launch_act<1, 1, 1>(p, grid, s); break;
+        case 0b101: launch_act<1, 0, 1>(p, grid, s); break;
+        case 0b011: launch_act<0, 1, 1>(p, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

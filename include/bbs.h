@@ -45,7 +45,7 @@ enum bbs_out_dtype { BBS_OUT_F32 = 0, BBS_OUT_BF16 = 1 };
 enum bbs_fmt { BBS_FMT_NVFP4 = 0, BBS_FMT_MXFP8 = 1 };
 
 /* Words of device workspace nvfp4_quantize needs for its amax partials. */
-#define BBS_AMAX_WS_FLOATS 4096
+#define BBS_AMAX_WS_FLOATS 11264
 
 /* One NVFP4 tensor: value = E2M1(code) x E4M3(block scale) x s_dec
  * ("value = FP4 code x FP8 block scale x FP32 outer scale"; Pretraining LLMs
@@ -107,7 +107,9 @@ typedef struct {
 
     int32_t tile2d; /* 1: 16x16 tile scales for row and col copies (col is then
                        the bit-identical transpose of row when both round RTN) */
-    float *amax_ws; /* device workspace, >= BBS_AMAX_WS_FLOATS floats, not kept */
+    float *amax_ws; /* device workspace, >= BBS_AMAX_WS_FLOATS floats, 16-byte
+                       aligned, not kept (amax partials; with gelu, also the
+                       GELU table the encode pass reads) */
 
     /* Activation options of the row copy (4bit.vizuara.ai, section 11;
      * End-to-End 4-Bit Training, recipe details); both need row_round ==
@@ -122,6 +124,20 @@ typedef struct {
      *   keep the first). */
     int32_t row_per_token;
     int32_t row_four_six;
+
+    /* gelu = 1: the copies are of GELU(x) instead of x, with GELU applied
+     * in FP32 inside the quantizer (4bit.vizuara.ai, section 13: the
+     * activation rides along with the quantize), in the tanh form of
+     * Hendrycks and Gimpel: 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715 x^3))),
+     * tanh(u) = 1 - 2 / (exp(2u) + 1), each step one FP32 operation rounded
+     * to nearest even, exp by Cody-Waite reduction (k = rint(v log2 e),
+     * ln2 split into 0x3F317200 + 0x35BFBE8E) and the degree-7 Taylor
+     * polynomial by Horner's rule, exp(v >= 88.5) = inf, exp(v <= -87) = 0.
+     * The amax (tensor or per token) is that of |GELU(x)|.  Applies to the
+     * row and row_mx8 copies (1x16, RTN or SR) and to the activation
+     * options; a col copy or tile2d with gelu is BBS_ENOTSUP.  gelu always
+     * needs amax_ws (per token too).  x finite. */
+    int32_t gelu;
 } bbs_quant_args;
 
 /* NVFP4 quantizer (Pretraining LLMs with NVFP4, "NVFP4 Format and

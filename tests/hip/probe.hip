@@ -114,3 +114,19 @@ extern "C" int probe_cvt_sr(const float *x, const uint32_t *h, int n, const floa
                        fp8);
     return (int)hipDeviceSynchronize();
 }
+
+// The library's own GELU and exp (tanh form, Cody-Waite exp), element by
+// element: the kernels' fused activation must equal the oracle's bit for bit.
+#include "../../bit_block_scaled_amd/csrc/bbs_device.hpp"
+
+__global__ void gelu_kernel(const float *x, int n, float *g, float *e) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    g[i] = bbs::gelu_tanh(x[i]);
+    e[i] = bbs::exp_cw(x[i]);
+}
+
+extern "C" int probe_gelu(const float *x, int n, float *g, float *e) {
+    hipLaunchKernelGGL(gelu_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, x, n, g, e);
+    return (int)hipDeviceSynchronize();
+}

@@ -147,3 +147,31 @@ def test_binding_has_no_cpu_fallback():
     import bit_block_scaled_amd as bbs
     src = open(bbs.__file__).read()
     assert "oracle" not in src.replace("no CPU fallback", "")
+
+
+def test_gelu_option_errors(lib):
+    """gelu: 0 or 1; with a column copy or 16x16 tiles it is unsupported."""
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    a = bbs.QuantArgs()
+    a.x, a.rows, a.cols, a.ld = 0x1000, 32, 64, 64
+    row = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 64, 0, 0)
+    a.row = C.pointer(row)
+    a.gelu = 2
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    a.gelu = 1
+    col = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 64, 32, 0, 0)
+    a.col = C.pointer(col)
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_ENOTSUP
+    a.col = None
+    a.tile2d, row.tile2d = 1, 1
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_ENOTSUP
+    assert b"gelu" in L.bbs_last_error()
+    # the GELU table lives in the workspace, also for a per-token copy
+    a.tile2d, row.tile2d = 0, 0
+    a.row_per_token, row.sdec_per_row = 1, 1
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"workspace" in L.bbs_last_error()
+    a.amax_ws = 0x4004
+    assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"aligned" in L.bbs_last_error()

@@ -113,3 +113,42 @@ def test_sr_conversions_match_oracle(probe):
     in8 = np.abs(x) <= 448                                # MXFP8 inputs never exceed 448
     want8 = O.e4m3_code(O.round_to(x[in8], O.E4M3, O.SR, u[in8]))
     assert np.array_equal(o8.cpu().numpy()[in8], want8)
+
+
+def test_gelu_and_exp_match_oracle(probe):
+    """The library's GELU and exp equal the oracle's bit for bit on every
+    finite BF16 input (the fused GELU + quantize sees BF16 inputs only) and
+    on a dense FP32 grid through both exp cut-offs; and the two properties
+    the GELU amax shortcut relies on hold for the device values."""
+    announce("GELU / exp on every finite BF16 value")
+    b = np.arange(65536, dtype=np.uint32)
+    xb = (b << 16).view(np.float32)
+    xb = xb[np.isfinite(xb)]
+    grid = np.linspace(-100.0, 100.0, 1 << 18).astype(np.float32)
+    x = np.concatenate([xb, grid, np.float32([-87.0, 88.5, 88.49999, -86.99999])])
+    xd = torch.from_numpy(x).to("cuda:0")
+    g = torch.empty_like(xd)
+    e = torch.empty_like(xd)
+    assert probe.probe_gelu(C.c_void_p(xd.data_ptr()), len(x), C.c_void_p(g.data_ptr()),
+                            C.c_void_p(e.data_ptr())) == 0
+    gh, eh = g.cpu().numpy(), e.cpu().numpy()
+    og, oe = O.gelu_f32(x), O.exp_f32(x)
+    bad = np.flatnonzero(gh.view(np.uint32) != og.view(np.uint32))
+    assert len(bad) == 0, f"GELU differs at x={x[bad[:4]]}: {gh[bad[:4]]} vs {og[bad[:4]]}"
+    bad = np.flatnonzero(eh.view(np.uint32) != oe.view(np.uint32))
+    assert len(bad) == 0, f"exp differs at x={x[bad[:4]]}: {eh[bad[:4]]} vs {oe[bad[:4]]}"
+    n = len(xb)
+    pos = xb >= 0
+    order = np.argsort(xb[pos], kind="stable")
+    assert np.all(np.diff(gh[:n][pos][order]) >= 0), "GELU decreases somewhere on x >= 0"
+    assert np.abs(gh[:n][~pos]).max() < 0.171875
+    # the identities the quantizers' GELU table relies on (BF16 exponent field
+    # below 102: 0.5 x; 130 and above: x, or -0 for negative x)
+    hb = xb.view(np.uint32) >> 16
+    ef = (hb >> 7) & 0xFF
+    gb = gh[:n]
+    tiny = ef < 102
+    assert np.array_equal(gb[tiny].view(np.uint32), (np.float32(0.5) * xb[tiny]).view(np.uint32))
+    big = ef >= 130
+    assert np.array_equal(gb[big & pos], xb[big & pos])
+    assert np.all(gb[big & ~pos].view(np.uint32) == 0x80000000)

@@ -253,10 +253,10 @@ def test_full_backward_quantize(bbs):
 ACT_SHAPES = [(16, 16), (48, 80), (64, 1040), (256, 4096), (32, 8192 + 528)]
 
 
-def _gpu_quantize_act(bbs, x, per_token, four_six):
+def _gpu_quantize_act(bbs, x, per_token, four_six, gelu=False):
     R, C = x.shape
     q = bbs.NVFP4Tensor.empty(R, C, device=dev(), sdec_per_row=per_token)
-    bbs.nvfp4_quantize(to_dev(x), q, row_per_token=per_token, row_four_six=four_six)
+    bbs.nvfp4_quantize(to_dev(x), q, row_per_token=per_token, row_four_six=four_six, gelu=gelu)
     torch.cuda.synchronize()
     return q
 
@@ -303,6 +303,139 @@ def test_full_activation_copy(bbs):
     x = synth.dense_forward()["x"]
     g = _gpu_quantize_act(bbs, x, True, True)
     o = O.nvfp4_quantize_act(x, True, True)
+    assert np.array_equal(host(g.scales), o.scales)
+    assert np.array_equal(host(g.codes), o.codes)
+    assert np.array_equal(host(g.s_dec), o.s_dec)
+
+
+# ---------------------------------------------------------------------------
+# Fused GELU + quantize (the copies are of GELU(x))
+# ---------------------------------------------------------------------------
+
+GELU_SHAPES = [(16, 16), (48, 80), (64, 1040), (256, 256), (144, 528), (272, 4096)]
+
+
+def _gpu_gelu(bbs, x, *, row=True, mx=False, row_round=O.RTN, row_rng=(0, 0), mx_round=O.RTN,
+              mx_rng=(0, 0)):
+    R, C = x.shape
+    rq = bbs.NVFP4Tensor.empty(R, C, device=dev()) if row else None
+    mq = bbs.MXFP8Tensor.empty(R, C, device=dev()) if mx else None
+    bbs.nvfp4_quantize(to_dev(x), rq, None, mq, row_round=row_round, row_rng=row_rng,
+                       mx8_round=mx_round, mx8_rng=mx_rng, gelu=True)
+    torch.cuda.synchronize()
+    return rq, mq
+
+
+@pytest.mark.parametrize("shape", GELU_SHAPES)
+def test_gelu_quantize(bbs, shape):
+    R, C = shape
+    announce(f"GELU + quantize {R}x{C}")
+    x = synth.normal_with_outliers(R, C, 900 + R + C)
+    rq, _ = _gpu_gelu(bbs, x)
+    _same_fp4(rq, O.gelu_quantize(x)[0], "GELU row RTN")
+    if C % 32 == 0:
+        rq, mq = _gpu_gelu(bbs, x, mx=True, row_round=O.SR, row_rng=(31, 2), mx_round=O.SR,
+                           mx_rng=(32, 3))
+        oq, om = O.gelu_quantize(x, mode=O.SR, seed=31, stream=2, mx_mode=O.SR, mx_seed=32,
+                                 mx_stream=3)
+        _same_fp4(rq, oq, "GELU row SR")
+        _same_mx8(mq, om, "GELU MXFP8 SR")
+        _, mq = _gpu_gelu(bbs, x, row=False, mx=True)
+        _same_mx8(mq, O.gelu_quantize(x, mx_mode=O.RTN)[1], "GELU MXFP8 RTN alone")
+
+
+def test_gelu_quantize_every_bf16_value(bbs):
+    """Every finite BF16 value (a seeded shuffle, zero-padded to 256 x 256)
+    through the fused GELU copies: the kernels' GELU table, its range
+    boundaries and the identities outside it, against the oracle."""
+    announce("GELU + quantize over every finite BF16 value")
+    h = np.arange(65536, dtype=np.uint32)
+    f = (h << 16).view(np.float32)
+    vals = h[np.isfinite(f)].astype(np.uint16)
+    x = np.zeros(65536, np.uint16)
+    x[:len(vals)] = np.random.default_rng(23).permutation(vals)
+    x = x.reshape(256, 256)
+    rq, mq = _gpu_gelu(bbs, x, mx=True, row_round=O.SR, row_rng=(5, 1), mx_round=O.SR,
+                       mx_rng=(6, 2))
+    oq, om = O.gelu_quantize(x, mode=O.SR, seed=5, stream=1, mx_mode=O.SR, mx_seed=6,
+                             mx_stream=2)
+    _same_fp4(rq, oq, "GELU row SR, all BF16")
+    _same_mx8(mq, om, "GELU MXFP8 SR, all BF16")
+    for pt, fs in [(True, True), (False, True), (True, False)]:
+        g = _gpu_quantize_act(bbs, x, pt, fs, gelu=True)
+        o = O.nvfp4_quantize_act(x, pt, fs, gelu=True)
+        assert np.array_equal(host(g.scales), o.scales)
+        assert np.array_equal(host(g.codes), o.codes)
+        assert np.array_equal(host(g.s_dec), np.atleast_1d(o.s_dec))
+
+
+def _gelu_edge_inputs():
+    """Inputs whose |GELU| maximum lies on the negative side (or is 0), so
+    the quantizers must evaluate the negative elements: all negative, all
+    small, zeros, and rows of large values next to rows of negatives."""
+    rng = np.random.default_rng(17)
+    base = rng.standard_normal((64, 544)).astype(np.float32)
+    cases = {
+        "all negative": -np.abs(base),
+        "all small": base * np.float32(0.05),
+        "near the minimum": np.float32(-0.75) + base * np.float32(0.01),
+        "zeros": np.zeros_like(base),
+    }
+    mixed = -np.abs(base)
+    mixed[:16] = np.abs(base[:16]) * 4
+    cases["mixed rows"] = mixed
+    return {k: synth.bf16_bits(v) for k, v in cases.items()}
+
+
+def test_gelu_quantize_negative_side(bbs):
+    announce("GELU + quantize where the negative side sets the amax")
+    for name, x in _gelu_edge_inputs().items():
+        rq, mq = _gpu_gelu(bbs, x, mx=True)
+        oq, om = O.gelu_quantize(x, mx_mode=O.RTN)
+        _same_fp4(rq, oq, f"GELU row, {name}")
+        _same_mx8(mq, om, f"GELU MXFP8, {name}")
+        for pt, fs in [(True, True), (True, False), (False, True)]:
+            g = _gpu_quantize_act(bbs, x, pt, fs, gelu=True)
+            o = O.nvfp4_quantize_act(x, pt, fs, gelu=True)
+            assert np.array_equal(host(g.scales), o.scales), f"{name} {pt} {fs}"
+            assert np.array_equal(host(g.codes), o.codes), f"{name} {pt} {fs}"
+            assert np.array_equal(host(g.s_dec), np.atleast_1d(o.s_dec)), f"{name} {pt} {fs}"
+
+
+@pytest.mark.parametrize("shape", ACT_SHAPES)
+@pytest.mark.parametrize("per_token,four_six", [(True, True), (True, False), (False, True)])
+def test_gelu_activation_copy(bbs, shape, per_token, four_six):
+    R, C = shape
+    announce(f"GELU activation copy {R}x{C} per_token={per_token} four_six={four_six}")
+    x = synth.normal_with_outliers(R, C, 950 + R + C)
+    g = _gpu_quantize_act(bbs, x, per_token, four_six, gelu=True)
+    o = O.nvfp4_quantize_act(x, per_token, four_six, gelu=True)
+    assert np.array_equal(host(g.scales), o.scales), "scales differ"
+    gc = host(g.codes)
+    if not np.array_equal(gc, o.codes):
+        bad = np.argwhere(gc != o.codes)
+        raise AssertionError(f"{len(bad)} code bytes differ, first at {bad[0].tolist()}")
+    assert np.array_equal(host(g.s_dec), np.atleast_1d(o.s_dec)), "decode scales differ"
+
+
+def test_full_gelu_quantize(bbs):
+    """The MLP hidden tensor H (8192 x 14336), as bench.py times it: the
+    NVFP4 copy of GELU(H) (RTN) and its MXFP8 copy (SR) from one pass."""
+    announce("full GELU + quantize 8192x14336 row RTN + MXFP8 SR")
+    d = synth.mlp_hidden()
+    rq, mq = _gpu_gelu(bbs, d["h"], mx=True, mx_round=O.SR, mx_rng=(d["seeds"]["mx8"], 0))
+    oq, om = O.gelu_quantize(d["h"], mx_mode=O.SR, mx_seed=d["seeds"]["mx8"])
+    _same_fp4(rq, oq, "GELU(H) row")
+    _same_mx8(mq, om, "GELU(H) MXFP8")
+
+
+def test_full_gelu_activation_copy(bbs):
+    """GELU(H) as the activation copy: per-token outer scale + Four Over Six
+    (rows of 14336 are read twice: the amax, then the encode)."""
+    announce("full GELU activation copy 8192x14336 per-token + 4/6")
+    h = synth.mlp_hidden()["h"]
+    g = _gpu_quantize_act(bbs, h, True, True, gelu=True)
+    o = O.nvfp4_quantize_act(h, True, True, gelu=True)
     assert np.array_equal(host(g.scales), o.scales)
     assert np.array_equal(host(g.codes), o.codes)
     assert np.array_equal(host(g.s_dec), o.s_dec)

@@ -11,6 +11,8 @@ Shapes and distributions follow the five workloads of the hot path:
   backward         dY [8192 x 14336] Laplace, std 1e-3
   MoE forward      X [65536 x 4096] as above, 64 experts, top-8 of Zipf(1.1),
                    W_up[g] [1536 x 4096], W_down[g] [4096 x 1536] N(0, 0.02)
+  MLP hidden       H [8192 x 14336], the pre-activation between the dense
+                   layer's two projections: N(0,1) + 0.5% x20 outliers
 All generators are numpy PCG64 seeded with fixed integers.
 """
 import numpy as np
@@ -119,6 +121,13 @@ def activation_sr(rows: int = 4096, cols: int = 4096):
 
 def dense_forward(m: int = 8192, k: int = 4096, n: int = 14336):
     return {"x": normal_with_outliers(m, k, 301), "w": normal(n, k, 302, 0.02)}
+
+
+MLP_SEEDS = {"mx8": 602}
+
+
+def mlp_hidden(m: int = 8192, n: int = 14336):
+    return {"h": normal_with_outliers(m, n, 601), "seeds": MLP_SEEDS}
 
 
 BWD_SEEDS = {"dy_col": 403, "dy_mx8": 404, "x_col": 405, "w_req": 406}
