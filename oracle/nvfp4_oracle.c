@@ -25,6 +25,11 @@
  *  Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
  *        Easy as 1, 2, 3", SC'11 (the generator is not on the pages; it is
  *        the counter-based generator both sides implement independently).
+ *  [E2E] "End-to-End 4-Bit Training", quantized communication: 32-point
+ *        RHT, then block-scaled S2F6 (int8 / 64, one E8M0 scale per 32);
+ *        [VZ] section 11 (the combine wire format, dequantize + sum on
+ *        receipt, then the inverse rotation).
+ *  [FTB] "FP4 Training on Blackwell", "The scaling math, worked": MXFP4.
  *  GELU: Hendrycks and Gimpel, "Gaussian Error Linear Units", tanh form; exp
  *        by Cody-Waite range reduction and a Taylor polynomial (neither is on
  *        the pages; both sides implement the same FP32 steps independently so
@@ -584,6 +589,182 @@ void orc_mxfp8_encode(const float *x, int64_t R, int64_t C, int mode, uint64_t s
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Combine wire format: 32-point RHT + block-scaled S2F6 ([E2E] quantized   */
+/* communication; [VZ] section 11)                                          */
+/* ------------------------------------------------------------------------ */
+
+/* y <- (y * S) * H32 / sqrt(32): flip the sign of y[i] where bit i of
+ * `signs` is set, then the natural-order Sylvester Hadamard matrix as five
+ * sum/difference stages (pair distance 1, 2, 4, 8, 16), then one multiply
+ * by 1/sqrt(32) rounded to FP32; every step in FP32. */
+static const float ORC_INV_SQRT32 = 0.17677669529663688f;
+
+void orc_rht32(float y[32], uint32_t signs)
+{
+    for (int i = 0; i < 32; ++i)
+        if ((signs >> i) & 1u) y[i] = -y[i];
+    for (int h = 1; h < 32; h <<= 1)
+        for (int i = 0; i < 32; ++i)
+            if ((i & h) == 0) {
+                float p = y[i], q = y[i + h];
+                y[i] = p + q;
+                y[i + h] = p - q;
+            }
+    for (int i = 0; i < 32; ++i) y[i] = y[i] * ORC_INV_SQRT32;
+}
+
+/* The inverse: H32 / sqrt(32) is its own inverse, so the same stages and
+ * multiply come first and the sign flips last. */
+void orc_rht32_inv(float y[32], uint32_t signs)
+{
+    for (int h = 1; h < 32; h <<= 1)
+        for (int i = 0; i < 32; ++i)
+            if ((i & h) == 0) {
+                float p = y[i], q = y[i + h];
+                y[i] = p + q;
+                y[i + h] = p - q;
+            }
+    for (int i = 0; i < 32; ++i) y[i] = y[i] * ORC_INV_SQRT32;
+    for (int i = 0; i < 32; ++i)
+        if ((signs >> i) & 1u) y[i] = -y[i];
+}
+
+/* S2F6 copy of x[R][C] (C % 32 == 0), blocks of 32 along the rows: with
+ * rht, each block is rotated first; k = the smallest integer (clamped to
+ * [-127, 127]) with amax <= (127/64) 2^k, so no value saturates; codes
+ * q = rint(y 2^-k 64) (nearest, ties to even) as int8, scale byte k + 127.
+ * The value of a code is q / 64 * 2^k. */
+void orc_s2f6_encode(const float *x, int64_t R, int64_t C, int rht, uint32_t signs,
+                     int8_t *codes, uint8_t *scales)
+{
+    const int64_t nb = C / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t b = 0; b < nb; ++b) {
+            float y[32];
+            for (int j = 0; j < 32; ++j) y[j] = x[i * C + b * 32 + j];
+            if (rht) orc_rht32(y, signs);
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j)
+                if (fabsf(y[j]) > amax) amax = fabsf(y[j]);
+            const int k = orc_e8m0_k_for(amax, 127.0 / 64.0);
+            scales[i * nb + b] = (uint8_t)(k + 127);
+            for (int j = 0; j < 32; ++j) {
+                float q = rintf(ldexpf(y[j], 6 - k));
+                if (q > 127.0f) q = 127.0f;
+                if (q < -128.0f) q = -128.0f;
+                codes[i * C + b * 32 + j] = (int8_t)q;
+            }
+        }
+}
+
+void orc_s2f6_quantize(const uint16_t *src, int64_t R, int64_t C, int64_t ld, int rht,
+                       uint32_t signs, int8_t *codes, uint8_t *scales)
+{
+    float *x = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    orc_bf16_to_f32(src, R, C, ld, x);
+    orc_s2f6_encode(x, R, C, rht, signs, codes, scales);
+    free(x);
+}
+
+/* Receiver side: out[t] = inverse RHT (if rht) of sum_j w[t][j] * deq(row
+ * src[t][j]) per block of 32, j = 0 .. K-1 in order (rows with a negative
+ * index are skipped; w == NULL means weight 1 and no multiply); every step
+ * in FP32: the decoded value q 2^(k-6) is exact, then the product with the
+ * weight and each addition round. */
+void orc_s2f6_combine(const int8_t *codes, const uint8_t *scales, int64_t C,
+                      const int32_t *src, const float *w, int64_t T, int K, int rht,
+                      uint32_t signs, float *out)
+{
+    const int64_t nb = C / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t b = 0; b < nb; ++b) {
+            float acc[32];
+            for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
+            for (int j = 0; j < K; ++j) {
+                const int32_t r = src[t * K + j];
+                if (r < 0) continue;
+                const int k = (int)scales[(int64_t)r * nb + b] - 127;
+                for (int i = 0; i < 32; ++i) {
+                    float d = ldexpf((float)codes[(int64_t)r * C + b * 32 + i], k - 6);
+                    if (w) d = w[t * K + j] * d;
+                    acc[i] = acc[i] + d;
+                }
+            }
+            if (rht) orc_rht32_inv(acc, signs);
+            for (int i = 0; i < 32; ++i) out[t * C + b * 32 + i] = acc[i];
+        }
+}
+
+void orc_s2f6_dequant_f64(const int8_t *codes, const uint8_t *scales, int64_t R, int64_t C,
+                          double *out)
+{
+    const int64_t nb = C / 32;
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j)
+            out[i * C + j] = ldexp((double)codes[i * C + j],
+                                   (int)scales[i * nb + j / 32] - 127 - 6);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4 ([FTB] "The scaling math, worked")                                  */
+/* ------------------------------------------------------------------------ */
+
+/* MXFP4 copy of x[R][C] (C % 32 == 0), blocks of 32 along the rows: scale
+ * 2^k with k = ceil(log2(amax / 6)), i.e. the smallest k with amax <= 6 2^k
+ * (clamped to [-127, 127]); elements x 2^-k rounded onto the E2M1 grid
+ * (nearest even, or stochastic with the element's draw), packed two per
+ * byte (even column in the low nibble); scale byte k + 127. */
+void orc_mxfp4_encode(const float *x, int64_t R, int64_t C, int mode, uint64_t seed,
+                      uint32_t stream, uint8_t *codes, uint8_t *scales)
+{
+    const int64_t nb = C / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t b = 0; b < nb; ++b) {
+            float amax_b = 0.0f;
+            for (int64_t j = b * 32; j < b * 32 + 32; ++j)
+                if (fabsf(x[i * C + j]) > amax_b) amax_b = fabsf(x[i * C + j]);
+            const int k = orc_e8m0_k_for(amax_b, 6.0);
+            scales[i * nb + b] = (uint8_t)(k + 127);
+            for (int64_t j = b * 32; j < b * 32 + 32; j += 2) {
+                uint32_t nib[2];
+                for (int e = 0; e < 2; ++e) {
+                    const float v = ldexpf(x[i * C + j + e], -k);
+                    const float u = (mode == ORC_SR)
+                                        ? orc_sr_uniform(seed, stream, (uint64_t)(i * C + j + e))
+                                        : 0.0f;
+                    nib[e] = orc_e2m1_code(orc_round(v, ORC_E2M1, mode, u));
+                }
+                codes[(i * C + j) / 2] = (uint8_t)(nib[0] | (nib[1] << 4));
+            }
+        }
+}
+
+void orc_mxfp4_quantize(const uint16_t *src, int64_t R, int64_t C, int64_t ld, int mode,
+                        uint64_t seed, uint32_t stream, uint8_t *codes, uint8_t *scales)
+{
+    float *x = (float *)malloc(sizeof(float) * (size_t)(R * C));
+    orc_bf16_to_f32(src, R, C, ld, x);
+    orc_mxfp4_encode(x, R, C, mode, seed, stream, codes, scales);
+    free(x);
+}
+
+void orc_mxfp4_dequant_f64(const uint8_t *codes, const uint8_t *scales, int64_t R, int64_t C,
+                           double *out)
+{
+    const int64_t nb = C / 32;
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j) {
+            const uint32_t byte = codes[(i * C + j) / 2];
+            const uint32_t nib = (j & 1) ? (byte >> 4) : (byte & 15u);
+            out[i * C + j] = orc_e2m1_value(nib) *
+                             ldexp(1.0, (int)scales[i * nb + j / 32] - 127);
+        }
+}
+
 /* Dequantize -> transpose -> requantize to MXFP8 ([VZ] sec 9-10; [TML]
  * "requantization with stochastic rounding"): the NVFP4 matrix src[R][C]
  * becomes the MXFP8 matrix of src^T, shape C x R, blocks of 32 along R. */
@@ -679,6 +860,14 @@ void orc_e4m3_code_n(const float *g, int64_t n, uint8_t *out)
 void orc_sr_uniform_n(uint64_t seed, uint32_t stream, const uint64_t *idx, int64_t n, float *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_sr_uniform(seed, stream, idx[i]);
+}
+
+void orc_rht32_n(float *y, int64_t nchunks, uint32_t signs, int inverse)
+{
+    for (int64_t i = 0; i < nchunks; ++i) {
+        if (inverse) orc_rht32_inv(y + 32 * i, signs);
+        else orc_rht32(y + 32 * i, signs);
+    }
 }
 
 void orc_rht16_n(float *y, int64_t nchunks, uint32_t signs)

@@ -34,6 +34,7 @@ def lib():
         u64p = np.ctypeslib.ndpointer(np.uint64, flags="C_CONTIGUOUS")
         i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
         i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+        i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
         i64, u64, u32, i32, f32 = C.c_int64, C.c_uint64, C.c_uint32, C.c_int, C.c_float
         sig = {
             "orc_e2m1_value": (C.c_double, [u32]),
@@ -73,6 +74,15 @@ def lib():
             "orc_exp_n": (None, [f32p, i64, f32p]),
             "orc_gelu_n": (None, [f32p, i64, f32p]),
             "orc_nvfp4_dequant_rows_f64": (None, [u8p, u8p, f32p, i64, i64, f64p]),
+            "orc_rht32_n": (None, [f32p, i64, u32, i32]),
+            "orc_s2f6_encode": (None, [f32p, i64, i64, i32, u32, i8p, u8p]),
+            "orc_s2f6_quantize": (None, [u16p, i64, i64, i64, i32, u32, i8p, u8p]),
+            "orc_s2f6_combine": (None, [i8p, u8p, i64, i32p, C.c_void_p, i64, i32, i32, u32,
+                                        f32p]),
+            "orc_s2f6_dequant_f64": (None, [i8p, u8p, i64, i64, f64p]),
+            "orc_mxfp4_encode": (None, [f32p, i64, i64, i32, u64, u32, u8p, u8p]),
+            "orc_mxfp4_quantize": (None, [u16p, i64, i64, i64, i32, u64, u32, u8p, u8p]),
+            "orc_mxfp4_dequant_f64": (None, [u8p, u8p, i64, i64, f64p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -331,6 +341,96 @@ def mxfp8_requantize_t(q: NVFP4, mode=SR, seed=0, stream=0) -> MXFP8:
                                  q.s_dec, R, Cc, int(q.tile2d), mode, seed, stream, codes,
                                  scales)
     return MXFP8(codes, scales, Cc, R)
+
+
+# --------------------------------------------------------------------------
+# Combine wire format (32-point RHT + block-scaled S2F6) and MXFP4
+# --------------------------------------------------------------------------
+
+def rht32(y, signs: int, inverse=False) -> np.ndarray:
+    """32-point RHT of each consecutive 32-chunk of y (FP32), or its inverse."""
+    y = np.array(y, np.float32, copy=True).reshape(-1)
+    assert y.size % 32 == 0
+    lib().orc_rht32_n(y, y.size // 32, signs, int(inverse))
+    return y
+
+
+class S2F6:
+    """One S2F6 copy: int8 codes [r][c], E8M0 scales [r][c/32]; value of a
+    code = code / 64 * 2^(scale - 127)."""
+
+    def __init__(self, codes, scales, rows, cols):
+        self.codes, self.scales, self.rows, self.cols = codes, scales, rows, cols
+
+    def dequant_f64(self) -> np.ndarray:
+        out = np.empty((self.rows, self.cols), np.float64)
+        lib().orc_s2f6_dequant_f64(self.codes, self.scales, self.rows, self.cols, out)
+        return out
+
+
+def s2f6_quantize(x_bf16: np.ndarray, rht=True, signs=0) -> S2F6:
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    R, Cc = x.shape
+    codes = np.zeros((R, Cc), np.int8)
+    scales = np.zeros((R, Cc // 32), np.uint8)
+    lib().orc_s2f6_quantize(x, R, Cc, Cc, int(rht), signs, codes, scales)
+    return S2F6(codes, scales, R, Cc)
+
+
+def s2f6_encode_f32(x: np.ndarray, rht=True, signs=0) -> S2F6:
+    x = np.ascontiguousarray(x, np.float32)
+    R, Cc = x.shape
+    codes = np.zeros((R, Cc), np.int8)
+    scales = np.zeros((R, Cc // 32), np.uint8)
+    lib().orc_s2f6_encode(x, R, Cc, int(rht), signs, codes, scales)
+    return S2F6(codes, scales, R, Cc)
+
+
+def s2f6_combine(q: S2F6, src, weights=None, rht=True, signs=0) -> np.ndarray:
+    """out[t] = inverse RHT of sum_j weights[t, j] * dequant(q row src[t, j])
+    (FP32; negative indices skipped; weights None = 1)."""
+    src = np.ascontiguousarray(src, np.int32)
+    T, K = src.shape
+    out = np.empty((T, q.cols), np.float32)
+    w = None
+    if weights is not None:
+        w = np.ascontiguousarray(weights, np.float32)
+        assert w.shape == (T, K)
+    lib().orc_s2f6_combine(np.ascontiguousarray(q.codes), np.ascontiguousarray(q.scales), q.cols,
+                           src, None if w is None else w.ctypes.data, T, K, int(rht), signs,
+                           out)
+    return out
+
+
+class MXFP4:
+    """One MXFP4 copy: E2M1 codes [r][c/2] (even column in the low nibble),
+    E8M0 scales [r][c/32]."""
+
+    def __init__(self, codes, scales, rows, cols):
+        self.codes, self.scales, self.rows, self.cols = codes, scales, rows, cols
+
+    def dequant_f64(self) -> np.ndarray:
+        out = np.empty((self.rows, self.cols), np.float64)
+        lib().orc_mxfp4_dequant_f64(self.codes, self.scales, self.rows, self.cols, out)
+        return out
+
+
+def mxfp4_quantize(x_bf16: np.ndarray, mode=RTN, seed=0, stream=0) -> MXFP4:
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    R, Cc = x.shape
+    codes = np.zeros((R, Cc // 2), np.uint8)
+    scales = np.zeros((R, Cc // 32), np.uint8)
+    lib().orc_mxfp4_quantize(x, R, Cc, Cc, mode, seed, stream, codes, scales)
+    return MXFP4(codes, scales, R, Cc)
+
+
+def mxfp4_encode_f32(x: np.ndarray, mode=RTN, seed=0, stream=0) -> MXFP4:
+    x = np.ascontiguousarray(x, np.float32)
+    R, Cc = x.shape
+    codes = np.zeros((R, Cc // 2), np.uint8)
+    scales = np.zeros((R, Cc // 32), np.uint8)
+    lib().orc_mxfp4_encode(x, R, Cc, mode, seed, stream, codes, scales)
+    return MXFP4(codes, scales, R, Cc)
 
 
 # --------------------------------------------------------------------------
