@@ -138,7 +138,9 @@ def moe_bench(torch, bbs, dev, reps):
     tokens x hidden 4096, 64 experts, top-8 Zipf(1.1) routing with 4 empty
     experts; up-projection 4096 -> 1536 over the gathered routed rows, then
     the up output is quantized (1x16, RTN) and projected 1536 -> 4096.  Each
-    expert's weight is its own NVFP4 tensor (16x16 scales, own s_dec)."""
+    expert's weight is its own NVFP4 tensor (16x16 scales, own s_dec).  The
+    down output then goes through the combine wire format (RHT-32 + S2F6
+    encode; weighted sum of each token's 8 rows + inverse RHT)."""
     from workloads import synth
     T_, H_, F_, E_, K_ = 65536, 4096, 1536, 64, 8
     d = synth.moe_forward(T_, H_, F_, E_, K_, with_weights=False)
@@ -146,6 +148,11 @@ def moe_bench(torch, bbs, dev, reps):
     x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
     ri = torch.from_numpy(d["row_index"]).to(dev)
     off = torch.from_numpy(d["group_offsets"]).to(dev)
+    # the combine: each token's K rows of the down output (expert order)
+    src = torch.from_numpy(np.argsort(d["row_index"], kind="stable").astype(np.int32)
+                           .reshape(T_, K_)).to(dev)
+    gate = torch.softmax(torch.randn((T_, K_), generator=torch.Generator().manual_seed(702)),
+                         dim=1).to(dev)
     del d
     ws = bbs.amax_workspace(dev)
     N4 = bbs.NVFP4Tensor
@@ -166,12 +173,21 @@ def moe_bench(torch, bbs, dev, reps):
     h = torch.empty((rows, F_), dtype=torch.int16, device=dev)
     hq = N4.empty(rows, F_, device=dev)
     y = torch.empty((rows, H_), dtype=torch.int16, device=dev)
+    yq = bbs.S2F6Tensor.empty(rows, H_, device=dev)
+    comb = torch.empty((T_, H_), dtype=torch.int16, device=dev)
+    signs = 0xB5297A4D
     ops = {
         "moe_up": lambda: bbs.grouped_nvfp4_gemm(xq, ri, off, E_, rows, w_up, F_, h, bbs.OUT_BF16),
         "moe_quant_h": lambda: bbs.nvfp4_quantize(h, hq, amax_ws=ws),
         "moe_down": lambda: bbs.grouped_nvfp4_gemm(hq, None, off, E_, rows, w_dn, H_, y,
                                                    bbs.OUT_BF16),
+        # combine wire format: RHT-32 + S2F6 encode of the down output, then
+        # the receiver's weighted sum over each token's K rows + inverse RHT
+        "combine_encode": lambda: bbs.s2f6_quantize(y, yq, rht=True, signs=signs),
+        "combine_decode": lambda: bbs.s2f6_combine(yq, src, comb, gate, rht=True, signs=signs),
     }
+    codec_bytes = {"combine_encode": rows * H_ * 2 + rows * H_ + rows * H_ // 32,
+                   "combine_decode": rows * (H_ + H_ // 32) + rows * 8 + T_ * H_ * 2}
     out = {}
     for name, f in ops.items():
         f()
@@ -184,7 +200,11 @@ def moe_bench(torch, bbs, dev, reps):
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / reps
         e = {"ms": round(ms, 4)}
-        if name != "moe_quant_h":
+        if name in codec_bytes:
+            gbps = codec_bytes[name] / (ms * 1e-3) / 1e9
+            e.update({"GB/s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                      "bytes": codec_bytes[name]})
+        elif name != "moe_quant_h":
             tf = 2.0 * rows * F_ * H_ / (ms * 1e-3) / 1e12
             e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
         out[name] = e

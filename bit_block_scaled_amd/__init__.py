@@ -32,6 +32,11 @@ class Mx8Desc(C.Structure):
                 ("cols", C.c_int64)]
 
 
+class S2F6Desc(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("rows", C.c_int64),
+                ("cols", C.c_int64)]
+
+
 class Rng(C.Structure):
     _fields_ = [("seed", C.c_uint64), ("stream", C.c_uint32)]
 
@@ -63,7 +68,11 @@ def _load():
     lib.nvfp4_gemm.argtypes = [i32, vp, vp, vp, i32, i64, vp]
     lib.grouped_nvfp4_gemm.argtypes = [C.POINTER(Fp4Desc), vp, vp, i32, i64, C.POINTER(Fp4Desc),
                                        i64, vp, i32, i64, vp]
-    for f in ("nvfp4_quantize", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm"):
+    lib.s2f6_quantize.argtypes = [vp, i64, i64, i64, i32, C.c_uint32, C.POINTER(S2F6Desc), vp]
+    lib.s2f6_combine.argtypes = [C.POINTER(S2F6Desc), vp, vp, i64, i32, i32, C.c_uint32, vp, i32,
+                                 i64, vp]
+    for f in ("nvfp4_quantize", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm",
+              "s2f6_quantize", "s2f6_combine"):
         getattr(lib, f).restype = C.c_int
     lib.bbs_strerror.argtypes = [C.c_int]
     lib.bbs_strerror.restype = C.c_char_p
@@ -133,6 +142,22 @@ class MXFP8Tensor:
         return Mx8Desc(_ptr(self.codes), _ptr(self.scales), self.rows, self.cols)
 
 
+class S2F6Tensor:
+    """codes [rows, cols] int8 (value code / 64), scales [rows, cols/32] u8 (E8M0)."""
+
+    def __init__(self, codes, scales, rows, cols):
+        self.codes, self.scales, self.rows, self.cols = codes, scales, rows, cols
+
+    @staticmethod
+    def empty(rows, cols, device="cuda"):
+        return S2F6Tensor(torch.empty((rows, cols), dtype=torch.int8, device=device),
+                          torch.empty((rows, cols // 32), dtype=torch.uint8, device=device),
+                          rows, cols)
+
+    def desc(self):
+        return S2F6Desc(_ptr(self.codes), _ptr(self.scales), self.rows, self.cols)
+
+
 def amax_workspace(device="cuda"):
     return torch.empty((AMAX_WS_FLOATS,), dtype=torch.float32, device=device)
 
@@ -183,3 +208,22 @@ def grouped_nvfp4_gemm(A, row_index, group_offsets, G, max_rows, B, N, C_out, c_
     ldc = C_out.stride(0) if ldc is None else ldc
     _check(lib.grouped_nvfp4_gemm(C.byref(ad), _ptr(row_index), _ptr(group_offsets), G, max_rows,
                                   C.byref(bd), N, _ptr(C_out), c_dtype, ldc, _stream(stream)))
+
+
+def s2f6_quantize(x, out, rht=True, signs=0, stream=None):
+    """Combine wire format encode of x (BF16 patterns [rows, cols]) into the
+    S2F6Tensor out, with the 32-point RHT when rht."""
+    d = out.desc()
+    _check(lib.s2f6_quantize(_ptr(x), x.shape[0], x.shape[1], x.stride(0), int(rht), signs,
+                             C.byref(d), _stream(stream)))
+
+
+def s2f6_combine(inp, src_index, out, weights=None, rht=True, signs=0, out_dtype=OUT_BF16,
+                 ldo=None, stream=None):
+    """out[t] = inverse RHT of sum_j weights[t, j] * decode(inp row src_index[t, j]);
+    src_index: int32 [tokens, k] device tensor, weights: float32 [tokens, k] or None."""
+    d = inp.desc()
+    T, K = src_index.shape
+    ldo = out.stride(0) if ldo is None else ldo
+    _check(lib.s2f6_combine(C.byref(d), _ptr(src_index), _ptr(weights), T, K, int(rht), signs,
+                            _ptr(out), out_dtype, ldo, _stream(stream)))

@@ -8,7 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbbs.so")
-SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "gemm_nvfp4.hip", "gemm_mxfp8.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemm.hip", "gemm_nvfp4.hip", "gemm_mxfp8.hip",
+           "codec.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

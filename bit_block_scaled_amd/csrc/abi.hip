@@ -58,9 +58,64 @@ int check_mx8(const bbs_mx8 *d, const char *name) {
 
 bool round_ok(int32_t r) { return r == BBS_RTN || r == BBS_SR; }
 
+int check_s2f6(const bbs_s2f6 *d, const char *name) {
+    if (!d) return fail(BBS_EINVAL, "%s: null descriptor", name);
+    if (!d->codes || !d->scales) return fail(BBS_EINVAL, "%s: null codes/scales", name);
+    if (d->rows <= 0 || d->cols <= 0 || d->cols % 32)
+        return fail(BBS_EINVAL, "%s: rows=%lld cols=%lld (cols must be a multiple of 32)", name,
+                    (long long)d->rows, (long long)d->cols);
+    if (!aligned(d->codes, 16)) return fail(BBS_EINVAL, "%s: codes not 16-byte aligned", name);
+    return BBS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int s2f6_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int32_t rht,
+                  uint32_t signs, const bbs_s2f6 *out, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if (!x) return fail(BBS_EINVAL, "null x");
+    if ((st = check_s2f6(out, "out"))) return st;
+    if (out->rows != rows || out->cols != cols) return fail(BBS_EINVAL, "out must be rows x cols");
+    if (ld < cols || ld % 8) return fail(BBS_EINVAL, "ld must be >= cols and a multiple of 8");
+    if (!aligned(x, 16)) return fail(BBS_EINVAL, "x not 16-byte aligned");
+    if (rht != 0 && rht != 1) return fail(BBS_EINVAL, "rht must be 0 or 1");
+    return hip_status(bbs::launch_s2f6_encode(x, rows, cols, ld, rht != 0, signs, out->codes,
+                                              out->scales, reinterpret_cast<hipStream_t>(stream)),
+                      "s2f6 encode launch");
+}
+
+int s2f6_combine(const bbs_s2f6 *in, const int32_t *src_index, const float *weights,
+                 int64_t tokens, int32_t k, int32_t rht, uint32_t signs, void *out,
+                 int32_t out_dtype, int64_t ldo, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_s2f6(in, "in"))) return st;
+    if (!src_index || !out) return fail(BBS_EINVAL, "null src_index / out");
+    if (tokens <= 0 || k <= 0) return fail(BBS_EINVAL, "tokens and k must be positive");
+    if (rht != 0 && rht != 1) return fail(BBS_EINVAL, "rht must be 0 or 1");
+    if (out_dtype != BBS_OUT_F32 && out_dtype != BBS_OUT_BF16)
+        return fail(BBS_EINVAL, "bad out_dtype");
+    const int64_t esz = out_dtype == BBS_OUT_BF16 ? 2 : 4;
+    if (ldo < in->cols || (ldo * esz) % 16 || !aligned(out, 16))
+        return fail(BBS_EINVAL, "out must be 16-byte aligned with ldo >= cols, ldo * size %% 16 == 0");
+    bbs::S2F6CombineParams p{};
+    p.codes = in->codes;
+    p.scales = in->scales;
+    p.C = in->cols;
+    p.src = src_index;
+    p.w = weights;
+    p.T = tokens;
+    p.K = k;
+    p.signs = signs;
+    p.out = out;
+    p.ldo = ldo;
+    return hip_status(bbs::launch_s2f6_combine(p, rht != 0, out_dtype == BBS_OUT_BF16,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                      "s2f6 combine launch");
+}
 
 const char *bbs_strerror(int status) {
     switch (status) {

@@ -82,6 +82,26 @@ struct Mx8GemmParams {
     int64_t ldc;
 };
 
+struct S2F6CombineParams {
+    const int8_t *codes;
+    const uint8_t *scales;
+    int64_t C;                 // values per row (C % 32 == 0)
+    const int32_t *src;        // T x K rows of codes (negative: skipped)
+    const float *w;            // T x K weights, or nullptr (weight 1)
+    int64_t T;
+    int K;
+    uint32_t signs;
+    void *out;
+    int64_t ldo;
+};
+
+// Combine wire format: S2F6 encode (optionally rotated) and the receiver's
+// weighted sum + inverse rotation.
+hipError_t launch_s2f6_encode(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool rht,
+                              uint32_t signs, int8_t *codes, uint8_t *scales, hipStream_t s);
+hipError_t launch_s2f6_combine(const S2F6CombineParams &p, bool rht, bool bf16_out,
+                               hipStream_t s);
+
 // One read of x: partial maxima of |x| (plain) into part and of the RHT'd
 // column chunks (rht) into part_rht; *n_part partials each.  With gelu (and
 // plain, without rht) the partials are maxima of |GELU(x)|, and the pass

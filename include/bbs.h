@@ -196,6 +196,43 @@ int grouped_nvfp4_gemm(const bbs_fp4 *A, const int32_t *row_index,
                        const bbs_fp4 *B, int64_t N, void *C, int32_t c_dtype, int64_t ldc,
                        void *stream);
 
+/* One S2F6 tensor (combine wire format; 4bit.vizuara.ai, section 11;
+ * End-to-End 4-Bit Training, "quantized communication"): value =
+ * code / 64 * 2^(scale - 127), int8 codes rows x cols, one E8M0 scale per
+ * 32 consecutive values of a row (rows x cols/32 bytes): 8.25 bits per
+ * value.  codes 16-byte aligned, cols % 32 == 0. */
+typedef struct {
+    int8_t *codes;
+    uint8_t *scales;
+    int64_t rows, cols;
+} bbs_s2f6;
+
+/* Encode of the combine wire format.  For each 32-value chunk of each row of
+ * the BF16 matrix x (rows x cols, row stride ld elements, x 16-byte aligned,
+ * ld % 8 == 0): with rht = 1, flip the sign of element i where bit i of
+ * signs is set, apply the natural-order Sylvester Hadamard matrix as five
+ * FP32 sum/difference stages (pair distance 1, 2, 4, 8, 16) and multiply by
+ * 1/sqrt(32) rounded to FP32; then k = the smallest integer in [-127, 127]
+ * with amax <= (127/64) 2^k, scale byte k + 127, codes rint(y 2^(6-k))
+ * (nearest, ties to even; no value saturates).  out->rows/cols must equal
+ * rows/cols.  Errors: BBS_EINVAL. */
+int s2f6_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int32_t rht,
+                  uint32_t signs, const bbs_s2f6 *out, void *stream);
+
+/* Receiver side of the combine: for each token t < tokens and each 32-value
+ * chunk, acc = sum over j = 0 .. k-1 (in order, FP32) of
+ * weights[t*k + j] * decode(row src_index[t*k + j] of in), where decode is
+ * exact and rows with a negative index are skipped (weights NULL: weight 1,
+ * no multiply); with rht = 1 the inverse rotation follows (the same stages
+ * and multiply, then the sign flips).  out is tokens x in->cols with row
+ * stride ldo elements of out_dtype (BBS_OUT_F32, or BBS_OUT_BF16 rounded to
+ * nearest even), 16-byte aligned with ldo * size % 16 == 0.  src_index
+ * entries must be < in->rows (not checked on the device).
+ * Errors: BBS_EINVAL. */
+int s2f6_combine(const bbs_s2f6 *in, const int32_t *src_index, const float *weights,
+                 int64_t tokens, int32_t k, int32_t rht, uint32_t signs, void *out,
+                 int32_t out_dtype, int64_t ldo, void *stream);
+
 /* Name of a status code. */
 const char *bbs_strerror(int status);
 

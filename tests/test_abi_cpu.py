@@ -175,3 +175,24 @@ def test_gelu_option_errors(lib):
     a.amax_ws = 0x4004
     assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL
     assert b"aligned" in L.bbs_last_error()
+
+
+def test_s2f6_errors(lib):
+    """Combine wire format: shapes, pointers and output layout are checked."""
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    d = bbs.S2F6Desc(0x1000, 0x2000, 8, 48)                 # cols not a multiple of 32
+    assert L.s2f6_quantize(C.c_void_p(0x1000), 8, 48, 48, 1, 0, C.byref(d), None) == bbs.BBS_EINVAL
+    d.cols = 64
+    assert L.s2f6_quantize(None, 8, 64, 64, 1, 0, C.byref(d), None) == bbs.BBS_EINVAL
+    assert L.s2f6_quantize(C.c_void_p(0x1000), 8, 64, 60, 1, 0, C.byref(d), None) == bbs.BBS_EINVAL
+    assert L.s2f6_quantize(C.c_void_p(0x1000), 8, 64, 64, 2, 0, C.byref(d), None) == bbs.BBS_EINVAL
+    assert L.s2f6_quantize(C.c_void_p(0x1000), 16, 64, 64, 1, 0, C.byref(d), None) == bbs.BBS_EINVAL
+    src, out = C.c_void_p(0x3000), C.c_void_p(0x4000)
+    assert L.s2f6_combine(C.byref(d), None, None, 4, 2, 1, 0, out, 1, 64, None) == bbs.BBS_EINVAL
+    assert L.s2f6_combine(C.byref(d), src, None, 0, 2, 1, 0, out, 1, 64, None) == bbs.BBS_EINVAL
+    assert L.s2f6_combine(C.byref(d), src, None, 4, 2, 1, 0, out, 7, 64, None) == bbs.BBS_EINVAL
+    assert L.s2f6_combine(C.byref(d), src, None, 4, 2, 1, 0, out, 1, 60, None) == bbs.BBS_EINVAL
+    assert L.s2f6_combine(C.byref(d), src, None, 4, 2, 1, 0, C.c_void_p(0x4004), 1, 64,
+                          None) == bbs.BBS_EINVAL
+    assert b"aligned" in L.bbs_last_error()

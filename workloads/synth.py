@@ -13,6 +13,10 @@ Shapes and distributions follow the five workloads of the hot path:
                    W_up[g] [1536 x 4096], W_down[g] [4096 x 1536] N(0, 0.02)
   MLP hidden       H [8192 x 14336], the pre-activation between the dense
                    layer's two projections: N(0,1) + 0.5% x20 outliers
+  MoE combine      Y [524288 x 4096], the routed expert outputs of the MoE
+                   forward in expert order (N(0,1) + 0.35% x10 outliers:
+                   kurtosis about 55, near the 59 of the pages' MLP outputs),
+                   each token's 8 rows and gate weights (softmax of N(0,1))
 All generators are numpy PCG64 seeded with fixed integers.
 """
 import numpy as np
@@ -121,6 +125,58 @@ def activation_sr(rows: int = 4096, cols: int = 4096):
 
 def dense_forward(m: int = 8192, k: int = 4096, n: int = 14336):
     return {"x": normal_with_outliers(m, k, 301), "w": normal(n, k, 302, 0.02)}
+
+
+def combine_values(rows: int, cols: int, seed: int, frac: float = 0.0035,
+                   factor: float = 10.0, chunk_rows: int = 4096) -> np.ndarray:
+    """BF16 [rows, cols]: N(0,1) with about a fraction `frac` of the entries
+    (binomial count, uniform positions) multiplied by `factor`, drawn in row
+    chunks (bounded memory)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((rows, cols), np.uint16)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = rng.standard_normal((r1 - r0) * cols, dtype=np.float32)
+        hit = rng.integers(0, x.size, rng.binomial(x.size, frac))
+        x[hit] *= np.float32(factor)
+        out[r0:r1] = bf16_bits(x).reshape(r1 - r0, cols)
+    return out
+
+
+def combine_values_device(rows: int, cols: int, seed: int, device, frac: float = 0.0035,
+                          factor: float = 10.0, chunk_rows: int = 65536):
+    """The same distribution as combine_values, drawn on a GPU with torch's
+    seeded generator (for sizes the host would take minutes to draw); BF16
+    bit patterns as an int16 device tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty((rows, cols), dtype=torch.int16, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = torch.randn((r1 - r0, cols), generator=g, device=device, dtype=torch.float32)
+        hit = torch.rand((r1 - r0, cols), generator=g, device=device) < frac
+        x = torch.where(hit, x * factor, x)
+        out[r0:r1] = x.to(torch.bfloat16).view(torch.int16)
+    return out
+
+
+def moe_combine(tokens: int = 65536, hidden: int = 4096, experts: int = 64, topk: int = 8,
+                device=None):
+    """Combine inputs of the MoE layer: expert outputs in expert order (a
+    device tensor when device is given), the rows of each token (src[t, j])
+    and its gate weights."""
+    row_index, _ = moe_routing(tokens, experts, topk, 502)
+    src = np.argsort(row_index, kind="stable").astype(np.int32).reshape(tokens, topk)
+    rng = np.random.Generator(np.random.PCG64(702))
+    g = rng.standard_normal((tokens, topk))
+    w = np.exp(g - g.max(axis=1, keepdims=True))
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    if device is None:
+        y = combine_values(tokens * topk, hidden, 701)
+    else:
+        y = combine_values_device(tokens * topk, hidden, 701, device)
+    return {"y": y, "src": src, "w": w, "signs": int(rng.integers(0, 1 << 32))}
 
 
 MLP_SEEDS = {"mx8": 602}
