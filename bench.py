@@ -398,6 +398,34 @@ def main():
     print(f"[bench] fused GELU + quantize of H {M}x{N}: {json.dumps(gelu)}", file=sys.stderr,
           flush=True)
 
+    # The MXFP4 comparison format: X and W as MXFP4 (E2M1, E8M0 per 32; RTN)
+    # and the same forward GEMM on the block-scaled MFMA with E2M1 operands.
+    x4, w4 = bbs.MXFP4Tensor.empty(M, K, device=dev), bbs.MXFP4Tensor.empty(N, K, device=dev)
+    mx4_ops = {
+        "mxfp4_quant_x": (lambda: bbs.mxfp4_quantize(x, x4), 2 * M * K + M * K // 2 + M * K // 32),
+        "mxfp4_quant_w": (lambda: bbs.mxfp4_quantize(w, w4), 2 * N * K + N * K // 2 + N * K // 32),
+        "mxfp4_fprop": (lambda: bbs.nvfp4_gemm(bbs.FMT_MXFP4, x4, w4, y, bbs.OUT_BF16), None),
+    }
+    mx4 = {}
+    for name, (f, b) in mx4_ops.items():
+        f()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        t_ms = s0.elapsed_time(s1) / args.steps
+        e = {"ms": round(t_ms, 4)}
+        if b is None:
+            tf = GEMM_FLOP / (t_ms * 1e-3) / 1e12
+            e.update({"TFLOP/s": round(tf, 1), "fp4_peak_frac": round(tf / PEAK_FP4_TFLOPS, 4)})
+        else:
+            e.update({"GB/s": round(b / (t_ms * 1e-3) / 1e9, 1), "bytes": b})
+        mx4[name] = e
+    del x4, w4
+    print(f"[bench] MXFP4 forward: {json.dumps(mx4)}", file=sys.stderr, flush=True)
+
     fprop_ms = per["fprop"]
     fprop_tf = GEMM_FLOP / (fprop_ms * 1e-3) / 1e12
     qbytes = ab["quant_x"] + ab["quant_w"]
@@ -430,6 +458,7 @@ def main():
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
         "activation_per_token_4over6": act,
         "gelu_quantize_mlp_hidden_8192x14336": gelu,
+        "mxfp4_forward_8192x14336x4096": mx4,
         "wall_s_timed": round(wall_s, 3),
     }
     if not args.no_moe:

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libbbs.so")
 BBS_OK, BBS_EINVAL, BBS_ENOTSUP, BBS_EHIP = 0, -1, -2, -3
 RTN, SR = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-FMT_NVFP4, FMT_MXFP8 = 0, 1
+FMT_NVFP4, FMT_MXFP8, FMT_MXFP4 = 0, 1, 2
 AMAX_WS_FLOATS = 11264
 
 
@@ -28,6 +28,11 @@ class Fp4Desc(C.Structure):
 
 
 class Mx8Desc(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("rows", C.c_int64),
+                ("cols", C.c_int64)]
+
+
+class Mx4Desc(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("rows", C.c_int64),
                 ("cols", C.c_int64)]
 
@@ -68,11 +73,12 @@ def _load():
     lib.nvfp4_gemm.argtypes = [i32, vp, vp, vp, i32, i64, vp]
     lib.grouped_nvfp4_gemm.argtypes = [C.POINTER(Fp4Desc), vp, vp, i32, i64, C.POINTER(Fp4Desc),
                                        i64, vp, i32, i64, vp]
+    lib.mxfp4_quantize.argtypes = [vp, i64, i64, i64, C.POINTER(Mx4Desc), i32, Rng, vp]
     lib.s2f6_quantize.argtypes = [vp, i64, i64, i64, i32, C.c_uint32, C.POINTER(S2F6Desc), vp]
     lib.s2f6_combine.argtypes = [C.POINTER(S2F6Desc), vp, vp, i64, i32, i32, C.c_uint32, vp, i32,
                                  i64, vp]
     for f in ("nvfp4_quantize", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm",
-              "s2f6_quantize", "s2f6_combine"):
+              "s2f6_quantize", "s2f6_combine", "mxfp4_quantize"):
         getattr(lib, f).restype = C.c_int
     lib.bbs_strerror.argtypes = [C.c_int]
     lib.bbs_strerror.restype = C.c_char_p
@@ -140,6 +146,22 @@ class MXFP8Tensor:
 
     def desc(self):
         return Mx8Desc(_ptr(self.codes), _ptr(self.scales), self.rows, self.cols)
+
+
+class MXFP4Tensor:
+    """codes [rows, cols/2] u8 (E2M1 pairs, even column low), scales [rows, cols/32] u8 (E8M0)."""
+
+    def __init__(self, codes, scales, rows, cols):
+        self.codes, self.scales, self.rows, self.cols = codes, scales, rows, cols
+
+    @staticmethod
+    def empty(rows, cols, device="cuda"):
+        return MXFP4Tensor(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device),
+                           torch.empty((rows, cols // 32), dtype=torch.uint8, device=device),
+                           rows, cols)
+
+    def desc(self):
+        return Mx4Desc(_ptr(self.codes), _ptr(self.scales), self.rows, self.cols)
 
 
 class S2F6Tensor:
@@ -227,3 +249,10 @@ def s2f6_combine(inp, src_index, out, weights=None, rht=True, signs=0, out_dtype
     ldo = out.stride(0) if ldo is None else ldo
     _check(lib.s2f6_combine(C.byref(d), _ptr(src_index), _ptr(weights), T, K, int(rht), signs,
                             _ptr(out), out_dtype, ldo, _stream(stream)))
+
+
+def mxfp4_quantize(x, out, round=RTN, rng=(0, 0), stream=None):
+    """MXFP4 copy of x (BF16 patterns [rows, cols]) into the MXFP4Tensor out."""
+    d = out.desc()
+    _check(lib.mxfp4_quantize(_ptr(x), x.shape[0], x.shape[1], x.stride(0), C.byref(d), round,
+                              Rng(*rng), _stream(stream)))

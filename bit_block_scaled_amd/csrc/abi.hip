@@ -58,6 +58,16 @@ int check_mx8(const bbs_mx8 *d, const char *name) {
 
 bool round_ok(int32_t r) { return r == BBS_RTN || r == BBS_SR; }
 
+int check_mx4(const bbs_mx4 *d, const char *name) {
+    if (!d) return fail(BBS_EINVAL, "%s: null descriptor", name);
+    if (!d->codes || !d->scales) return fail(BBS_EINVAL, "%s: null codes/scales", name);
+    if (d->rows <= 0 || d->cols <= 0 || d->cols % 32)
+        return fail(BBS_EINVAL, "%s: rows=%lld cols=%lld (cols must be a multiple of 32)", name,
+                    (long long)d->rows, (long long)d->cols);
+    if (!aligned(d->codes, 16)) return fail(BBS_EINVAL, "%s: codes not 16-byte aligned", name);
+    return BBS_OK;
+}
+
 int check_s2f6(const bbs_s2f6 *d, const char *name) {
     if (!d) return fail(BBS_EINVAL, "%s: null descriptor", name);
     if (!d->codes || !d->scales) return fail(BBS_EINVAL, "%s: null codes/scales", name);
@@ -71,6 +81,22 @@ int check_s2f6(const bbs_s2f6 *d, const char *name) {
 }  // namespace
 
 extern "C" {
+
+int mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                   const bbs_mx4 *out, int32_t round, bbs_rng rng, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if (!x) return fail(BBS_EINVAL, "null x");
+    if ((st = check_mx4(out, "out"))) return st;
+    if (out->rows != rows || out->cols != cols) return fail(BBS_EINVAL, "out must be rows x cols");
+    if (ld < cols || ld % 8) return fail(BBS_EINVAL, "ld must be >= cols and a multiple of 8");
+    if (!aligned(x, 16)) return fail(BBS_EINVAL, "x not 16-byte aligned");
+    if (!round_ok(round)) return fail(BBS_EINVAL, "bad round");
+    return hip_status(bbs::launch_mxfp4_quant(x, rows, cols, ld, out->codes, out->scales,
+                                              round == BBS_SR, rng.seed, rng.stream,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      "mxfp4 quantize launch");
+}
 
 int s2f6_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int32_t rht,
                   uint32_t signs, const bbs_s2f6 *out, void *stream) {
@@ -320,6 +346,29 @@ int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dty
         p.c = C;
         p.ldc = ldc;
         return hip_status(bbs::launch_mxfp8_gemm(p, c_dtype == BBS_OUT_BF16, s), "mxfp8 gemm launch");
+    }
+    if (fmt == BBS_FMT_MXFP4) {
+        const bbs_mx4 *a = static_cast<const bbs_mx4 *>(A), *b = static_cast<const bbs_mx4 *>(B);
+        if ((st = check_mx4(a, "A"))) return st;
+        if ((st = check_mx4(b, "B"))) return st;
+        if (a->cols != b->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+        if (ldc < b->rows) return fail(BBS_EINVAL, "ldc < N");
+        if (a->cols % 256) return fail(BBS_ENOTSUP, "MXFP4 GEMM needs K %% 256 == 0");
+        if (!aligned(a->scales, 4) || !aligned(b->scales, 4))
+            return fail(BBS_ENOTSUP, "MXFP4 GEMM needs 4-byte aligned scales");
+        if (b->rows % 4 || !aligned(C, 16) || ldc % 4)
+            return fail(BBS_ENOTSUP, "MXFP4 GEMM needs N %% 4 == 0, 16-byte aligned C, ldc %% 4 == 0");
+        bbs::Mx8GemmParams p{};
+        p.a_codes = a->codes;
+        p.a_scales = a->scales;
+        p.b_codes = b->codes;
+        p.b_scales = b->scales;
+        p.M = a->rows;
+        p.N = b->rows;
+        p.K = a->cols;
+        p.c = C;
+        p.ldc = ldc;
+        return hip_status(bbs::launch_mxfp4_gemm(p, c_dtype == BBS_OUT_BF16, s), "mxfp4 gemm launch");
     }
     return fail(BBS_EINVAL, "unknown fmt %d", fmt);
 }

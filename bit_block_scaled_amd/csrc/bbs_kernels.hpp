@@ -127,5 +127,12 @@ bool big_ok(const GemmParams &p, bool bf16_out);
 hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);
+// MXFP4 x MXFP4 (codes rows x K/2): K % 256 == 0, 16-byte aligned codes,
+// 4-byte aligned scales, N % 4 == 0, 16-byte aligned C with ldc % 4 == 0.
+hipError_t launch_mxfp4_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);
+// MXFP4 copy of a BF16 matrix (blocks of 32 along its rows).
+hipError_t launch_mxfp4_quant(const uint16_t *x, int64_t R, int64_t C, int64_t ld, uint8_t *codes,
+                              uint8_t *scales, bool sr, uint64_t seed, uint32_t stream,
+                              hipStream_t s);
 
 }  // namespace bbs

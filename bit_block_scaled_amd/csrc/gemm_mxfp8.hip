@@ -1,4 +1,5 @@
-// MXFP8 x MXFP8 GEMM, large-tile kernel for K % 128 == 0 (gfx950).
+// MXFP8 x MXFP8 GEMM, large-tile kernel for K % 128 == 0, and MXFP4 x MXFP4
+// for K % 256 == 0 (gfx950).
 //
 // C = sum over 32-blocks b of 2^(sa_b - 127) * 2^(sb_b - 127) * sum_{k in b}
 // a_k b_k with E4M3 elements (the dgrad GEMM of the backward pass,
@@ -20,6 +21,13 @@
 // g = l / 16; the scale of block b comes from byte 0 of lane group b's scale
 // operand.  So lane group g reads chunks g and 4 + g of its row and supplies
 // the scale of the slab's block g.
+//
+// The same kernel runs MXFP4 x MXFP4 (FP Training on Blackwell, 'The
+// scaling math, worked'; the OCP format with E2M1 elements): operand format
+// 4 of the same instruction, where lane l's first 16 bytes hold the 32
+// values of block g = l / 16 of row l % 16 (measured).  A slab is still 128
+// bytes of every row, now 256 K-values: two MFMA steps, the first reading
+// chunk g and the second chunk 4 + g, with 8 scale bytes per row.
 #include "bbs_device.hpp"
 #include "bbs_kernels.hpp"
 
@@ -29,21 +37,36 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> two BF16 (nearest even; one v_cvt_pk_bf16_f32), low first.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t h = __builtin_convertvector(f32x2_v{a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
 
 namespace mx {
 
 constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
 constexpr int GROUP_M = 8;
 
+// BK is in bytes of a row: 128 FP8 values or 256 FP4 values per slab.
+template <bool FP4>
 struct Stage {
     uint8_t a[BM * BK];
     uint8_t b[BN * BK];
-    uint32_t as[BM];              // 4 E8M0 bytes (the slab's 4 blocks) per row
-    uint32_t bs[BN];
+    uint32_t as[FP4 ? 2 : 1][BM];   // the slab's E8M0 bytes per row: 4 (FP8) or 8 (FP4)
+    uint32_t bs[FP4 ? 2 : 1][BN];
 };
+template <bool FP4>
 struct Smem {
-    Stage st[2];
+    Stage<FP4> st[2];
 };
+
+// Scale bytes (= 32-blocks) per row in one slab.
+template <bool FP4>
+constexpr int slab_blocks() { return FP4 ? 8 : 4; }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
@@ -57,19 +80,21 @@ struct Plan {
     uint32_t sa_off, sb_off;
 };
 
+template <bool FP4>
 __device__ __forceinline__ Plan make_plan(const Mx8GemmParams &p, int64_t m0, int64_t n0) {
     Plan pl;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    pl.a_base = p.a_codes + m0 * p.K;
-    pl.b_base = p.b_codes + n0 * p.K;
+    const int64_t rb = FP4 ? p.K / 2 : p.K;            // bytes per row
+    pl.a_base = p.a_codes + m0 * rb;
+    pl.b_base = p.b_codes + n0 * rb;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int row = (w * 8 + q) * 8 + (lane >> 3);     // tile row this lane fills
         const int pos = lane & 7;                          // LDS chunk position
         const int c = swz(row, pos);                       // global chunk stored there
         const int64_t am = min(m0 + row, p.M - 1) - m0, bn = min(n0 + row, p.N - 1) - n0;
-        pl.a_off[q] = (uint32_t)(am * p.K + 16 * c);
-        pl.b_off[q] = (uint32_t)(bn * p.K + 16 * c);
+        pl.a_off[q] = (uint32_t)(am * rb + 16 * c);
+        pl.b_off[q] = (uint32_t)(bn * rb + 16 * c);
     }
     const int64_t nkb = p.K / 32;
     pl.sa_base = p.a_scales + m0 * nkb;
@@ -79,17 +104,37 @@ __device__ __forceinline__ Plan make_plan(const Mx8GemmParams &p, int64_t m0, in
     return pl;
 }
 
-// Enqueue the copies of one slab into one LDS stage (asynchronous).
-__device__ __forceinline__ void issue(Stage &st, const Plan &pl, int64_t k0) {
+// The scale copies of slab s (4 bytes per row per copy).
+template <bool FP4>
+__device__ __forceinline__ void issue_scales(Stage<FP4> &st, const Plan &pl, int64_t s) {
     const int w = threadIdx.x >> 6;
+    const int64_t blk = s * slab_blocks<FP4>();
+#pragma unroll
+    for (int h = 0; h < (FP4 ? 2 : 1); ++h) {
+        copy_lds4(pl.sa_base + blk + 4 * h + pl.sa_off, st.as[h] + w * 64);
+        copy_lds4(pl.sb_base + blk + 4 * h + pl.sb_off, st.bs[h] + w * 64);
+    }
+}
+
+// Enqueue the copies of slab s into one LDS stage (asynchronous).
+template <bool FP4>
+__device__ __forceinline__ void issue(Stage<FP4> &st, const Plan &pl, int64_t s) {
+    const int w = threadIdx.x >> 6;
+    const int64_t k0 = s * BK;                          // byte offset in a row
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int seg = (w * 8 + q) * 1024;
         copy_lds16(pl.a_base + k0 + pl.a_off[q], st.a + seg);
         copy_lds16(pl.b_base + k0 + pl.b_off[q], st.b + seg);
     }
-    copy_lds4(pl.sa_base + k0 / 32 + pl.sa_off, st.as + w * 64);
-    copy_lds4(pl.sb_base + k0 / 32 + pl.sb_off, st.bs + w * 64);
+    issue_scales(st, pl, s);
+}
+
+// One 16-byte chunk of row r (FP4: the 32 values of one block); the upper
+// half of the operand is not read by the instruction.
+__device__ __forceinline__ i32x8 frag4(const uint8_t *tile, int r, int c) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(tile + r * BK + 16 * swz(r, c));
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
 }
 
 __device__ __forceinline__ i32x8 frag(const uint8_t *tile, int r, int g) {
@@ -100,63 +145,69 @@ __device__ __forceinline__ i32x8 frag(const uint8_t *tile, int r, int g) {
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
-// The MFMAs of one slab.  The copies of the next slab into stage nx are
-// issued along the way, four 1 KB copies after each of the first four row
-// blocks' MFMAs (and the scale copies after the fourth): the wave never
-// waits on one long burst of copy issues, and the copies still have half a
-// slab of MFMAs to land in.
-__device__ __forceinline__ void compute(const Stage &st, f32x4 (&acc)[8][8], int wm, int wn,
-                                        int lane, Stage &nx, const Plan &pl, int64_t kn) {
+// The MFMAs of one slab.  The copies of the next slab (index sn) into
+// stage nx are issued along the way, four 1 KB copies after each of the
+// first four row blocks' MFMAs (and the scale copies after the fourth): the
+// wave never waits on one long burst of copy issues, and the copies still
+// have half a slab of MFMAs to land in.  FP4 slabs take two MFMA steps
+// (chunks g, then 4 + g); the copies ride along the first.
+template <bool FP4>
+__device__ __forceinline__ void compute(const Stage<FP4> &st, f32x4 (&acc)[8][8], int wm, int wn,
+                                        int lane, Stage<FP4> &nx, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
     const int g = lane >> 4, rl = lane & 15;
-    i32x8 bf[8];
-    int bsc[8];
+    const int64_t kn = sn * BK;
+    constexpr int fmt = FP4 ? 4 : 0;                    // operand format: E2M1 or E4M3
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = wn * 128 + j * 16 + rl;
-        bf[j] = frag(st.b, r, g);
-        bsc[j] = (int)((st.bs[r] >> (8 * g)) & 0xFFu);
-    }
-    // A fragments are double-buffered by hand: row block i + 1 is read while
-    // the MFMAs of row block i run; the scheduling barrier keeps the compiler
-    // from hoisting every fragment read at once.
-    int r0 = wm * 128 + rl;
-    i32x8 an = frag(st.a, r0, g);
-    int ans = (int)((st.as[r0] >> (8 * g)) & 0xFFu);
+    for (int ks = 0; ks < (FP4 ? 2 : 1); ++ks) {
+        auto fr = [&](const uint8_t *tile, int r) {
+            return FP4 ? frag4(tile, r, 4 * ks + g) : frag(tile, r, g);
+        };
+        i32x8 bf[8];
+        int bsc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const i32x8 af = an;
-        const int asc = ans;
-        if (i + 1 < 8) {
-            const int r = wm * 128 + (i + 1) * 16 + rl;
-            an = frag(st.a, r, g);
-            ans = (int)((st.as[r] >> (8 * g)) & 0xFFu);
+        for (int j = 0; j < 8; ++j) {
+            const int r = wn * 128 + j * 16 + rl;
+            bf[j] = fr(st.b, r);
+            bsc[j] = (int)((st.bs[ks][r] >> (8 * g)) & 0xFFu);
         }
+        // A fragments are double-buffered by hand: row block i + 1 is read
+        // while the MFMAs of row block i run; the scheduling barrier keeps
+        // the compiler from hoisting every fragment read at once.
+        int r0 = wm * 128 + rl;
+        i32x8 an = fr(st.a, r0);
+        int ans = (int)((st.as[ks][r0] >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
-                                                                         bsc[j], 0, asc);
-        if (i < 4) {
-#pragma unroll
-            for (int q = 2 * i; q < 2 * i + 2; ++q) {
-                copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
-                copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
+        for (int i = 0; i < 8; ++i) {
+            const i32x8 af = an;
+            const int asc = ans;
+            if (i + 1 < 8) {
+                const int r = wm * 128 + (i + 1) * 16 + rl;
+                an = fr(st.a, r);
+                ans = (int)((st.as[ks][r] >> (8 * g)) & 0xFFu);
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    bf[j], af, acc[i][j], fmt, fmt, 0, bsc[j], 0, asc);
+            if (ks == 0 && i < 4) {
+#pragma unroll
+                for (int q = 2 * i; q < 2 * i + 2; ++q) {
+                    copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
+                    copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
+                }
+            }
+            if (ks == 0 && i == 3) issue_scales(nx, pl, sn);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (i == 3) {
-            copy_lds4(pl.sa_base + kn / 32 + pl.sa_off, nx.as + w * 64);
-            copy_lds4(pl.sb_base + kn / 32 + pl.sb_off, nx.bs + w * 64);
-        }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 }  // namespace mx
 
-template <bool BF16_OUT>
-__global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p) {
-    extern __shared__ __align__(16) uint8_t smem_raw[];
-    mx::Smem &sm = *reinterpret_cast<mx::Smem *>(smem_raw);
+template <bool FP4, bool BF16_OUT>
+__device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *smem_raw) {
+    mx::Smem<FP4> &sm = *reinterpret_cast<mx::Smem<FP4> *>(smem_raw);
     const int64_t tm = (p.M + mx::BM - 1) / mx::BM, tn = (p.N + mx::BN - 1) / mx::BN;
     const int64_t T = tm * tn;
     const int64_t bid = blockIdx.x, x = bid % 8, j = bid / 8;
@@ -169,7 +220,7 @@ __global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p)
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const mx::Plan pl = mx::make_plan(p, m0, n0);
+    const mx::Plan pl = mx::make_plan<FP4>(p, m0, n0);
 
     f32x4 acc[8][8];
 #pragma unroll
@@ -180,12 +231,12 @@ __global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p)
     mx::issue(sm.st[0], pl, 0);
     __builtin_amdgcn_s_waitcnt(0x3F70);               // vmcnt(0)
     __syncthreads();
-    const int64_t nslab = p.K / mx::BK;
+    const int64_t nslab = p.K / (FP4 ? 2 * mx::BK : mx::BK);
     for (int64_t s = 0; s < nslab; ++s) {
         // slab s + 1 goes to the other stage (past the end the last slab is
         // copied again into the stage nobody reads any more: no branch)
-        const int64_t kn = (s + 1 < nslab ? s + 1 : s) * mx::BK;
-        mx::compute(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, kn);
+        const int64_t sn = s + 1 < nslab ? s + 1 : s;
+        mx::compute(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
         __builtin_amdgcn_s_waitcnt(0x3F70);           // the next slab's copies have landed
         __syncthreads();
     }
@@ -203,8 +254,7 @@ __global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p)
             if (n >= p.N) continue;
             const f32x4 y = acc[i][jj];
             if (BF16_OUT) {
-                const uint2 w = make_uint2(f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16),
-                                           f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16));
+                const uint2 w = make_uint2(pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]));
                 *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = w;
             } else {
                 *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
@@ -214,18 +264,37 @@ __global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p)
     }
 }
 
-hipError_t launch_mxfp8_gemm_big(const Mx8GemmParams &p, bool bf16_out, hipStream_t s) {
+template <bool BF16_OUT>
+__global__ __launch_bounds__(mx::NT) void mxfp8_gemm_big_kernel(Mx8GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    mx_gemm_big<false, BF16_OUT>(p, smem_raw);
+}
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(mx::NT) void mxfp4_gemm_big_kernel(Mx8GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    mx_gemm_big<true, BF16_OUT>(p, smem_raw);
+}
+
+template <typename K_>
+static void launch_big(K_ kernel, size_t shm, const Mx8GemmParams &p, hipStream_t s) {
     const int64_t T = ((p.M + mx::BM - 1) / mx::BM) * ((p.N + mx::BN - 1) / mx::BN);
-    const size_t shm = sizeof(mx::Smem);
-    if (bf16_out) {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(mxfp8_gemm_big_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipLaunchKernelGGL(mxfp8_gemm_big_kernel<true>, dim3((unsigned)T), dim3(mx::NT), shm, s, p);
-    } else {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(mxfp8_gemm_big_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipLaunchKernelGGL(mxfp8_gemm_big_kernel<false>, dim3((unsigned)T), dim3(mx::NT), shm, s, p);
-    }
+    hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)T), dim3(mx::NT), shm, s, p);
+}
+
+hipError_t launch_mxfp8_gemm_big(const Mx8GemmParams &p, bool bf16_out, hipStream_t s) {
+    const size_t shm = sizeof(mx::Smem<false>);
+    if (bf16_out) launch_big(mxfp8_gemm_big_kernel<true>, shm, p, s);
+    else launch_big(mxfp8_gemm_big_kernel<false>, shm, p, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s) {
+    const size_t shm = sizeof(mx::Smem<true>);
+    if (bf16_out) launch_big(mxfp4_gemm_big_kernel<true>, shm, p, s);
+    else launch_big(mxfp4_gemm_big_kernel<false>, shm, p, s);
     return hipGetLastError();
 }
 

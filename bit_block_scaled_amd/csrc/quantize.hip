@@ -668,6 +668,61 @@ __global__ __launch_bounds__(kQT) void requant_kernel(RequantParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 copy (FP4 Training on Blackwell, 'The scaling math, worked'): blocks
+// of 32 along a row; scale 2^k with k the smallest integer such that
+// amax <= 6 * 2^k (with amax = m * 2^E, m in [0.5, 1): k = E - 3 if
+// m <= 0.75, else E - 2; clamped to [-127, 127]); elements x * 2^-k (exact)
+// rounded onto the E2M1 grid.  One block per lane.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mx4_k(float amax) {
+    if (amax == 0.0f) return -127;
+    int E;
+    const float m = frexpf(amax, &E);
+    const int k = (m <= 0.75f) ? E - 3 : E - 2;
+    return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+template <bool SR>
+__global__ __launch_bounds__(kQT) void mx4_quant_kernel(const uint16_t *__restrict__ x, int64_t R,
+                                                        int64_t C, int64_t ld,
+                                                        uint8_t *__restrict__ codes,
+                                                        uint8_t *__restrict__ scales,
+                                                        uint64_t seed, uint32_t stream) {
+    const int64_t nb = C / 32;
+    const int64_t b = (int64_t)blockIdx.x * kQT + threadIdx.x;
+    if (b >= R * nb) return;
+    const int64_t r = b / nb, cb = b - r * nb;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + r * ld + cb * 32);
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[8 * i + j] = elem(v, j);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    const int k = mx4_k(amax);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = ldexpf(y[i], -k);
+    uint32_t word[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (SR) {
+            uint32_t w[4];
+            sr_block(seed, stream, (uint64_t)(r * C + cb * 32) / 8 + i, w);
+            word[i] = e2m1_sr8(y + 8 * i, 1.0f, w);
+        } else {
+            word[i] = e2m1_rne8(y + 8 * i, 1.0f);
+        }
+    }
+    *reinterpret_cast<uint4 *>(codes + r * (C / 2) + cb * 16) =
+        make_uint4(word[0], word[1], word[2], word[3]);
+    scales[b] = (uint8_t)(k + 127);
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after argument checks).
 // ---------------------------------------------------------------------------
 
@@ -773,6 +828,20 @@ hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s) {
     else if (sr) hipLaunchKernelGGL((requant_kernel<true, false>), grid, dim3(kQT), 0, s, p);
     else if (p.tile2d) hipLaunchKernelGGL((requant_kernel<false, true>), grid, dim3(kQT), 0, s, p);
     else hipLaunchKernelGGL((requant_kernel<false, false>), grid, dim3(kQT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_quant(const uint16_t *x, int64_t R, int64_t C, int64_t ld, uint8_t *codes,
+                              uint8_t *scales, bool sr, uint64_t seed, uint32_t stream,
+                              hipStream_t s) {
+    const int64_t n = R * (C / 32);
+    const dim3 grid((unsigned)((n + kQT - 1) / kQT));
+    if (sr)
+        hipLaunchKernelGGL(mx4_quant_kernel<true>, grid, dim3(kQT), 0, s, x, R, C, ld, codes,
+                           scales, seed, stream);
+    else
+        hipLaunchKernelGGL(mx4_quant_kernel<false>, grid, dim3(kQT), 0, s, x, R, C, ld, codes,
+                           scales, seed, stream);
     return hipGetLastError();
 }
 

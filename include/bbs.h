@@ -42,7 +42,7 @@ extern "C" {
 
 enum bbs_round { BBS_RTN = 0, BBS_SR = 1 };
 enum bbs_out_dtype { BBS_OUT_F32 = 0, BBS_OUT_BF16 = 1 };
-enum bbs_fmt { BBS_FMT_NVFP4 = 0, BBS_FMT_MXFP8 = 1 };
+enum bbs_fmt { BBS_FMT_NVFP4 = 0, BBS_FMT_MXFP8 = 1, BBS_FMT_MXFP4 = 2 };
 
 /* Words of device workspace nvfp4_quantize needs for its amax partials. */
 #define BBS_AMAX_WS_FLOATS 11264
@@ -71,6 +71,17 @@ typedef struct {
     uint8_t *scales;
     int64_t rows, cols;
 } bbs_mx8;
+
+/* One MXFP4 tensor (FP4 Training on Blackwell, 'The scaling math, worked';
+ * the OCP microscaling format): value = E2M1(code) x 2^(scale-127), codes
+ * rows x cols/2 bytes (element 2j of a row in the low nibble of byte j),
+ * one E8M0 scale per 32 consecutive values of a row (rows x cols/32 bytes).
+ * codes 16-byte aligned; cols % 32 == 0. */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    int64_t rows, cols;
+} bbs_mx4;
 
 /* Key of the stochastic-rounding draws: element idx of an output copy
  * (its row-major index in that copy's own layout) uses 16-bit lane idx % 8
@@ -153,6 +164,16 @@ typedef struct {
  * output shapes not matching x), BBS_ENOTSUP (RHT on a tile2d copy). */
 int nvfp4_quantize(const bbs_quant_args *a, void *stream);
 
+/* MXFP4 copy of the BF16 matrix x (rows x cols, row stride ld elements,
+ * x 16-byte aligned, ld % 8 == 0, cols % 32 == 0): per block of 32 values
+ * of a row, scale 2^k with k = ceil(log2(amax / 6)) (the smallest k with
+ * amax <= 6 * 2^k, clamped to [-127, 127]; amax 0 gives k = -127), and the
+ * elements x * 2^-k rounded onto the E2M1 grid (nearest even, or stochastic
+ * with the draws of rng as for the other copies).  out must be rows x cols.
+ * Errors: BBS_EINVAL. */
+int mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
+                   const bbs_mx4 *out, int32_t round, bbs_rng rng, void *stream);
+
 /* Dequantize -> transpose -> requantize to MXFP8 (4bit.vizuara.ai, sections
  * 9-10; End-to-End 4-Bit Training, "requantization with stochastic
  * rounding").  src is an NVFP4 matrix R x C; dst receives the MXFP8 matrix of
@@ -170,6 +191,9 @@ int mxfp8_requantize_t(const bbs_fp4 *src, const bbs_mx8 *dst, int32_t round, bb
  *   fmt == BBS_FMT_NVFP4: A, B are const bbs_fp4 *; C = s_dec,A * s_dec,B *
  *      sum over blocks of (E4M3_A * E4M3_B * sum of E2M1 products).
  *   fmt == BBS_FMT_MXFP8: A, B are const bbs_mx8 *; K % 32 == 0.
+ *   fmt == BBS_FMT_MXFP4: A, B are const bbs_mx4 *; C = sum over 32-blocks
+ *      of 2^(sa-127) * 2^(sb-127) * (sum of E2M1 products); K % 256 == 0,
+ *      N % 4 == 0, 16-byte aligned C with ldc % 4 == 0 (else BBS_ENOTSUP).
  * C is M x N with row stride ldc (>= N) elements of c_dtype (BBS_OUT_F32 or
  * BBS_OUT_BF16, round to nearest even).  Output row i is scaled by
  * s_dec,A[i] * s_dec,B when A has a decode scale per row (then K % 128 == 0

@@ -74,7 +74,34 @@ __global__ void cvt_fp8_f32_kernel(const float *x, int n, const float *scale, ui
     out[i] = (uint16_t)r[0];
 }
 
+// The same with E2M1 operands (format 4): the one-hot operand holds 1.0
+// (code 2) only at nibble J of lane L's first 16 bytes, the other operand
+// 1.0 in every nibble of its first 16 bytes (the upper 16 bytes are unused).
+__global__ void mfma_scale_layout_fp4_kernel(int which, const int *one, float *out) {
+    const int lane = threadIdx.x;
+    const int L = blockIdx.x / 32, J = blockIdx.x % 32;
+    i32x8 h, o;
+    for (int v = 0; v < 8; ++v) {
+        h[v] = 0;
+        o[v] = v < 4 ? 0x22222222 : 0;
+    }
+    if (lane == L) h[J / 8] = 2 << (4 * (J % 8));
+    const int s_var = 127 * one[0] + (lane >> 4);
+    const int s_one = 127 * one[0];
+    f32x4 acc = {0, 0, 0, 0};
+    if (which == 0)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(h, o, acc, 4, 4, 0, s_var, 0, s_one);
+    else
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o, h, acc, 4, 4, 0, s_one, 0, s_var);
+    for (int v = 0; v < 4; ++v) out[(blockIdx.x * 64 + lane) * 4 + v] = acc[v];
+}
+
 extern "C" {
+int probe_mfma_scale_layout_fp4(int which, const int *one, float *out) {
+    hipLaunchKernelGGL(mfma_scale_layout_fp4_kernel, dim3(64 * 32), dim3(64), 0, 0, which, one,
+                       out);
+    return (int)hipDeviceSynchronize();
+}
 int probe_mfma_scale_layout(int which, const int *one, float *out) {
     hipLaunchKernelGGL(mfma_scale_layout_kernel, dim3(64 * 32), dim3(64), 0, 0, which, one, out);
     return (int)hipDeviceSynchronize();

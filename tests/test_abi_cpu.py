@@ -196,3 +196,21 @@ def test_s2f6_errors(lib):
     assert L.s2f6_combine(C.byref(d), src, None, 4, 2, 1, 0, C.c_void_p(0x4004), 1, 64,
                           None) == bbs.BBS_EINVAL
     assert b"aligned" in L.bbs_last_error()
+
+
+def test_mxfp4_errors(lib):
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    d = bbs.Mx4Desc(0x1000, 0x2000, 8, 48)                  # cols not a multiple of 32
+    assert L.mxfp4_quantize(C.c_void_p(0x1000), 8, 48, 48, C.byref(d), 0, bbs.Rng(0, 0),
+                            None) == bbs.BBS_EINVAL
+    d.cols = 64
+    assert L.mxfp4_quantize(C.c_void_p(0x1000), 8, 64, 64, C.byref(d), 5, bbs.Rng(0, 0),
+                            None) == bbs.BBS_EINVAL
+    a = bbs.Mx4Desc(0x1000, 0x2000, 32, 128)
+    b = bbs.Mx4Desc(0x1000, 0x2000, 32, 128)
+    assert L.nvfp4_gemm(2, C.byref(a), C.byref(b), C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_ENOTSUP
+    assert b"256" in L.bbs_last_error()
+    a.cols = b.cols = 256
+    b.rows = 30
+    assert L.nvfp4_gemm(2, C.byref(a), C.byref(b), C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_ENOTSUP

@@ -152,3 +152,38 @@ def test_gelu_and_exp_match_oracle(probe):
     big = ef >= 130
     assert np.array_equal(gb[big & pos], xb[big & pos])
     assert np.all(gb[big & ~pos].view(np.uint32) == 0x80000000)
+
+
+def test_scaled_fp4_mfma_layout(probe):
+    """E2M1 operands of v_mfma_scale_f32_16x16x128_f8f6f4 (format 4): which
+    row each lane feeds and which 32-block scale each of its 32 nibbles is
+    multiplied by (the MXFP4 GEMM relies on it)."""
+    announce("v_mfma_scale_f32_16x16x128_f8f6f4 E2M1 lane layout")
+    one = torch.ones(1, dtype=torch.int32, device=dev())
+    blocks = np.full((2, 64, 32), -1)
+    for which in (0, 1):
+        out = torch.zeros(2048 * 64 * 4, dtype=torch.float32, device=dev())
+        assert probe.probe_mfma_scale_layout_fp4(which, C.c_void_p(one.data_ptr()),
+                                                 C.c_void_p(out.data_ptr())) == 0
+        acc = out.cpu().numpy().reshape(64, 32, 64, 4)
+        for L in range(64):
+            for J in range(32):
+                D = np.zeros((16, 16))
+                a = acc[L, J]
+                for lane in range(64):
+                    D[4 * (lane // 16):4 * (lane // 16) + 4, lane % 16] = a[lane]
+                nz = np.unique(D[D != 0])
+                assert len(nz) == 1, (which, L, J, nz)
+                b = int(np.log2(nz[0]))
+                want = np.zeros((16, 16))
+                if which == 0:
+                    want[L % 16, :] = 2.0 ** b
+                else:
+                    want[:, L % 16] = 2.0 ** b
+                assert np.array_equal(D, want), (which, L, J)
+                blocks[which, L, J] = b
+    # lane l feeds row l % 16 and the 32 values of block l // 16 (its 16
+    # bytes), scaled by the scale that lane group supplies
+    for which in (0, 1):
+        for L in range(64):
+            assert np.all(blocks[which, L] == L // 16), (which, L)
