@@ -398,6 +398,39 @@ def main():
     print(f"[bench] fused GELU + quantize of H {M}x{N}: {json.dumps(gelu)}", file=sys.stderr,
           flush=True)
 
+    # The layer as a user calls it: the autograd function over the C ABI,
+    # forward alone and forward + backward (allocations and dispatch included).
+    from bit_block_scaled_amd.layer import QLinear
+    layer = QLinear(K, N, seed=seeds["x_col"], rht_signs=signs, device=dev)
+    with torch.no_grad():
+        layer.weight.copy_(w.view(torch.bfloat16))
+    xin = x.view(torch.bfloat16).detach().requires_grad_(True)
+    gin = dy.view(torch.bfloat16)
+
+    def layer_fwd():
+        layer(xin)
+
+    def layer_fwd_bwd():
+        layer(xin).backward(gin)
+        xin.grad = None
+        layer.weight.grad = None
+
+    layer_t = {}
+    for name, f in (("forward", layer_fwd), ("forward_backward", layer_fwd_bwd)):
+        f()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        t_ms = s0.elapsed_time(s1) / args.steps
+        flop = GEMM_FLOP * (1 if name == "forward" else 3)
+        layer_t[name] = {"ms": round(t_ms, 4), "TFLOP/s": round(flop / (t_ms * 1e-3) / 1e12, 1)}
+    del layer, xin
+    print(f"[bench] QLinear layer (autograd): {json.dumps(layer_t)}", file=sys.stderr, flush=True)
+
     # The MXFP4 comparison format: X and W as MXFP4 (E2M1, E8M0 per 32; RTN)
     # and the same forward GEMM on the block-scaled MFMA with E2M1 operands.
     x4, w4 = bbs.MXFP4Tensor.empty(M, K, device=dev), bbs.MXFP4Tensor.empty(N, K, device=dev)
@@ -459,6 +492,7 @@ def main():
         "activation_per_token_4over6": act,
         "gelu_quantize_mlp_hidden_8192x14336": gelu,
         "mxfp4_forward_8192x14336x4096": mx4,
+        "qlinear_layer_autograd": layer_t,
         "wall_s_timed": round(wall_s, 3),
     }
     if not args.no_moe:
