@@ -37,7 +37,7 @@ COPY_BYTES = 1 << 29                            # counter calibration copy (512 
 # WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
 # (profiles/fprop_gemm_8192x14336x4096_counters.md), valid only for the kernel
 # sources they were taken on: reported as null once those sources change.
-FPROP_TRAFFIC = {"bytes": 673631599, "sources_sha256_16": "21248190218e484e"}
+FPROP_TRAFFIC = {"bytes": 648037396, "sources_sha256_16": "ec9587a5946416d3"}
 FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
                  "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
 
@@ -174,6 +174,12 @@ def moe_bench(torch, bbs, dev, reps):
     hq = N4.empty(rows, F_, device=dev)
     y = torch.empty((rows, H_), dtype=torch.int16, device=dev)
     yq = bbs.S2F6Tensor.empty(rows, H_, device=dev)
+    hq2 = N4.empty(rows, F_, device=dev)
+    amax_h = torch.zeros(1, dtype=torch.float32, device=dev)
+    s_h = torch.ones(1, dtype=torch.float32, device=dev)
+    bbs.grouped_nvfp4_gemm_quant(xq, ri, off, E_, rows, w_up, F_, s_h, hq2, amax=amax_h)
+    torch.cuda.synchronize()
+    s_h.fill_(2688.0 / max(float(amax_h[0]), 1e-30))
     comb = torch.empty((T_, H_), dtype=torch.int16, device=dev)
     signs = 0xB5297A4D
     ops = {
@@ -181,6 +187,10 @@ def moe_bench(torch, bbs, dev, reps):
         "moe_quant_h": lambda: bbs.nvfp4_quantize(h, hq, amax_ws=ws),
         "moe_down": lambda: bbs.grouped_nvfp4_gemm(hq, None, off, E_, rows, w_dn, H_, y,
                                                    bbs.OUT_BF16),
+        # the up-projection with the quantize in its epilogue (scale from the
+        # first call's amax), in place of moe_up + moe_quant_h
+        "moe_up_quant": lambda: bbs.grouped_nvfp4_gemm_quant(xq, ri, off, E_, rows, w_up, F_,
+                                                             s_h, hq2, amax=amax_h),
         # combine wire format: RHT-32 + S2F6 encode of the down output, then
         # the receiver's weighted sum over each token's K rows + inverse RHT
         "combine_encode": lambda: bbs.s2f6_quantize(y, yq, rht=True, signs=signs),
@@ -204,7 +214,7 @@ def moe_bench(torch, bbs, dev, reps):
             gbps = codec_bytes[name] / (ms * 1e-3) / 1e9
             e.update({"GB/s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
                       "bytes": codec_bytes[name]})
-        elif name != "moe_quant_h":
+        elif name not in ("moe_quant_h",):
             tf = 2.0 * rows * F_ * H_ / (ms * 1e-3) / 1e12
             e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
         out[name] = e
@@ -394,9 +404,44 @@ def main():
         t_ms = s0.elapsed_time(s1) / args.steps
         gelu[name] = {"ms": round(t_ms, 4), "GB/s": round(b / (t_ms * 1e-3) / 1e9, 1),
                       "bytes": b, "Gelem/s": round(M * N / (t_ms * 1e-3) / 1e9, 1)}
-    del h, hq, hm, ha
+    # The forward GEMM with the quantize (and GELU) in its epilogue, against
+    # the same output through BF16 and a separate quantize pass.  The encode
+    # scale is 2688 / the output's amax, taken from a first call.
+    yq = T.empty(M, N, device=dev)
+    amax_y = torch.zeros(1, dtype=torch.float32, device=dev)
+    s_y = torch.ones(1, dtype=torch.float32, device=dev)
+    epi = {}
+    for g in (False, True):
+        bbs.nvfp4_gemm_quant(xq, wq, s_y, yq, gelu=g, amax=amax_y)
+        torch.cuda.synchronize()
+        s_y.fill_(2688.0 / max(float(amax_y[0]), 1e-30))
+        name = "fprop_gelu_quant" if g else "fprop_quant"
+        f = (lambda g=g: bbs.nvfp4_gemm_quant(xq, wq, s_y, yq, gelu=g, amax=amax_y))
+        f()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(args.steps):
+            f()
+        s1.record()
+        torch.cuda.synchronize()
+        t_ms = s0.elapsed_time(s1) / args.steps
+        epi[name] = {"ms": round(t_ms, 4), "TFLOP/s": round(GEMM_FLOP / (t_ms * 1e-3) / 1e12, 1)}
+    f = lambda: bbs.nvfp4_quantize(y, hq, amax_ws=ws)
+    f()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.steps):
+        f()
+    s1.record()
+    torch.cuda.synchronize()
+    q_ms = s0.elapsed_time(s1) / args.steps
+    epi["unfused_fprop_bf16_then_quant"] = {"ms": round(per["fprop"] + q_ms, 4)}
+    epi["unfused_fprop_bf16_then_gelu_quant"] = {
+        "ms": round(per["fprop"] + gelu["gelu_quant_row"]["ms"], 4)}
+    del h, hq, hm, ha, yq
     print(f"[bench] fused GELU + quantize of H {M}x{N}: {json.dumps(gelu)}", file=sys.stderr,
           flush=True)
+    print(f"[bench] quantize in the GEMM epilogue: {json.dumps(epi)}", file=sys.stderr, flush=True)
 
     # The layer as a user calls it: the autograd function over the C ABI,
     # forward alone and forward + backward (allocations and dispatch included).
@@ -491,6 +536,7 @@ def main():
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
         "activation_per_token_4over6": act,
         "gelu_quantize_mlp_hidden_8192x14336": gelu,
+        "gemm_epilogue_quantize_8192x14336x4096": epi,
         "mxfp4_forward_8192x14336x4096": mx4,
         "qlinear_layer_autograd": layer_t,
         "wall_s_timed": round(wall_s, 3),

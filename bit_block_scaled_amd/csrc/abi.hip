@@ -82,6 +82,87 @@ int check_s2f6(const bbs_s2f6 *d, const char *name) {
 
 extern "C" {
 
+namespace {
+
+// Shared checks of the quantizing GEMMs: the large-tile conditions and the
+// NVFP4 output descriptor (rows x N, 1x16, one decode scale).
+int check_quant_out(const bbs::GemmParams &p, const bbs_fp4 *Y, int64_t rows, const float *s_enc,
+                    const float *amax) {
+    int st;
+    if ((st = check_fp4(Y, "Y", true))) return st;
+    if (!s_enc) return fail(BBS_EINVAL, "null s_enc");
+    if (Y->rows != rows || Y->cols != p.N) return fail(BBS_EINVAL, "Y must be rows x N");
+    if (Y->tile2d || Y->sdec_per_row)
+        return fail(BBS_EINVAL, "Y is a 1x16 copy with one decode scale");
+    if (amax && !aligned(amax, 4)) return fail(BBS_EINVAL, "amax not 4-byte aligned");
+    if (p.K % 128 || !aligned(p.a.codes, 16) || !aligned(p.b.codes, 16) || !aligned(p.a.scales, 8) ||
+        !aligned(p.b.scales, 8))
+        return fail(BBS_ENOTSUP, "quantizing GEMM needs K %% 128 == 0 and aligned operands");
+    return BBS_OK;
+}
+
+bbs::QuantOut quant_out(const bbs_fp4 *Y, const float *s_enc, float *amax) {
+    return {Y->codes, Y->scales, Y->s_dec, s_enc, reinterpret_cast<unsigned *>(amax)};
+}
+
+}  // namespace
+
+int nvfp4_gemm_quant(const bbs_fp4 *A, const bbs_fp4 *B, const float *s_enc, int32_t gelu,
+                     const bbs_fp4 *Y, float *amax, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_fp4(A, "A", true))) return st;
+    if ((st = check_fp4(B, "B", true))) return st;
+    if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+    if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
+    if (gelu != 0 && gelu != 1) return fail(BBS_EINVAL, "gelu must be 0 or 1");
+    bbs::GemmParams p{};
+    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
+    p.b = {B->codes, B->scales, B->s_dec, B->rows, B->tile2d, 0};
+    p.M = A->rows;
+    p.N = B->rows;
+    p.K = A->cols;
+    if ((st = check_quant_out(p, Y, p.M, s_enc, amax))) return st;
+    p.q = quant_out(Y, s_enc, amax);
+    return hip_status(bbs::launch_nvfp4_gemm_quant(p, gelu != 0,
+                                                   reinterpret_cast<hipStream_t>(stream)),
+                      "quantizing gemm launch");
+}
+
+int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
+                             const int64_t *group_offsets, int32_t G, int64_t max_rows,
+                             const bbs_fp4 *B, int64_t N, const float *s_enc, int32_t gelu,
+                             const bbs_fp4 *Y, float *amax, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_fp4(A, "A", true))) return st;
+    if ((st = check_fp4(B, "B", true))) return st;
+    if (!group_offsets) return fail(BBS_EINVAL, "null group_offsets");
+    if (G <= 0 || G > 1024) return fail(BBS_EINVAL, "G must be in [1, 1024]");
+    if (N <= 0 || N % 16 || B->rows != (int64_t)G * N)
+        return fail(BBS_EINVAL, "B.rows must equal G * N with N %% 16 == 0");
+    if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+    if (max_rows <= 0) return fail(BBS_EINVAL, "max_rows must be positive");
+    if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
+    if (gelu != 0 && gelu != 1) return fail(BBS_EINVAL, "gelu must be 0 or 1");
+    bbs::GemmParams p{};
+    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
+    p.b = {B->codes, B->scales, B->s_dec, N, B->tile2d, 0};
+    p.M = max_rows;
+    p.N = N;
+    p.K = A->cols;
+    p.row_index = row_index;
+    p.group_offsets = group_offsets;
+    p.G = G;
+    p.max_rows = max_rows;
+    p.a_src_rows = A->rows;
+    if ((st = check_quant_out(p, Y, max_rows, s_enc, amax))) return st;
+    p.q = quant_out(Y, s_enc, amax);
+    return hip_status(bbs::launch_grouped_nvfp4_gemm_quant(p, gelu != 0,
+                                                           reinterpret_cast<hipStream_t>(stream)),
+                      "quantizing grouped gemm launch");
+}
+
 int mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
                    const bbs_mx4 *out, int32_t round, bbs_rng rng, void *stream) {
     g_err[0] = 0;

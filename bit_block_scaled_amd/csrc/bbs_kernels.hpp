@@ -62,8 +62,18 @@ struct Fp4View {
     int sdec_rows;      // s_dec holds one decode scale per row
 };
 
+// NVFP4 output of a GEMM quantized in its epilogue: 1x16 rows, nearest,
+// with a given encode scale (optionally of GELU of the product).
+struct QuantOut {
+    uint8_t *codes, *scales;
+    float *s_dec;            // receives 1 / s_enc
+    const float *s_enc;      // one FP32 encode scale (device)
+    unsigned *amax;          // max |y| of the quantized values as FP32 bits, or nullptr
+};
+
 struct GemmParams {
     Fp4View a, b;
+    QuantOut q;                    // the quantizing kernels only
     int64_t M, N, K;
     void *c;
     int64_t ldc;
@@ -126,6 +136,10 @@ hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six,
 bool big_ok(const GemmParams &p, bool bf16_out);
 hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
+// The same GEMMs (large-tile kernels only: big_ok must hold) writing p.q
+// instead of C; p.q.amax, when given, is cleared first.
+hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s);
+hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s);
 hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);
 // MXFP4 x MXFP4 (codes rows x K/2): K % 256 == 0, 16-byte aligned codes,
 // 4-byte aligned scales, N % 4 == 0, 16-byte aligned C with ldc % 4 == 0.

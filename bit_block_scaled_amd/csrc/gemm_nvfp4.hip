@@ -301,11 +301,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every store instruction writes complete 256- or 512-byte row segments.
 // Rows m < m_end and columns n < n_end are written; N being a multiple of 16
 // keeps every 16-byte segment wholly in or out.
-template <bool BF16_OUT, typename ScaleFn>
+//
+// Output modes: OUT_F32, OUT_BF16, and the quantizing modes OUT_Q / OUT_QG
+// (4bit.vizuara.ai, section 13; End-to-End 4-Bit Training, kernels for
+// low-precision training: the quantize rides in the GEMM's epilogue so the
+// output never goes through BF16).  These stage FP32 rows as OUT_F32 does;
+// on read-back each lane takes one 1x16 block of a row (16 consecutive FP32
+// values), applies GELU (OUT_QG), and encodes it with the given tensor
+// scale exactly as the quantizer does: E4M3 block scale of
+// (amax_b / 6) * s_enc (never below code 1), E2M1 codes of x * s_enc_b to
+// nearest even.  The largest |value| is folded into q.amax.
+constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_QG = 3;
+
+template <int OUT, typename ScaleFn>
 __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], int64_t m0,
                                          int64_t m_end, int64_t n0, int64_t n_end,
                                          ScaleFn scale_of, void *C, int64_t ldc, int wm, int wn,
-                                         int lane) {
+                                         int lane, const QuantOut &qo) {
+    constexpr bool BF16_OUT = OUT == OUT_BF16, QUANT = OUT >= OUT_Q;
     constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
     constexpr int RS = 128 * ES + 16;                 // staging row stride
     constexpr int PR = BF16_OUT ? 32 : 16;            // rows per piece
@@ -314,6 +327,11 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     uint8_t *buf = reinterpret_cast<uint8_t *>(&sm) + (threadIdx.x >> 6) * (PR * RS);
     const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
     const int lr = lane & 31;                          // the lane's row in a 32-row block
+    float s_enc = 1.0f, s_dec = 1.0f, amax = 0.0f;
+    if (QUANT) {
+        s_enc = qo.s_enc[0];
+        s_dec = 1.0f / s_enc;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         // output scale of the lane's row: s_dec,A (of that row) * s_dec,B
@@ -332,7 +350,7 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                         const float y1 = acc[i][j][4 * g + 1] * out_scale;
                         const float y2 = acc[i][j][4 * g + 2] * out_scale;
                         const float y3 = acc[i][j][4 * g + 3] * out_scale;
-                        if (BF16_OUT)
+                        if constexpr (BF16_OUT)
                             *reinterpret_cast<uint2 *>(row + c * 2) =
                                 make_uint2(f32_to_bf16(y0) | (f32_to_bf16(y1) << 16),
                                            f32_to_bf16(y2) | (f32_to_bf16(y3) << 16));
@@ -341,24 +359,74 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                     }
             }
             // a wave reads back only its own rows: LDS order suffices
+            if (!QUANT) {
 #pragma unroll
-            for (int q = 0; q < PR / RPI; ++q) {
-                const int r = q * RPI + lane / LPR;
-                const int cb = (lane % LPR) * 16;
-                const uint4 val = *reinterpret_cast<const uint4 *>(buf + r * RS + cb);
-                const int64_t m = mw + i * 32 + piece * PR + r;
-                const int64_t n = nw + cb / ES;
-                if (m < m_end && n < n_end)
-                    *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
+                for (int q = 0; q < PR / RPI; ++q) {
+                    const int r = q * RPI + lane / LPR;
+                    const int cb = (lane % LPR) * 16;
+                    const uint4 val = *reinterpret_cast<const uint4 *>(buf + r * RS + cb);
+                    const int64_t m = mw + i * 32 + piece * PR + r;
+                    const int64_t n = nw + cb / ES;
+                    if (m < m_end && n < n_end)
+                        *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
+                }
+            } else {
+                // 16 rows x 8 blocks of 16: two blocks per lane
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int r = q * 8 + lane / 8, b = lane % 8;
+                    float4 *src = reinterpret_cast<float4 *>(buf + r * RS + b * 64);
+                    if (OUT == OUT_QG) {
+                        // GELU in place, four values at a time (a rolled loop
+                        // keeps the register pressure of the tile low)
+#pragma unroll 1
+                        for (int v = 0; v < 4; ++v) {
+                            float4 w = src[v];
+                            w.x = gelu_tanh(w.x);
+                            w.y = gelu_tanh(w.y);
+                            w.z = gelu_tanh(w.z);
+                            w.w = gelu_tanh(w.w);
+                            src[v] = w;
+                        }
+                    }
+                    float f[16];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float4 w = src[v];
+                        f[4 * v] = w.x;
+                        f[4 * v + 1] = w.y;
+                        f[4 * v + 2] = w.z;
+                        f[4 * v + 3] = w.w;
+                    }
+                    const int64_t m = mw + i * 32 + piece * PR + r;
+                    const int64_t n = nw + b * 16;
+                    if (m < m_end && n < n_end) {
+                        float a = 0.0f;
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) a = fmaxf(a, fabsf(f[v]));
+                        amax = fmaxf(amax, a);
+                        const uint32_t sc = block_scale_code(a, s_enc);
+                        const float se = block_enc_scale(sc, s_dec);
+                        *reinterpret_cast<uint2 *>(qo.codes + m * (n_end / 2) + n / 2) =
+                            make_uint2(e2m1_rne8(f, se), e2m1_rne8(f + 8, se));
+                        qo.scales[m * (n_end / 16) + n / 16] = (uint8_t)sc;
+                    }
+                }
             }
         }
     }
+    if (QUANT && qo.amax) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        if (lane == 0) atomicMax(qo.amax, __float_as_uint(amax));
+    }
 }
 
-template <bool BF16_OUT, bool BT, typename RowMap, typename ScaleFn>
+template <int OUT, bool BT, typename RowMap, typename ScaleFn>
 __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &B, int64_t K,
                                      int64_t m0, int64_t m_end, int64_t n0, int64_t n_end,
-                                     RowMap a_row, ScaleFn scale_of, void *C, int64_t ldc) {
+                                     RowMap a_row, ScaleFn scale_of, void *C, int64_t ldc,
+                                     const QuantOut &qo) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const Plan pl = make_plan(A, B, K, m0, m_end, n0, n_end, a_row);
@@ -453,15 +521,15 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
     wait_vmcnt<0>();
     __syncthreads();
 
-    epilogue<BF16_OUT>(sm, acc, m0, m_end, n0, n_end, scale_of, C, ldc, wm, wn, lane);
+    epilogue<OUT>(sm, acc, m0, m_end, n0, n_end, scale_of, C, ldc, wm, wn, lane, qo);
 }
 
 }  // namespace big
 
-template <bool BF16_OUT>
-__global__ __launch_bounds__(big::NT) void nvfp4_gemm_big_kernel(GemmParams p) {
-    extern __shared__ __align__(16) uint8_t smem_raw[];
+template <int OUT>
+__device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_raw) {
     big::Smem &sm = *reinterpret_cast<big::Smem *>(smem_raw);
+    if (OUT >= big::OUT_Q && blockIdx.x == 0 && threadIdx.x == 0) p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t tm = (p.M + big::BM - 1) / big::BM, tn = (p.N + big::BN - 1) / big::BN;
     const int64_t T = tm * tn;
     // XCD-contiguous tile ranges
@@ -477,11 +545,11 @@ __global__ __launch_bounds__(big::NT) void nvfp4_gemm_big_kernel(GemmParams p) {
     const float sb = p.b.s_dec[0];
     auto run = [&](auto scale_of) {
         if (p.b.tile2d)
-            big::tile<BF16_OUT, true>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
-                                      ident, scale_of, p.c, p.ldc);
+            big::tile<OUT, true>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
+                                 ident, scale_of, p.c, p.ldc, p.q);
         else
-            big::tile<BF16_OUT, false>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
-                                       ident, scale_of, p.c, p.ldc);
+            big::tile<OUT, false>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
+                                  ident, scale_of, p.c, p.ldc, p.q);
     };
     if (p.a.sdec_rows) {
         const float *sa = p.a.s_dec;
@@ -492,14 +560,25 @@ __global__ __launch_bounds__(big::NT) void nvfp4_gemm_big_kernel(GemmParams p) {
     }
 }
 
+template <bool BF16_OUT>
+__global__ __launch_bounds__(big::NT) void nvfp4_gemm_big_kernel(GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    dense_body<BF16_OUT ? big::OUT_BF16 : big::OUT_F32>(p, smem_raw);
+}
+
+template <bool GELU>
+__global__ __launch_bounds__(big::NT) void nvfp4_gemm_quant_kernel(GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    dense_body<GELU ? big::OUT_QG : big::OUT_Q>(p, smem_raw);
+}
+
 constexpr int kMaxGroupsBig = 1024;
 
-template <bool BF16_OUT>
-__global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_big_kernel(GemmParams p) {
-    extern __shared__ __align__(16) uint8_t smem_raw[];
+template <int OUT>
+__device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_raw,
+                                             int64_t *tile_start, int64_t *row_start) {
     big::Smem &sm = *reinterpret_cast<big::Smem *>(smem_raw);
-    __shared__ int64_t tile_start[kMaxGroupsBig + 1];
-    __shared__ int64_t row_start[kMaxGroupsBig + 1];
+    if (OUT >= big::OUT_Q && blockIdx.x == 0 && threadIdx.x == 0) p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t n_tiles_n = (p.N + big::BN - 1) / big::BN;
     if (threadIdx.x == 0) {
         int64_t acc = 0, prev = 0;
@@ -534,11 +613,11 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_big_kernel(GemmPar
         const float sb = p.b.s_dec[g];
         auto run = [&](auto scale_of) {
             if (B.tile2d)
-                big::tile<BF16_OUT, true>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
-                                          p.ldc);
+                big::tile<OUT, true>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
+                                     p.ldc, p.q);
             else
-                big::tile<BF16_OUT, false>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
-                                           p.ldc);
+                big::tile<OUT, false>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
+                                      p.ldc, p.q);
         };
         if (p.a.sdec_rows) {
             const float *sa = p.a.s_dec;
@@ -553,6 +632,48 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_big_kernel(GemmPar
         }
         __syncthreads();
     }
+}
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_big_kernel(GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    __shared__ int64_t tile_start[kMaxGroupsBig + 1];
+    __shared__ int64_t row_start[kMaxGroupsBig + 1];
+    grouped_body<BF16_OUT ? big::OUT_BF16 : big::OUT_F32>(p, smem_raw, tile_start, row_start);
+}
+
+template <bool GELU>
+__global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_quant_kernel(GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    __shared__ int64_t tile_start[kMaxGroupsBig + 1];
+    __shared__ int64_t row_start[kMaxGroupsBig + 1];
+    grouped_body<GELU ? big::OUT_QG : big::OUT_Q>(p, smem_raw, tile_start, row_start);
+}
+
+__global__ void clear_amax_kernel(unsigned *amax) { *amax = 0u; }
+
+template <typename K_>
+static void launch_with_smem(K_ kernel, dim3 grid, const GemmParams &p, hipStream_t s) {
+    const size_t shm = sizeof(big::Smem);
+    hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipLaunchKernelGGL(kernel, grid, dim3(big::NT), shm, s, p);
+}
+
+hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s) {
+    if (p.q.amax) hipLaunchKernelGGL(clear_amax_kernel, dim3(1), dim3(1), 0, s, p.q.amax);
+    const int64_t T = ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
+    if (gelu) launch_with_smem(nvfp4_gemm_quant_kernel<true>, dim3((unsigned)T), p, s);
+    else launch_with_smem(nvfp4_gemm_quant_kernel<false>, dim3((unsigned)T), p, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s) {
+    if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
+    if (p.q.amax) hipLaunchKernelGGL(clear_amax_kernel, dim3(1), dim3(1), 0, s, p.q.amax);
+    if (gelu) launch_with_smem(grouped_nvfp4_gemm_quant_kernel<true>, dim3(512), p, s);
+    else launch_with_smem(grouped_nvfp4_gemm_quant_kernel<false>, dim3(512), p, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {

@@ -214,3 +214,25 @@ def test_mxfp4_errors(lib):
     a.cols = b.cols = 256
     b.rows = 30
     assert L.nvfp4_gemm(2, C.byref(a), C.byref(b), C.c_void_p(0x5000), 0, 32, None) == bbs.BBS_ENOTSUP
+
+
+def test_gemm_quant_errors(lib):
+    """The quantizing GEMMs: Y must be a rows x N 1x16 copy, s_enc given,
+    K % 128 (else unsupported)."""
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    A = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 128, 0, 0)
+    B = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 48, 128, 1, 0)
+    Y = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 48, 0, 0)
+    s = C.c_void_p(0x4000)
+    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), None, 0, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 2, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    Y.rows = 16
+    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 0, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    Y.rows, Y.tile2d = 32, 1
+    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 0, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    Y.tile2d = 0
+    A.cols = B.cols = 64
+    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 0, C.byref(Y), None, None) == bbs.BBS_ENOTSUP
+    assert L.grouped_nvfp4_gemm_quant(C.byref(A), None, None, 1, 32, C.byref(B), 48, s, 0,
+                                      C.byref(Y), None, None) == bbs.BBS_EINVAL

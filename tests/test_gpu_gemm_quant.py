@@ -1,0 +1,158 @@
+"""GEMMs with the NVFP4 quantize in their epilogue (4bit.vizuara.ai, section
+13; End-to-End 4-Bit Training, kernels for low-precision training).
+
+Where the FP32 products are exact (integer-valued codes with unit block
+scales and power-of-two decode scales) the codes, scales, decode scale and
+output amax must equal the oracle's encode of the exact product bit for bit,
+with and without GELU.  Elsewhere the FP32 sum order is free, so a value
+lying at a rounding boundary may round either way: there the test bounds the
+fraction of code and scale bytes that differ from the oracle's encode of the
+FP64 product.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_util import announce, dev, host, to_dev, upload_nvfp4
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def bbs():
+    import bit_block_scaled_amd as b
+    return b
+
+
+def _unit_scale_operand(R, K, seed, s_dec, tile2d=False):
+    rng = np.random.default_rng(seed)
+    shape = (R // 16, K // 16) if tile2d else (R, K // 16)
+    return O.NVFP4(rng.integers(0, 256, (R, K // 2), dtype=np.uint8),
+                   np.full(shape, 0x38, np.uint8), np.float32(s_dec), R, K, tile2d)
+
+
+def _ref(a, b, gelu):
+    y = O.gemm_f64(a.dequant_f64(), b.dequant_f64()).astype(np.float32)
+    return O.gelu_f32(y) if gelu else y
+
+
+def _run(bbs, a, b, s_enc, gelu, M, N):
+    Y = bbs.NVFP4Tensor.empty(M, N, device=dev())
+    se = torch.tensor([s_enc], dtype=torch.float32, device=dev())
+    amax = torch.full((1,), -1.0, dtype=torch.float32, device=dev())
+    bbs.nvfp4_gemm_quant(a, b, se, Y, gelu=gelu, amax=amax)
+    torch.cuda.synchronize()
+    return Y, float(host(amax)[0])
+
+
+@pytest.mark.parametrize("gelu", [False, True])
+@pytest.mark.parametrize("M,N,K,tb", [(272, 400, 1024, True), (128, 256, 128, False),
+                                      (304, 16, 256, True)])
+def test_exact_case(bbs, gelu, M, N, K, tb):
+    announce(f"quantizing GEMM, exact products M={M} N={N} K={K} gelu={gelu}")
+    a = _unit_scale_operand(M, K, M + K, 0.5)
+    b = _unit_scale_operand(N, K, N + K, 0.25, tb)
+    y = _ref(a, b, gelu)
+    amax = float(np.abs(y).max())
+    s_enc = O.tensor_s_enc(amax)
+    Y, got_amax = _run(bbs, upload_nvfp4(a, bbs), upload_nvfp4(b, bbs), s_enc, gelu, M, N)
+    o = O.nvfp4_encode_f32(y, s_enc)
+    assert np.array_equal(host(Y.scales), o.scales)
+    assert np.array_equal(host(Y.codes), o.codes)
+    assert host(Y.s_dec)[0] == o.s_dec
+    assert got_amax == amax
+
+
+def test_saturating_scale(bbs):
+    """An encode scale chosen for a smaller amax (a stale one) saturates the
+    block scale at 448, exactly as the oracle's encode does."""
+    announce("quantizing GEMM with a stale (too large) encode scale")
+    a = _unit_scale_operand(128, 256, 5, 1.0)
+    b = _unit_scale_operand(128, 256, 6, 1.0, True)
+    y = _ref(a, b, False)
+    s_enc = O.tensor_s_enc(float(np.abs(y).max()) / 8)
+    Y, _ = _run(bbs, upload_nvfp4(a, bbs), upload_nvfp4(b, bbs), s_enc, False, 128, 128)
+    o = O.nvfp4_encode_f32(y, s_enc)
+    assert (host(Y.scales) == 0x7E).any()
+    assert np.array_equal(host(Y.scales), o.scales)
+    assert np.array_equal(host(Y.codes), o.codes)
+
+
+def _mismatch(g, o):
+    return float(np.mean(g != o))
+
+
+@pytest.mark.parametrize("gelu", [False, True])
+def test_general_operands(bbs, gelu):
+    announce(f"quantizing GEMM, quantized X / W operands gelu={gelu}")
+    x = synth.normal_with_outliers(256, 1024, 90)
+    w = synth.normal(384, 1024, 91, 0.05)
+    ox, ow = O.nvfp4_quantize(x), O.nvfp4_quantize(w, tile2d=True)
+    y = _ref(ox, ow, gelu)
+    s_enc = O.tensor_s_enc(float(np.abs(y).max()))
+    Y, got_amax = _run(bbs, upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs), s_enc, gelu, 256, 384)
+    o = O.nvfp4_encode_f32(y, s_enc)
+    assert _mismatch(host(Y.scales), o.scales) < 2e-3
+    assert _mismatch(host(Y.codes), o.codes) < 2e-3
+    assert abs(got_amax - float(np.abs(y).max())) <= 1e-5 * float(np.abs(y).max())
+
+
+def test_grouped_exact_case(bbs):
+    """The grouped (MoE) GEMM with the row gather and per-expert decode
+    scales, exact products, GELU + quantize in the epilogue."""
+    announce("quantizing grouped GEMM, exact products, GELU")
+    G, N, K, T = 4, 128, 256, 96
+    a = _unit_scale_operand(T, K, 40, 0.5)
+    rng = np.random.default_rng(41)
+    counts = np.array([40, 0, 100, 52])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = int(offsets[-1])
+    row_index = rng.integers(0, T, rows).astype(np.int32)
+    ws = [_unit_scale_operand(N, K, 50 + g, 2.0 ** -(g + 1), True) for g in range(G)]
+    y = np.zeros((rows, N), np.float32)
+    A64 = a.dequant_f64()
+    for g in range(G):
+        r0, r1 = offsets[g], offsets[g + 1]
+        y[r0:r1] = O.gemm_f64(A64[row_index[r0:r1]], ws[g].dequant_f64()).astype(np.float32)
+    y = O.gelu_f32(y)
+    s_enc = O.tensor_s_enc(float(np.abs(y).max()))
+    B = bbs.NVFP4Tensor.empty(G * N, K, tile2d=True, n_scales=G, device=dev())
+    for g in range(G):
+        B.codes[g * N:(g + 1) * N] = to_dev(ws[g].codes)
+        B.scales[g * N // 16:(g + 1) * N // 16] = to_dev(ws[g].scales)
+        B.s_dec[g] = float(ws[g].s_dec)
+    Y = bbs.NVFP4Tensor.empty(rows, N, device=dev())
+    se = torch.tensor([s_enc], dtype=torch.float32, device=dev())
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    bbs.grouped_nvfp4_gemm_quant(upload_nvfp4(a, bbs), to_dev(row_index), to_dev(offsets), G, rows,
+                                 B, N, se, Y, gelu=True, amax=amax)
+    torch.cuda.synchronize()
+    o = O.nvfp4_encode_f32(y, s_enc)
+    assert np.array_equal(host(Y.scales), o.scales)
+    assert np.array_equal(host(Y.codes), o.codes)
+    assert float(host(amax)[0]) == float(np.abs(y).max())
+
+
+def test_full_size_sampled(bbs):
+    """The dense forward 8192 x 14336 x 4096 with GELU + quantize in the
+    epilogue, in the configuration bench.py times: sampled rows against the
+    oracle's encode of the FP64 product."""
+    announce("quantizing GEMM 8192x14336x4096 + GELU (sampled rows)")
+    d = synth.dense_forward()
+    ox, ow = O.nvfp4_quantize(d["x"]), O.nvfp4_quantize(d["w"], tile2d=True)
+    rows = np.sort(np.random.default_rng(3).choice(8192, 48, replace=False))
+    rows[-1] = 8191
+    sub = O.NVFP4(np.ascontiguousarray(ox.codes[rows]), np.ascontiguousarray(ox.scales[rows]),
+                  ox.s_dec, len(rows), 4096, False)
+    y = O.gelu_f32(O.gemm_f64(sub.dequant_f64(), ow.dequant_f64()).astype(np.float32))
+    s_enc = O.tensor_s_enc(40.0)
+    Y, got_amax = _run(bbs, upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs), s_enc, True, 8192,
+                       14336)
+    o = O.nvfp4_encode_f32(y, s_enc)
+    ridx = torch.from_numpy(rows).to(dev())
+    assert _mismatch(host(Y.scales[ridx]), o.scales) < 2e-3
+    assert _mismatch(host(Y.codes[ridx]), o.codes) < 2e-3
+    assert got_amax >= float(np.abs(y).max()) * (1 - 1e-5)
