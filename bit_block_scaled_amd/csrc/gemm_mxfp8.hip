@@ -22,12 +22,14 @@
 // operand.  So lane group g reads chunks g and 4 + g of its row and supplies
 // the scale of the slab's block g.
 //
-// The same kernel runs MXFP4 x MXFP4 (FP Training on Blackwell, 'The
-// scaling math, worked'; the OCP format with E2M1 elements): operand format
-// 4 of the same instruction, where lane l's first 16 bytes hold the 32
-// values of block g = l / 16 of row l % 16 (measured).  A slab is still 128
-// bytes of every row, now 256 K-values: two MFMA steps, the first reading
-// chunk g and the second chunk 4 + g, with 8 scale bytes per row.
+// The same tiles, LDS ring and copy plan run MXFP4 x MXFP4 (FP4 Training on
+// Blackwell, 'The scaling math, worked'; the OCP format with E2M1 elements)
+// on v_mfma_scale_f32_32x32x64_f8f6f4 with operand format 4, where lane l's
+// first 16 bytes hold the 32 values of block l / 32 of row l % 32
+// (measured).  A slab is still 128 bytes of every row, now 256 K-values: four
+// 64-value MFMA steps, with 8 scale bytes per row.
+#include <type_traits>
+
 #include "bbs_device.hpp"
 #include "bbs_kernels.hpp"
 
@@ -35,6 +37,7 @@ namespace bbs {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -130,7 +133,7 @@ __device__ __forceinline__ void issue(Stage<FP4> &st, const Plan &pl, int64_t s)
     issue_scales(st, pl, s);
 }
 
-// One 16-byte chunk of row r (FP4: the 32 values of one block); the upper
+// One 16-byte chunk c of row r (FP4: the 32 values of one block); the upper
 // half of the operand is not read by the instruction.
 __device__ __forceinline__ i32x8 frag4(const uint8_t *tile, int r, int c) {
     const uint4 x = *reinterpret_cast<const uint4 *>(tile + r * BK + 16 * swz(r, c));
@@ -145,59 +148,102 @@ __device__ __forceinline__ i32x8 frag(const uint8_t *tile, int r, int g) {
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
-// The MFMAs of one slab.  The copies of the next slab (index sn) into
+// The MFMAs of one FP8 slab.  The copies of the next slab (index sn) into
 // stage nx are issued along the way, four 1 KB copies after each of the
 // first four row blocks' MFMAs (and the scale copies after the fourth): the
 // wave never waits on one long burst of copy issues, and the copies still
-// have half a slab of MFMAs to land in.  FP4 slabs take two MFMA steps
-// (chunks g, then 4 + g); the copies ride along the first.
-template <bool FP4>
-__device__ __forceinline__ void compute(const Stage<FP4> &st, f32x4 (&acc)[8][8], int wm, int wn,
-                                        int lane, Stage<FP4> &nx, const Plan &pl, int64_t sn) {
+// have half a slab of MFMAs to land in.
+__device__ __forceinline__ void compute(const Stage<false> &st, f32x4 (&acc)[8][8], int wm, int wn,
+                                        int lane, Stage<false> &nx, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
     const int g = lane >> 4, rl = lane & 15;
     const int64_t kn = sn * BK;
-    constexpr int fmt = FP4 ? 4 : 0;                    // operand format: E2M1 or E4M3
+    i32x8 bf[8];
+    int bsc[8];
 #pragma unroll
-    for (int ks = 0; ks < (FP4 ? 2 : 1); ++ks) {
-        auto fr = [&](const uint8_t *tile, int r) {
-            return FP4 ? frag4(tile, r, 4 * ks + g) : frag(tile, r, g);
-        };
-        i32x8 bf[8];
-        int bsc[8];
+    for (int j = 0; j < 8; ++j) {
+        const int r = wn * 128 + j * 16 + rl;
+        bf[j] = frag(st.b, r, g);
+        bsc[j] = (int)((st.bs[0][r] >> (8 * g)) & 0xFFu);
+    }
+    // A fragments are double-buffered by hand: row block i + 1 is read while
+    // the MFMAs of row block i run; the scheduling barrier keeps the compiler
+    // from hoisting every fragment read at once.
+    int r0 = wm * 128 + rl;
+    i32x8 an = frag(st.a, r0, g);
+    int ans = (int)((st.as[0][r0] >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = wn * 128 + j * 16 + rl;
-            bf[j] = fr(st.b, r);
-            bsc[j] = (int)((st.bs[ks][r] >> (8 * g)) & 0xFFu);
+    for (int i = 0; i < 8; ++i) {
+        const i32x8 af = an;
+        const int asc = ans;
+        if (i + 1 < 8) {
+            const int r = wm * 128 + (i + 1) * 16 + rl;
+            an = frag(st.a, r, g);
+            ans = (int)((st.as[0][r] >> (8 * g)) & 0xFFu);
         }
-        // A fragments are double-buffered by hand: row block i + 1 is read
-        // while the MFMAs of row block i run; the scheduling barrier keeps
-        // the compiler from hoisting every fragment read at once.
-        int r0 = wm * 128 + rl;
-        i32x8 an = fr(st.a, r0);
-        int ans = (int)((st.as[ks][r0] >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int j = 0; j < 8; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
+                                                                         bsc[j], 0, asc);
+        if (i < 4) {
+#pragma unroll
+            for (int q = 2 * i; q < 2 * i + 2; ++q) {
+                copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
+                copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
+            }
+        }
+        if (i == 3) issue_scales(nx, pl, sn);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// FP4 slabs on v_mfma_scale_f32_32x32x64_f8f6f4, the full-rate form for
+// E2M1 operands (the 16 x 16 x 128 form issues E2M1 at about half its rate,
+// measured): lane l feeds row l % 32 and block l / 32 of a 64-value step (its
+// 16 bytes of the row's chunk 2 * ks + l / 32), with that block's scale.  A
+// wave's 128 x 128 tile is 4 x 4 MFMA blocks of 32 x 32; a slab is 4 steps.
+// The next slab's copies ride along the first two steps, one A and one B copy
+// after each row block's MFMAs, the scale copies after the last of them.
+__device__ __forceinline__ void compute4(const Stage<true> &st, f32x16 (&acc)[4][4], int wm,
+                                         int wn, int lane, Stage<true> &nx, const Plan &pl,
+                                         int64_t sn) {
+    const int w = threadIdx.x >> 6;
+    const int h = lane >> 5, rl = lane & 31;
+    const int64_t kn = sn * BK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int c = 2 * ks + h;                      // the lane's 16-byte chunk
+        const int sh = 8 * (c & 3);                    // its scale byte within the word
+        i32x8 bf[4];
+        int bsc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = wn * 128 + j * 32 + rl;
+            bf[j] = frag4(st.b, r, c);
+            bsc[j] = (int)((st.bs[c >> 2][r] >> sh) & 0xFFu);
+        }
+        int r0 = wm * 128 + rl;
+        i32x8 an = frag4(st.a, r0, c);
+        int ans = (int)((st.as[c >> 2][r0] >> sh) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
             const i32x8 af = an;
             const int asc = ans;
-            if (i + 1 < 8) {
-                const int r = wm * 128 + (i + 1) * 16 + rl;
-                an = fr(st.a, r);
-                ans = (int)((st.as[ks][r] >> (8 * g)) & 0xFFu);
+            if (i + 1 < 4) {
+                const int r = wm * 128 + (i + 1) * 32 + rl;
+                an = frag4(st.a, r, c);
+                ans = (int)((st.as[c >> 2][r] >> sh) & 0xFFu);
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bf[j], af, acc[i][j], fmt, fmt, 0, bsc[j], 0, asc);
-            if (ks == 0 && i < 4) {
-#pragma unroll
-                for (int q = 2 * i; q < 2 * i + 2; ++q) {
-                    copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
-                    copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
-                }
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 4, 4,
+                                                                            0, bsc[j], 0, asc);
+            if (ks < 2) {
+                const int q = 4 * ks + i;
+                copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
+                copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
             }
-            if (ks == 0 && i == 3) issue_scales(nx, pl, sn);
+            if (ks == 1 && i == 3) issue_scales(nx, pl, sn);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -222,11 +268,20 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
     const int wm = wave >> 1, wn = wave & 1;
     const mx::Plan pl = mx::make_plan<FP4>(p, m0, n0);
 
-    f32x4 acc[8][8];
+    // FP8: 8 x 8 blocks of 16 x 16; FP4: 4 x 4 blocks of 32 x 32 (256 FP32 each)
+    typedef std::conditional_t<FP4, f32x16[4][4], f32x4[8][8]> Acc;
+    Acc acc;
+    if constexpr (FP4) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc[i][jj] = f32x4{0, 0, 0, 0};
+            for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x16{0};
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) acc[i][jj] = f32x4{0, 0, 0, 0};
+    }
 
     mx::issue(sm.st[0], pl, 0);
     __builtin_amdgcn_s_waitcnt(0x3F70);               // vmcnt(0)
@@ -236,11 +291,40 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
         // slab s + 1 goes to the other stage (past the end the last slab is
         // copied again into the stage nobody reads any more: no branch)
         const int64_t sn = s + 1 < nslab ? s + 1 : s;
-        mx::compute(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
+        if constexpr (FP4) mx::compute4(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
+        else mx::compute(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
         __builtin_amdgcn_s_waitcnt(0x3F70);           // the next slab's copies have landed
         __syncthreads();
     }
 
+    auto store4 = [&](int64_t m, int64_t n, float y0, float y1, float y2, float y3) {
+        if (BF16_OUT) {
+            const uint2 w = make_uint2(pk_bf16(y0, y1), pk_bf16(y2, y3));
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = w;
+        } else {
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
+                make_float4(y0, y1, y2, y3);
+        }
+    };
+    if constexpr (FP4) {
+        // block (i, jj) holds the transposed 32 x 32 product: lane l has output
+        // row l % 32 and columns 8 * (v / 4) + 4 * (l / 32) + v % 4
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
+            if (m >= p.M) continue;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int64_t n = n0 + wn * 128 + jj * 32 + 8 * gq + 4 * (lane >> 5);
+                    if (n >= p.N) continue;
+                    const f32x16 &y = acc[i][jj];
+                    store4(m, n, y[4 * gq], y[4 * gq + 1], y[4 * gq + 2], y[4 * gq + 3]);
+                }
+        }
+        return;
+    } else {
     // The MFMAs take the B fragment first, so block (i, jj) holds the
     // transposed 16 x 16 product: lane l has output row l % 16 and columns
     // 4 * (l / 16) + v, four consecutive columns stored at once.
@@ -253,14 +337,9 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
             const int64_t n = n0 + wn * 128 + jj * 16 + 4 * (lane >> 4);
             if (n >= p.N) continue;
             const f32x4 y = acc[i][jj];
-            if (BF16_OUT) {
-                const uint2 w = make_uint2(pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]));
-                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + n) = w;
-            } else {
-                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.c) + m * p.ldc + n) =
-                    make_float4(y[0], y[1], y[2], y[3]);
-            }
+            store4(m, n, y[0], y[1], y[2], y[3]);
         }
+    }
     }
 }
 

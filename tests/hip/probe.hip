@@ -96,7 +96,35 @@ __global__ void mfma_scale_layout_fp4_kernel(int which, const int *one, float *o
     for (int v = 0; v < 4; ++v) out[(blockIdx.x * 64 + lane) * 4 + v] = acc[v];
 }
 
+// The 32 x 32 x 64 form with E2M1 operands: one-hot nibble J (< 32) of lane
+// L's first 16 bytes, scales 2^(lane / 32) on the one-hot operand.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__global__ void mfma32_scale_layout_fp4_kernel(int which, const int *one, float *out) {
+    const int lane = threadIdx.x;
+    const int L = blockIdx.x / 32, J = blockIdx.x % 32;
+    i32x8 h, o;
+    for (int v = 0; v < 8; ++v) {
+        h[v] = 0;
+        o[v] = v < 4 ? 0x22222222 : 0;
+    }
+    if (lane == L) h[J / 8] = 2 << (4 * (J % 8));
+    const int s_var = 127 * one[0] + (lane >> 5);
+    const int s_one = 127 * one[0];
+    f32x16_t acc;
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    if (which == 0)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h, o, acc, 4, 4, 0, s_var, 0, s_one);
+    else
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o, h, acc, 4, 4, 0, s_one, 0, s_var);
+    for (int v = 0; v < 16; ++v) out[(blockIdx.x * 64 + lane) * 16 + v] = acc[v];
+}
+
 extern "C" {
+int probe_mfma32_scale_layout_fp4(int which, const int *one, float *out) {
+    hipLaunchKernelGGL(mfma32_scale_layout_fp4_kernel, dim3(64 * 32), dim3(64), 0, 0, which, one,
+                       out);
+    return (int)hipDeviceSynchronize();
+}
 int probe_mfma_scale_layout_fp4(int which, const int *one, float *out) {
     hipLaunchKernelGGL(mfma_scale_layout_fp4_kernel, dim3(64 * 32), dim3(64), 0, 0, which, one,
                        out);

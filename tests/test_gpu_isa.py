@@ -187,3 +187,30 @@ def test_scaled_fp4_mfma_layout(probe):
     for which in (0, 1):
         for L in range(64):
             assert np.all(blocks[which, L] == L // 16), (which, L)
+
+
+def test_scaled_fp4_mfma32_layout(probe):
+    """E2M1 operands of v_mfma_scale_f32_32x32x64_f8f6f4 (the full-rate FP4
+    form): lane l feeds row l % 32 and the 32 values of block l / 32 (its
+    first 16 bytes), scaled by the scale that lane half supplies; the output
+    register v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32."""
+    announce("v_mfma_scale_f32_32x32x64_f8f6f4 E2M1 lane layout")
+    one = torch.ones(1, dtype=torch.int32, device=dev())
+    for which in (0, 1):
+        out = torch.zeros(2048 * 64 * 16, dtype=torch.float32, device=dev())
+        assert probe.probe_mfma32_scale_layout_fp4(which, C.c_void_p(one.data_ptr()),
+                                                   C.c_void_p(out.data_ptr())) == 0
+        acc = out.cpu().numpy().reshape(64, 32, 64, 16)
+        for L in range(64):
+            for J in range(32):
+                D = np.zeros((32, 32))
+                a = acc[L, J]
+                for lane in range(64):
+                    for v in range(16):
+                        D[8 * (v // 4) + 4 * (lane // 32) + v % 4, lane % 32] = a[lane, v]
+                want = np.zeros((32, 32))
+                if which == 0:
+                    want[L % 32, :] = 2.0 ** (L // 32)
+                else:
+                    want[:, L % 32] = 2.0 ** (L // 32)
+                assert np.array_equal(D, want), (which, L, J)
