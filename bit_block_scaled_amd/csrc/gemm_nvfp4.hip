@@ -594,7 +594,15 @@ __device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_
     }
     __syncthreads();
     const int64_t total = tile_start[p.G];
-    for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    // Each XCD (workgroup b runs on XCD b % 8; the grid is a multiple of 8)
+    // works through one contiguous eighth of the tile sequence, so the tiles
+    // in flight on an XCD share an expert's weights and their token rows in
+    // that XCD's L2.
+    const int64_t xcd = blockIdx.x % 8, per_xcd = gridDim.x / 8;
+    const int64_t share = total / 8, extra = total % 8;
+    const int64_t first = xcd * share + (xcd < extra ? xcd : extra);
+    const int64_t last = first + share + (xcd < extra ? 1 : 0);
+    for (int64_t tile = first + blockIdx.x / 8; tile < last; tile += per_xcd) {
         int g = 0;
         while (g + 1 < p.G && tile_start[g + 1] <= tile) ++g;
         const int64_t local = tile - tile_start[g];
