@@ -57,6 +57,19 @@ __global__ void cvt_bf16_fp4_kernel(const float *scales, int ns, uint32_t *out) 
     out[i * 4 + 3] = __builtin_bit_cast(uint32_t, r3);
 }
 
+// cvt_scalef32_pk_f16_fp4 at arbitrary FP32 scales: does the instruction
+// multiply by the whole scale or by its power of two only?
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__global__ void cvt_f16_fp4_kernel(const float *scales, int ns, uint32_t *out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ns * 256) return;
+    const int si = i / 256, b = i % 256;
+    const uint32_t src = (uint32_t)b * 0x01010101u;
+    const float s = scales[si];
+    f16x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, s, 0);
+    out[i] = __builtin_bit_cast(uint32_t, r0);
+}
+
 // cvt_scalef32_pk_fp4_f32 with scale 1.0: the packed byte for (x[i], -x[i]).
 __global__ void cvt_fp4_f32_kernel(const float *x, int n, const float *scale, uint8_t *out) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -137,6 +150,11 @@ int probe_mfma_scale_layout(int which, const int *one, float *out) {
 int probe_cvt_bf16_fp4(const float *scales, int ns, uint32_t *out) {
     const int n = ns * 256;
     hipLaunchKernelGGL(cvt_bf16_fp4_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, scales, ns, out);
+    return (int)hipDeviceSynchronize();
+}
+int probe_cvt_f16_fp4(const float *scales, int ns, uint32_t *out) {
+    const int n = ns * 256;
+    hipLaunchKernelGGL(cvt_f16_fp4_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, scales, ns, out);
     return (int)hipDeviceSynchronize();
 }
 int probe_cvt_fp4_f32(const float *x, int n, const float *scale, uint8_t *out) {

@@ -214,3 +214,21 @@ def test_scaled_fp4_mfma32_layout(probe):
                 else:
                     want[:, L % 32] = 2.0 ** (L // 32)
                 assert np.array_equal(D, want), (which, L, J)
+
+
+def test_fp4_to_f16_scale_uses_exponent_only(probe):
+    """v_cvt_scalef32_pk_f16_fp4 multiplies by 2^exponent(scale) only, so an
+    E4M3 block scale (with mantissa bits) cannot ride in the conversion: the
+    NVFP4 GEMM multiplies by the decoded block scale separately."""
+    announce("v_cvt_scalef32_pk_f16_fp4: scale exponent only")
+    scales = np.array([1.0, 1.125, 0.6875, 448.0, 3.0], np.float32)
+    sd = torch.from_numpy(scales).to(dev())
+    out = torch.zeros(len(scales) * 256, dtype=torch.int32, device=dev())
+    assert probe.probe_cvt_f16_fp4(C.c_void_p(sd.data_ptr()), len(scales),
+                                   C.c_void_p(out.data_ptr())) == 0
+    r = out.cpu().numpy().view(np.uint32).reshape(len(scales), 256)
+    dec = np.array([O.e2m1_value(c) for c in range(16)])
+    for si, s in enumerate(scales):
+        lo = (r[si] & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+        p2 = 2.0 ** np.floor(np.log2(s))
+        assert np.array_equal(lo, dec[np.arange(256) & 15] * p2), s
