@@ -75,10 +75,10 @@ def _load():
                                        i64, vp, i32, i64, vp]
     lib.mxfp4_quantize.argtypes = [vp, i64, i64, i64, C.POINTER(Mx4Desc), i32, Rng, vp]
     lib.nvfp4_gemm_quant.argtypes = [C.POINTER(Fp4Desc), C.POINTER(Fp4Desc), vp, i32,
-                                     C.POINTER(Fp4Desc), vp, vp]
+                                     C.POINTER(Fp4Desc), vp, vp, vp]
     lib.grouped_nvfp4_gemm_quant.argtypes = [C.POINTER(Fp4Desc), vp, vp, i32, i64,
                                              C.POINTER(Fp4Desc), i64, vp, i32, C.POINTER(Fp4Desc),
-                                             vp, vp]
+                                             vp, vp, vp]
     lib.s2f6_quantize.argtypes = [vp, i64, i64, i64, i32, C.c_uint32, C.POINTER(S2F6Desc), vp]
     lib.s2f6_combine.argtypes = [C.POINTER(S2F6Desc), vp, vp, i64, i32, i32, C.c_uint32, vp, i32,
                                  i64, vp]
@@ -264,18 +264,22 @@ def mxfp4_quantize(x, out, round=RTN, rng=(0, 0), stream=None):
                               Rng(*rng), _stream(stream)))
 
 
-def nvfp4_gemm_quant(A, B, s_enc, Y, gelu=False, amax=None, stream=None):
-    """Y (NVFP4Tensor, 1x16) = NVFP4 copy of (GELU of) A * B^T with the encode
-    scale s_enc (a one-element float32 device tensor); amax (optional
-    one-element float32 device tensor) receives max |y|."""
+def nvfp4_gemm_quant(A, B, s_enc, Y, gelu=False, amax=None, ws=None, stream=None):
+    """Y (NVFP4Tensor, 1x16) = NVFP4 copy of (GELU of) the BF16 product A * B^T
+    with the encode scale s_enc (a one-element float32 device tensor); amax
+    (optional one-element float32 device tensor) receives max |y|."""
     ad, bd, yd = A.desc(), B.desc(), Y.desc()
+    if gelu and ws is None:
+        ws = amax_workspace(s_enc.device)
     _check(lib.nvfp4_gemm_quant(C.byref(ad), C.byref(bd), _ptr(s_enc), int(gelu), C.byref(yd),
-                                _ptr(amax), _stream(stream)))
+                                _ptr(amax), _ptr(ws), _stream(stream)))
 
 
 def grouped_nvfp4_gemm_quant(A, row_index, group_offsets, G, max_rows, B, N, s_enc, Y,
-                             gelu=False, amax=None, stream=None):
+                             gelu=False, amax=None, ws=None, stream=None):
     ad, bd, yd = A.desc(), B.desc(), Y.desc()
+    if gelu and ws is None:
+        ws = amax_workspace(s_enc.device)
     _check(lib.grouped_nvfp4_gemm_quant(C.byref(ad), _ptr(row_index), _ptr(group_offsets), G,
                                         max_rows, C.byref(bd), N, _ptr(s_enc), int(gelu),
-                                        C.byref(yd), _ptr(amax), _stream(stream)))
+                                        C.byref(yd), _ptr(amax), _ptr(ws), _stream(stream)))

@@ -87,10 +87,13 @@ namespace {
 // Shared checks of the quantizing GEMMs: the large-tile conditions and the
 // NVFP4 output descriptor (rows x N, 1x16, one decode scale).
 int check_quant_out(const bbs::GemmParams &p, const bbs_fp4 *Y, int64_t rows, const float *s_enc,
-                    const float *amax) {
+                    const float *amax, int32_t gelu, const float *ws) {
     int st;
     if ((st = check_fp4(Y, "Y", true))) return st;
     if (!s_enc) return fail(BBS_EINVAL, "null s_enc");
+    if (gelu != 0 && gelu != 1) return fail(BBS_EINVAL, "gelu must be 0 or 1");
+    if (gelu && (!ws || !aligned(ws, 16)))
+        return fail(BBS_EINVAL, "gelu needs a 16-byte aligned workspace");
     if (Y->rows != rows || Y->cols != p.N) return fail(BBS_EINVAL, "Y must be rows x N");
     if (Y->tile2d || Y->sdec_per_row)
         return fail(BBS_EINVAL, "Y is a 1x16 copy with one decode scale");
@@ -101,29 +104,29 @@ int check_quant_out(const bbs::GemmParams &p, const bbs_fp4 *Y, int64_t rows, co
     return BBS_OK;
 }
 
-bbs::QuantOut quant_out(const bbs_fp4 *Y, const float *s_enc, float *amax) {
-    return {Y->codes, Y->scales, Y->s_dec, s_enc, reinterpret_cast<unsigned *>(amax)};
+bbs::QuantOut quant_out(const bbs_fp4 *Y, const float *s_enc, float *amax, float *ws) {
+    return {Y->codes, Y->scales, Y->s_dec, s_enc, reinterpret_cast<unsigned *>(amax),
+            ws ? ws + bbs::kGeluTabOffset : nullptr};
 }
 
 }  // namespace
 
 int nvfp4_gemm_quant(const bbs_fp4 *A, const bbs_fp4 *B, const float *s_enc, int32_t gelu,
-                     const bbs_fp4 *Y, float *amax, void *stream) {
+                     const bbs_fp4 *Y, float *amax, float *ws, void *stream) {
     g_err[0] = 0;
     int st;
     if ((st = check_fp4(A, "A", true))) return st;
     if ((st = check_fp4(B, "B", true))) return st;
     if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
     if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
-    if (gelu != 0 && gelu != 1) return fail(BBS_EINVAL, "gelu must be 0 or 1");
     bbs::GemmParams p{};
     p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
     p.b = {B->codes, B->scales, B->s_dec, B->rows, B->tile2d, 0};
     p.M = A->rows;
     p.N = B->rows;
     p.K = A->cols;
-    if ((st = check_quant_out(p, Y, p.M, s_enc, amax))) return st;
-    p.q = quant_out(Y, s_enc, amax);
+    if ((st = check_quant_out(p, Y, p.M, s_enc, amax, gelu, ws))) return st;
+    p.q = quant_out(Y, s_enc, amax, ws);
     return hip_status(bbs::launch_nvfp4_gemm_quant(p, gelu != 0,
                                                    reinterpret_cast<hipStream_t>(stream)),
                       "quantizing gemm launch");
@@ -132,7 +135,7 @@ int nvfp4_gemm_quant(const bbs_fp4 *A, const bbs_fp4 *B, const float *s_enc, int
 int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
                              const int64_t *group_offsets, int32_t G, int64_t max_rows,
                              const bbs_fp4 *B, int64_t N, const float *s_enc, int32_t gelu,
-                             const bbs_fp4 *Y, float *amax, void *stream) {
+                             const bbs_fp4 *Y, float *amax, float *ws, void *stream) {
     g_err[0] = 0;
     int st;
     if ((st = check_fp4(A, "A", true))) return st;
@@ -144,7 +147,6 @@ int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
     if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
     if (max_rows <= 0) return fail(BBS_EINVAL, "max_rows must be positive");
     if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
-    if (gelu != 0 && gelu != 1) return fail(BBS_EINVAL, "gelu must be 0 or 1");
     bbs::GemmParams p{};
     p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
     p.b = {B->codes, B->scales, B->s_dec, N, B->tile2d, 0};
@@ -156,8 +158,8 @@ int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
     p.G = G;
     p.max_rows = max_rows;
     p.a_src_rows = A->rows;
-    if ((st = check_quant_out(p, Y, max_rows, s_enc, amax))) return st;
-    p.q = quant_out(Y, s_enc, amax);
+    if ((st = check_quant_out(p, Y, max_rows, s_enc, amax, gelu, ws))) return st;
+    p.q = quant_out(Y, s_enc, amax, ws);
     return hip_status(bbs::launch_grouped_nvfp4_gemm_quant(p, gelu != 0,
                                                            reinterpret_cast<hipStream_t>(stream)),
                       "quantizing grouped gemm launch");

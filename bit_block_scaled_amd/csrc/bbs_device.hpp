@@ -304,6 +304,19 @@ __device__ __forceinline__ void gelu_table_load(float *lds, const float *tab) {
         reinterpret_cast<float4 *>(lds)[i] = reinterpret_cast<const float4 *>(tab)[i];
 }
 
+// The same without a branch (for code where a wave-uniform branch per
+// element would split the control flow too finely).
+__device__ __forceinline__ float gelu_bf16_select(uint32_t h, const float *tab) {
+    const uint32_t a = h & 0x7FFFu;
+    const uint32_t d = a - (uint32_t)(kGeluTabE0 << 7);
+    const uint32_t i = min(d, (uint32_t)kGeluTabHalf - 1u) + (h >> 15) * (uint32_t)kGeluTabHalf;
+    const float t = tab[i];                  // always in the table: loaded unconditionally
+    const float x = __uint_as_float(h << 16);
+    const float big = (h & 0x8000u) ? -0.0f : x;
+    const float out = a < (uint32_t)(kGeluTabE0 << 7) ? 0.5f * x : big;
+    return d >= (uint32_t)kGeluTabHalf ? out : t;
+}
+
 __device__ __forceinline__ float gelu_bf16(uint32_t h, const float *tab) {
     const uint32_t a = h & 0x7FFFu;
     const uint32_t d = a - (uint32_t)(kGeluTabE0 << 7);     // wraps below the table

@@ -69,6 +69,7 @@ struct QuantOut {
     float *s_dec;            // receives 1 / s_enc
     const float *s_enc;      // one FP32 encode scale (device)
     unsigned *amax;          // max |y| of the quantized values as FP32 bits, or nullptr
+    const float *gelu_tab;   // the GELU table (GELU modes)
 };
 
 struct GemmParams {
@@ -137,7 +138,8 @@ bool big_ok(const GemmParams &p, bool bf16_out);
 hipError_t launch_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStream_t s);
 // The same GEMMs (large-tile kernels only: big_ok must hold) writing p.q
-// instead of C; p.q.amax, when given, is cleared first.
+// instead of C; p.q.amax, when given, is cleared first; with gelu the GELU
+// table is written to p.q.gelu_tab first.
 hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s);
 hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);

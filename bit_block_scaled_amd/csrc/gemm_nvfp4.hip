@@ -305,20 +305,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Output modes: OUT_F32, OUT_BF16, and the quantizing modes OUT_Q / OUT_QG
 // (4bit.vizuara.ai, section 13; End-to-End 4-Bit Training, kernels for
 // low-precision training: the quantize rides in the GEMM's epilogue so the
-// output never goes through BF16).  These stage FP32 rows as OUT_F32 does;
-// on read-back each lane takes one 1x16 block of a row (16 consecutive FP32
-// values), applies GELU (OUT_QG), and encodes it with the given tensor
-// scale exactly as the quantizer does: E4M3 block scale of
+// output never makes a round trip through memory).  These stage FP32 rows as
+// OUT_BF16 does (the BF16 values the plain GEMM stores); on read-back each
+// lane takes one 1x16 block of a row (16 consecutive values), applies GELU
+// by the quantizers' table (OUT_QG; the table is copied from
+// q.gelu_tab into the idle ring), and encodes the block with the given
+// tensor scale exactly as the quantizer does: E4M3 block scale of
 // (amax_b / 6) * s_enc (never below code 1), E2M1 codes of x * s_enc_b to
-// nearest even.  The largest |value| is folded into q.amax.
+// nearest even.  The result is bit for bit the BF16 GEMM followed by the
+// quantizer with that scale.  The largest |value| is folded into q.amax.
 constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_QG = 3;
+
+// Order a wave's LDS writes and later reads (or reads and later writes) of
+// the same staging rows: wait for its LDS operations and fence the compiler.
+__device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int OUT, typename ScaleFn>
 __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], int64_t m0,
                                          int64_t m_end, int64_t n0, int64_t n_end,
                                          ScaleFn scale_of, void *C, int64_t ldc, int wm, int wn,
                                          int lane, const QuantOut &qo) {
-    constexpr bool BF16_OUT = OUT == OUT_BF16, QUANT = OUT >= OUT_Q;
+    constexpr bool QUANT = OUT >= OUT_Q;
+    constexpr bool BF16_OUT = OUT == OUT_BF16 || QUANT;    // BF16 staging
     constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
     constexpr int RS = 128 * ES + 16;                 // staging row stride
     constexpr int PR = BF16_OUT ? 32 : 16;            // rows per piece
@@ -328,9 +336,16 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
     const int lr = lane & 31;                          // the lane's row in a 32-row block
     float s_enc = 1.0f, s_dec = 1.0f, amax = 0.0f;
+    // GELU table (OUT_QG): in the idle ring past the staging rows (4 waves x
+    // 32 rows x 272 bytes)
+    float *tab = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&sm) + 65536);
     if (QUANT) {
         s_enc = qo.s_enc[0];
         s_dec = 1.0f / s_enc;
+        if (OUT == OUT_QG) {
+            gelu_table_load(tab, qo.gelu_tab);
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -358,7 +373,10 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                             *reinterpret_cast<float4 *>(row + c * 4) = make_float4(y0, y1, y2, y3);
                     }
             }
-            // a wave reads back only its own rows: LDS order suffices
+            // a wave reads back only its own rows, written by other lanes of
+            // the same wave: LDS executes a wave's operations in order, and
+            // the barrier keeps the compiler from moving reads above writes
+            lds_order();
             if (!QUANT) {
 #pragma unroll
                 for (int q = 0; q < PR / RPI; ++q) {
@@ -371,32 +389,22 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                         *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
                 }
             } else {
-                // 16 rows x 8 blocks of 16: two blocks per lane
+                // 32 rows x 8 blocks of 16 BF16 values: four blocks per lane
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
+                for (int q = 0; q < 4; ++q) {
                     const int r = q * 8 + lane / 8, b = lane % 8;
-                    float4 *src = reinterpret_cast<float4 *>(buf + r * RS + b * 64);
-                    if (OUT == OUT_QG) {
-                        // GELU in place, four values at a time (a rolled loop
-                        // keeps the register pressure of the tile low)
-#pragma unroll 1
-                        for (int v = 0; v < 4; ++v) {
-                            float4 w = src[v];
-                            w.x = gelu_tanh(w.x);
-                            w.y = gelu_tanh(w.y);
-                            w.z = gelu_tanh(w.z);
-                            w.w = gelu_tanh(w.w);
-                            src[v] = w;
-                        }
-                    }
+                    const uint4 *src = reinterpret_cast<const uint4 *>(buf + r * RS + b * 32);
+                    // the BF16 value the plain GEMM stores, GELU of it by the table
                     float f[16];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float4 w = src[v];
-                        f[4 * v] = w.x;
-                        f[4 * v + 1] = w.y;
-                        f[4 * v + 2] = w.z;
-                        f[4 * v + 3] = w.w;
+                    for (int v = 0; v < 2; ++v) {
+                        const uint4 w = src[v];
+                        const uint32_t hw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t hb = (e & 1) ? (hw[e >> 1] >> 16) : (hw[e >> 1] & 0xFFFFu);
+                            f[8 * v + e] = OUT == OUT_QG ? gelu_bf16_select(hb, tab) : bf16_to_f32(hb);
+                        }
                     }
                     const int64_t m = mw + i * 32 + piece * PR + r;
                     const int64_t n = nw + b * 16;
@@ -413,6 +421,7 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                     }
                 }
             }
+            lds_order();                          // before the next piece is staged
         }
     }
     if (QUANT && qo.amax) {
@@ -670,6 +679,10 @@ static void launch_with_smem(K_ kernel, dim3 grid, const GemmParams &p, hipStrea
 
 hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s) {
     if (p.q.amax) hipLaunchKernelGGL(clear_amax_kernel, dim3(1), dim3(1), 0, s, p.q.amax);
+    if (gelu) {
+        const hipError_t e = launch_gelu_table(const_cast<float *>(p.q.gelu_tab), s);
+        if (e != hipSuccess) return e;
+    }
     const int64_t T = ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
     if (gelu) launch_with_smem(nvfp4_gemm_quant_kernel<true>, dim3((unsigned)T), p, s);
     else launch_with_smem(nvfp4_gemm_quant_kernel<false>, dim3((unsigned)T), p, s);
@@ -679,6 +692,10 @@ hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s
 hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s) {
     if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
     if (p.q.amax) hipLaunchKernelGGL(clear_amax_kernel, dim3(1), dim3(1), 0, s, p.q.amax);
+    if (gelu) {
+        const hipError_t e = launch_gelu_table(const_cast<float *>(p.q.gelu_tab), s);
+        if (e != hipSuccess) return e;
+    }
     if (gelu) launch_with_smem(grouped_nvfp4_gemm_quant_kernel<true>, dim3(512), p, s);
     else launch_with_smem(grouped_nvfp4_gemm_quant_kernel<false>, dim3(512), p, s);
     return hipGetLastError();

@@ -259,27 +259,30 @@ int s2f6_combine(const bbs_s2f6 *in, const int32_t *src_index, const float *weig
 
 /* NVFP4 GEMM whose epilogue quantizes the product (4bit.vizuara.ai,
  * section 13; End-to-End 4-Bit Training, kernels for low-precision
- * training): the output never goes through BF16.  With y = the FP32 value
- * nvfp4_gemm would produce (C = s_dec,A * s_dec,B * sum ...), and with
- * gelu = 1 y = GELU(y) in FP32 (the tanh form of bbs_quant_args.gelu),
- * Y receives the 1x16 NVFP4 copy of y encoded with the given tensor encode
- * scale *s_enc (device, one FP32; e.g. 2688 / a previous amax): per block,
- * E4M3 code of (amax_b / 6) * s_enc (nearest even, saturating at 448, never
- * below code 1), s_enc_b = 1 / (E4M3 * (1 / s_enc)), E2M1 codes of
- * y * s_enc_b to nearest even; Y->s_dec[0] = 1 / s_enc.  Values beyond
+ * training): the output never makes a round trip through memory.  With y =
+ * the BF16 value nvfp4_gemm with BBS_OUT_BF16 would store, and with gelu = 1
+ * y = GELU(y) (the tanh form of bbs_quant_args.gelu), Y receives the 1x16
+ * NVFP4 copy of y encoded with the given tensor encode scale *s_enc (device,
+ * one FP32; e.g. 2688 / a previous amax): per block, E4M3 code of
+ * (amax_b / 6) * s_enc (nearest even, saturating at 448, never below code
+ * 1), s_enc_b = 1 / (E4M3 * (1 / s_enc)), E2M1 codes of y * s_enc_b to
+ * nearest even; Y->s_dec[0] = 1 / s_enc.  This is bit for bit the BF16 GEMM
+ * followed by nvfp4_quantize with that encode scale.  Values beyond
  * 2688 / s_enc saturate.  amax (device, optional) receives max |y| over the
- * whole output (cleared by the call), e.g. the next call's scale.  Y must be
- * rows x N (tile2d 0, one decode scale); K % 128 == 0 and 16-byte aligned
- * codes, 8-byte aligned scales (else BBS_ENOTSUP).  Errors: BBS_EINVAL. */
+ * whole output (cleared by the call), e.g. the next call's scale.  ws
+ * (BBS_AMAX_WS_FLOATS floats, 16-byte aligned) is needed with gelu (it
+ * receives the GELU table).  Y must be rows x N (tile2d 0, one decode
+ * scale); K % 128 == 0 and 16-byte aligned codes, 8-byte aligned scales
+ * (else BBS_ENOTSUP).  Errors: BBS_EINVAL. */
 int nvfp4_gemm_quant(const bbs_fp4 *A, const bbs_fp4 *B, const float *s_enc, int32_t gelu,
-                     const bbs_fp4 *Y, float *amax, void *stream);
+                     const bbs_fp4 *Y, float *amax, float *ws, void *stream);
 
 /* The grouped GEMM (as grouped_nvfp4_gemm) with the same quantizing
  * epilogue: Y is max_rows x N. */
 int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
                              const int64_t *group_offsets, int32_t G, int64_t max_rows,
                              const bbs_fp4 *B, int64_t N, const float *s_enc, int32_t gelu,
-                             const bbs_fp4 *Y, float *amax, void *stream);
+                             const bbs_fp4 *Y, float *amax, float *ws, void *stream);
 
 /* Name of a status code. */
 const char *bbs_strerror(int status);

@@ -225,14 +225,18 @@ def test_gemm_quant_errors(lib):
     B = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 48, 128, 1, 0)
     Y = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 48, 0, 0)
     s = C.c_void_p(0x4000)
-    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), None, 0, C.byref(Y), None, None) == bbs.BBS_EINVAL
-    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 2, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    q = lambda s_, g, ws=None: L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s_, g, C.byref(Y), None,
+                                                  ws, None)
+    assert q(None, 0) == bbs.BBS_EINVAL
+    assert q(s, 2) == bbs.BBS_EINVAL
+    assert q(s, 1) == bbs.BBS_EINVAL                      # GELU needs the workspace
+    assert b"workspace" in L.bbs_last_error()
     Y.rows = 16
-    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 0, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    assert q(s, 0) == bbs.BBS_EINVAL
     Y.rows, Y.tile2d = 32, 1
-    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 0, C.byref(Y), None, None) == bbs.BBS_EINVAL
+    assert q(s, 0) == bbs.BBS_EINVAL
     Y.tile2d = 0
     A.cols = B.cols = 64
-    assert L.nvfp4_gemm_quant(C.byref(A), C.byref(B), s, 0, C.byref(Y), None, None) == bbs.BBS_ENOTSUP
+    assert q(s, 0) == bbs.BBS_ENOTSUP
     assert L.grouped_nvfp4_gemm_quant(C.byref(A), None, None, 1, 32, C.byref(B), 48, s, 0,
-                                      C.byref(Y), None, None) == bbs.BBS_EINVAL
+                                      C.byref(Y), None, None, None) == bbs.BBS_EINVAL

@@ -1,13 +1,16 @@
 """GEMMs with the NVFP4 quantize in their epilogue (4bit.vizuara.ai, section
 13; End-to-End 4-Bit Training, kernels for low-precision training).
 
-Where the FP32 products are exact (integer-valued codes with unit block
-scales and power-of-two decode scales) the codes, scales, decode scale and
-output amax must equal the oracle's encode of the exact product bit for bit,
-with and without GELU.  Elsewhere the FP32 sum order is free, so a value
-lying at a rounding boundary may round either way: there the test bounds the
-fraction of code and scale bytes that differ from the oracle's encode of the
-FP64 product.
+The epilogue encodes the BF16 value the plain GEMM would store (and GELU of
+it), so its result is the BF16 GEMM followed by the quantizer.  Where the
+FP32 products are exact (integer-valued codes with unit block scales and
+power-of-two decode scales) the codes, scales, decode scale and output amax
+must equal the oracle's encode of the exact product (rounded to BF16) bit for
+bit, with and without GELU.  Elsewhere the FP32 sum order is free, so a
+value lying at a rounding boundary may round either way: there the test
+bounds the fraction of code and scale bytes that differ from the oracle's
+encode of the FP64 product, and checks at full size that the fused kernel
+equals the library's own unfused GEMM + quantize bit for bit.
 """
 import numpy as np
 import pytest
@@ -35,7 +38,7 @@ def _unit_scale_operand(R, K, seed, s_dec, tile2d=False):
 
 
 def _ref(a, b, gelu):
-    y = O.gemm_f64(a.dequant_f64(), b.dequant_f64()).astype(np.float32)
+    y = O.bf16_rne(O.gemm_f64(a.dequant_f64(), b.dequant_f64())).astype(np.float32)
     return O.gelu_f32(y) if gelu else y
 
 
@@ -116,7 +119,7 @@ def test_grouped_exact_case(bbs):
     A64 = a.dequant_f64()
     for g in range(G):
         r0, r1 = offsets[g], offsets[g + 1]
-        y[r0:r1] = O.gemm_f64(A64[row_index[r0:r1]], ws[g].dequant_f64()).astype(np.float32)
+        y[r0:r1] = O.bf16_rne(O.gemm_f64(A64[row_index[r0:r1]], ws[g].dequant_f64()))
     y = O.gelu_f32(y)
     s_enc = O.tensor_s_enc(float(np.abs(y).max()))
     B = bbs.NVFP4Tensor.empty(G * N, K, tile2d=True, n_scales=G, device=dev())
@@ -147,12 +150,24 @@ def test_full_size_sampled(bbs):
     rows[-1] = 8191
     sub = O.NVFP4(np.ascontiguousarray(ox.codes[rows]), np.ascontiguousarray(ox.scales[rows]),
                   ox.s_dec, len(rows), 4096, False)
-    y = O.gelu_f32(O.gemm_f64(sub.dequant_f64(), ow.dequant_f64()).astype(np.float32))
+    y = O.gelu_f32(O.bf16_rne(O.gemm_f64(sub.dequant_f64(), ow.dequant_f64())).astype(np.float32))
     s_enc = O.tensor_s_enc(40.0)
-    Y, got_amax = _run(bbs, upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs), s_enc, True, 8192,
-                       14336)
+    xq, wq = upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs)
+    Y, got_amax = _run(bbs, xq, wq, s_enc, True, 8192, 14336)
     o = O.nvfp4_encode_f32(y, s_enc)
     ridx = torch.from_numpy(rows).to(dev())
     assert _mismatch(host(Y.scales[ridx]), o.scales) < 2e-3
     assert _mismatch(host(Y.codes[ridx]), o.codes) < 2e-3
     assert got_amax >= float(np.abs(y).max()) * (1 - 1e-5)
+    # at full size: the fused kernel equals the BF16 GEMM followed by the
+    # fused GELU quantizer, whose amax pass finds the same amax, bit for bit
+    h = torch.empty((8192, 14336), dtype=torch.int16, device=dev())
+    bbs.nvfp4_gemm(bbs.FMT_NVFP4, xq, wq, h, bbs.OUT_BF16)
+    U = bbs.NVFP4Tensor.empty(8192, 14336, device=dev())
+    bbs.nvfp4_quantize(h, U, gelu=True)
+    Y2, amax2 = _run(bbs, xq, wq, np.float32(2688.0) / np.float32(got_amax), True, 8192, 14336)
+    assert amax2 == got_amax
+    torch.cuda.synchronize()
+    assert torch.equal(U.s_dec, Y2.s_dec)
+    assert torch.equal(U.scales, Y2.scales)
+    assert torch.equal(U.codes, Y2.codes)
