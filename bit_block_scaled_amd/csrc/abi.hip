@@ -215,6 +215,7 @@ int s2f6_combine(const bbs_s2f6 *in, const int32_t *src_index, const float *weig
     p.scales = in->scales;
     p.C = in->cols;
     p.src = src_index;
+    p.src_rows = in->rows;
     p.w = weights;
     p.T = tokens;
     p.K = k;

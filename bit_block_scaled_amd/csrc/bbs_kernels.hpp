@@ -97,7 +97,8 @@ struct S2F6CombineParams {
     const int8_t *codes;
     const uint8_t *scales;
     int64_t C;                 // values per row (C % 32 == 0)
-    const int32_t *src;        // T x K rows of codes (negative: skipped)
+    const int32_t *src;        // T x K rows of codes (negative or >= src_rows: skipped)
+    int64_t src_rows;
     const float *w;            // T x K weights, or nullptr (weight 1)
     int64_t T;
     int K;

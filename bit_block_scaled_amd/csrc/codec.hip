@@ -103,14 +103,14 @@ __global__ __launch_bounds__(kCodecThreads) void s2f6_encode_kernel(const uint16
 
 // out[t] chunk = inverse RHT of sum_j w[t][j] * decode(row src[t][j]);
 // decode(code) = code * 2^(k-6) (exact); the weight multiply and every
-// addition round once, in slot order; rows with a negative index are
-// skipped.  The inverse of the rotation is the same butterflies and
+// addition round once, in slot order; rows with a negative index (or one
+// past the input) are skipped.  The inverse of the rotation is the same butterflies and
 // multiply, then the sign flips.
 template <bool RHT, bool WEIGHTS, bool BF16_OUT>
 __global__ __launch_bounds__(kCodecThreads) void s2f6_combine_kernel(
     const int8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int64_t C,
     const int32_t *__restrict__ src, const float *__restrict__ w, int64_t T, int K,
-    uint32_t signs, void *__restrict__ out, int64_t ldo) {
+    int64_t src_rows, uint32_t signs, void *__restrict__ out, int64_t ldo) {
     const int64_t nb = C / 32;
     const int64_t b = (int64_t)blockIdx.x * kCodecThreads + threadIdx.x;
     if (b >= T * nb) return;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kCodecThreads) void s2f6_combine_kernel(
     for (int i = 0; i < 32; ++i) acc[i] = 0.0f;
     for (int j = 0; j < K; ++j) {
         const int32_t row = src[t * K + j];
-        if (row < 0) continue;
+        if (row < 0 || row >= src_rows) continue;     // a dropped slot (or a bad index)
         const uint4 *p = reinterpret_cast<const uint4 *>(codes + (int64_t)row * C + cb * 32);
         const uint4 c0 = p[0], c1 = p[1];
         const float unit = ldexpf(1.0f, (int)scales[(int64_t)row * nb + cb] - 127 - 6);
@@ -170,7 +170,8 @@ hipError_t launch_s2f6_encode(const uint16_t *x, int64_t R, int64_t C, int64_t l
 template <bool R_, bool W_, bool B_>
 static void launch_comb(const S2F6CombineParams &p, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((s2f6_combine_kernel<R_, W_, B_>), grid, dim3(kCodecThreads), 0, s,
-                       p.codes, p.scales, p.C, p.src, p.w, p.T, p.K, p.signs, p.out, p.ldo);
+                       p.codes, p.scales, p.C, p.src, p.w, p.T, p.K, p.src_rows, p.signs, p.out,
+                       p.ldo);
 }
 
 hipError_t launch_s2f6_combine(const S2F6CombineParams &p, bool rht, bool bf16_out,

@@ -251,7 +251,7 @@ int s2f6_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int
  * and multiply, then the sign flips).  out is tokens x in->cols with row
  * stride ldo elements of out_dtype (BBS_OUT_F32, or BBS_OUT_BF16 rounded to
  * nearest even), 16-byte aligned with ldo * size % 16 == 0.  src_index
- * entries must be < in->rows (not checked on the device).
+ * entries outside [0, in->rows) are skipped like negative ones.
  * Errors: BBS_EINVAL. */
 int s2f6_combine(const bbs_s2f6 *in, const int32_t *src_index, const float *weights,
                  int64_t tokens, int32_t k, int32_t rht, uint32_t signs, void *out,

@@ -109,6 +109,23 @@ def test_combine(bbs, rht, weighted, bf16):
         assert len(bad) == 0, f"{len(bad)} values differ, first {got.reshape(-1)[bad[0]]} vs {ref.reshape(-1)[bad[0]]}"
 
 
+def test_combine_out_of_range_rows_skipped(bbs):
+    """Source indices at or past the number of encoded rows are skipped like
+    negative ones (a dropped slot): the result equals the oracle's with those
+    slots set to -1."""
+    announce("S2F6 combine with out-of-range source rows")
+    rng = np.random.default_rng(32)
+    x = synth.normal_with_outliers(64, 256, 57, frac=0.0035, factor=10.0)
+    o = O.s2f6_quantize(x, rht=True, signs=SIGNS)
+    src = rng.integers(0, 64, (24, 4)).astype(np.int32)
+    src[1, 0], src[5, 3], src[9, :] = 64, 1 << 30, 70
+    w = rng.uniform(0.05, 1.0, (24, 4)).astype(np.float32)
+    clean = np.where(src >= 64, -1, src).astype(np.int32)
+    ref = O.s2f6_combine(o, clean, w, rht=True, signs=SIGNS)
+    got = _combine(bbs, _upload_s2f6(bbs, o), src, w, True, False)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
 def test_encode_then_combine_round_trip(bbs):
     """Device encode then device combine of single copies: within the wire
     format's error of the input."""
