@@ -23,6 +23,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> two BF16 (nearest even, as f32_to_bf16 for finite
+// values; one v_cvt_pk_bf16_f32), low half first.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t h = __builtin_convertvector(f32x2_v{a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
 // Unbiased binade exponent floor(log2 a) read from the FP32 bits (a >= 0);
 // zero and FP32 subnormals give -127, below every clamp used here.
 __device__ __forceinline__ int binade(float a) {

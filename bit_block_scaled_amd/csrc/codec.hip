@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kCodecThreads) void s2f6_combine_kernel(
     if (BF16_OUT) {
         uint32_t pk[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pk[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
+        for (int i = 0; i < 16; ++i) pk[i] = pk_bf16(acc[2 * i], acc[2 * i + 1]);
         uint4 *o = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + t * ldo + cb * 32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]);

@@ -40,15 +40,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_v __attribute__((ext_vector_type(2)));
-
-// Two FP32 values -> two BF16 (nearest even; one v_cvt_pk_bf16_f32), low first.
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-    const bf16x2_t h = __builtin_convertvector(f32x2_v{a, b}, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, h);
-}
-
 namespace mx {
 
 constexpr int BM = 256, BN = 256, BK = 128, NT = 256;

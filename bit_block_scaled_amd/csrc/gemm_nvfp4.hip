@@ -367,8 +367,7 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                         const float y3 = acc[i][j][4 * g + 3] * out_scale;
                         if constexpr (BF16_OUT)
                             *reinterpret_cast<uint2 *>(row + c * 2) =
-                                make_uint2(f32_to_bf16(y0) | (f32_to_bf16(y1) << 16),
-                                           f32_to_bf16(y2) | (f32_to_bf16(y3) << 16));
+                                make_uint2(pk_bf16(y0, y1), pk_bf16(y2, y3));
                         else
                             *reinterpret_cast<float4 *>(row + c * 4) = make_float4(y0, y1, y2, y3);
                     }
