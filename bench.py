@@ -174,6 +174,7 @@ def moe_bench(torch, bbs, dev, reps):
     hq = N4.empty(rows, F_, device=dev)
     y = torch.empty((rows, H_), dtype=torch.int16, device=dev)
     yq = bbs.S2F6Tensor.empty(rows, H_, device=dev)
+    yq2 = bbs.S2F6Tensor.empty(rows, H_, device=dev)
     hq2 = N4.empty(rows, F_, device=dev)
     amax_h = torch.zeros(1, dtype=torch.float32, device=dev)
     s_h = torch.ones(1, dtype=torch.float32, device=dev)
@@ -194,6 +195,10 @@ def moe_bench(torch, bbs, dev, reps):
         # combine wire format: RHT-32 + S2F6 encode of the down output, then
         # the receiver's weighted sum over each token's K rows + inverse RHT
         "combine_encode": lambda: bbs.s2f6_quantize(y, yq, rht=True, signs=signs),
+        # the down projection with that encode in its epilogue, in place of
+        # moe_down + combine_encode (the BF16 output never goes to memory)
+        "moe_down_s2f6": lambda: bbs.grouped_nvfp4_gemm_s2f6(hq, None, off, E_, rows, w_dn, H_, yq2,
+                                                             rht=True, signs=signs),
         "combine_decode": lambda: bbs.s2f6_combine(yq, src, comb, gate, rht=True, signs=signs),
     }
     codec_bytes = {"combine_encode": rows * H_ * 2 + rows * H_ + rows * H_ // 32,

@@ -79,12 +79,17 @@ def _load():
     lib.grouped_nvfp4_gemm_quant.argtypes = [C.POINTER(Fp4Desc), vp, vp, i32, i64,
                                              C.POINTER(Fp4Desc), i64, vp, i32, C.POINTER(Fp4Desc),
                                              vp, vp, vp]
+    lib.nvfp4_gemm_s2f6.argtypes = [C.POINTER(Fp4Desc), C.POINTER(Fp4Desc), i32, C.c_uint32,
+                                    C.POINTER(S2F6Desc), vp]
+    lib.grouped_nvfp4_gemm_s2f6.argtypes = [C.POINTER(Fp4Desc), vp, vp, i32, i64,
+                                            C.POINTER(Fp4Desc), i64, i32, C.c_uint32,
+                                            C.POINTER(S2F6Desc), vp]
     lib.s2f6_quantize.argtypes = [vp, i64, i64, i64, i32, C.c_uint32, C.POINTER(S2F6Desc), vp]
     lib.s2f6_combine.argtypes = [C.POINTER(S2F6Desc), vp, vp, i64, i32, i32, C.c_uint32, vp, i32,
                                  i64, vp]
     for f in ("nvfp4_quantize", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm",
               "s2f6_quantize", "s2f6_combine", "mxfp4_quantize", "nvfp4_gemm_quant",
-              "grouped_nvfp4_gemm_quant"):
+              "grouped_nvfp4_gemm_quant", "nvfp4_gemm_s2f6", "grouped_nvfp4_gemm_s2f6"):
         getattr(lib, f).restype = C.c_int
     lib.bbs_strerror.argtypes = [C.c_int]
     lib.bbs_strerror.restype = C.c_char_p
@@ -283,3 +288,19 @@ def grouped_nvfp4_gemm_quant(A, row_index, group_offsets, G, max_rows, B, N, s_e
     _check(lib.grouped_nvfp4_gemm_quant(C.byref(ad), _ptr(row_index), _ptr(group_offsets), G,
                                         max_rows, C.byref(bd), N, _ptr(s_enc), int(gelu),
                                         C.byref(yd), _ptr(amax), _ptr(ws), _stream(stream)))
+
+
+def nvfp4_gemm_s2f6(A, B, Y, rht=True, signs=0, stream=None):
+    """Y (S2F6Tensor) = combine wire format encode of the BF16 product A * B^T."""
+    ad, bd, yd = A.desc(), B.desc(), Y.desc()
+    _check(lib.nvfp4_gemm_s2f6(C.byref(ad), C.byref(bd), int(rht), signs, C.byref(yd),
+                               _stream(stream)))
+
+
+def grouped_nvfp4_gemm_s2f6(A, row_index, group_offsets, G, max_rows, B, N, Y, rht=True, signs=0,
+                            stream=None):
+    """The grouped GEMM with the combine wire format encode of its BF16 output."""
+    ad, bd, yd = A.desc(), B.desc(), Y.desc()
+    _check(lib.grouped_nvfp4_gemm_s2f6(C.byref(ad), _ptr(row_index), _ptr(group_offsets), G,
+                                       max_rows, C.byref(bd), N, int(rht), signs, C.byref(yd),
+                                       _stream(stream)))

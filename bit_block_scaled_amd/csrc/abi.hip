@@ -165,6 +165,84 @@ int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
                       "quantizing grouped gemm launch");
 }
 
+namespace {
+
+// Shared checks of the GEMMs with the combine encode in the epilogue: the
+// large-tile conditions and the S2F6 output (rows x N, N % 32 == 0).
+int check_s2f6_out(const bbs::GemmParams &p, const bbs_s2f6 *Y, int64_t rows, int32_t rht) {
+    int st;
+    if ((st = check_s2f6(Y, "Y"))) return st;
+    if (Y->rows != rows || Y->cols != p.N) return fail(BBS_EINVAL, "Y must be rows x N");
+    if (rht != 0 && rht != 1) return fail(BBS_EINVAL, "rht must be 0 or 1");
+    if (p.K % 128 || !aligned(p.a.codes, 16) || !aligned(p.b.codes, 16) || !aligned(p.a.scales, 8) ||
+        !aligned(p.b.scales, 8))
+        return fail(BBS_ENOTSUP, "encoding GEMM needs K %% 128 == 0 and aligned operands");
+    return BBS_OK;
+}
+
+bbs::QuantOut s2f6_out(const bbs_s2f6 *Y, int32_t rht, uint32_t signs) {
+    bbs::QuantOut q{};
+    q.codes = reinterpret_cast<uint8_t *>(Y->codes);
+    q.scales = Y->scales;
+    q.signs = signs;
+    q.rht = rht;
+    return q;
+}
+
+}  // namespace
+
+int nvfp4_gemm_s2f6(const bbs_fp4 *A, const bbs_fp4 *B, int32_t rht, uint32_t signs,
+                    const bbs_s2f6 *Y, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_fp4(A, "A", true))) return st;
+    if ((st = check_fp4(B, "B", true))) return st;
+    if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+    if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
+    bbs::GemmParams p{};
+    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
+    p.b = {B->codes, B->scales, B->s_dec, B->rows, B->tile2d, 0};
+    p.M = A->rows;
+    p.N = B->rows;
+    p.K = A->cols;
+    if ((st = check_s2f6_out(p, Y, p.M, rht))) return st;
+    p.q = s2f6_out(Y, rht, signs);
+    return hip_status(bbs::launch_nvfp4_gemm_s2f6(p, reinterpret_cast<hipStream_t>(stream)),
+                      "encoding gemm launch");
+}
+
+int grouped_nvfp4_gemm_s2f6(const bbs_fp4 *A, const int32_t *row_index,
+                            const int64_t *group_offsets, int32_t G, int64_t max_rows,
+                            const bbs_fp4 *B, int64_t N, int32_t rht, uint32_t signs,
+                            const bbs_s2f6 *Y, void *stream) {
+    g_err[0] = 0;
+    int st;
+    if ((st = check_fp4(A, "A", true))) return st;
+    if ((st = check_fp4(B, "B", true))) return st;
+    if (!group_offsets) return fail(BBS_EINVAL, "null group_offsets");
+    if (G <= 0 || G > 1024) return fail(BBS_EINVAL, "G must be in [1, 1024]");
+    if (N <= 0 || N % 16 || B->rows != (int64_t)G * N)
+        return fail(BBS_EINVAL, "B.rows must equal G * N with N %% 16 == 0");
+    if (A->cols != B->cols) return fail(BBS_EINVAL, "A.cols != B.cols");
+    if (max_rows <= 0) return fail(BBS_EINVAL, "max_rows must be positive");
+    if (B->sdec_per_row) return fail(BBS_ENOTSUP, "B with a per-row decode scale");
+    bbs::GemmParams p{};
+    p.a = {A->codes, A->scales, A->s_dec, A->rows, A->tile2d, A->sdec_per_row};
+    p.b = {B->codes, B->scales, B->s_dec, N, B->tile2d, 0};
+    p.M = max_rows;
+    p.N = N;
+    p.K = A->cols;
+    p.row_index = row_index;
+    p.group_offsets = group_offsets;
+    p.G = G;
+    p.max_rows = max_rows;
+    p.a_src_rows = A->rows;
+    if ((st = check_s2f6_out(p, Y, max_rows, rht))) return st;
+    p.q = s2f6_out(Y, rht, signs);
+    return hip_status(bbs::launch_grouped_nvfp4_gemm_s2f6(p, reinterpret_cast<hipStream_t>(stream)),
+                      "encoding grouped gemm launch");
+}
+
 int mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
                    const bbs_mx4 *out, int32_t round, bbs_rng rng, void *stream) {
     g_err[0] = 0;

@@ -70,6 +70,8 @@ struct QuantOut {
     const float *s_enc;      // one FP32 encode scale (device)
     unsigned *amax;          // max |y| of the quantized values as FP32 bits, or nullptr
     const float *gelu_tab;   // the GELU table (GELU modes)
+    uint32_t signs;          // combine wire format (S2F6 mode): RHT sign flips
+    int rht;                 //   and whether to rotate
 };
 
 struct GemmParams {
@@ -143,6 +145,10 @@ hipError_t launch_grouped_nvfp4_gemm(const GemmParams &p, bool bf16_out, hipStre
 // table is written to p.q.gelu_tab first.
 hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s);
 hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s);
+// The same GEMMs with the combine wire format encode (32-point RHT + S2F6)
+// of the BF16 output in the epilogue; q.codes / q.scales receive it.
+hipError_t launch_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s);
+hipError_t launch_grouped_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s);
 hipError_t launch_mxfp8_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s);
 // MXFP4 x MXFP4 (codes rows x K/2): K % 256 == 0, 16-byte aligned codes,
 // 4-byte aligned scales, N % 4 == 0, 16-byte aligned C with ldc % 4 == 0.

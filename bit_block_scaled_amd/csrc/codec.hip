@@ -15,51 +15,6 @@
 namespace bbs {
 
 constexpr int kCodecThreads = 256;
-constexpr float kInvSqrt32 = 0.17677669529663688f;   // 1/sqrt(32), rounded to FP32
-
-// Five sum / difference stages (pair distance 1, 2, 4, 8, 16) and the
-// multiply by 1/sqrt(32); every step one FP32 operation.
-__device__ __forceinline__ void hadamard32(float y[32]) {
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if ((i & h) == 0) {
-                const float p = y[i], q = y[i + h];
-                y[i] = p + q;
-                y[i + h] = p - q;
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) y[i] = y[i] * kInvSqrt32;
-}
-
-__device__ __forceinline__ void flip_signs32(float y[32], uint32_t signs) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-        y[i] = __uint_as_float(__float_as_uint(y[i]) ^ (((signs >> i) & 1u) << 31));
-}
-
-// The smallest k with amax <= (127/64) 2^k, clamped to [-127, 127]: with
-// amax = m 2^E, m in [0.5, 1), 127/64 = 0.9921875 * 2: k = E - 1 if
-// m <= 0.9921875, else E.
-__device__ __forceinline__ int s2f6_k(float amax) {
-    if (amax == 0.0f) return -127;
-    int E;
-    const float m = frexpf(amax, &E);
-    const int k = (m <= 0.9921875f) ? E - 1 : E;
-    return k < -127 ? -127 : (k > 127 ? 127 : k);
-}
-
-// S2F6 code byte of y * 2^(6-k): nearest integer, ties to even, within
-// [-128, 127].  Adding 1.5 * 2^23 rounds to an integer (nearest even) and
-// leaves it, two's complement, in the low bits of the sum.
-__device__ __forceinline__ uint32_t s2f6_byte(float y, int k) {
-    const float t = fminf(fmaxf(ldexpf(y, 6 - k), -128.0f), 127.0f);
-    return __float_as_uint(t + 12582912.0f) & 0xFFu;
-}
-
 template <bool RHT>
 __global__ __launch_bounds__(kCodecThreads) void s2f6_encode_kernel(const uint16_t *__restrict__ x,
                                                                     int64_t R, int64_t C, int64_t ld,

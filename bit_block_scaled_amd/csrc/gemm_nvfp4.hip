@@ -314,7 +314,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (amax_b / 6) * s_enc (never below code 1), E2M1 codes of x * s_enc_b to
 // nearest even.  The result is bit for bit the BF16 GEMM followed by the
 // quantizer with that scale.  The largest |value| is folded into q.amax.
-constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_QG = 3;
+//
+// OUT_S2F6 encodes the staged BF16 rows in the combine wire format instead
+// (4bit.vizuara.ai, section 11; End-to-End 4-Bit Training, "quantized
+// communication"): each lane takes 32 consecutive values of a row, rotates
+// them by the 32-point RHT (q.rht) and stores the S2F6 codes and E8M0 scale,
+// so the BF16 output of an expert never goes to memory.  Bit for bit the
+// BF16 GEMM followed by the combine encode.
+constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_QG = 3, OUT_S2F6 = 4;
 
 // Order a wave's LDS writes and later reads (or reads and later writes) of
 // the same staging rows: wait for its LDS operations and fence the compiler.
@@ -325,7 +332,9 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                                          int64_t m_end, int64_t n0, int64_t n_end,
                                          ScaleFn scale_of, void *C, int64_t ldc, int wm, int wn,
                                          int lane, const QuantOut &qo) {
-    constexpr bool QUANT = OUT >= OUT_Q;
+    constexpr bool NVQ = OUT == OUT_Q || OUT == OUT_QG;   // NVFP4 encode
+    constexpr bool S2 = OUT == OUT_S2F6;                   // combine wire format
+    constexpr bool QUANT = NVQ || S2;
     constexpr bool BF16_OUT = OUT == OUT_BF16 || QUANT;    // BF16 staging
     constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
     constexpr int RS = 128 * ES + 16;                 // staging row stride
@@ -339,7 +348,7 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     // GELU table (OUT_QG): in the idle ring past the staging rows (4 waves x
     // 32 rows x 272 bytes)
     float *tab = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&sm) + 65536);
-    if (QUANT) {
+    if (NVQ) {
         s_enc = qo.s_enc[0];
         s_dec = 1.0f / s_enc;
         if (OUT == OUT_QG) {
@@ -376,7 +385,7 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
             // the same wave: LDS executes a wave's operations in order, and
             // the barrier keeps the compiler from moving reads above writes
             lds_order();
-            if (!QUANT) {
+            if constexpr (!QUANT) {
 #pragma unroll
                 for (int q = 0; q < PR / RPI; ++q) {
                     const int r = q * RPI + lane / LPR;
@@ -386,6 +395,45 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
                     const int64_t n = nw + cb / ES;
                     if (m < m_end && n < n_end)
                         *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(C) + (m * ldc + n) * ES) = val;
+                }
+            } else if constexpr (S2) {
+                // 32 rows x 4 chunks of 32 BF16 values: two chunks per lane
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int r = q * 16 + lane / 4, c = lane % 4;
+                    const uint4 *src = reinterpret_cast<const uint4 *>(buf + r * RS + c * 64);
+                    float y[32];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint4 w = src[v];
+                        const uint32_t hw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            y[8 * v + 2 * e] = __uint_as_float(hw[e] << 16);
+                            y[8 * v + 2 * e + 1] = __uint_as_float(hw[e] & 0xFFFF0000u);
+                        }
+                    }
+                    if (qo.rht) {
+                        flip_signs32(y, qo.signs);
+                        hadamard32(y);
+                    }
+                    float a = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 32; ++v) a = fmaxf(a, fabsf(y[v]));
+                    const int k = s2f6_k(a);
+                    uint32_t wd[8];
+#pragma unroll
+                    for (int v = 0; v < 8; ++v)
+                        wd[v] = pack_bytes4(s2f6_byte(y[4 * v], k), s2f6_byte(y[4 * v + 1], k),
+                                            s2f6_byte(y[4 * v + 2], k), s2f6_byte(y[4 * v + 3], k));
+                    const int64_t m = mw + i * 32 + piece * PR + r;
+                    const int64_t n = nw + c * 32;
+                    if (m < m_end && n < n_end) {
+                        uint4 *dst = reinterpret_cast<uint4 *>(qo.codes + m * n_end + n);
+                        dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                        dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+                        qo.scales[m * (n_end / 32) + n / 32] = (uint8_t)(k + 127);
+                    }
                 }
             } else {
                 // 32 rows x 8 blocks of 16 BF16 values: four blocks per lane
@@ -423,7 +471,7 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
             lds_order();                          // before the next piece is staged
         }
     }
-    if (QUANT && qo.amax) {
+    if (NVQ && qo.amax) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
         if (lane == 0) atomicMax(qo.amax, __float_as_uint(amax));
@@ -537,7 +585,8 @@ __device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &
 template <int OUT>
 __device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_raw) {
     big::Smem &sm = *reinterpret_cast<big::Smem *>(smem_raw);
-    if (OUT >= big::OUT_Q && blockIdx.x == 0 && threadIdx.x == 0) p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
+    if ((OUT == big::OUT_Q || OUT == big::OUT_QG) && blockIdx.x == 0 && threadIdx.x == 0)
+        p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t tm = (p.M + big::BM - 1) / big::BM, tn = (p.N + big::BN - 1) / big::BN;
     const int64_t T = tm * tn;
     // XCD-contiguous tile ranges
@@ -580,13 +629,19 @@ __global__ __launch_bounds__(big::NT) void nvfp4_gemm_quant_kernel(GemmParams p)
     dense_body<GELU ? big::OUT_QG : big::OUT_Q>(p, smem_raw);
 }
 
+__global__ __launch_bounds__(big::NT) void nvfp4_gemm_s2f6_kernel(GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    dense_body<big::OUT_S2F6>(p, smem_raw);
+}
+
 constexpr int kMaxGroupsBig = 1024;
 
 template <int OUT>
 __device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_raw,
                                              int64_t *tile_start, int64_t *row_start) {
     big::Smem &sm = *reinterpret_cast<big::Smem *>(smem_raw);
-    if (OUT >= big::OUT_Q && blockIdx.x == 0 && threadIdx.x == 0) p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
+    if ((OUT == big::OUT_Q || OUT == big::OUT_QG) && blockIdx.x == 0 && threadIdx.x == 0)
+        p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t n_tiles_n = (p.N + big::BN - 1) / big::BN;
     if (threadIdx.x == 0) {
         int64_t acc = 0, prev = 0;
@@ -666,6 +721,13 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_quant_kernel(GemmP
     grouped_body<GELU ? big::OUT_QG : big::OUT_Q>(p, smem_raw, tile_start, row_start);
 }
 
+__global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_s2f6_kernel(GemmParams p) {
+    extern __shared__ __align__(16) uint8_t smem_raw[];
+    __shared__ int64_t tile_start[kMaxGroupsBig + 1];
+    __shared__ int64_t row_start[kMaxGroupsBig + 1];
+    grouped_body<big::OUT_S2F6>(p, smem_raw, tile_start, row_start);
+}
+
 __global__ void clear_amax_kernel(unsigned *amax) { *amax = 0u; }
 
 template <typename K_>
@@ -697,6 +759,18 @@ hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipSt
     }
     if (gelu) launch_with_smem(grouped_nvfp4_gemm_quant_kernel<true>, dim3(512), p, s);
     else launch_with_smem(grouped_nvfp4_gemm_quant_kernel<false>, dim3(512), p, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
+    const int64_t T = ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
+    launch_with_smem(nvfp4_gemm_s2f6_kernel, dim3((unsigned)T), p, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
+    if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
+    launch_with_smem(grouped_nvfp4_gemm_s2f6_kernel, dim3(512), p, s);
     return hipGetLastError();
 }
 

@@ -284,6 +284,24 @@ int grouped_nvfp4_gemm_quant(const bbs_fp4 *A, const int32_t *row_index,
                              const bbs_fp4 *B, int64_t N, const float *s_enc, int32_t gelu,
                              const bbs_fp4 *Y, float *amax, float *ws, void *stream);
 
+/* NVFP4 GEMM whose epilogue encodes the product in the combine wire format
+ * (4bit.vizuara.ai, section 11; End-to-End 4-Bit Training, "quantized
+ * communication"): with y = the BF16 value nvfp4_gemm with BBS_OUT_BF16
+ * would store, Y receives exactly what s2f6_quantize(y, rht, signs) writes,
+ * without the BF16 output going to memory.  Y is rows x N (N % 32 == 0,
+ * codes 16-byte aligned); K % 128 == 0 and 16-byte aligned codes, 8-byte
+ * aligned scales (else BBS_ENOTSUP).  Errors: BBS_EINVAL. */
+int nvfp4_gemm_s2f6(const bbs_fp4 *A, const bbs_fp4 *B, int32_t rht, uint32_t signs,
+                    const bbs_s2f6 *Y, void *stream);
+
+/* The grouped GEMM (as grouped_nvfp4_gemm) with the same encoding epilogue,
+ * e.g. the experts' down projection feeding the combine: Y is
+ * max_rows x N. */
+int grouped_nvfp4_gemm_s2f6(const bbs_fp4 *A, const int32_t *row_index,
+                            const int64_t *group_offsets, int32_t G, int64_t max_rows,
+                            const bbs_fp4 *B, int64_t N, int32_t rht, uint32_t signs,
+                            const bbs_s2f6 *Y, void *stream);
+
 /* Name of a status code. */
 const char *bbs_strerror(int status);
 

@@ -240,3 +240,30 @@ def test_gemm_quant_errors(lib):
     assert q(s, 0) == bbs.BBS_ENOTSUP
     assert L.grouped_nvfp4_gemm_quant(C.byref(A), None, None, 1, 32, C.byref(B), 48, s, 0,
                                       C.byref(Y), None, None, None) == bbs.BBS_EINVAL
+
+
+def test_gemm_s2f6_errors(lib):
+    """The GEMMs with the combine encode in the epilogue: Y must be an S2F6
+    rows x N tensor with N % 32 == 0, rht 0 or 1, K % 128 (else unsupported)."""
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    A = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 128, 0, 0)
+    B = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 64, 128, 1, 0)
+    Y = bbs.S2F6Desc(0x1000, 0x2000, 32, 64)
+    e = lambda r=1: L.nvfp4_gemm_s2f6(C.byref(A), C.byref(B), r, 0x1234, C.byref(Y), None)
+    assert e(2) == bbs.BBS_EINVAL
+    Y.rows = 16
+    assert e() == bbs.BBS_EINVAL
+    Y.rows, Y.cols = 32, 48
+    assert e() == bbs.BBS_EINVAL                          # cols not a multiple of 32
+    Y.cols = 64
+    Y.codes = 0x1008
+    assert e() == bbs.BBS_EINVAL                          # codes not 16-byte aligned
+    Y.codes = 0x1000
+    A.cols = B.cols = 64
+    assert e() == bbs.BBS_ENOTSUP
+    A.cols = B.cols = 128
+    assert L.grouped_nvfp4_gemm_s2f6(C.byref(A), None, None, 1, 32, C.byref(B), 64, 1, 0,
+                                     C.byref(Y), None) == bbs.BBS_EINVAL     # no offsets
+    assert L.grouped_nvfp4_gemm_s2f6(C.byref(A), None, C.c_void_p(0x4000), 2, 32, C.byref(B), 64,
+                                     1, 0, C.byref(Y), None) == bbs.BBS_EINVAL  # B.rows != G N
