@@ -9,7 +9,10 @@
 //
 // A workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of C; a wave owns
 // 128 x 128 = 8 x 8 MFMAs (256 FP32 accumulators per lane).  K advances in
-// slabs of 128 (one MFMA deep), double-buffered in LDS.  Slabs are copied
+// slabs of 128 (one MFMA deep) through two LDS stages (a slab is 66 KB, so
+// no third fits); each wave reads all of a slab's fragments into registers
+// at its start, which frees the stage after one barrier and lets the copies
+// of the slab two ahead go into it.  Slabs are copied
 // global -> LDS with global_load_lds_dwordx4 (no staging registers): each
 // instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so a wave
 // writes 8 rows of 128 bytes per instruction.  Within a row the 16-byte chunk
@@ -139,51 +142,68 @@ __device__ __forceinline__ i32x8 frag(const uint8_t *tile, int r, int g) {
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
-// The MFMAs of one FP8 slab.  The copies of the next slab (index sn) into
-// stage nx are issued along the way, four 1 KB copies after each of the
-// first four row blocks' MFMAs (and the scale copies after the fourth): the
-// wave never waits on one long burst of copy issues, and the copies still
-// have half a slab of MFMAs to land in.
-__device__ __forceinline__ void compute(const Stage<false> &st, f32x4 (&acc)[8][8], int wm, int wn,
-                                        int lane, Stage<false> &nx, const Plan &pl, int64_t sn) {
+// s_waitcnt vmcnt(n), other counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | (((N >> 4) & 3) << 14));
+}
+
+// Copies one wave issues per FP8 slab: 8 + 8 code copies, 2 scale copies.
+constexpr int kIssued8 = 18;
+
+// The MFMAs of one FP8 slab with all of the wave's fragments read into
+// registers at its start (8 A + 8 B, 128 VGPRs).  After row block 1 every
+// wave has its fragments, so after one barrier the stage is free and the
+// copies of slab sn (two slabs ahead) go into it during row blocks 2-5:
+// they get most of two slabs to land, where copying into the other stage of
+// a two-stage ring gives them one.
+__device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8], int wm,
+                                             int wn, int lane, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
     const int g = lane >> 4, rl = lane & 15;
     const int64_t kn = sn * BK;
-    i32x8 bf[8];
-    int bsc[8];
+    i32x8 af[8], bf[8];
+    int asc[8], bsc[8];
+    // A fragment 0 and the B fragments first: LDS returns in order, so the
+    // first row block's MFMAs wait only for the reads they use
+    {
+        const int r = wm * 128 + rl;
+        af[0] = frag(st.a, r, g);
+        asc[0] = (int)((st.as[0][r] >> (8 * g)) & 0xFFu);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int r = wn * 128 + j * 16 + rl;
         bf[j] = frag(st.b, r, g);
         bsc[j] = (int)((st.bs[0][r] >> (8 * g)) & 0xFFu);
     }
-    // A fragments are double-buffered by hand: row block i + 1 is read while
-    // the MFMAs of row block i run; the scheduling barrier keeps the compiler
-    // from hoisting every fragment read at once.
-    int r0 = wm * 128 + rl;
-    i32x8 an = frag(st.a, r0, g);
-    int ans = (int)((st.as[0][r0] >> (8 * g)) & 0xFFu);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        const int r = wm * 128 + i * 16 + rl;
+        af[i] = frag(st.a, r, g);
+        asc[i] = (int)((st.as[0][r] >> (8 * g)) & 0xFFu);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const i32x8 af = an;
-        const int asc = ans;
-        if (i + 1 < 8) {
-            const int r = wm * 128 + (i + 1) * 16 + rl;
-            an = frag(st.a, r, g);
-            ans = (int)((st.as[0][r] >> (8 * g)) & 0xFFu);
-        }
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0,
-                                                                         bsc[j], 0, asc);
-        if (i < 4) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0,
+                                                                         bsc[j], 0, asc[i]);
+        if (i == 1) {
+            // this wave's fragment reads are complete; once every wave's are,
+            // nobody reads the stage again in this slab
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+        if (i >= 2 && i < 6) {
 #pragma unroll
-            for (int q = 2 * i; q < 2 * i + 2; ++q) {
-                copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
-                copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
+            for (int q = 2 * (i - 2); q < 2 * (i - 2) + 2; ++q) {
+                copy_lds16(pl.a_base + kn + pl.a_off[q], st.a + (w * 8 + q) * 1024);
+                copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
             }
         }
-        if (i == 3) issue_scales(nx, pl, sn);
+        if (i == 5) issue_scales(st, pl, sn);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -274,18 +294,35 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
             for (int jj = 0; jj < 8; ++jj) acc[i][jj] = f32x4{0, 0, 0, 0};
     }
 
+    const int64_t nslab = p.K / (FP4 ? 2 * mx::BK : mx::BK);
+    if constexpr (!FP4) {
+        // Slab s lives in stage s % 2 and is copied while slab s - 2 is
+        // multiplied (compute_held); past the end the last slab is copied
+        // again into the freed stage, which keeps the loop free of branches.
+        mx::issue(sm.st[0], pl, 0);
+        mx::issue(sm.st[1], pl, nslab > 1 ? 1 : 0);
+        mx::wait_vmcnt<mx::kIssued8>();                // slab 0 has landed
+        __syncthreads();
+        for (int64_t s = 0; s < nslab; ++s) {
+            const int64_t sn = s + 2 < nslab ? s + 2 : nslab - 1;
+            mx::compute_held(sm.st[s & 1], acc, wm, wn, lane, pl, sn);
+            mx::wait_vmcnt<mx::kIssued8>();            // slab s + 1 has landed
+            __syncthreads();
+        }
+        mx::wait_vmcnt<0>();
+    }
+    if constexpr (FP4) {
     mx::issue(sm.st[0], pl, 0);
     __builtin_amdgcn_s_waitcnt(0x3F70);               // vmcnt(0)
     __syncthreads();
-    const int64_t nslab = p.K / (FP4 ? 2 * mx::BK : mx::BK);
     for (int64_t s = 0; s < nslab; ++s) {
         // slab s + 1 goes to the other stage (past the end the last slab is
         // copied again into the stage nobody reads any more: no branch)
         const int64_t sn = s + 1 < nslab ? s + 1 : s;
-        if constexpr (FP4) mx::compute4(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
-        else mx::compute(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
+        mx::compute4(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
         __builtin_amdgcn_s_waitcnt(0x3F70);           // the next slab's copies have landed
         __syncthreads();
+    }
     }
 
     auto store4 = [&](int64_t m, int64_t n, float y0, float y1, float y2, float y3) {
