@@ -213,14 +213,50 @@ __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8
 // measured): lane l feeds row l % 32 and block l / 32 of a 64-value step (its
 // 16 bytes of the row's chunk 2 * ks + l / 32), with that block's scale.  A
 // wave's 128 x 128 tile is 4 x 4 MFMA blocks of 32 x 32; a slab is 4 steps.
-// The next slab's copies ride along the first two steps, one A and one B copy
-// after each row block's MFMAs, the scale copies after the last of them.
-__device__ __forceinline__ void compute4(const Stage<true> &st, f32x16 (&acc)[4][4], int wm,
-                                         int wn, int lane, Stage<true> &nx, const Plan &pl,
-                                         int64_t sn) {
+
+// Copies one wave issues per FP4 slab: 8 + 8 code copies, 4 scale copies.
+constexpr int kIssued4 = 20;
+
+// The FP4 slab with every fragment held in registers, as compute_held: the
+// 16 code chunks (4 steps x (4 A + 4 B) x 16 bytes, 128 VGPRs) and the
+// slab's scale words are read at its start; after step 0's row block 1 the
+// stage is free and the copies of slab sn go into it.  An MFMA operand is
+// the chunk in the low half of eight registers (the instruction reads only
+// those 16 bytes for E2M1).
+__device__ __forceinline__ void compute4_held(Stage<true> &st, f32x16 (&acc)[4][4], int wm,
+                                              int wn, int lane, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
     const int h = lane >> 5, rl = lane & 31;
     const int64_t kn = sn * BK;
+    uint4 ad[4][4], bd[4][4];                      // [step][row block]
+    uint32_t as0[4], as1[4], bs0[4], bs1[4];       // the slab's 8 scale bytes per row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + rl;
+        as0[i] = st.as[0][r];
+        as1[i] = st.as[1][r];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + j * 32 + rl;
+        bs0[j] = st.bs[0][r];
+        bs1[j] = st.bs[1][r];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int c = 2 * ks + h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = wn * 128 + j * 32 + rl;
+            bd[ks][j] = *reinterpret_cast<const uint4 *>(st.b + r * BK + 16 * swz(r, c));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + i * 32 + rl;
+            ad[ks][i] = *reinterpret_cast<const uint4 *>(st.a + r * BK + 16 * swz(r, c));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int c = 2 * ks + h;                      // the lane's 16-byte chunk
@@ -229,32 +265,32 @@ __device__ __forceinline__ void compute4(const Stage<true> &st, f32x16 (&acc)[4]
         int bsc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = wn * 128 + j * 32 + rl;
-            bf[j] = frag4(st.b, r, c);
-            bsc[j] = (int)((st.bs[c >> 2][r] >> sh) & 0xFFu);
+            const uint4 x = bd[ks][j];
+            bf[j] = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+            bsc[j] = (int)((((c >> 2) ? bs1[j] : bs0[j]) >> sh) & 0xFFu);
         }
-        int r0 = wm * 128 + rl;
-        i32x8 an = frag4(st.a, r0, c);
-        int ans = (int)((st.as[c >> 2][r0] >> sh) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const i32x8 af = an;
-            const int asc = ans;
-            if (i + 1 < 4) {
-                const int r = wm * 128 + (i + 1) * 32 + rl;
-                an = frag4(st.a, r, c);
-                ans = (int)((st.as[c >> 2][r] >> sh) & 0xFFu);
-            }
+            const uint4 x = ad[ks][i];
+            const i32x8 af = i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+            const int asc = (int)((((c >> 2) ? as1[i] : as0[i]) >> sh) & 0xFFu);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[j], af, acc[i][j], 4, 4,
                                                                             0, bsc[j], 0, asc);
-            if (ks < 2) {
-                const int q = 4 * ks + i;
-                copy_lds16(pl.a_base + kn + pl.a_off[q], nx.a + (w * 8 + q) * 1024);
-                copy_lds16(pl.b_base + kn + pl.b_off[q], nx.b + (w * 8 + q) * 1024);
+            const int slot = ks * 4 + i;
+            if (slot == 1) {
+                // this wave's reads are complete; once every wave's are, the
+                // stage is free for the copies of slab sn
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __syncthreads();
             }
-            if (ks == 1 && i == 3) issue_scales(nx, pl, sn);
+            if (slot >= 2 && slot < 10) {
+                const int q = slot - 2;
+                copy_lds16(pl.a_base + kn + pl.a_off[q], st.a + (w * 8 + q) * 1024);
+                copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
+            }
+            if (slot == 9) issue_scales(st, pl, sn);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -312,17 +348,18 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
         mx::wait_vmcnt<0>();
     }
     if constexpr (FP4) {
-    mx::issue(sm.st[0], pl, 0);
-    __builtin_amdgcn_s_waitcnt(0x3F70);               // vmcnt(0)
-    __syncthreads();
-    for (int64_t s = 0; s < nslab; ++s) {
-        // slab s + 1 goes to the other stage (past the end the last slab is
-        // copied again into the stage nobody reads any more: no branch)
-        const int64_t sn = s + 1 < nslab ? s + 1 : s;
-        mx::compute4(sm.st[s & 1], acc, wm, wn, lane, sm.st[(s + 1) & 1], pl, sn);
-        __builtin_amdgcn_s_waitcnt(0x3F70);           // the next slab's copies have landed
+        // the same two-stage schedule for FP4 slabs
+        mx::issue(sm.st[0], pl, 0);
+        mx::issue(sm.st[1], pl, nslab > 1 ? 1 : 0);
+        mx::wait_vmcnt<mx::kIssued4>();                // slab 0 has landed
         __syncthreads();
-    }
+        for (int64_t s = 0; s < nslab; ++s) {
+            const int64_t sn = s + 2 < nslab ? s + 2 : nslab - 1;
+            mx::compute4_held(sm.st[s & 1], acc, wm, wn, lane, pl, sn);
+            mx::wait_vmcnt<mx::kIssued4>();            // slab s + 1 has landed
+            __syncthreads();
+        }
+        mx::wait_vmcnt<0>();
     }
 
     auto store4 = [&](int64_t m, int64_t n, float y0, float y1, float y2, float y3) {
@@ -386,8 +423,8 @@ __global__ __launch_bounds__(mx::NT) void mxfp4_gemm_big_kernel(Mx8GemmParams p)
 template <typename K_>
 static void launch_big(K_ kernel, size_t shm, const Mx8GemmParams &p, hipStream_t s) {
     const int64_t T = ((p.M + mx::BM - 1) / mx::BM) * ((p.N + mx::BN - 1) / mx::BN);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     hipLaunchKernelGGL(kernel, dim3((unsigned)T), dim3(mx::NT), shm, s, p);
 }
 
