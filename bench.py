@@ -37,6 +37,7 @@ COPY_BYTES = 1 << 29                            # counter calibration copy (512 
 # WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
 # (profiles/fprop_gemm_8192x14336x4096_counters.md), valid only for the kernel
 # sources they were taken on: reported as null once those sources change.
+ROTATE = 8                                     # buffer sets the timed runs cycle through
 FPROP_TRAFFIC = {"bytes": 647347494, "sources_sha256_16": "30207739a62e6379"}
 FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
                  "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
@@ -259,36 +260,52 @@ def main():
     def up(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
 
-    x, w, dy = up(fw["x"]), up(fw["w"]), up(bw["dy"])
+    x0, w0, dy0 = up(fw["x"]), up(fw["w"]), up(bw["dy"])
     del fw, bw
     T = bbs.NVFP4Tensor
-    xq, xc = T.empty(M, K, device=dev), T.empty(K, M, device=dev)
-    wq = T.empty(N, K, tile2d=True, device=dev)
-    gc = T.empty(N, M, device=dev)
-    gm = bbs.MXFP8Tensor.empty(M, N, device=dev)
-    wt = bbs.MXFP8Tensor.empty(K, N, device=dev)
-    y = torch.empty((M, N), dtype=torch.int16, device=dev)
-    dx = torch.empty((M, K), dtype=torch.int16, device=dev)
-    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
     ws = bbs.amax_workspace(dev)
 
-    ops = {
-        "quant_x": lambda: bbs.nvfp4_quantize(x, xq, xc, col_round=bbs.SR,
-                                              col_rng=(seeds["x_col"], 0), col_rht=True,
-                                              rht_signs=signs, amax_ws=ws),
-        "quant_w": lambda: bbs.nvfp4_quantize(w, wq, tile2d=True, amax_ws=ws),
-        "fprop": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, xq, wq, y, bbs.OUT_BF16),
-        "quant_dy": lambda: bbs.nvfp4_quantize(dy, None, gc, gm, col_round=bbs.SR,
-                                               col_rng=(seeds["dy_col"], 0), col_rht=True,
-                                               rht_signs=signs, mx8_round=bbs.SR,
-                                               mx8_rng=(seeds["dy_mx8"], 0), amax_ws=ws),
-        "requant_w": lambda: bbs.mxfp8_requantize_t(wq, wt, bbs.SR, (seeds["w_req"], 0)),
-        "dgrad": lambda: bbs.nvfp4_gemm(bbs.FMT_MXFP8, gm, wt, dx, bbs.OUT_BF16),
-        "wgrad": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, gc, xc, dw, bbs.OUT_F32),
-    }
+    def make_set(x, w, dy):
+        """One complete set of the step's buffers (inputs, copies, outputs)."""
+        xq, xc = T.empty(M, K, device=dev), T.empty(K, M, device=dev)
+        wq = T.empty(N, K, tile2d=True, device=dev)
+        gc = T.empty(N, M, device=dev)
+        gm = bbs.MXFP8Tensor.empty(M, N, device=dev)
+        wt = bbs.MXFP8Tensor.empty(K, N, device=dev)
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+        dx = torch.empty((M, K), dtype=torch.int16, device=dev)
+        dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+        bufs = {"xq": xq, "xc": xc, "wq": wq, "gc": gc, "gm": gm, "wt": wt, "y": y, "dx": dx,
+                "dw": dw}
+        return bufs, {
+            "quant_x": lambda: bbs.nvfp4_quantize(x, xq, xc, col_round=bbs.SR,
+                                                  col_rng=(seeds["x_col"], 0), col_rht=True,
+                                                  rht_signs=signs, amax_ws=ws),
+            "quant_w": lambda: bbs.nvfp4_quantize(w, wq, tile2d=True, amax_ws=ws),
+            "fprop": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, xq, wq, y, bbs.OUT_BF16),
+            "quant_dy": lambda: bbs.nvfp4_quantize(dy, None, gc, gm, col_round=bbs.SR,
+                                                   col_rng=(seeds["dy_col"], 0), col_rht=True,
+                                                   rht_signs=signs, mx8_round=bbs.SR,
+                                                   mx8_rng=(seeds["dy_mx8"], 0), amax_ws=ws),
+            "requant_w": lambda: bbs.mxfp8_requantize_t(wq, wt, bbs.SR, (seeds["w_req"], 0)),
+            "dgrad": lambda: bbs.nvfp4_gemm(bbs.FMT_MXFP8, gm, wt, dx, bbs.OUT_BF16),
+            "wgrad": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, gc, xc, dw, bbs.OUT_F32),
+        }
 
-    def step():
-        for f in ops.values():
+    # Timed runs rotate over ROTATE complete buffer sets (about 1.3 GB each,
+    # the same values in every set), so no kernel finds its inputs in the
+    # 256 MB MALL from the previous launch; --only (the counter runs) uses one.
+    n_sets = 1 if args.only else ROTATE
+    bufs, ops = make_set(x0, w0, dy0)
+    sets = [ops]
+    for _ in range(n_sets - 1):
+        sets.append(make_set(x0.clone(), w0.clone(), dy0.clone())[1])
+    # set 0's buffers serve the sections after the step
+    x, w, dy = x0, w0, dy0
+    xq, xc, wq, y = bufs["xq"], bufs["xc"], bufs["wq"], bufs["y"]
+
+    def step(i=0):
+        for f in sets[i % n_sets].values():
             f()
 
     if args.only:
@@ -307,18 +324,19 @@ def main():
         print(json.dumps({"only": args.only, "ms": s0.elapsed_time(s1) / args.steps}), flush=True)
         return
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, n_sets)):
+        step(i)
     torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} steps done", file=sys.stderr, flush=True)
+    print(f"[bench] warmup {args.warmup} steps done ({n_sets} buffer sets)", file=sys.stderr,
+          flush=True)
 
     # whole-step timing
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     end.record()
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
@@ -327,12 +345,13 @@ def main():
 
     # per-kernel timing: the same launches back to back on the same stream
     per = {}
-    for name, f in ops.items():
-        f()
+    for name in ops:
+        for st in sets:
+            st[name]()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record()
-        for _ in range(args.steps):
-            f()
+        for i in range(args.steps):
+            sets[i % n_sets][name]()
         s1.record()
         torch.cuda.synchronize()
         per[name] = s0.elapsed_time(s1) / args.steps
@@ -547,7 +566,7 @@ def main():
         "wall_s_timed": round(wall_s, 3),
     }
     if not args.no_moe:
-        del x, w, dy, xq, xc, wq, gc, gm, wt, y, dx, dw
+        del x, w, dy, x0, w0, dy0, xq, xc, wq, y, bufs, ops, sets
         torch.cuda.empty_cache()
         print("[bench] MoE grouped GEMMs (65536 tokens, 64 experts, top-8)", file=sys.stderr,
               flush=True)
