@@ -78,30 +78,45 @@ struct Plan {
     const uint8_t *sa[2], *sb[2]; // scale copies: 32 rows x 8 bytes per instruction
 };
 
+// The A rows one lane copies for a tile: 4 code rows, 2 scale rows (source
+// rows after the row map; a row map miss reads row 0).
+struct ARows {
+    int32_t c[4], s[2];
+};
+
 template <typename RowMap>
+__device__ __forceinline__ ARows a_rows(int64_t m0, int64_t m_end, RowMap a_row) {
+    ARows ar;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    auto arow = [&](int r) -> int32_t {
+        const int64_t m = min(m0 + r, m_end - 1);
+        const int64_t s = a_row(m);
+        return s < 0 ? 0 : (int32_t)s;
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ar.c[q] = arow((w * 4 + q) * 16 + (lane >> 2));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) ar.s[q] = arow((w * 2 + q) * 32 + (lane >> 1));
+    return ar;
+}
+
 __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, int64_t K,
-                                          int64_t m0, int64_t m_end, int64_t n0, int64_t n_end,
-                                          RowMap a_row) {
+                                          const ARows &ar, int64_t n0, int64_t n_end) {
     Plan pl;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int64_t kb = K / 2, ks = K / 16;
-    auto arow = [&](int r) -> int64_t {
-        const int64_t m = min(m0 + r, m_end - 1);
-        const int64_t s = a_row(m);
-        return s < 0 ? 0 : s;
-    };
     auto brow = [&](int r) -> int64_t { return min(n0 + r, n_end - 1); };
     const int pos = swz(lane >> 2, lane & 3);     // (row >> 2) & 3 == (lane >> 4) & 3 here
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int r = (w * 4 + q) * 16 + (lane >> 2);
-        pl.a[q] = A.codes + arow(r) * kb + 16 * pos;
+        pl.a[q] = A.codes + (int64_t)ar.c[q] * kb + 16 * pos;
         pl.b[q] = B.codes + brow(r) * kb + 16 * pos;
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int r = (w * 2 + q) * 32 + (lane >> 1);
-        const int64_t sa_row = A.tile2d ? arow(r) / 16 : arow(r);
+        const int64_t sa_row = A.tile2d ? ar.s[q] / 16 : ar.s[q];
         pl.sa[q] = A.scales + sa_row * ks + 4 * (lane & 1);
         if (B.tile2d) {
             // 16 tile rows: lanes 0..31 (the upper lanes repeat them)
@@ -297,7 +312,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // output row l % 32 and columns 8 * (v / 4) + 4 * (l / 32) + v % 4, i.e. each
 // group of four registers is four consecutive columns of one row.  Each wave
 // writes those groups (8 bytes of BF16, 16 of FP32) into its own staging rows
-// in the (now idle) slab ring, then stores whole rows, 16 bytes per lane, so
+// in the ring stage the tile's last slab used (the next tile's first two
+// slabs are meanwhile copied into the other two), then stores whole rows, 16
+// bytes per lane, so
 // every store instruction writes complete 256- or 512-byte row segments.
 // Rows m < m_end and columns n < n_end are written; N being a multiple of 16
 // keeps every 16-byte segment wholly in or out.
@@ -308,8 +325,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // output never makes a round trip through memory).  These stage FP32 rows as
 // OUT_BF16 does (the BF16 values the plain GEMM stores); on read-back each
 // lane takes one 1x16 block of a row (16 consecutive values), applies GELU
-// by the quantizers' table (OUT_QG; the table is copied from
-// q.gelu_tab into the idle ring), and encodes the block with the given
+// by the quantizers' table (OUT_QG; the workgroup copies it from
+// q.gelu_tab to LDS past the ring once), and encodes the block with the given
 // tensor scale exactly as the quantizer does: E4M3 block scale of
 // (amax_b / 6) * s_enc (never below code 1), E2M1 codes of x * s_enc_b to
 // nearest even.  The result is bit for bit the BF16 GEMM followed by the
@@ -328,10 +345,11 @@ constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_QG = 3, OUT_S2F6 = 4;
 __device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int OUT, typename ScaleFn>
-__device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], int64_t m0,
-                                         int64_t m_end, int64_t n0, int64_t n_end,
-                                         ScaleFn scale_of, void *C, int64_t ldc, int wm, int wn,
-                                         int lane, const QuantOut &qo) {
+__device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
+                                         const f32x16 (&acc)[4][4], int64_t m0, int64_t m_end,
+                                         int64_t n0, int64_t n_end, ScaleFn scale_of, void *C,
+                                         int64_t ldc, int wm, int wn, int lane,
+                                         const QuantOut &qo) {
     constexpr bool NVQ = OUT == OUT_Q || OUT == OUT_QG;   // NVFP4 encode
     constexpr bool S2 = OUT == OUT_S2F6;                   // combine wire format
     constexpr bool QUANT = NVQ || S2;
@@ -341,20 +359,13 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     constexpr int PR = BF16_OUT ? 32 : 16;            // rows per piece
     constexpr int LPR = 128 * ES / 16;                // lanes per row on read-back
     constexpr int RPI = 64 / LPR;                     // rows per read-back instruction
-    uint8_t *buf = reinterpret_cast<uint8_t *>(&sm) + (threadIdx.x >> 6) * (PR * RS);
+    uint8_t *buf = stage + (threadIdx.x >> 6) * (PR * RS);
     const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
     const int lr = lane & 31;                          // the lane's row in a 32-row block
     float s_enc = 1.0f, s_dec = 1.0f, amax = 0.0f;
-    // GELU table (OUT_QG): in the idle ring past the staging rows (4 waves x
-    // 32 rows x 272 bytes)
-    float *tab = reinterpret_cast<float *>(reinterpret_cast<uint8_t *>(&sm) + 65536);
     if (NVQ) {
         s_enc = qo.s_enc[0];
         s_dec = 1.0f / s_enc;
-        if (OUT == OUT_QG) {
-            gelu_table_load(tab, qo.gelu_tab);
-            __syncthreads();
-        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -478,142 +489,224 @@ __device__ __forceinline__ void epilogue(Smem &sm, const f32x16 (&acc)[4][4], in
     }
 }
 
-template <int OUT, bool BT, typename RowMap, typename ScaleFn>
-__device__ __forceinline__ void tile(Smem &sm, const Fp4View &A, const Fp4View &B, int64_t K,
-                                     int64_t m0, int64_t m_end, int64_t n0, int64_t n_end,
-                                     RowMap a_row, ScaleFn scale_of, void *C, int64_t ldc,
-                                     const QuantOut &qo) {
+// One output tile of a workgroup's sequence: rows [m0, m_end) of the
+// (row-mapped) A, columns [n0, n0 + BN) of group g's B.
+struct TileRef {
+    int64_t m0, m_end, n0;
+    int g;
+};
+
+// A persistent workgroup (one per CU) takes its tiles one after another, and
+// the slab ring runs on across them: while a tile's last two slabs are
+// multiplied, the next tile's first two slabs are copied into the stages
+// they free, and the epilogue stages its output in the third.  The slab loop
+// itself is the single-tile one; only its last two iterations (peeled)
+// switch the copies to the next tile.
+//   next_tile(TileRef &)   the workgroup's next tile, false when done
+//   b_view(g)              group g's B operand
+//   a_row(m)               source row of A for output row m (< 0: none)
+//   scale_of(m, g)         output scale of row m in group g's tile
+template <int OUT, bool BT, typename Next, typename BView, typename RowMap, typename ScaleFn>
+__device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams &p,
+                                          Next next_tile, BView b_view, RowMap a_row,
+                                          ScaleFn scale_of) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const Plan pl = make_plan(A, B, K, m0, m_end, n0, n_end, a_row);
+    const int64_t K = p.K, N = p.N;
     // global_load_lds instructions one wave issues per slab
     constexpr int kIssued = 4 + 4 + 2 + (BT ? 1 : 2);
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
-
     const int64_t nslab = K / BK;
-    // Three LDS stages: slab s lives in stage s % 3.  Slabs 0 and 1 are in
-    // flight before the loop; iteration s copies slab s + 2 during its first
-    // MFMA steps (past the end it repeats the last slab into a free stage,
-    // which keeps the loop body free of branches).
+
+    TileRef cur;
+    if (!next_tile(cur)) return;
+    if (OUT == OUT_QG) gelu_table_load(tab, p.q.gelu_tab);   // ordered by the first barrier
+    Plan pl = make_plan(p.a, b_view(cur.g), K, a_rows(cur.m0, cur.m_end, a_row), cur.n0, N);
+    int cs = 0;                                   // stage holding the current slab
     issue<BT>(sm.st[0], pl, 0);
-    if (nslab > 1) {
-        issue<BT>(sm.st[1], pl, BK);
-        wait_vmcnt<kIssued>();
-    } else {
+    if (nslab > 1) issue<BT>(sm.st[1], pl, BK);
+
+    for (;;) {
+        // the next tile (the last tile repeats itself: its copies land in
+        // stages nobody reads again)
+        TileRef nxt;
+        const bool more = next_tile(nxt);
+        if (!more) nxt = cur;
+        const ARows nar = a_rows(nxt.m0, nxt.m_end, a_row);
+        // this tile's first slabs have landed (the previous tile's stores too:
+        // vmcnt counts both)
         wait_vmcnt<0>();
-    }
-    __syncthreads();
-
-    uint2 sca[4], scb[4];
-    Chunk c0, c1;
-    Pairs p0, p1;
-    f16x8 af[4], bf[4], an[4], bn[4];
-    int cs = 0;                                   // stage holding slab s
-    load_scales<BT>(sca, scb, sm.st[0], wm, wn, lane);
-    load_chunk(c0, sm.st[0], 0, wm, wn, lane);
-    load_pairs(p0, sca, scb, 0, lane);
-    expand_step(af, bf, c0, p0, 0);
-
-    // Each iteration: the 8 MFMA steps of slab s, with the expansion of step
-    // k + 1 under the MFMAs of step k.  Stage cs is read only by the chunk and
-    // scale loads at its start, so the slab barrier can come after step 4:
-    // the last three steps then cover the next slab's LDS reads.
-    for (int64_t s = 0; s + 1 < nslab; ++s) {
-        const int ns = cs == 2 ? 0 : cs + 1;      // stage of slab s + 1
-        const int n2 = ns == 2 ? 0 : ns + 1;      // stage of slab s + 2
-        const int64_t kn = (s + 2 < nslab ? s + 2 : nslab - 1) * BK;
-        const Stage &cur = sm.st[cs];
-        Stage &dst = sm.st[n2];
-        auto none = [](int) {};
-        auto copy_a = [&](int q) {
-            copy_lds16(pl.a[q] + kn / 2, dst.a + (wave * 4 + q) * 1024);
-        };
-        auto copy_b = [&](int q) {
-            copy_lds16(pl.b[q] + kn / 2, dst.b + (wave * 4 + q) * 1024);
-        };
-        auto copy_s = [&](int q) {
-            if (q < 2) copy_lds4(pl.sa[q] + kn / 16, dst.as + (wave * 2 + q) * 256);
-            else if (!BT) copy_lds4(pl.sb[q - 2] + kn / 16, dst.bs + (wave * 2 + q - 2) * 256);
-            else if (q == 2) copy_lds4(pl.sb[0] + kn / 16, dst.bs);
-        };
-        load_chunk(c1, cur, 1, wm, wn, lane);
-        load_pairs(p1, sca, scb, 1, lane);
-        step_q(acc, af, bf, an, bn, c0, p0, 1, copy_a);
-        step_q(acc, an, bn, af, bf, c0, p0, 2, copy_b);
-        step_q(acc, af, bf, an, bn, c0, p0, 3, copy_s);
-        step_q(acc, an, bn, af, bf, c1, p1, 0, none);
-        step_q(acc, af, bf, an, bn, c1, p1, 1, none);
-        // slab s + 1 is complete once every wave has seen its own copies land
-        wait_vmcnt<kIssued>();
         __syncthreads();
-        load_scales<BT>(sca, scb, sm.st[ns], wm, wn, lane);
-        load_chunk(c0, sm.st[ns], 0, wm, wn, lane);
-        step_q(acc, an, bn, af, bf, c1, p1, 2, none);
-        step_q(acc, af, bf, an, bn, c1, p1, 3, none);
-        load_pairs(p0, sca, scb, 0, lane);
-        step_q(acc, an, bn, af, bf, c0, p0, 0, none);
-        cs = ns;
-    }
-    // the last slab
-    {
-        auto none = [](int) {};
-        load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
-        load_pairs(p1, sca, scb, 1, lane);
-        step_q(acc, af, bf, an, bn, c0, p0, 1, none);
-        step_q(acc, an, bn, af, bf, c0, p0, 2, none);
-        step_q(acc, af, bf, an, bn, c0, p0, 3, none);
-        step_q(acc, an, bn, af, bf, c1, p1, 0, none);
-        step_q(acc, af, bf, an, bn, c1, p1, 1, none);
-        step_q(acc, an, bn, af, bf, c1, p1, 2, none);
-        step_q(acc, af, bf, an, bn, c1, p1, 3, none);
-        mfma_step(acc, an, bn);
-    }
-    // no copy in flight and every wave done with the ring: it becomes staging
-    wait_vmcnt<0>();
-    __syncthreads();
 
-    epilogue<OUT>(sm, acc, m0, m_end, n0, n_end, scale_of, C, ldc, wm, wn, lane, qo);
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+
+        uint2 sca[4], scb[4];
+        Chunk c0, c1;
+        Pairs p0, p1;
+        f16x8 af[4], bf[4], an[4], bn[4];
+        load_scales<BT>(sca, scb, sm.st[cs], wm, wn, lane);
+        load_chunk(c0, sm.st[cs], 0, wm, wn, lane);
+        load_pairs(p0, sca, scb, 0, lane);
+        expand_step(af, bf, c0, p0, 0);
+
+        // The 8 MFMA steps of the current slab, with the expansion of step
+        // k + 1 under the MFMAs of step k, and the copies of the slab at
+        // byte offset kn (two ahead) into stage dst during the first steps.
+        // Stage cs is read only by the chunk and scale loads at its start,
+        // so the slab barrier can come after step 4: the last three steps
+        // then cover the next slab's LDS reads.
+        auto slab = [&](int64_t kn, Stage &dst) __attribute__((always_inline)) {
+            const int ns = cs == 2 ? 0 : cs + 1;      // stage of the next slab
+            auto none = [](int) {};
+            auto copy_a = [&](int q) {
+                copy_lds16(pl.a[q] + kn / 2, dst.a + (wave * 4 + q) * 1024);
+            };
+            auto copy_b = [&](int q) {
+                copy_lds16(pl.b[q] + kn / 2, dst.b + (wave * 4 + q) * 1024);
+            };
+            auto copy_s = [&](int q) {
+                if (q < 2) copy_lds4(pl.sa[q] + kn / 16, dst.as + (wave * 2 + q) * 256);
+                else if (!BT) copy_lds4(pl.sb[q - 2] + kn / 16, dst.bs + (wave * 2 + q - 2) * 256);
+                else if (q == 2) copy_lds4(pl.sb[0] + kn / 16, dst.bs);
+            };
+            load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
+            load_pairs(p1, sca, scb, 1, lane);
+            step_q(acc, af, bf, an, bn, c0, p0, 1, copy_a);
+            step_q(acc, an, bn, af, bf, c0, p0, 2, copy_b);
+            step_q(acc, af, bf, an, bn, c0, p0, 3, copy_s);
+            step_q(acc, an, bn, af, bf, c1, p1, 0, none);
+            step_q(acc, af, bf, an, bn, c1, p1, 1, none);
+            // the next slab is complete once every wave has seen its own copies land
+            wait_vmcnt<kIssued>();
+            __syncthreads();
+            load_scales<BT>(sca, scb, sm.st[ns], wm, wn, lane);
+            load_chunk(c0, sm.st[ns], 0, wm, wn, lane);
+            step_q(acc, an, bn, af, bf, c1, p1, 2, none);
+            step_q(acc, af, bf, an, bn, c1, p1, 3, none);
+            load_pairs(p0, sca, scb, 0, lane);
+            step_q(acc, an, bn, af, bf, c0, p0, 0, none);
+            cs = ns;
+        };
+        auto two_ahead = [&]() -> Stage & {
+            const int ns = cs == 2 ? 0 : cs + 1;
+            return sm.st[ns == 2 ? 0 : ns + 1];
+        };
+        for (int64_t s = 0; s + 2 < nslab; ++s) slab((s + 2) * BK, two_ahead());
+        if (nslab > 1) {
+            // the second-to-last slab: its look-ahead copy is the next tile's slab 0
+            pl = make_plan(p.a, b_view(nxt.g), K, nar, nxt.n0, N);
+            slab(0, two_ahead());
+        }
+        // The last slab, copying the next tile's slab 1 into the stage the
+        // slab before used (a single-slab tile: the next tile's slab 0 into
+        // the free stage).
+        {
+            const int c1s = cs == 2 ? 0 : cs + 1, c2s = c1s == 2 ? 0 : c1s + 1;
+            if (nslab == 1) pl = make_plan(p.a, b_view(nxt.g), K, nar, nxt.n0, N);
+            const int64_t kl = nslab > 1 ? BK : 0;
+            Stage &dst = sm.st[nslab > 1 ? c2s : c1s];
+            auto none = [](int) {};
+            auto copy_a = [&](int q) {
+                copy_lds16(pl.a[q] + kl / 2, dst.a + (wave * 4 + q) * 1024);
+            };
+            auto copy_b = [&](int q) {
+                copy_lds16(pl.b[q] + kl / 2, dst.b + (wave * 4 + q) * 1024);
+            };
+            auto copy_s = [&](int q) {
+                if (q < 2) copy_lds4(pl.sa[q] + kl / 16, dst.as + (wave * 2 + q) * 256);
+                else if (!BT) copy_lds4(pl.sb[q - 2] + kl / 16, dst.bs + (wave * 2 + q - 2) * 256);
+                else if (q == 2) copy_lds4(pl.sb[0] + kl / 16, dst.bs);
+            };
+            load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
+            load_pairs(p1, sca, scb, 1, lane);
+            step_q(acc, af, bf, an, bn, c0, p0, 1, copy_a);
+            step_q(acc, an, bn, af, bf, c0, p0, 2, copy_b);
+            step_q(acc, af, bf, an, bn, c0, p0, 3, copy_s);
+            step_q(acc, an, bn, af, bf, c1, p1, 0, none);
+            step_q(acc, af, bf, an, bn, c1, p1, 1, none);
+            step_q(acc, an, bn, af, bf, c1, p1, 2, none);
+            step_q(acc, af, bf, an, bn, c1, p1, 3, none);
+            mfma_step(acc, an, bn);
+        }
+        // every wave is done reading stage cs: it becomes the staging area
+        __syncthreads();
+        const int g = cur.g;
+        epilogue<OUT>(reinterpret_cast<uint8_t *>(&sm.st[cs]), tab, acc, cur.m0, cur.m_end,
+                      cur.n0, N, [&](int64_t m) { return scale_of(m, g); }, p.c, p.ldc, wm, wn,
+                      lane, p.q);
+        if (!more) break;
+        cur = nxt;
+        cs = cs == 2 ? 0 : cs + 1;                // the next tile's slab 0
+    }
+    // the last tile's repeated copies land before the workgroup ends
+    wait_vmcnt<0>();
 }
 
 }  // namespace big
 
+// A persistent workgroup's share of a tile sequence: workgroup b runs on XCD
+// b % 8, each XCD owns one contiguous eighth of the sequence (so the tiles in
+// flight on an XCD share operand panels in its L2), and the workgroups of an
+// XCD take its tiles in turn.
+struct TileWalk {
+    int64_t next, last, stride;
+    __device__ TileWalk(int64_t total) {
+        const int64_t x = blockIdx.x % 8, grid = gridDim.x;
+        const int64_t share = total / 8, extra = total % 8;
+        const int64_t first = x * share + (x < extra ? x : extra);
+        last = first + share + (x < extra ? 1 : 0);
+        stride = (grid - x + 7) / 8;              // workgroups on this XCD
+        next = first + blockIdx.x / 8;
+    }
+    __device__ bool take(int64_t &tile) {
+        if (next >= last) return false;
+        tile = next;
+        next += stride;
+        return true;
+    }
+};
+
 template <int OUT>
 __device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_raw) {
     big::Smem &sm = *reinterpret_cast<big::Smem *>(smem_raw);
+    float *tab = reinterpret_cast<float *>(smem_raw + sizeof(big::Smem));
     if ((OUT == big::OUT_Q || OUT == big::OUT_QG) && blockIdx.x == 0 && threadIdx.x == 0)
         p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t tm = (p.M + big::BM - 1) / big::BM, tn = (p.N + big::BN - 1) / big::BN;
-    const int64_t T = tm * tn;
-    // XCD-contiguous tile ranges
-    const int64_t bid = blockIdx.x, x = bid % 8, j = bid / 8;
-    const int64_t per = T / 8, rem = T % 8;
-    const int64_t tid = x * per + (x < rem ? x : rem) + j;
-    // grouped order: GROUP_M tiles down M, then along N
-    const int64_t gsize = big::GROUP_M * tn;
-    const int64_t g = tid / gsize, in = tid - g * gsize;
-    const int64_t gm = (tm - g * big::GROUP_M) < big::GROUP_M ? (tm - g * big::GROUP_M) : big::GROUP_M;
-    const int64_t mt = g * big::GROUP_M + in % gm, nt = in / gm;
+    TileWalk walk(tm * tn);
+    const int64_t M = p.M;
+    auto next_tile = [&](big::TileRef &r) -> bool {
+        int64_t tid;
+        if (!walk.take(tid)) return false;
+        // grouped order: GROUP_M tiles down M, then along N
+        const int64_t gsize = big::GROUP_M * tn;
+        const int64_t g = tid / gsize, in = tid - g * gsize;
+        const int64_t gm = (tm - g * big::GROUP_M) < big::GROUP_M ? (tm - g * big::GROUP_M) : big::GROUP_M;
+        r.m0 = (g * big::GROUP_M + in % gm) * big::BM;
+        r.m_end = M;
+        r.n0 = (in / gm) * big::BN;
+        r.g = 0;
+        return true;
+    };
+    const Fp4View B = p.b;
+    auto b_view = [B](int) { return B; };
     auto ident = [](int64_t r) { return r; };
     const float sb = p.b.s_dec[0];
     auto run = [&](auto scale_of) {
         if (p.b.tile2d)
-            big::tile<OUT, true>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
-                                 ident, scale_of, p.c, p.ldc, p.q);
+            big::run_tiles<OUT, true>(sm, tab, p, next_tile, b_view, ident, scale_of);
         else
-            big::tile<OUT, false>(sm, p.a, p.b, p.K, mt * big::BM, p.M, nt * big::BN, p.N,
-                                  ident, scale_of, p.c, p.ldc, p.q);
+            big::run_tiles<OUT, false>(sm, tab, p, next_tile, b_view, ident, scale_of);
     };
     if (p.a.sdec_rows) {
         const float *sa = p.a.s_dec;
-        run([sa, sb](int64_t m) { return sa[m] * sb; });
+        run([sa, sb](int64_t m, int) { return sa[m] * sb; });
     } else {
         const float out_scale = p.a.s_dec[0] * sb;
-        run([out_scale](int64_t) { return out_scale; });
+        run([out_scale](int64_t, int) { return out_scale; });
     }
 }
 
@@ -640,6 +733,7 @@ template <int OUT>
 __device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_raw,
                                              int64_t *tile_start, int64_t *row_start) {
     big::Smem &sm = *reinterpret_cast<big::Smem *>(smem_raw);
+    float *tab = reinterpret_cast<float *>(smem_raw + sizeof(big::Smem));
     if ((OUT == big::OUT_Q || OUT == big::OUT_QG) && blockIdx.x == 0 && threadIdx.x == 0)
         p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t n_tiles_n = (p.N + big::BN - 1) / big::BN;
@@ -656,52 +750,52 @@ __device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_
         }
     }
     __syncthreads();
-    const int64_t total = tile_start[p.G];
-    // Each XCD (workgroup b runs on XCD b % 8; the grid is a multiple of 8)
-    // works through one contiguous eighth of the tile sequence, so the tiles
-    // in flight on an XCD share an expert's weights and their token rows in
-    // that XCD's L2.
-    const int64_t xcd = blockIdx.x % 8, per_xcd = gridDim.x / 8;
-    const int64_t share = total / 8, extra = total % 8;
-    const int64_t first = xcd * share + (xcd < extra ? xcd : extra);
-    const int64_t last = first + share + (xcd < extra ? 1 : 0);
-    for (int64_t tile = first + blockIdx.x / 8; tile < last; tile += per_xcd) {
+    TileWalk walk(tile_start[p.G]);
+    const int G = p.G;
+    auto next_tile = [&](big::TileRef &r) -> bool {
+        int64_t tile;
+        if (!walk.take(tile)) return false;
         int g = 0;
-        while (g + 1 < p.G && tile_start[g + 1] <= tile) ++g;
+        while (g + 1 < G && tile_start[g + 1] <= tile) ++g;
         const int64_t local = tile - tile_start[g];
         const int64_t mt = local / n_tiles_n, nt = local - mt * n_tiles_n;
-        const int64_t re = row_start[g + 1];
-        const int64_t m0 = row_start[g] + mt * big::BM, n0 = nt * big::BN;
-        Fp4View B = p.b;
-        B.codes = p.b.codes + (int64_t)g * p.N * (p.K / 2);
-        B.scales = p.b.scales + (int64_t)g * (B.tile2d ? (p.N / 16) : p.N) * (p.K / 16);
-        const int32_t *ri = p.row_index;
-        const int64_t src_rows = p.a_src_rows;
-        auto gather = [ri, src_rows](int64_t r) -> int64_t {
-            const int64_t s = ri ? (int64_t)ri[r] : r;
-            return (s >= 0 && s < src_rows) ? s : -1;
-        };
-        const float sb = p.b.s_dec[g];
-        auto run = [&](auto scale_of) {
-            if (B.tile2d)
-                big::tile<OUT, true>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
-                                     p.ldc, p.q);
-            else
-                big::tile<OUT, false>(sm, p.a, B, p.K, m0, re, n0, p.N, gather, scale_of, p.c,
-                                      p.ldc, p.q);
-        };
-        if (p.a.sdec_rows) {
-            const float *sa = p.a.s_dec;
-            // the decode scale of the A row the output row was computed from
-            run([sa, sb, gather](int64_t m) {
-                const int64_t s = gather(m);
-                return sa[s < 0 ? 0 : s] * sb;
-            });
-        } else {
-            const float out_scale = p.a.s_dec[0] * sb;
-            run([out_scale](int64_t) { return out_scale; });
-        }
-        __syncthreads();
+        r.m0 = row_start[g] + mt * big::BM;
+        r.m_end = row_start[g + 1];
+        r.n0 = nt * big::BN;
+        r.g = g;
+        return true;
+    };
+    const Fp4View B0 = p.b;
+    const int64_t b_codes = p.N * (p.K / 2), b_scales = (B0.tile2d ? (p.N / 16) : p.N) * (p.K / 16);
+    auto b_view = [B0, b_codes, b_scales](int g) {
+        Fp4View B = B0;
+        B.codes = B0.codes + (int64_t)g * b_codes;
+        B.scales = B0.scales + (int64_t)g * b_scales;
+        return B;
+    };
+    const int32_t *ri = p.row_index;
+    const int64_t src_rows = p.a_src_rows;
+    auto gather = [ri, src_rows](int64_t r) -> int64_t {
+        const int64_t s = ri ? (int64_t)ri[r] : r;
+        return (s >= 0 && s < src_rows) ? s : -1;
+    };
+    const float *sdb = p.b.s_dec;
+    auto run = [&](auto scale_of) {
+        if (B0.tile2d)
+            big::run_tiles<OUT, true>(sm, tab, p, next_tile, b_view, gather, scale_of);
+        else
+            big::run_tiles<OUT, false>(sm, tab, p, next_tile, b_view, gather, scale_of);
+    };
+    if (p.a.sdec_rows) {
+        const float *sa = p.a.s_dec;
+        // the decode scale of the A row the output row was computed from
+        run([sa, sdb, gather](int64_t m, int g) {
+            const int64_t s = gather(m);
+            return sa[s < 0 ? 0 : s] * sdb[g];
+        });
+    } else {
+        const float sa0 = p.a.s_dec[0];
+        run([sa0, sdb](int64_t, int g) { return sa0 * sdb[g]; });
     }
 }
 
@@ -730,13 +824,37 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_s2f6_kernel(GemmPa
 
 __global__ void clear_amax_kernel(unsigned *amax) { *amax = 0u; }
 
-template <typename K_>
-static void launch_with_smem(K_ kernel, dim3 grid, const GemmParams &p, hipStream_t s) {
-    const size_t shm = sizeof(big::Smem);
-    hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(kernel, grid, dim3(big::NT), shm, s, p);
+// Persistent grid: one workgroup per CU (the LDS ring admits one), a
+// multiple of 8 so every XCD holds the same number; never more than the
+// tiles when those are known.
+static int64_t persistent_grid(int64_t tiles) {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+            n = 256;
+        cus[dev] = n;
+    }
+    const int64_t g = cus[dev] / 8 * 8;
+    return tiles > 0 && tiles < g ? tiles : g;
 }
+
+template <typename K_>
+static void launch_with_smem(K_ kernel, int64_t grid, size_t shm, const GemmParams &p,
+                             hipStream_t s) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(big::NT), shm, s, p);
+}
+
+static int64_t dense_tiles(const GemmParams &p) {
+    return ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
+}
+
+constexpr size_t kSmemBig = sizeof(big::Smem);
+constexpr size_t kSmemGelu = sizeof(big::Smem) + kGeluTabSize * sizeof(float);
 
 hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s) {
     if (p.q.amax) hipLaunchKernelGGL(clear_amax_kernel, dim3(1), dim3(1), 0, s, p.q.amax);
@@ -744,9 +862,9 @@ hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s
         const hipError_t e = launch_gelu_table(const_cast<float *>(p.q.gelu_tab), s);
         if (e != hipSuccess) return e;
     }
-    const int64_t T = ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
-    if (gelu) launch_with_smem(nvfp4_gemm_quant_kernel<true>, dim3((unsigned)T), p, s);
-    else launch_with_smem(nvfp4_gemm_quant_kernel<false>, dim3((unsigned)T), p, s);
+    const int64_t grid = persistent_grid(dense_tiles(p));
+    if (gelu) launch_with_smem(nvfp4_gemm_quant_kernel<true>, grid, kSmemGelu, p, s);
+    else launch_with_smem(nvfp4_gemm_quant_kernel<false>, grid, kSmemBig, p, s);
     return hipGetLastError();
 }
 
@@ -757,51 +875,35 @@ hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipSt
         const hipError_t e = launch_gelu_table(const_cast<float *>(p.q.gelu_tab), s);
         if (e != hipSuccess) return e;
     }
-    if (gelu) launch_with_smem(grouped_nvfp4_gemm_quant_kernel<true>, dim3(512), p, s);
-    else launch_with_smem(grouped_nvfp4_gemm_quant_kernel<false>, dim3(512), p, s);
+    const int64_t grid = persistent_grid(0);
+    if (gelu) launch_with_smem(grouped_nvfp4_gemm_quant_kernel<true>, grid, kSmemGelu, p, s);
+    else launch_with_smem(grouped_nvfp4_gemm_quant_kernel<false>, grid, kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
-    const int64_t T = ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
-    launch_with_smem(nvfp4_gemm_s2f6_kernel, dim3((unsigned)T), p, s);
+    launch_with_smem(nvfp4_gemm_s2f6_kernel, persistent_grid(dense_tiles(p)), kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
     if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
-    launch_with_smem(grouped_nvfp4_gemm_s2f6_kernel, dim3(512), p, s);
+    launch_with_smem(grouped_nvfp4_gemm_s2f6_kernel, persistent_grid(0), kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
-    const int64_t T = ((p.M + big::BM - 1) / big::BM) * ((p.N + big::BN - 1) / big::BN);
-    const size_t shm = sizeof(big::Smem);
-    if (bf16_out) {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(nvfp4_gemm_big_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipLaunchKernelGGL(nvfp4_gemm_big_kernel<true>, dim3((unsigned)T), dim3(big::NT), shm, s, p);
-    } else {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(nvfp4_gemm_big_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipLaunchKernelGGL(nvfp4_gemm_big_kernel<false>, dim3((unsigned)T), dim3(big::NT), shm, s, p);
-    }
+    const int64_t grid = persistent_grid(dense_tiles(p));
+    if (bf16_out) launch_with_smem(nvfp4_gemm_big_kernel<true>, grid, kSmemBig, p, s);
+    else launch_with_smem(nvfp4_gemm_big_kernel<false>, grid, kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
     if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
-    const size_t shm = sizeof(big::Smem);
-    const dim3 grid(512);
-    if (bf16_out) {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(grouped_nvfp4_gemm_big_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipLaunchKernelGGL(grouped_nvfp4_gemm_big_kernel<true>, grid, dim3(big::NT), shm, s, p);
-    } else {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(grouped_nvfp4_gemm_big_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        hipLaunchKernelGGL(grouped_nvfp4_gemm_big_kernel<false>, grid, dim3(big::NT), shm, s, p);
-    }
+    const int64_t grid = persistent_grid(0);
+    if (bf16_out) launch_with_smem(grouped_nvfp4_gemm_big_kernel<true>, grid, kSmemBig, p, s);
+    else launch_with_smem(grouped_nvfp4_gemm_big_kernel<false>, grid, kSmemBig, p, s);
     return hipGetLastError();
 }
 
