@@ -205,6 +205,58 @@ def test_grouped_small(bbs, sizes, gather, bf16):
     _check(y, ref, bf16, "grouped")
 
 
+def _unit(R, K, seed, tile2d):
+    rng = np.random.default_rng(seed)
+    shape = (R // 16, K // 16) if tile2d else (R, K // 16)
+    return O.NVFP4(rng.integers(0, 256, (R, K // 2), dtype=np.uint8),
+                   np.full(shape, 0x38, np.uint8), np.float32(1), R, K, tile2d)
+
+
+@pytest.mark.parametrize("K,bf16", [(128, False), (256, True), (384, False)])
+def test_persistent_handover_exact(bbs, K, bf16):
+    """More tiles than CUs (17 x 17) with one, two and three slabs per tile:
+    each workgroup takes several tiles and copies the next tile's first
+    slabs during the current tile's last ones.  Unit scales make every sum
+    exact, so sampled outputs must equal the oracle bit for bit (BF16 out:
+    its rounding of the exact sum)."""
+    M, N = 17 * 256, 16 * 256 + 64
+    announce(f"persistent GEMM hand-over M={M} N={N} K={K} bf16={bf16}")
+    a, b = _unit(M, K, K + 1, False), _unit(N, K, K + 2, True)
+    y = _run_gemm(bbs, bbs.FMT_NVFP4, upload_nvfp4(a, bbs), upload_nvfp4(b, bbs), M, N, bf16)
+    rng = np.random.default_rng(K)
+    rows = np.concatenate([rng.integers(0, M, 6000), np.arange(M), np.full(N, M - 1)])
+    cols = np.concatenate([rng.integers(0, N, 6000), np.arange(M) % N, np.arange(N)])
+    ref = O.gemm_f64_sampled(a.dequant_f64(), b.dequant_f64(), rows, cols)
+    if bf16:
+        ref = O.bf16_rne(ref)
+    assert np.array_equal(y[rows, cols], ref)
+
+
+def test_grouped_persistent_handover_exact(bbs):
+    """The grouped kernel with more tiles than CUs at K = 256 (two slabs per
+    tile): 64 experts of 300-ish rows, N = 1024, unit scales, exact."""
+    announce("grouped persistent hand-over, 64 experts, K=256, N=1024")
+    G, N, K = 64, 1024, 256
+    sizes = np.random.default_rng(5).integers(200, 420, G)
+    sizes[[3, 40]] = 0
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    rows = int(offsets[-1])
+    a = _unit((rows + 15) // 16 * 16, K, 11, False)         # A rows: a multiple of 16
+    ws = [_unit(N, K, 100 + g, True) for g in range(G)]
+    B = O.NVFP4(np.concatenate([w.codes for w in ws]), np.concatenate([w.scales for w in ws]),
+                np.float32(1), G * N, K, True)
+    c = torch.empty((rows, N), dtype=torch.float32, device=dev())
+    bbs.grouped_nvfp4_gemm(upload_nvfp4(a, bbs), None, to_dev(offsets), G, rows,
+                           upload_nvfp4(B, bbs, n_scales=np.ones(G, np.float32)), N, c, bbs.OUT_F32)
+    torch.cuda.synchronize()
+    y = host(c)
+    A64 = a.dequant_f64()
+    for g in [0, 1, 2, 39, 41, 63]:
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        ref = O.gemm_f64(A64[r0:r1], ws[g].dequant_f64())
+        assert np.array_equal(y[r0:r1].astype(np.float64), ref), f"expert {g}"
+
+
 def test_grouped_routed_medium(bbs):
     announce("grouped, Zipf top-8 routing, 2048 tokens, 64 experts, 512 -> 192")
     row_index, offsets = synth.moe_routing(2048, 64, 8, 77)
