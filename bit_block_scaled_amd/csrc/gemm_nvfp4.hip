@@ -359,7 +359,12 @@ __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
     constexpr int PR = BF16_OUT ? 32 : 16;            // rows per piece
     constexpr int LPR = 128 * ES / 16;                // lanes per row on read-back
     constexpr int RPI = 64 / LPR;                     // rows per read-back instruction
-    uint8_t *buf = stage + (threadIdx.x >> 6) * (PR * RS);
+    // plain output: pieces alternate between the stage and a second buffer
+    // past the ring (where the GELU modes keep their table), so a piece's
+    // read-back needs no wait before the next piece is staged
+    uint8_t *const buf0 = stage + (threadIdx.x >> 6) * (PR * RS);
+    uint8_t *const buf1 = reinterpret_cast<uint8_t *>(const_cast<float *>(tab)) +
+                          (threadIdx.x >> 6) * (PR * RS);
     const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
     const int lr = lane & 31;                          // the lane's row in a 32-row block
     float s_enc = 1.0f, s_dec = 1.0f, amax = 0.0f;
@@ -374,6 +379,7 @@ __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
         const float out_scale = scale_of(mr < m_end ? mr : m_end - 1);
 #pragma unroll
         for (int piece = 0; piece < 32 / PR; ++piece) {
+            uint8_t *const buf = (!QUANT && ((i * (32 / PR) + piece) & 1)) ? buf1 : buf0;
             if (lr / PR == piece) {
                 uint8_t *row = buf + (lr - piece * PR) * RS;
 #pragma unroll
@@ -479,7 +485,7 @@ __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
                     }
                 }
             }
-            lds_order();                          // before the next piece is staged
+            if constexpr (QUANT) lds_order();     // before the next piece is staged
         }
     }
     if (NVQ && qo.amax) {
@@ -854,6 +860,8 @@ static int64_t dense_tiles(const GemmParams &p) {
 }
 
 constexpr size_t kSmemBig = sizeof(big::Smem);
+// plain output: the second staging buffer (4 waves x 32 rows x 272 bytes)
+constexpr size_t kSmemPlain = sizeof(big::Smem) + 4 * 32 * 272;
 constexpr size_t kSmemGelu = sizeof(big::Smem) + kGeluTabSize * sizeof(float);
 
 hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s) {
@@ -894,16 +902,16 @@ hipError_t launch_grouped_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
 
 hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
     const int64_t grid = persistent_grid(dense_tiles(p));
-    if (bf16_out) launch_with_smem(nvfp4_gemm_big_kernel<true>, grid, kSmemBig, p, s);
-    else launch_with_smem(nvfp4_gemm_big_kernel<false>, grid, kSmemBig, p, s);
+    if (bf16_out) launch_with_smem(nvfp4_gemm_big_kernel<true>, grid, kSmemPlain, p, s);
+    else launch_with_smem(nvfp4_gemm_big_kernel<false>, grid, kSmemPlain, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
     if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
     const int64_t grid = persistent_grid(0);
-    if (bf16_out) launch_with_smem(grouped_nvfp4_gemm_big_kernel<true>, grid, kSmemBig, p, s);
-    else launch_with_smem(grouped_nvfp4_gemm_big_kernel<false>, grid, kSmemBig, p, s);
+    if (bf16_out) launch_with_smem(grouped_nvfp4_gemm_big_kernel<true>, grid, kSmemPlain, p, s);
+    else launch_with_smem(grouped_nvfp4_gemm_big_kernel<false>, grid, kSmemPlain, p, s);
     return hipGetLastError();
 }
 
