@@ -33,11 +33,11 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
 COPY_BYTES = 1 << 29                            # counter calibration copy (512 MiB)
 
+ROTATE = 8                                     # buffer sets the timed runs cycle through
 # HBM bytes per launch of the fprop GEMM, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
-# (profiles/fprop_gemm_8192x14336x4096_counters.md), valid only for the kernel
+# (profiles/hbm_traffic_step_moe_codec_counters.md), valid only for the kernel
 # sources they were taken on: reported as null once those sources change.
-ROTATE = 8                                     # buffer sets the timed runs cycle through
 FPROP_TRAFFIC = {"bytes": 630826517, "sources_sha256_16": "56e8331e16905a73"}
 FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
                  "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
