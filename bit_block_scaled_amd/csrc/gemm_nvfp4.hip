@@ -28,7 +28,9 @@
 //
 // Tile order is XCD-aware: workgroup i runs on XCD i % 8, so each XCD is given
 // a contiguous range of tile ids, and ids walk 8 M-tiles down before moving
-// along N, keeping operand panels shared inside one XCD's L2.
+// along N, keeping operand panels shared inside one XCD's L2.  The kernels
+// are persistent: one workgroup per CU takes its XCD's tiles in turn, and
+// the slab ring runs on from one tile into the next (run_tiles).
 #include "bbs_device.hpp"
 #include "bbs_kernels.hpp"
 
