@@ -212,13 +212,14 @@ def _unit(R, K, seed, tile2d):
                    np.full(shape, 0x38, np.uint8), np.float32(1), R, K, tile2d)
 
 
-@pytest.mark.parametrize("K,bf16", [(128, False), (256, True), (384, False)])
+@pytest.mark.parametrize("K,bf16", [(128, False), (256, True), (384, False), (512, False),
+                                    (512, True)])
 def test_persistent_handover_exact(bbs, K, bf16):
-    """More tiles than CUs (17 x 17) with one, two and three slabs per tile:
-    each workgroup takes several tiles and copies the next tile's first
-    slabs during the current tile's last ones.  Unit scales make every sum
-    exact, so sampled outputs must equal the oracle bit for bit (BF16 out:
-    its rounding of the exact sum)."""
+    """More tiles than CUs (17 x 17) with one to four slabs per tile: each
+    workgroup takes several tiles and copies the next tile's first slabs
+    during the current tile's last ones.  Unit scales make every sum exact,
+    so sampled outputs must equal the oracle bit for bit (BF16 out: its
+    rounding of the exact sum)."""
     M, N = 17 * 256, 16 * 256 + 64
     announce(f"persistent GEMM hand-over M={M} N={N} K={K} bf16={bf16}")
     a, b = _unit(M, K, K + 1, False), _unit(N, K, K + 2, True)
