@@ -397,6 +397,34 @@ def main():
         act[name] = e
     print(f"[bench] per-token + 4/6 activation path: {json.dumps(act)}", file=sys.stderr, flush=True)
 
+    # The activation quantize with both copies stochastic (4096 x 4096
+    # Student-t(3), row and column NVFP4 SR, no RHT), amax pass included,
+    # over ROTATE input buffers: 33.55 MB read + 18.87 MB written.
+    d2 = synth.activation_sr()
+    x2 = [up(d2["x"])]
+    for _ in range(ROTATE - 1):
+        x2.append(x2[0].clone())
+    R2 = d2["x"].shape[0]
+    r2, c2 = T.empty(R2, R2, device=dev), T.empty(R2, R2, device=dev)
+    q2 = lambda i: bbs.nvfp4_quantize(x2[i % ROTATE], r2, c2, row_round=bbs.SR,
+                                      row_rng=(d2["seed"], d2["row_stream"]), col_round=bbs.SR,
+                                      col_rng=(d2["seed"], d2["col_stream"]), amax_ws=ws)
+    for i in range(ROTATE):
+        q2(i)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(args.steps):
+        q2(i)
+    s1.record()
+    torch.cuda.synchronize()
+    t_ms = s0.elapsed_time(s1) / args.steps
+    b2 = 2 * R2 * R2 + 2 * nvfp4_bytes(R2, R2)
+    act_sr = {"ms": round(t_ms, 4), "GB/s": round(b2 / (t_ms * 1e-3) / 1e9, 1),
+              "hbm_frac": round(b2 / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bytes": b2}
+    del x2, r2, c2
+    print(f"[bench] activation SR row + col 4096x4096: {json.dumps(act_sr)}", file=sys.stderr,
+          flush=True)
+
     # Fused GELU + quantize of the MLP hidden tensor H [M x N] (between the
     # layer's two projections): the NVFP4 copy of GELU(H) alone, with its
     # MXFP8 SR copy for the backward pass, and as the per-token + 4/6
@@ -559,6 +587,7 @@ def main():
                      "peak_fp4": PEAK_FP4_TFLOPS,
                      "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
         "activation_per_token_4over6": act,
+        "activation_sr_row_col_4096x4096": act_sr,
         "gelu_quantize_mlp_hidden_8192x14336": gelu,
         "gemm_epilogue_quantize_8192x14336x4096": epi,
         "mxfp4_forward_8192x14336x4096": mx4,
