@@ -59,6 +59,24 @@ def test_exact_case(bbs, rht, M, N, K):
     _same(Y, O.s2f6_encode_f32(y, rht=rht, signs=SIGNS), "dense")
 
 
+def test_per_token_A_exact(bbs):
+    """A with a decode scale per row (the per-token activation copy): each
+    output row is scaled by its own row's s_dec before the BF16 rounding and
+    the encode.  Power-of-two row scales keep every product exact."""
+    announce("encoding GEMM, per-row A decode scales, exact products")
+    M, N, K = 272, 288, 512
+    a = _unit_scale_operand(M, K, 91, 1.0)
+    s_rows = np.float32(2.0) ** -(np.arange(M) % 5).astype(np.float32)
+    ar = O.NVFP4Rows(a.codes, a.scales, s_rows, M, K)
+    b = _unit_scale_operand(N, K, 92, 0.5, True)
+    y = O.bf16_rne(O.gemm_f64(ar.dequant_f64(), b.dequant_f64())).astype(np.float32)
+    A = bbs.NVFP4Tensor(to_dev(a.codes), to_dev(a.scales), to_dev(s_rows), M, K, False, True)
+    Y = bbs.S2F6Tensor.empty(M, N, device=dev())
+    bbs.nvfp4_gemm_s2f6(A, upload_nvfp4(b, bbs), Y, rht=True, signs=SIGNS)
+    torch.cuda.synchronize()
+    _same(Y, O.s2f6_encode_f32(y, rht=True, signs=SIGNS), "per-row A")
+
+
 def test_grouped_exact_case(bbs):
     """Row gather, empty and ragged groups, per-expert decode scales."""
     announce("encoding grouped GEMM, exact products")
