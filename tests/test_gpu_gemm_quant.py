@@ -69,6 +69,30 @@ def test_exact_case(bbs, gelu, M, N, K, tb):
     assert got_amax == amax
 
 
+@pytest.mark.parametrize("gelu", [False, True])
+def test_per_token_A_exact(bbs, gelu):
+    """A with a decode scale per row (the per-token activation copy): each
+    output row is scaled by its own row's s_dec before the BF16 rounding,
+    GELU and the encode.  Power-of-two row scales keep every product exact."""
+    announce(f"quantizing GEMM, per-row A decode scales, exact products, gelu={gelu}")
+    M, N, K = 272, 288, 512
+    a = _unit_scale_operand(M, K, 93, 1.0)
+    s_rows = np.float32(2.0) ** -(np.arange(M) % 5).astype(np.float32)
+    ar = O.NVFP4Rows(a.codes, a.scales, s_rows, M, K)
+    b = _unit_scale_operand(N, K, 94, 0.5, True)
+    y = O.bf16_rne(O.gemm_f64(ar.dequant_f64(), b.dequant_f64())).astype(np.float32)
+    if gelu:
+        y = O.gelu_f32(y)
+    amax = float(np.abs(y).max())
+    s_enc = O.tensor_s_enc(amax)
+    A = bbs.NVFP4Tensor(to_dev(a.codes), to_dev(a.scales), to_dev(s_rows), M, K, False, True)
+    Y, got_amax = _run(bbs, A, upload_nvfp4(b, bbs), s_enc, gelu, M, N)
+    o = O.nvfp4_encode_f32(y, s_enc)
+    assert np.array_equal(host(Y.scales), o.scales)
+    assert np.array_equal(host(Y.codes), o.codes)
+    assert got_amax == amax
+
+
 def test_saturating_scale(bbs):
     """An encode scale chosen for a smaller amax (a stale one) saturates the
     block scale at 448, exactly as the oracle's encode does."""
