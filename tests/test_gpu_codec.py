@@ -91,15 +91,16 @@ def _upload_s2f6(bbs, o):
 @pytest.mark.parametrize("rht", [True, False])
 @pytest.mark.parametrize("weighted", [True, False])
 @pytest.mark.parametrize("bf16", [True, False])
-def test_combine(bbs, rht, weighted, bf16):
-    announce(f"S2F6 combine rht={rht} weighted={weighted} bf16={bf16}")
+@pytest.mark.parametrize("k", [5, 8])
+def test_combine(bbs, rht, weighted, bf16, k):
+    announce(f"S2F6 combine rht={rht} weighted={weighted} bf16={bf16} k={k}")
     rng = np.random.default_rng(31)
     x = synth.normal_with_outliers(96, 544, 55, frac=0.0035, factor=10.0)
     o = O.s2f6_quantize(x, rht=rht, signs=SIGNS)
-    src = rng.integers(0, 96, (40, 5)).astype(np.int32)
+    src = rng.integers(0, 96, (40, k)).astype(np.int32)
     src[3, 2] = -1
     src[7, :] = -1                                  # a token with no rows: zeros
-    w = rng.uniform(0.05, 1.0, (40, 5)).astype(np.float32) if weighted else None
+    w = rng.uniform(0.05, 1.0, (40, k)).astype(np.float32) if weighted else None
     ref = O.s2f6_combine(o, src, w, rht=rht, signs=SIGNS)
     got = _combine(bbs, _upload_s2f6(bbs, o), src, w, rht, bf16, ldo=544 + 32)
     if bf16:
@@ -109,17 +110,19 @@ def test_combine(bbs, rht, weighted, bf16):
         assert len(bad) == 0, f"{len(bad)} values differ, first {got.reshape(-1)[bad[0]]} vs {ref.reshape(-1)[bad[0]]}"
 
 
-def test_combine_out_of_range_rows_skipped(bbs):
+@pytest.mark.parametrize("k", [4, 8])
+def test_combine_out_of_range_rows_skipped(bbs, k):
     """Source indices at or past the number of encoded rows are skipped like
     negative ones (a dropped slot): the result equals the oracle's with those
     slots set to -1."""
-    announce("S2F6 combine with out-of-range source rows")
+    announce(f"S2F6 combine with out-of-range source rows, k={k}")
     rng = np.random.default_rng(32)
     x = synth.normal_with_outliers(64, 256, 57, frac=0.0035, factor=10.0)
     o = O.s2f6_quantize(x, rht=True, signs=SIGNS)
-    src = rng.integers(0, 64, (24, 4)).astype(np.int32)
+    src = rng.integers(0, 64, (24, k)).astype(np.int32)
     src[1, 0], src[5, 3], src[9, :] = 64, 1 << 30, 70
-    w = rng.uniform(0.05, 1.0, (24, 4)).astype(np.float32)
+    src[11, 1] = -1
+    w = rng.uniform(0.05, 1.0, (24, k)).astype(np.float32)
     clean = np.where(src >= 64, -1, src).astype(np.int32)
     ref = O.s2f6_combine(o, clean, w, rht=True, signs=SIGNS)
     got = _combine(bbs, _upload_s2f6(bbs, o), src, w, True, False)
