@@ -69,6 +69,7 @@ def _load():
     lib = C.CDLL(LIB_PATH)
     vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
     lib.nvfp4_quantize.argtypes = [C.POINTER(QuantArgs), vp]
+    lib.nvfp4_quantize_noalloc.argtypes = [C.POINTER(QuantArgs), vp]
     lib.mxfp8_requantize_t.argtypes = [C.POINTER(Fp4Desc), C.POINTER(Mx8Desc), i32, Rng, vp]
     lib.nvfp4_gemm.argtypes = [i32, vp, vp, vp, i32, i64, vp]
     lib.grouped_nvfp4_gemm.argtypes = [C.POINTER(Fp4Desc), vp, vp, i32, i64, C.POINTER(Fp4Desc),
@@ -87,7 +88,7 @@ def _load():
     lib.s2f6_quantize.argtypes = [vp, i64, i64, i64, i32, C.c_uint32, C.POINTER(S2F6Desc), vp]
     lib.s2f6_combine.argtypes = [C.POINTER(S2F6Desc), vp, vp, i64, i32, i32, C.c_uint32, vp, i32,
                                  i64, vp]
-    for f in ("nvfp4_quantize", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm",
+    for f in ("nvfp4_quantize", "nvfp4_quantize_noalloc", "mxfp8_requantize_t", "nvfp4_gemm", "grouped_nvfp4_gemm",
               "s2f6_quantize", "s2f6_combine", "mxfp4_quantize", "nvfp4_gemm_quant",
               "grouped_nvfp4_gemm_quant", "nvfp4_gemm_s2f6", "grouped_nvfp4_gemm_s2f6"):
         getattr(lib, f).restype = C.c_int
@@ -221,6 +222,24 @@ def nvfp4_quantize(x, row=None, col=None, row_mx8=None, *, row_round=RTN, row_rn
                   int(tile2d), _ptr(amax_ws), int(row_per_token), int(row_four_six),
                   int(gelu))
     _check(lib.nvfp4_quantize(C.byref(a), _stream(stream)))
+
+
+def nvfp4_quantize_noalloc(x, row=None, col=None, row_mx8=None, *, row_round=RTN, row_rng=(0, 0),
+                           col_round=RTN, col_rng=(0, 0), col_rht=False, rht_signs=0,
+                           mx8_round=RTN, mx8_rng=(0, 0), tile2d=False, row_per_token=False,
+                           row_four_six=False, gelu=False, stream=None):
+    """nvfp4_quantize without a workspace argument: the library's own per-GPU
+    scratch holds the amax partials (nothing is allocated by the call)."""
+    rd = row.desc() if row is not None else None
+    cd = col.desc() if col is not None else None
+    md = row_mx8.desc() if row_mx8 is not None else None
+    a = QuantArgs(_ptr(x), x.shape[0], x.shape[1], x.stride(0),
+                  C.pointer(rd) if rd else None, row_round, Rng(*row_rng),
+                  C.pointer(cd) if cd else None, col_round, Rng(*col_rng),
+                  int(col_rht), rht_signs,
+                  C.pointer(md) if md else None, mx8_round, Rng(*mx8_rng),
+                  int(tile2d), None, int(row_per_token), int(row_four_six), int(gelu))
+    _check(lib.nvfp4_quantize_noalloc(C.byref(a), _stream(stream)))
 
 
 def mxfp8_requantize_t(src, dst, round=SR, rng=(0, 0), stream=None):

@@ -4,11 +4,19 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/bbs.h"
 #include "bbs_kernels.hpp"
 
 static_assert(bbs::kWorkspaceFloats == BBS_AMAX_WS_FLOATS, "workspace size mismatch");
+
+// The fixed device scratch of nvfp4_quantize_noalloc: the amax partials and
+// the GELU table, BBS_AMAX_WS_FLOATS floats (45056 bytes) per GPU, held until
+// the process ends.  Host code never uses the array's name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is what the kernels receive.
+static __device__ __align__(256) float scratch[BBS_AMAX_WS_FLOATS];
 
 namespace {
 
@@ -317,8 +325,11 @@ const char *bbs_strerror(int status) {
 
 const char *bbs_last_error(void) { return g_err; }
 
-int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
-    g_err[0] = 0;
+namespace {
+
+// The quantizer behind nvfp4_quantize and nvfp4_quantize_noalloc: ws is the
+// amax workspace (BBS_AMAX_WS_FLOATS floats, 16-byte aligned) or nullptr.
+int quantize_impl(const bbs_quant_args *a, float *ws_in, hipStream_t s) {
     if (!a) return fail(BBS_EINVAL, "null args");
     if (!a->x) return fail(BBS_EINVAL, "null x");
     if (!a->row && !a->col && !a->row_mx8) return fail(BBS_EINVAL, "no output copy requested");
@@ -339,10 +350,10 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     if (act && (!a->row || a->col || a->row_mx8 || a->tile2d || a->row_round != BBS_RTN))
         return fail(BBS_ENOTSUP, "per-token / Four Over Six apply to a lone 1x16 RTN row copy");
     const bool need_ws = (a->row && !a->row_per_token) || a->col || gelu;
-    if (need_ws && !a->amax_ws) return fail(BBS_EINVAL, "null amax workspace");
-    if (need_ws && !aligned(a->amax_ws, 16))
+    if (need_ws && !ws_in) return fail(BBS_EINVAL, "null amax workspace");
+    if (need_ws && !aligned(ws_in, 16))
         return fail(BBS_EINVAL, "amax workspace not 16-byte aligned");
-    float *gelu_tab = gelu ? a->amax_ws + bbs::kGeluTabOffset : nullptr;
+    float *gelu_tab = gelu ? ws_in + bbs::kGeluTabOffset : nullptr;
     int st;
     if (a->row) {
         if ((st = check_fp4(a->row, "row", true))) return st;
@@ -371,7 +382,6 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
         if (!round_ok(a->mx8_round)) return fail(BBS_EINVAL, "bad mx8_round");
     }
 
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     bbs::QuantParams p{};
     p.x = a->x;
     p.R = a->rows;
@@ -381,10 +391,10 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     if (act) {
         if (!a->row_per_token) {
             hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, true, false, 0,
-                                            a->amax_ws, a->amax_ws + bbs::kAmaxPartials,
+                                            ws_in, ws_in + bbs::kAmaxPartials,
                                             &p.n_part, s, gelu_tab);
             if ((st = hip_status(e, "amax launch"))) return st;
-            p.part = a->amax_ws;
+            p.part = ws_in;
         } else if (gelu) {
             if ((st = hip_status(bbs::launch_gelu_table(gelu_tab, s), "GELU table launch")))
                 return st;
@@ -399,7 +409,7 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     const bool rht = a->col && a->col_rht;
     const bool plain = a->row || (a->col && !rht);
     if (plain || rht) {
-        float *ws = a->amax_ws;
+        float *ws = ws_in;
         hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, plain, rht, a->rht_signs,
                                         ws, ws + bbs::kAmaxPartials, &p.n_part, s, gelu_tab);
         if ((st = hip_status(e, "amax launch"))) return st;
@@ -436,6 +446,54 @@ int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
     hipError_t e = bbs::launch_quant_tile(p, a->row != nullptr, a->col != nullptr,
                                           a->row_mx8 != nullptr, a->tile2d != 0, rht, s, gelu);
     return hip_status(e, "quantize launch");
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that runs `s`.
+int scratch_of(hipStream_t s, float **out) {
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "device of the stream");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BBS_ENOTSUP, "device %d is beyond the %d devices the scratch serves", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e, "hipGetDevice");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (e2 != hipSuccess) return hip_status(e2, "hipSetDevice (restore)");
+        if (!p || !aligned(p, 16)) return fail(BBS_EHIP, "scratch address unusable");
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return BBS_OK;
+}
+
+}  // namespace
+
+int nvfp4_quantize(const bbs_quant_args *a, void *stream) {
+    g_err[0] = 0;
+    return quantize_impl(a, a ? a->amax_ws : nullptr, reinterpret_cast<hipStream_t>(stream));
+}
+
+int nvfp4_quantize_noalloc(const bbs_quant_args *a, void *stream) {
+    g_err[0] = 0;
+    if (!a) return fail(BBS_EINVAL, "null args");
+    if (a->amax_ws)
+        return fail(BBS_EINVAL, "nvfp4_quantize_noalloc uses its own scratch: amax_ws must be NULL");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    float *ws = nullptr;
+    int st = scratch_of(s, &ws);
+    if (st) return st;
+    return quantize_impl(a, ws, s);
 }
 
 int mxfp8_requantize_t(const bbs_fp4 *src, const bbs_mx8 *dst, int32_t round, bbs_rng rng,

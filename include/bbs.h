@@ -164,6 +164,22 @@ typedef struct {
  * output shapes not matching x), BBS_ENOTSUP (RHT on a tile2d copy). */
 int nvfp4_quantize(const bbs_quant_args *a, void *stream);
 
+/* nvfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same arguments, checks and results, except that a->amax_ws must be
+ * NULL (else BBS_EINVAL): the amax partials and the GELU table go to a
+ * scratch array of BBS_AMAX_WS_FLOATS floats (45056 bytes) that the library
+ * holds in each GPU's memory until the process ends.  Its size does not
+ * depend on the input: the amax pass writes at most 2048 partials for any
+ * shape, so no shape is rejected for size.  The call allocates nothing (no
+ * hipMalloc, no library allocation); its first call on a device looks up
+ * that device's scratch address once.  Every call on one GPU shares that
+ * GPU's scratch and nothing in it needs clearing (each call writes what it
+ * reads), but calls that overlap in time on one GPU (two streams, or two
+ * threads) race on it: order them on one stream.  Errors: as nvfp4_quantize;
+ * BBS_EHIP if the scratch address cannot be found. */
+int nvfp4_quantize_noalloc(const bbs_quant_args *a, void *stream);
+
 /* MXFP4 copy of the BF16 matrix x (rows x cols, row stride ld elements,
  * x 16-byte aligned, ld % 8 == 0, cols % 32 == 0): per block of 32 values
  * of a row, scale 2^k with k = ceil(log2(amax / 6)) (the smallest k with

@@ -267,3 +267,16 @@ def test_gemm_s2f6_errors(lib):
                                      C.byref(Y), None) == bbs.BBS_EINVAL     # no offsets
     assert L.grouped_nvfp4_gemm_s2f6(C.byref(A), None, C.c_void_p(0x4000), 2, 32, C.byref(B), 64,
                                      1, 0, C.byref(Y), None) == bbs.BBS_EINVAL  # B.rows != G N
+
+
+def test_noalloc_error_paths_need_no_gpu(lib):
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    assert L.nvfp4_quantize_noalloc(None, None) == bbs.BBS_EINVAL
+    d = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 32, 32, 0)
+    a = bbs.QuantArgs()
+    a.x, a.rows, a.cols, a.ld = 0x1000, 32, 32, 32
+    a.row = C.pointer(d)
+    a.amax_ws = 0x4000          # the variant brings its own scratch
+    assert L.nvfp4_quantize_noalloc(C.byref(a), None) == bbs.BBS_EINVAL
+    assert b"amax_ws must be NULL" in L.bbs_last_error()
