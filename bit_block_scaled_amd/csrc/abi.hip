@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "../../include/bbs.h"
@@ -87,6 +88,26 @@ int check_s2f6(const bbs_s2f6 *d, const char *name) {
 }
 
 }  // namespace
+
+namespace bbs {
+
+int device_cus(hipStream_t s) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (!s || hipStreamGetDevice(s, &dev) != hipSuccess)
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev < 0 || dev >= 64) dev = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace bbs
 
 extern "C" {
 

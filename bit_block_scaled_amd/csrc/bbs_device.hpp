@@ -85,10 +85,14 @@ __device__ __forceinline__ uint32_t pack_bytes4(uint32_t b0, uint32_t b1, uint32
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
+// The conversions below only write part of their destination word; the
+// rest comes from their first operand, whose bits are never used here, so
+// a dead input is passed there (no register needs clearing first).
+
 // E2M1 round-to-nearest-even of (a, b): byte with a in bits 3:0 (upper bits
 // of the returned word are unspecified).
 __device__ __forceinline__ uint32_t e2m1_rne_pair(float a, float b) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(a), a, b, 1.0f, 0);
 }
 
 // Eight values times s, rounded to nearest, packed little-endian.
@@ -101,10 +105,11 @@ __device__ __forceinline__ uint32_t e2m1_rne8(const float *f, float s) {
 __device__ __forceinline__ uint32_t sr_word_lo(uint32_t w) { return (w << 16) | 0x8000u; }
 __device__ __forceinline__ uint32_t sr_word_hi(uint32_t w) { return (w & 0xFFFF0000u) | 0x8000u; }
 
-// Stochastic E2M1 code of one value (nibble in bits 3:0, bits 7:4 zero).
+// Stochastic E2M1 code of one value (nibble in bits 3:0, bits 7:4 zero,
+// upper bytes unspecified).
 __device__ __forceinline__ uint32_t e2m1_sr1(float v, uint32_t r) {
     f32x2_t p = {v, 0.0f};
-    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, r, 1.0f, 0);
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(__float_as_uint(v), p, r, 1.0f, 0);
 }
 
 // Eight values times s, stochastically rounded with the eight 16-bit
@@ -115,32 +120,34 @@ __device__ __forceinline__ uint32_t e2m1_sr8(const float *f, float s, const uint
     for (int i = 0; i < 4; ++i) {
         const uint32_t lo = e2m1_sr1(f[2 * i] * s, sr_word_lo(w[i]));
         const uint32_t hi = e2m1_sr1(f[2 * i + 1] * s, sr_word_hi(w[i]));
-        b[i] = (hi << 4) | lo;
+        b[i] = (hi << 4) | (lo & 0xFu);
     }
     return pack_bytes4(b[0], b[1], b[2], b[3]);
 }
 
+__device__ __forceinline__ i16x2_t as_i16x2(float f) { return __builtin_bit_cast(i16x2_t, f); }
+
 // E4M3 round-to-nearest-even code of t >= 0 (saturating at 448).
 __device__ __forceinline__ uint32_t e4m3_rne_code(float t) {
     t = fminf(t, 448.0f);
-    i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, t, t, 1.0f, false);
+    i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(t), t, t, 1.0f, false);
     return (uint32_t)r[0] & 0xFFu;
 }
 
 // Four values (|y| <= 448) rounded to nearest E4M3, bytes little-endian.
 __device__ __forceinline__ uint32_t e4m3_rne4(float y0, float y1, float y2, float y3) {
-    i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, y0, y1, 1.0f, false);
-    i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2_t{0, 0}, y2, y3, 1.0f, false);
+    i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y0), y0, y1, 1.0f, false);
+    i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y2), y2, y3, 1.0f, false);
     return __builtin_amdgcn_perm((uint32_t)(uint16_t)hi[0], (uint32_t)(uint16_t)lo[0],
                                  0x05040100u);
 }
 
 // Four values (|y| <= 448) stochastically rounded to E4M3 with random
-// operands r0..r3, bytes little-endian.
+// operands r0..r3, bytes little-endian (the four byte writes cover the word).
 __device__ __forceinline__ uint32_t e4m3_sr4(float y0, float y1, float y2, float y3,
                                              uint32_t r0, uint32_t r1, uint32_t r2,
                                              uint32_t r3) {
-    int w = 0;
+    int w = __float_as_int(y0);
     w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y0, r0, 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y1, r1, 1.0f, 1);
     w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y2, r2, 1.0f, 2);
@@ -159,18 +166,42 @@ __device__ __forceinline__ float tensor_s_enc(float amax) {
     return (s > 3.40282347e38f) ? 3.40282347e38f : s;
 }
 
+// a / 6 rounded to nearest even (a >= 0 finite), as IEEE division gives it:
+// q = a * RN(1/6) and one FMA correction, q + RN(1/6) * (a - 6q), whose
+// remainder a - 6q is exact.  Over every non-negative finite FP32 a this
+// equals the correctly rounded quotient whenever the quotient is normal
+// (exhaustive host check); below a = 2^-124 the division itself is taken.
+__device__ __forceinline__ float div6(float a) {
+    constexpr float kInv6 = 0x1.555556p-3f;             // RN(1/6)
+    float q = a * kInv6;
+    q = __builtin_fmaf(__builtin_fmaf(-q, 6.0f, a), kInv6, q);
+    if (__builtin_amdgcn_ballot_w64(a < 0x1p-124f))       // rare: wave-uniform branch
+        if (a < 0x1p-124f) q = a / 6.0f;
+    return q;
+}
+
 // Block scale code: E4M3(rne((amax_b / top) * s_enc)), never below code 1.
 // top = 6 puts the block's largest magnitude on the top of the E2M1 grid;
-// Four Over Six also tries top = 4.
+// Four Over Six also tries top = 4 (a division by 4 is the multiply by 1/4,
+// rounded the same way).
 __device__ __forceinline__ uint32_t block_scale_code(float amax_b, float s_enc,
                                                      float top = 6.0f) {
-    const uint32_t c = e4m3_rne_code((amax_b / top) * s_enc);
+    const float q = top == 4.0f ? amax_b * 0.25f : (top == 6.0f ? div6(amax_b) : amax_b / top);
+    const uint32_t c = e4m3_rne_code(q * s_enc);
     return c ? c : 1u;
 }
 
 // s_enc_b = 1 / (E4M3(code) * s_dec).
 __device__ __forceinline__ float block_enc_scale(uint32_t code, float s_dec) {
     return 1.0f / (__builtin_amdgcn_cvt_scalef32_f32_fp8((int)code, 1.0f, 0) * s_dec);
+}
+
+// The encode scales of every positive E4M3 code for one decode scale, into
+// an LDS table of 128 floats (entry c = block_enc_scale(c, s_dec), entry 0
+// unused).  Threads 0..127 of the workgroup each write one entry; the
+// caller synchronises before the first lookup.
+__device__ __forceinline__ void enc_scale_table(float *tab, float s_dec) {
+    if (threadIdx.x < 128) tab[threadIdx.x] = block_enc_scale(threadIdx.x, s_dec);
 }
 
 // MXFP8 block exponent: the smallest k with amax <= 448 * 2^k.  With
@@ -182,6 +213,46 @@ __device__ __forceinline__ int e8m0_k(float amax) {
     float m = frexpf(amax, &E);
     int k = (m <= 0.875f) ? E - 9 : E - 8;
     return k < -127 ? -127 : (k > 127 ? 127 : k);
+}
+
+// The same exponent as its E8M0 byte k + 127, from the FP32 bits of amax
+// (>= 0, finite): with amax = (1 + f / 2^23) 2^(e - 127), 448 = 1.75 * 2^8,
+// k + 127 = e - 8 when f <= 0x600000 and e - 7 above, i.e.
+// ((bits + 0x1FFFFF) >> 23) - 8; zero and subnormal amax give a negative
+// value, clamped to byte 0 (k = -127).
+__device__ __forceinline__ uint32_t e8m0_byte(float amax) {
+    const int b = (int)((__float_as_uint(amax) + 0x1FFFFFu) >> 23) - 8;
+    return (uint32_t)(b < 0 ? 0 : b);
+}
+
+// Conversion scale 2^k of an E8M0 byte (byte >= 1): the FP8 conversions
+// divide their input by it exactly before rounding (checked on the device
+// against ldexp at scale 1.0).  Byte 0 (2^-127) is not an FP32 normal; its
+// blocks are converted at 2^-126 after doubling their values (exact).
+__device__ __forceinline__ float e8m0_cvt_scale(uint32_t byte) {
+    return __uint_as_float((byte < 1u ? 1u : byte) << 23);
+}
+
+// Four values rounded to nearest E4M3 after division by the scale,
+// bytes little-endian.
+__device__ __forceinline__ uint32_t e4m3_rne4_scaled(float y0, float y1, float y2, float y3,
+                                                     float scale) {
+    i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y0), y0, y1, scale, false);
+    i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y2), y2, y3, scale, false);
+    return __builtin_amdgcn_perm((uint32_t)(uint16_t)hi[0], (uint32_t)(uint16_t)lo[0],
+                                 0x05040100u);
+}
+
+// Four values stochastically rounded to E4M3 after division by the scale.
+__device__ __forceinline__ uint32_t e4m3_sr4_scaled(float y0, float y1, float y2, float y3,
+                                                    uint32_t r0, uint32_t r1, uint32_t r2,
+                                                    uint32_t r3, float scale) {
+    int w = __float_as_int(y0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y0, r0, scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y1, r1, scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y2, r2, scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(w, y3, r3, scale, 3);
+    return (uint32_t)w;
 }
 
 // ---------------------------------------------------------------------------
@@ -197,11 +268,12 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
                                                uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        // full 64-bit products (one v_mad_u64_u32 each)
+        // full 64-bit products (one v_mad_u64_u32 each); each three-way XOR
+        // is one v_bitop3_b32 (truth table 0x96)
         const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
         const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
         c0 = n0;
         c1 = (uint32_t)p1;
         c2 = n2;

@@ -109,6 +109,10 @@ struct S2F6CombineParams {
     int64_t ldo;
 };
 
+// Compute units of the device that runs stream s (the current device for
+// the NULL stream); cached per device, safe to call from several threads.
+int device_cus(hipStream_t s);
+
 // Combine wire format: S2F6 encode (optionally rotated) and the receiver's
 // weighted sum + inverse rotation.
 hipError_t launch_s2f6_encode(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool rht,

@@ -420,25 +420,31 @@ __global__ __launch_bounds__(mx::NT) void mxfp4_gemm_big_kernel(Mx8GemmParams p)
     mx_gemm_big<true, BF16_OUT>(p, smem_raw);
 }
 
-template <typename K_>
-static void launch_big(K_ kernel, size_t shm, const Mx8GemmParams &p, hipStream_t s) {
+// The kernel's dynamic LDS limit is raised once per kernel (thread-safe
+// static initialisation).
+template <auto Kernel>
+static void launch_big(size_t shm, const Mx8GemmParams &p, hipStream_t s) {
     const int64_t T = ((p.M + mx::BM - 1) / mx::BM) * ((p.N + mx::BN - 1) / mx::BN);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)T), dim3(mx::NT), shm, s, p);
+    static const bool attr_set = [shm] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        return true;
+    }();
+    (void)attr_set;
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)T), dim3(mx::NT), shm, s, p);
 }
 
 hipError_t launch_mxfp8_gemm_big(const Mx8GemmParams &p, bool bf16_out, hipStream_t s) {
     const size_t shm = sizeof(mx::Smem<false>);
-    if (bf16_out) launch_big(mxfp8_gemm_big_kernel<true>, shm, p, s);
-    else launch_big(mxfp8_gemm_big_kernel<false>, shm, p, s);
+    if (bf16_out) launch_big<mxfp8_gemm_big_kernel<true>>(shm, p, s);
+    else launch_big<mxfp8_gemm_big_kernel<false>>(shm, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_mxfp4_gemm(const Mx8GemmParams &p, bool bf16_out, hipStream_t s) {
     const size_t shm = sizeof(mx::Smem<true>);
-    if (bf16_out) launch_big(mxfp4_gemm_big_kernel<true>, shm, p, s);
-    else launch_big(mxfp4_gemm_big_kernel<false>, shm, p, s);
+    if (bf16_out) launch_big<mxfp4_gemm_big_kernel<true>>(shm, p, s);
+    else launch_big<mxfp4_gemm_big_kernel<false>>(shm, p, s);
     return hipGetLastError();
 }
 

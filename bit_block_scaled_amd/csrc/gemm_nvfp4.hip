@@ -832,29 +832,26 @@ __global__ __launch_bounds__(big::NT) void grouped_nvfp4_gemm_s2f6_kernel(GemmPa
 
 __global__ void clear_amax_kernel(unsigned *amax) { *amax = 0u; }
 
-// Persistent grid: one workgroup per CU (the LDS ring admits one), a
-// multiple of 8 so every XCD holds the same number; never more than the
-// tiles when those are known.
-static int64_t persistent_grid(int64_t tiles) {
-    static int cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
-            n = 256;
-        cus[dev] = n;
-    }
-    const int64_t g = cus[dev] / 8 * 8;
+// Persistent grid: one workgroup per CU of the stream's device (the LDS ring
+// admits one), a multiple of 8 so every XCD holds the same number; never
+// more than the tiles when those are known.
+static int64_t persistent_grid(int64_t tiles, hipStream_t s) {
+    const int n = device_cus(s);
+    const int64_t g = n >= 8 ? n / 8 * 8 : 8;
     return tiles > 0 && tiles < g ? tiles : g;
 }
 
-template <typename K_>
-static void launch_with_smem(K_ kernel, int64_t grid, size_t shm, const GemmParams &p,
-                             hipStream_t s) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(big::NT), shm, s, p);
+// Launch with `shm` bytes of dynamic LDS; the kernel's limit is raised once
+// per kernel (thread-safe static initialisation).
+template <auto Kernel>
+static void launch_with_smem(int64_t grid, size_t shm, const GemmParams &p, hipStream_t s) {
+    static const bool attr_set = [shm] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        return true;
+    }();
+    (void)attr_set;
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)grid), dim3(big::NT), shm, s, p);
 }
 
 static int64_t dense_tiles(const GemmParams &p) {
@@ -872,9 +869,9 @@ hipError_t launch_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipStream_t s
         const hipError_t e = launch_gelu_table(const_cast<float *>(p.q.gelu_tab), s);
         if (e != hipSuccess) return e;
     }
-    const int64_t grid = persistent_grid(dense_tiles(p));
-    if (gelu) launch_with_smem(nvfp4_gemm_quant_kernel<true>, grid, kSmemGelu, p, s);
-    else launch_with_smem(nvfp4_gemm_quant_kernel<false>, grid, kSmemBig, p, s);
+    const int64_t grid = persistent_grid(dense_tiles(p), s);
+    if (gelu) launch_with_smem<nvfp4_gemm_quant_kernel<true>>(grid, kSmemGelu, p, s);
+    else launch_with_smem<nvfp4_gemm_quant_kernel<false>>(grid, kSmemBig, p, s);
     return hipGetLastError();
 }
 
@@ -885,35 +882,35 @@ hipError_t launch_grouped_nvfp4_gemm_quant(const GemmParams &p, bool gelu, hipSt
         const hipError_t e = launch_gelu_table(const_cast<float *>(p.q.gelu_tab), s);
         if (e != hipSuccess) return e;
     }
-    const int64_t grid = persistent_grid(0);
-    if (gelu) launch_with_smem(grouped_nvfp4_gemm_quant_kernel<true>, grid, kSmemGelu, p, s);
-    else launch_with_smem(grouped_nvfp4_gemm_quant_kernel<false>, grid, kSmemBig, p, s);
+    const int64_t grid = persistent_grid(0, s);
+    if (gelu) launch_with_smem<grouped_nvfp4_gemm_quant_kernel<true>>(grid, kSmemGelu, p, s);
+    else launch_with_smem<grouped_nvfp4_gemm_quant_kernel<false>>(grid, kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
-    launch_with_smem(nvfp4_gemm_s2f6_kernel, persistent_grid(dense_tiles(p)), kSmemBig, p, s);
+    launch_with_smem<nvfp4_gemm_s2f6_kernel>(persistent_grid(dense_tiles(p), s), kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
     if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
-    launch_with_smem(grouped_nvfp4_gemm_s2f6_kernel, persistent_grid(0), kSmemBig, p, s);
+    launch_with_smem<grouped_nvfp4_gemm_s2f6_kernel>(persistent_grid(0, s), kSmemBig, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
-    const int64_t grid = persistent_grid(dense_tiles(p));
-    if (bf16_out) launch_with_smem(nvfp4_gemm_big_kernel<true>, grid, kSmemPlain, p, s);
-    else launch_with_smem(nvfp4_gemm_big_kernel<false>, grid, kSmemPlain, p, s);
+    const int64_t grid = persistent_grid(dense_tiles(p), s);
+    if (bf16_out) launch_with_smem<nvfp4_gemm_big_kernel<true>>(grid, kSmemPlain, p, s);
+    else launch_with_smem<nvfp4_gemm_big_kernel<false>>(grid, kSmemPlain, p, s);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
     if (p.G > kMaxGroupsBig) return hipErrorInvalidValue;
-    const int64_t grid = persistent_grid(0);
-    if (bf16_out) launch_with_smem(grouped_nvfp4_gemm_big_kernel<true>, grid, kSmemPlain, p, s);
-    else launch_with_smem(grouped_nvfp4_gemm_big_kernel<false>, grid, kSmemPlain, p, s);
+    const int64_t grid = persistent_grid(0, s);
+    if (bf16_out) launch_with_smem<grouped_nvfp4_gemm_big_kernel<true>>(grid, kSmemPlain, p, s);
+    else launch_with_smem<grouped_nvfp4_gemm_big_kernel<false>>(grid, kSmemPlain, p, s);
     return hipGetLastError();
 }
 

@@ -4,19 +4,26 @@
 // Procedure", steps 1-4; 4bit.vizuara.ai sections 5-6, 13):
 //   pass 1  amax_kernel: per-workgroup maxima of |x| and / or of the RHT'd
 //           16-row column chunks, from one read of x; no atomics, no zeroing.
-//   pass 2  quant_kernel: every wave folds the partials into the tensor amax
-//           (bit-identical everywhere).  A workgroup owns a 256-row x
-//           128-column tile of x; each thread a 16 x 8 piece of it, loaded as
-//           16 rows of 16 bytes.  From that one read it writes any of: the
+//           A wave reads 16 rows x 512 columns per step (each load a 1 KB
+//           run of one row) and loads its next step while reducing this one.
+//   pass 2  quant_kernel: every workgroup folds the partials into the tensor
+//           amax (bit-identical everywhere) and walks a run of 256-row x
+//           128-column tiles of x, loading the next tile while it encodes
+//           this one.  A thread owns a 16 x 8 piece of a tile, loaded as 16
+//           rows of 16 bytes.  From that one read it writes any of: the
 //           row-wise NVFP4 copy (a 1x16 block is two neighbouring lanes), the
 //           column-wise NVFP4 copy of x^T (eight full column blocks per
 //           thread, optional RHT), and the row-wise MXFP8 copy (a block of 32
-//           is four lanes).  With 256 tile rows, each transposed row's 128
-//           code bytes are written by one workgroup, so HBM sees whole lines.
-//           Block scales are gathered in LDS and written as contiguous runs.
+//           is four lanes).  The column copy's codes and every copy's block
+//           scales are gathered in LDS and written as whole runs: each
+//           transposed row's 128 code bytes of a tile are one store of eight
+//           lanes.  Block encode scales 1 / (E4M3 x s_dec) come from a table
+//           of the 127 E4M3 codes built once per workgroup.
 // Requantize (4bit.vizuara.ai sections 9-10): requant_kernel dequantizes a
-// 32-row x 8-column piece of an NVFP4 matrix in FP32 and writes its 8
-// transposed rows of 32 as MXFP8 (E8M0 per 32, E4M3 elements, RTN or SR).
+// 32-row x 8-column piece of an NVFP4 matrix in FP32 per lane and encodes
+// its 8 transposed rows of 32 as MXFP8 (E8M0 per 32, E4M3 elements, RTN or
+// SR); a workgroup's 512 destination rows x 128 bytes are gathered in LDS and
+// stored as whole rows.  It also walks a run of tiles, loading ahead.
 //
 // Workgroups are mapped to tiles so that each of the 8 XCDs works through a
 // contiguous run of tiles (neighbouring tiles share output lines in L2).
@@ -29,11 +36,10 @@ namespace bbs {
 
 constexpr int kQT = 256;                       // threads per workgroup
 constexpr int kTileR = 256, kTileC = 128;      // quantizer tile of x
-constexpr int kAmaxGrid = 512;                 // workgroups (= partials) of pass 1
 constexpr int kReqR = 128, kReqC = 512;        // requantizer tile of the source
 
-static_assert(kAmaxGrid <= kAmaxPartials, "amax partials exceed the workspace");
 static_assert(kGeluTabOffset + kGeluTabSize <= kWorkspaceFloats, "GELU table exceeds the workspace");
+static_assert(kQT == 256, "the partial fold assumes four waves");
 static_assert(kGeluTabOffset % 4 == 0, "GELU table must stay 16-byte aligned");
 
 // Tile t of T when workgroup b runs on XCD b % 8: XCD x takes a contiguous
@@ -41,6 +47,23 @@ static_assert(kGeluTabOffset % 4 == 0, "GELU table must stay 16-byte aligned");
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t T) {
     const int64_t x = b % 8, j = b / 8, per = T / 8, rem = T % 8;
     return x * per + (x < rem ? x : rem) + j;
+}
+
+// The tiles a workgroup of a persistent grid walks: the workgroups of XCD
+// b % 8 share that XCD's contiguous eighth of the tiles, taking every
+// (workgroups on the XCD)-th one.  Grids of fewer than 8 workgroups stride
+// over all tiles.
+struct TileWalk {
+    int64_t first, end, step;
+};
+__device__ __forceinline__ TileWalk xcd_walk(int64_t T) {
+    const int64_t G = gridDim.x, b = blockIdx.x;
+    if (G < 8) return {b, T, G};
+    const int64_t x = b % 8, j = b / 8, per = T / 8, rem = T % 8;
+    const int64_t lo = x * per + (x < rem ? x : rem);
+    const int64_t hi = lo + per + (x < rem ? 1 : 0);
+    const int64_t gx = G / 8 + (x < G % 8 ? 1 : 0);
+    return {lo + j, hi, gx};
 }
 
 // A thread's 16 x 8 piece of a quantizer tile.
@@ -97,6 +120,11 @@ __device__ __forceinline__ float wave_max(float m) {
 
 // ---------------------------------------------------------------------------
 // Pass 1: partial amax of |x| (PLAIN) and of |RHT(column chunks)| (RHT).
+// A wave step covers 16 rows x 512 columns: lane l reads columns
+// 8l .. 8l + 7 of each row (one 16-byte load per row), so a load of the wave
+// is a 1 KB run of one row and the lane holds eight full 16-row column
+// chunks for the RHT.  Steps past the last column (C % 512 != 0) read a
+// valid piece and are not counted.
 // ---------------------------------------------------------------------------
 // GELU: the partials are maxima of |GELU(x)|, found without evaluating GELU
 // on most elements.  GELU is non-decreasing for x >= 0, so the largest value
@@ -104,6 +132,8 @@ __device__ __forceinline__ float wave_max(float m) {
 // element has |GELU| < kGeluNegBound, so the negative elements of a wave's
 // pieces are evaluated only when GELU of the wave's largest element is below
 // that bound (wave-uniform branch).  The result is the exact maximum.
+constexpr int kAmaxStepC = 512;
+
 template <bool PLAIN, bool RHT, bool GELU>
 __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ x, int64_t R,
                                                    int64_t C, int64_t ld, uint32_t signs,
@@ -115,20 +145,30 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
         for (int i = blockIdx.x * kQT + threadIdx.x; i < kGeluTabSize; i += gridDim.x * kQT)
             gelu_tab[i] = gelu_table_entry(i);
     __shared__ float red[2][kQT / 64];
-    const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t steps_c = (C + kAmaxStepC - 1) / kAmaxStepC;
+    const int64_t T = (R / 16) * steps_c;
+    const int64_t stride = (int64_t)gridDim.x * (kQT / 64);
     float m = 0.0f, mr = 0.0f;
     float mx = 0.0f;     // GELU: largest element seen (0 if none is positive)
-    // The next tile's piece is loaded while this one is reduced.
-    int64_t tile = blockIdx.x;
-    Piece q = piece_of(tile, R, C);
+    auto load = [&](int64_t t, uint4 d[16]) -> bool __attribute__((always_inline)) {
+        const int64_t tr = t / steps_c;
+        int64_t c = (t - tr * steps_c) * kAmaxStepC + lane * 8;
+        const bool ok = c < C;
+        if (!ok) c = C - 8;
+        const uint16_t *src = x + tr * 16 * ld + c;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * ld);
+        return ok;
+    };
+    int64_t t = (int64_t)blockIdx.x * (kQT / 64) + w;
     uint4 v[16];
-    if (tile < T) load_piece(x, R, C, ld, q, v);
-    while (tile < T) {
-        const int64_t next = tile + gridDim.x;
-        const Piece qn = piece_of(next < T ? next : tile, R, C);
+    bool ok = t < T ? load(t, v) : false;
+    while (t < T) {                                   // wave-uniform
+        const int64_t tn = t + stride;
         uint4 vn[16];
-        if (next < T) load_piece(x, R, C, ld, qn, vn);
-        if (q.in) {
+        const bool okn = tn < T ? load(tn, vn) : false;
+        if (ok) {
         if (PLAIN) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -149,22 +189,22 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
         }
         if (GELU) {
             float pm = 0.0f;
-            if (q.in) {
+            if (ok) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) pm = fmaxf(pm, elem(v[r], j));
             }
             mx = fmaxf(mx, pm);
-            if (gelu_tanh(wave_max(pm)) < kGeluNegBound && q.in) {
+            if (gelu_tanh(wave_max(pm)) < kGeluNegBound && ok) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(gelu_tanh(elem(v[r], j))));
             }
         }
-        tile = next;
-        q = qn;
+        t = tn;
+        ok = okn;
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = vn[i];
     }
@@ -174,8 +214,7 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
     if (GELU) m = fmaxf(m, gelu_tanh(mx));
     m = wave_max(m);
     mr = wave_max(mr);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
+    if (lane == 0) {
         red[0][w] = m;
         red[1][w] = mr;
     }
@@ -216,43 +255,38 @@ __device__ __forceinline__ void put_run(uint8_t *dst, const uint8_t *src, int64_
     }
 }
 
-// GELU: the row-wise copies are of GELU(x), evaluated once per element in
-// FP32 (the pages' fused activation + quantize); the amax partials are those
-// of |GELU(x)|.
-template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT, bool GELU>
-__global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
-    static_assert(!GELU || (!HAS_COL && !TILE2D && !RHT), "GELU feeds the row-wise copies");
-    __shared__ __align__(16) uint8_t s_row[kTileR * 8];    // row copy scales
-    __shared__ __align__(16) uint8_t s_col[kTileC * 16];   // column copy scales
-    __shared__ __align__(16) uint8_t s_mx[kTileR * 4];     // MXFP8 scales
-    __shared__ __align__(16) float s_gelu[GELU ? kGeluTabSize : 1];
-    const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
-    const Piece q = piece_of(xcd_tile(blockIdx.x, T), p.R, p.C);
-    uint4 v[16];
-    load_piece(p.x, p.R, p.C, p.ld, q, v);
+// LDS of the encode kernel.  The column copy's codes: 128 transposed rows of
+// 128 bytes, 16-byte groups swizzled by (row >> 3) & 7 so that the eight
+// lanes writing one group index hit different banks.
+template <bool GELU>
+struct QuantLds {
+    uint8_t row[kTileR * 8];           // row copy scales (1x16; 16x16 uses 16 x 8)
+    uint8_t col[kTileC * 16];          // column copy scales
+    uint8_t mx[kTileR * 4];            // MXFP8 scales
+    uint8_t colc[kTileC * 128];        // column copy codes
+    float tab[2][128];                 // encode scale per E4M3 code: row, column copy
+    float fold[2][kQT / 64];           // per-wave maxima of the amax partials
+    float gelu[GELU ? kGeluTabSize : 1];
+};
+__device__ __forceinline__ int colc_off(int row, int group) {
+    return row * 128 + ((group ^ ((row >> 3) & 7)) << 4);
+}
 
-    // Tensor scales, identical in every wave.
-    float s_enc_row = 1.0f, s_enc_col = 1.0f;
-    if (HAS_ROW || (HAS_COL && !RHT)) s_enc_row = tensor_s_enc(fold_partials(p.part, p.n_part));
-    if (HAS_COL) s_enc_col = RHT ? tensor_s_enc(fold_partials(p.part_rht, p.n_part_rht)) : s_enc_row;
-    const float s_dec_row = 1.0f / s_enc_row;
-    const float s_dec_col = 1.0f / s_enc_col;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (HAS_ROW) p.row_sdec[0] = s_dec_row;
-        if (HAS_COL) p.col_sdec[0] = s_dec_col;
-    }
+// Encode one tile (piece q, values v) into every requested copy.  Every
+// thread of the workgroup calls it (two barriers inside).
+// SR: some copy rounds stochastically (else every copy rounds to nearest and
+// the stochastic paths are not compiled).
+template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT, bool GELU, bool SR>
+__device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q,
+                                            const uint4 (&v)[16], float s_enc_row,
+                                            float s_enc_col, QuantLds<GELU> &L) {
     const int lane = threadIdx.x & 63;
-    if constexpr (GELU) {
-        gelu_table_load(s_gelu, p.gelu_tab);        // while the piece is in flight
-        __syncthreads();
-    }
     // Element j of row r of the piece, as the row-wise copies see it (GELU:
     // looked up where it is used, so the piece stays in its BF16 registers).
-    auto val = [&](int r, int j) -> float __attribute__((always_inline)) {
-        if constexpr (GELU) return gelu_bf16(elem_bits(v[r], j), s_gelu);
+    auto val = [&](int r, int j) -> float {
+        if constexpr (GELU) return gelu_bf16(elem_bits(v[r], j), L.gelu);
         else return elem(v[r], j);
     };
-
 
     // 16x16 tile amax (two lanes hold one tile; TILE2D excludes RHT).
     float tile_amax = 0.0f;
@@ -269,11 +303,14 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
     float ts = 0.0f;
     if (HAS_ROW && TILE2D) {
         tsc = block_scale_code(tile_amax, s_enc_row);
-        ts = block_enc_scale(tsc, s_dec_row);
+        ts = L.tab[0][tsc];
     }
+    // counters of the first row's Philox blocks; each further row adds C / 8
+    const uint64_t n_row0 = (uint64_t)(q.r0 * p.C + q.c0) / 8;
+    const uint64_t n_step = (uint64_t)p.C / 8;
     // NVFP4 copy of row r of the piece (values f)
-    auto row_copy = [&](auto sr_tag, int r, const float f[8]) __attribute__((always_inline)) {
-        constexpr bool SR = decltype(sr_tag)::value;
+    auto row_copy = [&](auto sr_tag, int r, const float f[8]) {
+        constexpr bool RSR = decltype(sr_tag)::value;
         uint32_t sc = tsc;
         float s = ts;
         if (!TILE2D) {
@@ -281,13 +318,13 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
             sc = block_scale_code(max_lane_pair(a), s_enc_row);
-            s = block_enc_scale(sc, s_dec_row);
-            if ((lane & 1) == 0) s_row[(q.band * 16 + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
+            s = L.tab[0][sc];
+            if ((lane & 1) == 0) L.row[(q.band * 16 + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
         }
         uint32_t packed;
-        if (SR) {
+        if constexpr (RSR) {
             uint32_t w[4];
-            sr_block(p.row_seed, p.row_stream, (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
+            sr_block(p.row_seed, p.row_stream, n_row0 + (uint64_t)r * n_step, w);
             packed = e2m1_sr8(f, s, w);
         } else {
             packed = e2m1_rne8(f, s);
@@ -295,35 +332,44 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
         if (q.in) *reinterpret_cast<uint32_t *>(p.row_codes + (q.r0 + r) * (p.C / 2) + q.c0 / 2) =
             packed;
     };
-    // MXFP8 copy of row r of the piece (values f)
-    auto mx_copy = [&](auto sr_tag, int r, const float f[8]) __attribute__((always_inline)) {
-        constexpr bool SR = decltype(sr_tag)::value;
+    // MXFP8 copy of row r of the piece (values f): the block's power of two
+    // rides in the conversion's scale operand
+    auto mx_copy = [&](auto sr_tag, int r, const float (&f)[8]) {
+        constexpr bool MSR = decltype(sr_tag)::value;
         float y[8];
         float a = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
-        const int k = e8m0_k(max_lane_quad(a));
+        for (int j = 0; j < 8; ++j) {
+            y[j] = f[j];
+            a = fmaxf(a, fabsf(f[j]));
+        }
+        const uint32_t kb = e8m0_byte(max_lane_quad(a));
+        if (__builtin_amdgcn_ballot_w64(kb == 0)) {   // rare, wave-uniform test
+            if (kb == 0) {                             // 2^-127: convert 2y at 2^-126
 #pragma unroll
-        for (int j = 0; j < 8; ++j) y[j] = ldexpf(f[j], -k);   // exact
+                for (int j = 0; j < 8; ++j) y[j] = y[j] * 2.0f;
+            }
+        }
+        const float cs = e8m0_cvt_scale(kb);
         uint32_t lo, hi;
-        if (SR) {
+        if constexpr (MSR) {
             uint32_t w[4];
-            sr_block(p.mx_seed, p.mx_stream, (uint64_t)((q.r0 + r) * p.C + q.c0) / 8, w);
-            lo = e4m3_sr4(y[0], y[1], y[2], y[3], sr_word_lo(w[0]), sr_word_hi(w[0]),
-                          sr_word_lo(w[1]), sr_word_hi(w[1]));
-            hi = e4m3_sr4(y[4], y[5], y[6], y[7], sr_word_lo(w[2]), sr_word_hi(w[2]),
-                          sr_word_lo(w[3]), sr_word_hi(w[3]));
+            sr_block(p.mx_seed, p.mx_stream, n_row0 + (uint64_t)r * n_step, w);
+            lo = e4m3_sr4_scaled(y[0], y[1], y[2], y[3], sr_word_lo(w[0]), sr_word_hi(w[0]),
+                                 sr_word_lo(w[1]), sr_word_hi(w[1]), cs);
+            hi = e4m3_sr4_scaled(y[4], y[5], y[6], y[7], sr_word_lo(w[2]), sr_word_hi(w[2]),
+                                 sr_word_lo(w[3]), sr_word_hi(w[3]), cs);
         } else {
-            lo = e4m3_rne4(y[0], y[1], y[2], y[3]);
-            hi = e4m3_rne4(y[4], y[5], y[6], y[7]);
+            lo = e4m3_rne4_scaled(y[0], y[1], y[2], y[3], cs);
+            hi = e4m3_rne4_scaled(y[4], y[5], y[6], y[7], cs);
         }
         if (q.in) *reinterpret_cast<uint2 *>(p.mx_codes + (q.r0 + r) * p.C + q.c0) = make_uint2(lo, hi);
-        if ((lane & 3) == 0) s_mx[(q.band * 16 + r) * 4 + (q.cg >> 2)] = (uint8_t)(k + 127);
+        if ((lane & 3) == 0) L.mx[(q.band * 16 + r) * 4 + (q.cg >> 2)] = (uint8_t)kb;
     };
     // (two loops of 8 rows: each stays under the compiler's full-unroll
     // limit, so the piece's registers are never indexed at run time)
-    auto rows = [&](auto row_sr, auto mx_sr) __attribute__((always_inline)) {
-        auto one = [&](int r) __attribute__((always_inline)) {
+    auto rows = [&](auto row_sr, auto mx_sr) {
+        auto one = [&](int r) {
             float f[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) f[j] = val(r, j);
@@ -335,91 +381,192 @@ __global__ __launch_bounds__(kQT) void quant_kernel(QuantParams p) {
 #pragma unroll
         for (int r = 8; r < 16; ++r) one(r);
     };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
     if (HAS_ROW || HAS_MX) {
-        const bool row_sr = HAS_ROW && p.row_round == 1, mx_sr = HAS_MX && p.mx_round == 1;
-        if (row_sr && mx_sr) rows(std::true_type{}, std::true_type{});
-        else if (row_sr) rows(std::true_type{}, std::false_type{});
-        else if (mx_sr) rows(std::false_type{}, std::true_type{});
-        else rows(std::false_type{}, std::false_type{});
+        if constexpr (SR) {
+            const bool row_sr = HAS_ROW && p.row_round == 1, mx_sr = HAS_MX && p.mx_round == 1;
+            if (row_sr && mx_sr) rows(T_{}, T_{});
+            else if (row_sr) rows(T_{}, F_{});
+            else if (mx_sr) rows(F_{}, T_{});
+            else rows(F_{}, F_{});
+        } else {
+            rows(F_{}, F_{});
+        }
     }
-    if (HAS_ROW && TILE2D && (lane & 1) == 0) s_row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
+    if (HAS_ROW && TILE2D && (lane & 1) == 0) L.row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
 
     // ---- column-wise NVFP4 copy (of x^T) ---------------------------------------
     if (HAS_COL) {
-        uint32_t tsc = 0;
-        float ts = 0.0f;
+        uint32_t csc = 0;
+        float cts = 0.0f;
         if (TILE2D) {
-            tsc = block_scale_code(tile_amax, s_enc_col);
-            ts = block_enc_scale(tsc, s_dec_col);
+            csc = block_scale_code(tile_amax, s_enc_col);
+            cts = L.tab[1][csc];
         }
         auto cols = [&](auto sr_tag) {
-            constexpr bool SR = decltype(sr_tag)::value;
+            constexpr bool CSR = decltype(sr_tag)::value;
+            // counter of the first block of column q.c0's chunk; column j adds R / 8
+            const uint64_t n0 = (uint64_t)(q.c0 * p.R + q.r0) / 8;
+            const uint64_t nstep = (uint64_t)p.R / 8;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float y[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
                 if (RHT) rht16(y, p.rht_signs);
-                uint32_t sc = tsc;
-                float s = ts;
+                uint32_t sc = csc;
+                float s = cts;
                 if (!TILE2D) {
                     float a = 0.0f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(y[r]));
                     sc = block_scale_code(a, s_enc_col);
-                    s = block_enc_scale(sc, s_dec_col);
-                    s_col[(q.cg * 8 + j) * 16 + q.band] = (uint8_t)sc;
+                    s = L.tab[1][sc];
+                    L.col[(q.cg * 8 + j) * 16 + q.band] = (uint8_t)sc;
                 }
-                const int64_t c = q.c0 + j;                 // row of the transposed copy
                 uint32_t w0, w1;
-                if (SR) {
-                    const uint64_t n0 = (uint64_t)(c * p.R + q.r0) / 8;
+                if constexpr (CSR) {
+                    const uint64_t n = n0 + (uint64_t)j * nstep;
                     uint32_t w[4];
-                    sr_block(p.col_seed, p.col_stream, n0, w);
+                    sr_block(p.col_seed, p.col_stream, n, w);
                     w0 = e2m1_sr8(y, s, w);
-                    sr_block(p.col_seed, p.col_stream, n0 + 1, w);
+                    sr_block(p.col_seed, p.col_stream, n + 1, w);
                     w1 = e2m1_sr8(y + 8, s, w);
                 } else {
                     w0 = e2m1_rne8(y, s);
                     w1 = e2m1_rne8(y + 8, s);
                 }
-                if (q.in)
-                    *reinterpret_cast<uint2 *>(p.col_codes + c * (p.R / 2) + q.r0 / 2) =
-                        make_uint2(w0, w1);
+                // transposed row q.cg * 8 + j of the tile, bytes band * 8 .. + 7
+                const int trow = q.cg * 8 + j;
+                *reinterpret_cast<uint2 *>(L.colc + colc_off(trow, q.band >> 1) + (q.band & 1) * 8) =
+                    make_uint2(w0, w1);
             }
         };
-        if (p.col_round == 1) cols(std::true_type{});
-        else cols(std::false_type{});
-        if (TILE2D && (lane & 1) == 0) s_col[(q.cg >> 1) * 16 + q.band] = (uint8_t)tsc;
+        if constexpr (SR) {
+            if (p.col_round == 1) cols(T_{});
+            else cols(F_{});
+        } else {
+            cols(F_{});
+        }
+        if (TILE2D && (lane & 1) == 0) L.col[(q.cg >> 1) * 16 + q.band] = (uint8_t)csc;
     }
 
-    // ---- block scales, as contiguous runs ------------------------------------
+    // ---- column codes and block scales, as whole runs -------------------------
     __syncthreads();
     const int t = threadIdx.x;
     const int64_t nb_row = (p.C - q.C0) / 16, nb_col = (p.R - q.R0) / 16;
+    if (HAS_COL) {
+        // 128 transposed rows x 16 halves of 8 bytes (16 source rows each):
+        // 8 passes of 256 threads, 16 lanes per 128-byte row
+        const int64_t rows_in = p.C - q.C0 < kTileC ? p.C - q.C0 : kTileC;
+        const int64_t halves_in = (p.R - q.R0) / 16;              // bands inside x
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = i * kQT + t, trow = idx >> 4, h = idx & 15;
+            if (trow < rows_in && h < halves_in)
+                *reinterpret_cast<uint2 *>(p.col_codes + (q.C0 + trow) * (p.R / 2) + q.R0 / 2 + h * 8) =
+                    *reinterpret_cast<const uint2 *>(L.colc + colc_off(trow, h >> 1) + (h & 1) * 8);
+        }
+    }
     if (HAS_ROW) {
         if (!TILE2D) {
             if (q.R0 + t < p.R)
-                put_run<8>(p.row_scales + (q.R0 + t) * (p.C / 16) + q.C0 / 16, s_row + t * 8,
+                put_run<8>(p.row_scales + (q.R0 + t) * (p.C / 16) + q.C0 / 16, L.row + t * 8,
                            nb_row < 8 ? nb_row : 8);
         } else if (t < 16 && q.R0 / 16 + t < p.R / 16) {
-            put_run<8>(p.row_scales + (q.R0 / 16 + t) * (p.C / 16) + q.C0 / 16, s_row + t * 8,
+            put_run<8>(p.row_scales + (q.R0 / 16 + t) * (p.C / 16) + q.C0 / 16, L.row + t * 8,
                        nb_row < 8 ? nb_row : 8);
         }
     }
     if (HAS_MX && q.R0 + t < p.R) {
         const int64_t nb = (p.C - q.C0) / 32;
-        put_run<4>(p.mx_scales + (q.R0 + t) * (p.C / 32) + q.C0 / 32, s_mx + t * 4,
+        put_run<4>(p.mx_scales + (q.R0 + t) * (p.C / 32) + q.C0 / 32, L.mx + t * 4,
                    nb < 4 ? nb : 4);
     }
     if (HAS_COL) {
         if (!TILE2D) {
             if (t < kTileC && q.C0 + t < p.C)
-                put_run<16>(p.col_scales + (q.C0 + t) * (p.R / 16) + q.R0 / 16, s_col + t * 16,
+                put_run<16>(p.col_scales + (q.C0 + t) * (p.R / 16) + q.R0 / 16, L.col + t * 16,
                             nb_col < 16 ? nb_col : 16);
         } else if (t < kTileC / 16 && q.C0 / 16 + t < p.C / 16) {
-            put_run<16>(p.col_scales + (q.C0 / 16 + t) * (p.R / 16) + q.R0 / 16, s_col + t * 16,
+            put_run<16>(p.col_scales + (q.C0 / 16 + t) * (p.R / 16) + q.R0 / 16, L.col + t * 16,
                         nb_col < 16 ? nb_col : 16);
+        }
+    }
+    __syncthreads();                       // LDS is rewritten by the next tile
+}
+
+// GELU: the row-wise copies are of GELU(x), evaluated once per element in
+// FP32 (the pages' fused activation + quantize); the amax partials are those
+// of |GELU(x)|.
+// WALK = false: one tile per workgroup (XCD-contiguous mapping), registers
+// capped for MINW waves per SIMD.  WALK = true: a resident grid walks runs
+// of tiles, loading the next tile while it encodes the current one.
+template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT, bool GELU, bool SR,
+          bool WALK, int MINW>
+__global__ __launch_bounds__(kQT, MINW) void quant_kernel(QuantParams p) {
+    static_assert(!GELU || (!HAS_COL && !TILE2D && !RHT), "GELU feeds the row-wise copies");
+    __shared__ __align__(16) QuantLds<GELU> L;
+    const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
+    const TileWalk walk = WALK ? xcd_walk(T) : TileWalk{xcd_tile(blockIdx.x, T), 0, 1};
+    // the first tile's piece is in flight while the scales are set up
+    uint4 v[16];
+    Piece q = piece_of(!WALK || walk.first < walk.end ? walk.first : 0, p.R, p.C);
+    if (!WALK || walk.first < walk.end) load_piece(p.x, p.R, p.C, p.ld, q, v);
+
+    // Tensor scales, identical in every wave: the partials are folded once
+    // per workgroup (each thread a strided share, then the four waves).
+    const bool plain_amax = HAS_ROW || (HAS_COL && !RHT);
+    {
+        float a = 0.0f, b = 0.0f;
+        if (plain_amax)
+            for (int i = threadIdx.x; i < p.n_part; i += kQT) a = fmaxf(a, p.part[i]);
+        if (HAS_COL && RHT)
+            for (int i = threadIdx.x; i < p.n_part_rht; i += kQT) b = fmaxf(b, p.part_rht[i]);
+        a = wave_max(a);
+        b = wave_max(b);
+        if ((threadIdx.x & 63) == 0) {
+            L.fold[0][threadIdx.x >> 6] = a;
+            L.fold[1][threadIdx.x >> 6] = b;
+        }
+    }
+    __syncthreads();
+    float s_enc_row = 1.0f, s_enc_col = 1.0f;
+    if (plain_amax)
+        s_enc_row = tensor_s_enc(fmaxf(fmaxf(L.fold[0][0], L.fold[0][1]), fmaxf(L.fold[0][2], L.fold[0][3])));
+    if (HAS_COL)
+        s_enc_col = RHT ? tensor_s_enc(fmaxf(fmaxf(L.fold[1][0], L.fold[1][1]),
+                                             fmaxf(L.fold[1][2], L.fold[1][3])))
+                        : s_enc_row;
+    const float s_dec_row = 1.0f / s_enc_row;
+    const float s_dec_col = 1.0f / s_enc_col;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (HAS_ROW) p.row_sdec[0] = s_dec_row;
+        if (HAS_COL) p.col_sdec[0] = s_dec_col;
+    }
+    if (HAS_ROW) enc_scale_table(L.tab[0], s_dec_row);
+    if (HAS_COL) enc_scale_table(L.tab[1], s_dec_col);
+    if constexpr (GELU) gelu_table_load(L.gelu, p.gelu_tab);
+    __syncthreads();
+
+    if constexpr (!WALK) {
+        encode_tile<HAS_ROW, HAS_COL, HAS_MX, TILE2D, RHT, GELU, SR>(p, q, v, s_enc_row, s_enc_col,
+                                                                     L);
+    } else {
+        for (int64_t t = walk.first; t < walk.end; t += walk.step) {     // workgroup-uniform
+            const int64_t tn = t + walk.step;
+            uint4 vn[16];
+            Piece qn = q;
+            if (tn < walk.end) {
+                qn = piece_of(tn, p.R, p.C);
+                load_piece(p.x, p.R, p.C, p.ld, qn, vn);
+            }
+            encode_tile<HAS_ROW, HAS_COL, HAS_MX, TILE2D, RHT, GELU, SR>(p, q, v, s_enc_row,
+                                                                         s_enc_col, L);
+            q = qn;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = vn[i];
         }
     }
 }
@@ -591,80 +738,170 @@ __global__ __launch_bounds__(kQT) void quant_act_kernel(QuantParams p) {
 
 // ---------------------------------------------------------------------------
 // Requantize: NVFP4 [R x C] -> MXFP8 of the transpose [C x R].
-// A workgroup takes 128 source rows (a 32-row band per wave) x 512 source
-// columns (8 per lane), so each destination row's 128 bytes come from one
-// workgroup.  Each lane: 32 rows x 8 columns -> 8 destination rows of 32.
+// A tile is 128 source rows (a 32-row band per wave) x 512 source columns (8
+// per lane); each lane turns its 32 rows x 8 columns into 8 destination rows
+// of 32.  The tile's 512 destination rows x 128 code bytes are gathered in
+// LDS (16-byte groups swizzled by (row >> 3) & 7) and stored as whole rows,
+// its 512 x 4 scale bytes as 4-byte runs.  Workgroups walk XCD-contiguous
+// runs of tiles, loading the next tile's codes while encoding this one.
 // ---------------------------------------------------------------------------
-template <bool SR, bool TILE2D>
-__global__ __launch_bounds__(kQT) void requant_kernel(RequantParams p) {
+struct RequantLds {
+    uint8_t codes[kReqC * 128];
+    uint8_t scales[kReqC * 4];
+};
+__device__ __forceinline__ int req_off(int row, int group) {
+    return row * 128 + ((group ^ ((row >> 3) & 7)) << 4);
+}
+
+// WALK = false: one tile per workgroup (XCD-contiguous mapping), registers
+// capped for MINW waves per SIMD; WALK = true: a resident grid walks runs
+// of tiles, loading the next tile's codes while it encodes the current one.
+template <bool SR, bool TILE2D, bool WALK, int MINW>
+__global__ __launch_bounds__(kQT, MINW) void requant_kernel(RequantParams p) {
+    __shared__ __align__(16) RequantLds L;
     const int64_t tiles_c = (p.C + kReqC - 1) / kReqC;
     const int64_t T = ((p.R + kReqR - 1) / kReqR) * tiles_c;
-    const int64_t tile = xcd_tile(blockIdx.x, T);
-    const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r0 = tr * kReqR + w * 32, c0 = tc * kReqC + lane * 8;
-    if (r0 >= p.R || c0 >= p.C) return;              // no barriers or lane exchange below
     const float s_dec = p.s_dec[0];
     const int64_t nsb = p.C / 16;                    // scale bytes per scale row
+    constexpr int NB = TILE2D ? 2 : 32;              // block scales per lane
 
-    uint32_t cw[32];                                 // 8 nibbles of each source row
-    float bs[TILE2D ? 2 : 32];                       // E4M3 block scales, decoded
+    // Source of tile t for this lane: 32 rows x 8 columns (invalid pieces
+    // read a valid piece and store nothing).
+    struct Src {
+        int64_t r0, c0;
+        bool in;
+    };
+    auto src_of = [&](int64_t tile) -> Src {
+        const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
+        Src s;
+        s.r0 = tr * kReqR + w * 32;
+        s.c0 = tc * kReqC + lane * 8;
+        s.in = s.r0 < p.R && s.c0 < p.C;
+        return s;
+    };
+    auto load = [&](const Src &s, uint32_t (&cw)[32], uint32_t (&sb)[NB]) {
+        const int64_t r0 = s.r0 < p.R ? s.r0 : p.R - 32;
+        const int64_t c0 = s.c0 < p.C ? s.c0 : p.C - 8;
 #pragma unroll
-    for (int r = 0; r < 32; ++r)
-        cw[r] = *reinterpret_cast<const uint32_t *>(p.codes + (r0 + r) * (p.C / 2) + c0 / 2);
+        for (int r = 0; r < 32; ++r)
+            cw[r] = *reinterpret_cast<const uint32_t *>(p.codes + (r0 + r) * (p.C / 2) + c0 / 2);
 #pragma unroll
-    for (int i = 0; i < (TILE2D ? 2 : 32); ++i) {
-        const int64_t srow = TILE2D ? r0 / 16 + i : r0 + i;
-        bs[i] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)p.scales[srow * nsb + c0 / 16], 1.0f, 0);
-    }
+        for (int i = 0; i < NB; ++i) {
+            const int64_t srow = TILE2D ? r0 / 16 + i : r0 + i;
+            sb[i] = p.scales[srow * nsb + c0 / 16];
+        }
+    };
 
-    auto emit = [&](const float (&x)[32], int64_t c) {
-        float a = 0.0f;
+    const TileWalk walk = WALK ? xcd_walk(T) : TileWalk{xcd_tile(blockIdx.x, T), xcd_tile(blockIdx.x, T) + 1, 1};
+    uint32_t cw[32], sb[NB];
+    Src s = src_of(walk.first < walk.end ? walk.first : 0);
+    if (walk.first < walk.end) load(s, cw, sb);
+    for (int64_t t = walk.first; t < walk.end; t += walk.step) {    // workgroup-uniform
+        const int64_t tn = t + walk.step;
+        uint32_t cwn[WALK ? 32 : 1], sbn[WALK ? NB : 1];
+        Src sn = s;
+        if (WALK && tn < walk.end) {
+            sn = src_of(tn);
+            load(sn, *reinterpret_cast<uint32_t(*)[32]>(cwn), *reinterpret_cast<uint32_t(*)[NB]>(sbn));
+        }
+        float bs[NB];
 #pragma unroll
-        for (int r = 0; r < 32; ++r) a = fmaxf(a, fabsf(x[r]));
-        const int k = e8m0_k(a);
-        uint32_t out[8];
+        for (int i = 0; i < NB; ++i) bs[i] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sb[i], 1.0f, 0);
+        // destination row (in the tile) lane * 8 + j, bytes w * 32 .. + 31
+        auto emit = [&](const float (&x)[32], int j) {
+            float a = 0.0f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float y[8];
+            for (int r = 0; r < 32; ++r) a = fmaxf(a, fabsf(x[r]));
+            const uint32_t kb = e8m0_byte(a);
+            float y[32];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = ldexpf(x[8 * g + i], -k);   // exact
-            if (SR) {
-                uint32_t wd[4];
-                sr_block(p.seed, p.stream, (uint64_t)(c * p.R + r0) / 8 + g, wd);
-                out[2 * g] = e4m3_sr4(y[0], y[1], y[2], y[3], sr_word_lo(wd[0]), sr_word_hi(wd[0]),
-                                      sr_word_lo(wd[1]), sr_word_hi(wd[1]));
-                out[2 * g + 1] = e4m3_sr4(y[4], y[5], y[6], y[7], sr_word_lo(wd[2]),
-                                          sr_word_hi(wd[2]), sr_word_lo(wd[3]), sr_word_hi(wd[3]));
-            } else {
-                out[2 * g] = e4m3_rne4(y[0], y[1], y[2], y[3]);
-                out[2 * g + 1] = e4m3_rne4(y[4], y[5], y[6], y[7]);
+            for (int r = 0; r < 32; ++r) y[r] = x[r];
+            if (__builtin_amdgcn_ballot_w64(kb == 0)) {   // rare, wave-uniform test
+                if (kb == 0) {                             // 2^-127: convert 2y at 2^-126
+#pragma unroll
+                    for (int r = 0; r < 32; ++r) y[r] = y[r] * 2.0f;
+                }
+            }
+            const float cs = e8m0_cvt_scale(kb);
+            const int64_t c = s.c0 + j;                  // destination row
+            uint32_t out[8];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if constexpr (SR) {
+                    uint32_t wd[4];
+                    sr_block(p.seed, p.stream, (uint64_t)(c * p.R + s.r0) / 8 + g, wd);
+                    out[2 * g] = e4m3_sr4_scaled(y[8 * g], y[8 * g + 1], y[8 * g + 2], y[8 * g + 3],
+                                                 sr_word_lo(wd[0]), sr_word_hi(wd[0]),
+                                                 sr_word_lo(wd[1]), sr_word_hi(wd[1]), cs);
+                    out[2 * g + 1] = e4m3_sr4_scaled(y[8 * g + 4], y[8 * g + 5], y[8 * g + 6],
+                                                     y[8 * g + 7], sr_word_lo(wd[2]),
+                                                     sr_word_hi(wd[2]), sr_word_lo(wd[3]),
+                                                     sr_word_hi(wd[3]), cs);
+                } else {
+                    out[2 * g] = e4m3_rne4_scaled(y[8 * g], y[8 * g + 1], y[8 * g + 2], y[8 * g + 3], cs);
+                    out[2 * g + 1] = e4m3_rne4_scaled(y[8 * g + 4], y[8 * g + 5], y[8 * g + 6],
+                                                      y[8 * g + 7], cs);
+                }
+            }
+            const int drow = lane * 8 + j;
+            *reinterpret_cast<uint4 *>(L.codes + req_off(drow, 2 * w)) =
+                make_uint4(out[0], out[1], out[2], out[3]);
+            *reinterpret_cast<uint4 *>(L.codes + req_off(drow, 2 * w + 1)) =
+                make_uint4(out[4], out[5], out[6], out[7]);
+            L.scales[drow * 4 + w] = (uint8_t)kb;
+        };
+        auto pair = [&](auto jp_tag) {                   // source columns 2jp, 2jp + 1
+            constexpr int jp = decltype(jp_tag)::value;
+            float xe[32], xo[32];
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                const f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[r], 1.0f, jp);
+                const float b = bs[TILE2D ? r / 16 : r];
+                // (E2M1 x E4M3) is exact; the multiply by s_dec is one FP32 rounding.
+                xe[r] = (e[0] * b) * s_dec;
+                xo[r] = (e[1] * b) * s_dec;
+            }
+            emit(xe, 2 * jp);
+            emit(xo, 2 * jp + 1);
+        };
+        pair(std::integral_constant<int, 0>{});
+        pair(std::integral_constant<int, 1>{});
+        pair(std::integral_constant<int, 2>{});
+        pair(std::integral_constant<int, 3>{});
+        __syncthreads();
+        // 512 destination rows x 8 groups of 16 bytes: 16 passes of 256 threads;
+        // then 512 x 4 scale bytes
+        {
+            const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
+            const int64_t R0 = tr * kReqR, C0 = tc * kReqC;
+            const int64_t drows = p.C - C0 < kReqC ? p.C - C0 : kReqC;
+            const int64_t groups = (p.R - R0) / 16 < 8 ? (p.R - R0) / 16 : 8;   // R % 32 == 0
+#pragma unroll 4
+            for (int i = 0; i < 16; ++i) {
+                const int idx = i * kQT + threadIdx.x, drow = idx >> 3, g = idx & 7;
+                if (drow < drows && g < groups)
+                    *reinterpret_cast<uint4 *>(p.out_codes + (C0 + drow) * p.R + R0 + g * 16) =
+                        *reinterpret_cast<const uint4 *>(L.codes + req_off(drow, g));
+            }
+            const int64_t nsc = (p.R - R0) / 32 < 4 ? (p.R - R0) / 32 : 4;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int drow = i * kQT + threadIdx.x;
+                if (drow < drows)
+                    put_run<4>(p.out_scales + (C0 + drow) * (p.R / 32) + R0 / 32, L.scales + drow * 4,
+                               nsc);
             }
         }
-        uint4 *dst = reinterpret_cast<uint4 *>(p.out_codes + c * p.R + r0);
-        dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-        dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-        p.out_scales[c * (p.R / 32) + r0 / 32] = (uint8_t)(k + 127);
-    };
-
-    auto pair = [&](auto jp_tag) {                   // source columns 2jp, 2jp + 1
-        constexpr int jp = decltype(jp_tag)::value;
-        float xe[32], xo[32];
+        __syncthreads();
+        if constexpr (WALK) {
+            s = sn;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[r], 1.0f, jp);
-            const float b = bs[TILE2D ? r / 16 : r];
-            // (E2M1 x E4M3) is exact; the multiply by s_dec is one FP32 rounding.
-            xe[r] = (e[0] * b) * s_dec;
-            xo[r] = (e[1] * b) * s_dec;
+            for (int r = 0; r < 32; ++r) cw[r] = cwn[r];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) sb[i] = sbn[i];
         }
-        emit(xe, c0 + 2 * jp);
-        emit(xo, c0 + 2 * jp + 1);
-    };
-    pair(std::integral_constant<int, 0>{});
-    pair(std::integral_constant<int, 1>{});
-    pair(std::integral_constant<int, 2>{});
-    pair(std::integral_constant<int, 3>{});
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -726,11 +963,31 @@ __global__ __launch_bounds__(kQT) void mx4_quant_kernel(const uint16_t *__restri
 // Host-side launchers (called by the C ABI after argument checks).
 // ---------------------------------------------------------------------------
 
+// Workgroups of a persistent launch of `kernel` (kQT threads): as many as
+// are resident on the stream's device at once, at most `tiles`, at least 1.
+// The occupancy per CU is the kernel's and is looked up once (thread-safe
+// static initialisation).
+template <auto Kernel>
+static int persistent_grid(int64_t tiles, hipStream_t s) {
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kQT, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    const int64_t g = (int64_t)per_cu * device_cus(s);
+    return (int)(tiles < g ? (tiles < 1 ? 1 : tiles) : g);
+}
+
 hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
                        uint32_t signs, float *part, float *part_rht, int *n_part,
                        hipStream_t s, float *gelu_tab) {
-    const int64_t T = ((R + kTileR - 1) / kTileR) * ((C + kTileC - 1) / kTileC);
-    const int grid = (int)(T < kAmaxGrid ? T : kAmaxGrid);
+    // one wave per 16 x 512 step; up to 1024 workgroups (2048 with the RHT
+    // maximum alone, whose butterflies make the read slower per byte)
+    const int64_t steps = (R / 16) * ((C + kAmaxStepC - 1) / kAmaxStepC);
+    const int64_t cap = (rht && !plain) ? kAmaxPartials : kAmaxPartials / 2;
+    const int64_t want = (steps + kQT / 64 - 1) / (kQT / 64);
+    const int grid = (int)(want < cap ? want : cap);
     *n_part = grid;
     if (gelu_tab) {
         if (rht || !plain) return hipErrorInvalidValue;
@@ -759,43 +1016,72 @@ hipError_t launch_gelu_table(float *gelu_tab, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The encode kernel variants the library launches (timed per variant):
+// copies rounding to nearest with 16x16 tiles (weights) are light on ALU
+// work and walk runs of tiles at two waves per SIMD, loading ahead; the
+// others take one tile per workgroup with registers capped for four waves
+// per SIMD (three where four would spill: row + column copies without the
+// RHT).
+template <bool T_, bool SR_>
+constexpr bool quant_walk() { return T_ && !SR_; }
+template <bool R_, bool C_, bool M_, bool T_, bool H_, bool SR_>
+constexpr int quant_min_waves() {
+    if (T_) return SR_ ? 3 : 2;
+    if (R_ && C_ && !H_ && SR_) return 3;
+    return 4;
+}
+
+template <bool R_, bool C_, bool M_, bool T_, bool H_, bool G_, bool SR_, bool W_, int MW_>
+static void launch_qk(const QuantParams &p, hipStream_t s) {
+    const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
+    constexpr auto k = quant_kernel<R_, C_, M_, T_, H_, G_, SR_, W_, MW_>;
+    const int grid = W_ ? persistent_grid<k>(T, s) : (int)T;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kQT), 0, s, p);
+}
+
 template <bool R_, bool C_, bool M_, bool T_, bool H_, bool G_ = false>
-static void launch_q(const QuantParams &p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((quant_kernel<R_, C_, M_, T_, H_, G_>), grid, dim3(kQT), 0, s, p);
+static void launch_q(const QuantParams &p, bool sr, hipStream_t s) {
+    if (sr)
+        launch_qk<R_, C_, M_, T_, H_, G_, true, quant_walk<T_, true>(),
+                  quant_min_waves<R_, C_, M_, T_, H_, true>()>(p, s);
+    else
+        launch_qk<R_, C_, M_, T_, H_, G_, false, quant_walk<T_, false>(),
+                  quant_min_waves<R_, C_, M_, T_, H_, false>()>(p, s);
 }
 
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
                              bool tile2d, bool rht, hipStream_t s, bool gelu) {
-    const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
-    const dim3 grid((unsigned)T);
+    // the stochastic paths are compiled only into the variant that needs them
+    const bool sr = (has_row && p.row_round == 1) || (has_col && p.col_round == 1) ||
+                    (has_mx && p.mx_round == 1);
     if (gelu) {
         if (has_col || tile2d || rht) return hipErrorInvalidValue;
-        if (has_row && has_mx) launch_q<1, 0, 1, 0, 0, 1>(p, grid, s);
-        else if (has_row) launch_q<1, 0, 0, 0, 0, 1>(p, grid, s);
-        else if (has_mx) launch_q<0, 0, 1, 0, 0, 1>(p, grid, s);
+        if (has_row && has_mx) launch_q<1, 0, 1, 0, 0, 1>(p, sr, s);
+        else if (has_row) launch_q<1, 0, 0, 0, 0, 1>(p, sr, s);
+        else if (has_mx) launch_q<0, 0, 1, 0, 0, 1>(p, sr, s);
         else return hipErrorInvalidValue;
         return hipGetLastError();
     }
     // The combinations the quantizer supports (RHT only on a 1x16 column copy).
     const int key = (has_row << 4) | (has_col << 3) | (has_mx << 2) | (tile2d << 1) | rht;
     switch (key) {
-        case 0b10000: launch_q<1, 0, 0, 0, 0>(p, grid, s); break;
-        case 0b10010: launch_q<1, 0, 0, 1, 0>(p, grid, s); break;
-        case 0b11000: launch_q<1, 1, 0, 0, 0>(p, grid, s); break;
-        case 0b11010: launch_q<1, 1, 0, 1, 0>(p, grid, s); break;
-        case 0b11001: launch_q<1, 1, 0, 0, 1>(p, grid, s); break;
-        case 0b01000: launch_q<0, 1, 0, 0, 0>(p, grid, s); break;
-        case 0b01010: launch_q<0, 1, 0, 1, 0>(p, grid, s); break;
-        case 0b01001: launch_q<0, 1, 0, 0, 1>(p, grid, s); break;
-        case 0b00100: launch_q<0, 0, 1, 0, 0>(p, grid, s); break;
-        case 0b10100: launch_q<1, 0, 1, 0, 0>(p, grid, s); break;
-        case 0b10110: launch_q<1, 0, 1, 1, 0>(p, grid, s); break;
-        case 0b01100: launch_q<0, 1, 1, 0, 0>(p, grid, s); break;
-        case 0b01101: launch_q<0, 1, 1, 0, 1>(p, grid, s); break;
-        case 0b11100: launch_q<1, 1, 1, 0, 0>(p, grid, s); break;
-        case 0b11101: launch_q<1, 1, 1, 0, 1>(p, grid, s); break;
-        case 0b01110: launch_q<0, 1, 1, 1, 0>(p, grid, s); break;
-        case 0b11110: launch_q<1, 1, 1, 1, 0>(p, grid, s); break;
+        case 0b10000: launch_q<1, 0, 0, 0, 0>(p, sr, s); break;
+        case 0b10010: launch_q<1, 0, 0, 1, 0>(p, sr, s); break;
+        case 0b11000: launch_q<1, 1, 0, 0, 0>(p, sr, s); break;
+        case 0b11010: launch_q<1, 1, 0, 1, 0>(p, sr, s); break;
+        case 0b11001: launch_q<1, 1, 0, 0, 1>(p, sr, s); break;
+        case 0b01000: launch_q<0, 1, 0, 0, 0>(p, sr, s); break;
+        case 0b01010: launch_q<0, 1, 0, 1, 0>(p, sr, s); break;
+        case 0b01001: launch_q<0, 1, 0, 0, 1>(p, sr, s); break;
+        case 0b00100: launch_q<0, 0, 1, 0, 0>(p, sr, s); break;
+        case 0b10100: launch_q<1, 0, 1, 0, 0>(p, sr, s); break;
+        case 0b10110: launch_q<1, 0, 1, 1, 0>(p, sr, s); break;
+        case 0b01100: launch_q<0, 1, 1, 0, 0>(p, sr, s); break;
+        case 0b01101: launch_q<0, 1, 1, 0, 1>(p, sr, s); break;
+        case 0b11100: launch_q<1, 1, 1, 0, 0>(p, sr, s); break;
+        case 0b11101: launch_q<1, 1, 1, 0, 1>(p, sr, s); break;
+        case 0b01110: launch_q<0, 1, 1, 1, 0>(p, sr, s); break;
+        case 0b11110: launch_q<1, 1, 1, 1, 0>(p, sr, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -821,13 +1107,24 @@ hipError_t launch_quant_act(const QuantParams &p, bool per_token, bool four_six,
     return hipGetLastError();
 }
 
-hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s) {
+template <bool SR, bool TILE2D, bool WALK, int MINW>
+static void launch_rqk(const RequantParams &p, hipStream_t s) {
     const int64_t T = ((p.R + kReqR - 1) / kReqR) * ((p.C + kReqC - 1) / kReqC);
-    const dim3 grid((unsigned)T);
-    if (sr && p.tile2d) hipLaunchKernelGGL((requant_kernel<true, true>), grid, dim3(kQT), 0, s, p);
-    else if (sr) hipLaunchKernelGGL((requant_kernel<true, false>), grid, dim3(kQT), 0, s, p);
-    else if (p.tile2d) hipLaunchKernelGGL((requant_kernel<false, true>), grid, dim3(kQT), 0, s, p);
-    else hipLaunchKernelGGL((requant_kernel<false, false>), grid, dim3(kQT), 0, s, p);
+    constexpr auto k = requant_kernel<SR, TILE2D, WALK, MINW>;
+    hipLaunchKernelGGL(k, dim3(WALK ? persistent_grid<k>(T, s) : (int)T), dim3(kQT), 0, s, p);
+}
+
+// The requantizer variant the library launches: one tile per workgroup,
+// registers capped for four waves per SIMD (walking runs of tiles at two
+// waves per SIMD measured 36% slower).
+constexpr bool kReqWalk = false;
+constexpr int kReqMinW = 4;
+
+hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s) {
+    if (sr && p.tile2d) launch_rqk<true, true, kReqWalk, kReqMinW>(p, s);
+    else if (sr) launch_rqk<true, false, kReqWalk, kReqMinW>(p, s);
+    else if (p.tile2d) launch_rqk<false, true, kReqWalk, kReqMinW>(p, s);
+    else launch_rqk<false, false, kReqWalk, kReqMinW>(p, s);
     return hipGetLastError();
 }
 

@@ -203,3 +203,78 @@ extern "C" int probe_gelu(const float *x, int n, float *g, float *e) {
     hipLaunchKernelGGL(gelu_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, x, n, g, e);
     return (int)hipDeviceSynchronize();
 }
+
+// The quantizers' a / 6 (bbs::div6: constant reciprocal and one FMA
+// correction) against IEEE division over every non-negative finite FP32 a
+// (bit patterns 0 .. 0x7F7FFFFF); mismatches are counted.
+__global__ void div6_kernel(unsigned long long *bad) {
+    unsigned long long cnt = 0;
+    for (uint64_t u = blockIdx.x * 256ull + threadIdx.x; u <= 0x7F7FFFFFull;
+         u += (uint64_t)gridDim.x * 256ull) {
+        const float a = __uint_as_float((uint32_t)u);
+        if (__float_as_uint(bbs::div6(a)) != __float_as_uint(a / 6.0f)) ++cnt;
+    }
+    if (cnt) atomicAdd(bad, cnt);
+}
+
+// The MXFP8 exponent from the FP32 bits (bbs::e8m0_byte) against the frexp
+// form of the rule (bbs::e8m0_k + 127) over every non-negative finite FP32.
+__global__ void e8m0_kernel(unsigned long long *bad) {
+    unsigned long long cnt = 0;
+    for (uint64_t u = blockIdx.x * 256ull + threadIdx.x; u <= 0x7F7FFFFFull;
+         u += (uint64_t)gridDim.x * 256ull) {
+        const float a = __uint_as_float((uint32_t)u);
+        if (bbs::e8m0_byte(a) != (uint32_t)(bbs::e8m0_k(a) + 127)) ++cnt;
+    }
+    if (cnt) atomicAdd(bad, cnt);
+}
+
+// FP8 conversions at scale 2^k (as the MXFP8 copies issue them, with the
+// 2^-127 blocks doubled and converted at 2^-126) against the value divided
+// by 2^k with ldexp and converted at scale 1.0, for every E8M0 byte 0..254
+// and `per` hashed values x (|x 2^-k| <= 448, magnitudes from 2^-30 up) and
+// random operands per byte; bad[0] counts stochastic mismatches, bad[1]
+// nearest-even ones.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t h) {
+    h ^= h >> 16; h *= 0x7feb352du; h ^= h >> 15; h *= 0x846ca68bu; h ^= h >> 16;
+    return h;
+}
+__global__ void fp8_scale_kernel(int per, unsigned long long *bad) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= 255 * per) return;
+    const uint32_t kb = (uint32_t)(i / per);
+    const int k = (int)kb - 127;
+    const uint32_t h1 = probe_hash(2u * i + 1u), h2 = probe_hash(2u * i + 2u);
+    int e = (int)(h1 % 39u) - 30;                          // |x 2^-k| in [2^-30, 2^9)
+    if (e + k > 126) e = 126 - k;                          // x stays finite
+    float t = ldexpf(1.0f + (h2 >> 9) * 0x1p-23f, e);
+    t = fminf(t, 448.0f);
+    if (h1 & 1u) t = -t;
+    const float x = ldexpf(t, k);                          // exact unless x is an FP32 subnormal
+    const float xr = ldexpf(x, -k);                        // the value the copy must round
+    const uint32_t r = probe_hash(i * 7u + 11u);
+    const float y = kb == 0 ? x * 2.0f : x;
+    const float cs = bbs::e8m0_cvt_scale(kb);
+    const int a = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, xr, r, 1.0f, 0) & 0xFF;
+    const int b = __builtin_amdgcn_cvt_scalef32_sr_fp8_f32(0, y, r, cs, 0) & 0xFF;
+    const i16x2 ra = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, xr, 0.0f, 1.0f, false);
+    const i16x2 rb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, y, 0.0f, cs, false);
+    if (a != b) atomicAdd(&bad[0], 1ull);
+    if ((ra[0] & 0xFF) != (rb[0] & 0xFF)) atomicAdd(&bad[1], 1ull);
+}
+
+extern "C" {
+int probe_div6(unsigned long long *bad) {
+    hipLaunchKernelGGL(div6_kernel, dim3(8192), dim3(256), 0, 0, bad);
+    return (int)hipDeviceSynchronize();
+}
+int probe_e8m0(unsigned long long *bad) {
+    hipLaunchKernelGGL(e8m0_kernel, dim3(8192), dim3(256), 0, 0, bad);
+    return (int)hipDeviceSynchronize();
+}
+int probe_fp8_scale(int per, unsigned long long *bad) {
+    const int n = 255 * per;
+    hipLaunchKernelGGL(fp8_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, per, bad);
+    return (int)hipDeviceSynchronize();
+}
+}

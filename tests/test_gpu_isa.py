@@ -232,3 +232,34 @@ def test_fp4_to_f16_scale_uses_exponent_only(probe):
         lo = (r[si] & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
         p2 = 2.0 ** np.floor(np.log2(s))
         assert np.array_equal(lo, dec[np.arange(256) & 15] * p2), s
+
+
+def test_div6_equals_ieee_division_everywhere(probe):
+    """The block scale's amax / 6 is taken as q = a RN(1/6) plus one FMA
+    correction (exact below 2^-124 by a division): it must equal the
+    correctly rounded quotient for every non-negative finite FP32 a."""
+    announce("div6 vs IEEE a / 6 over all 2^31 non-negative FP32")
+    bad = torch.zeros(1, dtype=torch.int64, device=dev())
+    assert probe.probe_div6(C.c_void_p(bad.data_ptr())) == 0
+    assert int(bad.item()) == 0
+
+
+def test_e8m0_byte_equals_frexp_rule(probe):
+    """The MXFP8 scale byte from the FP32 bits equals k + 127 of the rule
+    'smallest k with amax <= 448 * 2^k' (clamped) for every amax."""
+    announce("e8m0_byte vs frexp rule over all 2^31 non-negative FP32")
+    bad = torch.zeros(1, dtype=torch.int64, device=dev())
+    assert probe.probe_e8m0(C.c_void_p(bad.data_ptr())) == 0
+    assert int(bad.item()) == 0
+
+
+def test_fp8_conversion_scale_divides_exactly(probe):
+    """v_cvt_scalef32_sr_fp8_f32 / v_cvt_scalef32_pk_fp8_f32 at scale 2^k
+    round x / 2^k (exactly scaled) as the same instruction rounds
+    ldexp(x, -k) at scale 1.0: the MXFP8 copies pass their block's power of
+    two as the conversion scale (byte 0 as 2x at 2^-126), for every byte."""
+    announce("FP8 conversions at scale 2^k, k = -127 .. 127")
+    bad = torch.zeros(2, dtype=torch.int64, device=dev())
+    assert probe.probe_fp8_scale(4096, C.c_void_p(bad.data_ptr())) == 0
+    sr_bad, rne_bad = (int(v) for v in bad.cpu())
+    assert sr_bad == 0 and rne_bad == 0, (sr_bad, rne_bad)
