@@ -346,7 +346,10 @@ constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_Q = 2, OUT_QG = 3, OUT_S2F6 = 4;
 // the same staging rows: wait for its LDS operations and fence the compiler.
 __device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int OUT, typename ScaleFn>
+// DROP: output rows may be dropped slots of a grouped GEMM, whose scale is
+// 0; adding +0 turns their -0 products into +0, so they come out as the
+// zero rows (and zero blocks) the header promises.
+template <int OUT, bool DROP, typename ScaleFn>
 __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
                                          const f32x16 (&acc)[4][4], int64_t m0, int64_t m_end,
                                          int64_t n0, int64_t n_end, ScaleFn scale_of, void *C,
@@ -389,10 +392,16 @@ __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int c = j * 32 + 8 * g + 4 * (lane >> 5);
-                        const float y0 = acc[i][j][4 * g] * out_scale;
-                        const float y1 = acc[i][j][4 * g + 1] * out_scale;
-                        const float y2 = acc[i][j][4 * g + 2] * out_scale;
-                        const float y3 = acc[i][j][4 * g + 3] * out_scale;
+                        float y0 = acc[i][j][4 * g] * out_scale;
+                        float y1 = acc[i][j][4 * g + 1] * out_scale;
+                        float y2 = acc[i][j][4 * g + 2] * out_scale;
+                        float y3 = acc[i][j][4 * g + 3] * out_scale;
+                        if constexpr (DROP) {
+                            y0 = y0 + 0.0f;
+                            y1 = y1 + 0.0f;
+                            y2 = y2 + 0.0f;
+                            y3 = y3 + 0.0f;
+                        }
                         if constexpr (BF16_OUT)
                             *reinterpret_cast<uint2 *>(row + c * 2) =
                                 make_uint2(pk_bf16(y0, y1), pk_bf16(y2, y3));
@@ -514,7 +523,7 @@ struct TileRef {
 //   b_view(g)              group g's B operand
 //   a_row(m)               source row of A for output row m (< 0: none)
 //   scale_of(m, g)         output scale of row m in group g's tile
-template <int OUT, bool BT, typename Next, typename BView, typename RowMap, typename ScaleFn>
+template <int OUT, bool BT, bool DROP, typename Next, typename BView, typename RowMap, typename ScaleFn>
 __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams &p,
                                           Next next_tile, BView b_view, RowMap a_row,
                                           ScaleFn scale_of) {
@@ -642,7 +651,7 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
         // every wave is done reading stage cs: it becomes the staging area
         __syncthreads();
         const int g = cur.g;
-        epilogue<OUT>(reinterpret_cast<uint8_t *>(&sm.st[cs]), tab, acc, cur.m0, cur.m_end,
+        epilogue<OUT, DROP>(reinterpret_cast<uint8_t *>(&sm.st[cs]), tab, acc, cur.m0, cur.m_end,
                       cur.n0, N, [&](int64_t m) { return scale_of(m, g); }, p.c, p.ldc, wm, wn,
                       lane, p.q);
         if (!more) break;
@@ -705,9 +714,9 @@ __device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_ra
     const float sb = p.b.s_dec[0];
     auto run = [&](auto scale_of) {
         if (p.b.tile2d)
-            big::run_tiles<OUT, true>(sm, tab, p, next_tile, b_view, ident, scale_of);
+            big::run_tiles<OUT, true, false>(sm, tab, p, next_tile, b_view, ident, scale_of);
         else
-            big::run_tiles<OUT, false>(sm, tab, p, next_tile, b_view, ident, scale_of);
+            big::run_tiles<OUT, false, false>(sm, tab, p, next_tile, b_view, ident, scale_of);
     };
     if (p.a.sdec_rows) {
         const float *sa = p.a.s_dec;
@@ -790,20 +799,22 @@ __device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_
     const float *sdb = p.b.s_dec;
     auto run = [&](auto scale_of) {
         if (B0.tile2d)
-            big::run_tiles<OUT, true>(sm, tab, p, next_tile, b_view, gather, scale_of);
+            big::run_tiles<OUT, true, true>(sm, tab, p, next_tile, b_view, gather, scale_of);
         else
-            big::run_tiles<OUT, false>(sm, tab, p, next_tile, b_view, gather, scale_of);
+            big::run_tiles<OUT, false, true>(sm, tab, p, next_tile, b_view, gather, scale_of);
     };
+    // the output scale of row m: the decode scale of the A row it was
+    // computed from times the expert's; 0 for a dropped slot (its copies
+    // read A row 0 in place of a row the map misses)
     if (p.a.sdec_rows) {
         const float *sa = p.a.s_dec;
-        // the decode scale of the A row the output row was computed from
         run([sa, sdb, gather](int64_t m, int g) {
             const int64_t s = gather(m);
-            return sa[s < 0 ? 0 : s] * sdb[g];
+            return s < 0 ? 0.0f : sa[s] * sdb[g];
         });
     } else {
         const float sa0 = p.a.s_dec[0];
-        run([sa0, sdb](int64_t, int g) { return sa0 * sdb[g]; });
+        run([sa0, sdb, gather](int64_t m, int g) { return gather(m) < 0 ? 0.0f : sa0 * sdb[g]; });
     }
 }
 

@@ -11,7 +11,8 @@ forward   X -> NVFP4 rows (1x16, nearest) for the forward GEMM, and the
 backward  dY -> the NVFP4 copy of dY^T (RHT, stochastic) and the MXFP8 rows
           of dY (stochastic); W's NVFP4 copy -> MXFP8 of W^T (stochastic);
           dX = dY W (MXFP8 GEMM, BF16 out); dW = dY^T X (NVFP4 GEMM over the
-          two RHT'd copies, FP32 out).
+          two RHT'd copies, FP32 accumulation, written by the kernel in the
+          weight's dtype: BF16, nearest even, or FP32).
 
 Every step runs in the library's kernels; this module only allocates the
 outputs and passes pointers.  The stochastic roundings of call t draw from
@@ -73,9 +74,14 @@ class QLinearFn(torch.autograd.Function):
         mxfp8_requantize_t(wq, wt, SR, (seed, 4 * step + 3))
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         nvfp4_gemm(FMT_MXFP8, gm, wt, dx.view(torch.int16), OUT_BF16)
-        dw = torch.empty((N, K), dtype=torch.float32, device=dev)
-        nvfp4_gemm(FMT_NVFP4, gc, xc, dw, OUT_F32)
-        return dx.reshape(*lead, K), dw.to(wdtype), None, None, None
+        if wdtype == torch.bfloat16:
+            dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+            nvfp4_gemm(FMT_NVFP4, gc, xc, dw.view(torch.int16), OUT_BF16)
+        else:
+            dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+            nvfp4_gemm(FMT_NVFP4, gc, xc, dw, OUT_F32)
+            dw = dw.to(wdtype)
+        return dx.reshape(*lead, K), dw, None, None, None
 
 
 class QLinear(torch.nn.Module):

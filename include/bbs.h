@@ -24,7 +24,9 @@
  *  - Calls are thread-safe.  Calls on one stream run in order.
  *  - Precondition of the quantizers: finite inputs, and a tensor amax that
  *    is either 0 or at least 2^-100 (smaller non-zero maxima overflow the
- *    FP32 encode scales; the result is then unspecified).
+ *    FP32 encode scales; the result is then unspecified).  With the RHT the
+ *    transformed values must be finite too (|x| < 2^126 suffices: a 16-point
+ *    transform grows a magnitude by at most 4x).
  */
 #ifndef BBS_H
 #define BBS_H
@@ -224,7 +226,11 @@ int nvfp4_gemm(int32_t fmt, const void *A, const void *B, void *C, int32_t c_dty
  * expert g, rows [group_offsets[g], group_offsets[g+1]) of the routed
  * activations times expert g's weights:
  *   C[i, :] = A_row(i) * B_g^T,   B_g = rows [g*N, (g+1)*N) of B, s_dec = B.s_dec[g]
- * A_row(i) is row row_index[i] of A, or row i when row_index is NULL.
+ * A_row(i) is row row_index[i] of A, or row i when row_index is NULL.  A
+ * dropped slot, i.e. a row_index entry that is negative or >= A.rows (or,
+ * with row_index NULL, a routed row i >= A.rows), gives an output row of +0
+ * (in the quantizing and encoding variants: the encode of a zero row, which
+ * also leaves the reported amax unchanged).
  * group_offsets: device array of G+1 non-decreasing int64 (offsets[0] = 0);
  * empty groups are allowed.  max_rows bounds the routed rows C can hold
  * (rows beyond it are not computed).  B.rows == G * N, N % 16 == 0.

@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from gpu_util import announce, bf16_bits_to_f64, dev, host, to_dev, upload_mxfp8, upload_nvfp4
+from gpu_util import (accumulation_bound, announce, bf16_bits_to_f64, check_bounded_outputs, dev,
+                      host, tile_samples, to_dev, upload_mxfp8, upload_nvfp4)
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -92,13 +93,17 @@ def test_random_operands(bbs, M, N, K, ta, tb, bf16):
     _check(y, O.gemm_f64(a.dequant_f64(), b.dequant_f64()), bf16, "random")
 
 
-def _sampled_check(y_full, A64, B64, bf16, what, n=4096, seed=0):
+def _sampled_check(y_full, A64, B64, bf16, what, per_tile=4, seed=0):
+    """Sampled outputs of a full-size GEMM: per_tile outputs inside every
+    256 x 256 output tile, the whole last row and 2048 more at random, each
+    held to its accumulation bound against the FP64 sum (gpu_util); prints
+    the global relative error and the worst tile."""
     M, N = y_full.shape
-    rng = np.random.default_rng(seed)
-    rows = np.concatenate([rng.integers(0, M, n), np.full(N, M - 1), np.arange(N) * 0])
-    cols = np.concatenate([rng.integers(0, N, n), np.arange(N), np.arange(N)])
-    ref = O.gemm_f64_sampled(A64, B64, rows, cols)
-    return _check(y_full[rows, cols], ref, bf16, what)
+    rows, cols, tiles = tile_samples(M, N, per_tile, seed, extra=2048)
+    y64 = O.gemm_f64_sampled(A64, B64, rows, cols)
+    E = accumulation_bound(O.gemm_f64_sampled(np.abs(A64), np.abs(B64), rows, cols),
+                           A64.shape[1])
+    return check_bounded_outputs(y_full[rows, cols], y64, E, bf16, what, tiles)
 
 
 def test_full_dense_forward(bbs):
@@ -276,32 +281,55 @@ def _moe_operands(n_rows, k, experts, seed0):
     return ws, B, np.array([w.s_dec for w in ws], np.float32)
 
 
-def _moe_sampled_ref(A, a_rows, ws, offsets, rows, cols):
+def _moe_sampled_ref(A, a_rows, ws, offsets, rows, cols, chunk=4096):
     """FP64 reference of sampled outputs (rows, cols) of a grouped GEMM whose
-    routed row i reads A row a_rows[i] and expert g = the group holding i."""
+    routed row i reads A row a_rows[i] and expert g = the group holding i,
+    and the sum of |products| of each (for its accumulation bound)."""
     g_of = np.searchsorted(offsets, rows, side="right") - 1
-    toks = np.unique(a_rows[rows])
-    sub = O.NVFP4(np.ascontiguousarray(A.codes[toks]), np.ascontiguousarray(A.scales[toks]),
-                  A.s_dec, len(toks), A.cols, False).dequant_f64()
-    pos = {t: i for i, t in enumerate(toks)}
-    ref = np.zeros(rows.size)
-    for g in np.unique(g_of):
-        Bg = ws[g].dequant_f64()
-        sel = np.nonzero(g_of == g)[0]
-        arows = sub[[pos[t] for t in a_rows[rows[sel]]]]
-        ref[sel] = np.einsum("ij,ij->i", arows, Bg[cols[sel]])
+    ref, ab = np.zeros(rows.size), np.zeros(rows.size)
+    Bs = {}
+    for c0 in range(0, rows.size, chunk):
+        sl = slice(c0, c0 + chunk)
+        toks = np.unique(a_rows[rows[sl]])
+        sub = O.NVFP4(np.ascontiguousarray(A.codes[toks]), np.ascontiguousarray(A.scales[toks]),
+                      A.s_dec, len(toks), A.cols, False).dequant_f64()
+        pos = np.searchsorted(toks, a_rows[rows[sl]])
+        for g in np.unique(g_of[sl]):
+            if g not in Bs:
+                Bs[g] = ws[g].dequant_f64()
+            sel = np.nonzero(g_of[sl] == g)[0]
+            arows, brows = sub[pos[sel]], Bs[g][cols[sl][sel]]
+            ref[c0 + sel] = np.einsum("ij,ij->i", arows, brows)
+            ab[c0 + sel] = np.einsum("ij,ij->i", np.abs(arows), np.abs(brows))
     assert np.abs(ref).max() > 0
-    return ref
+    return ref, ab
 
 
-def _moe_samples(offsets, n_cols, seed, n=2048):
+def _moe_samples(offsets, n_cols, seed, per_tile=1, tile=256):
+    """Samples in every tile x tile output tile of every expert (the grouped
+    GEMM tiles each expert's rows from its own offset), plus each expert's
+    first and last row; returns rows, cols and a tile id per sample."""
     rng = np.random.default_rng(seed)
-    total = int(offsets[-1])
-    firsts = [offsets[g] for g in range(len(offsets) - 1) if offsets[g + 1] > offsets[g]]
-    lasts = [offsets[g + 1] - 1 for g in range(len(offsets) - 1) if offsets[g + 1] > offsets[g]]
-    rows = np.concatenate([rng.integers(0, total, n), firsts, lasts]).astype(np.int64)
-    cols = rng.integers(0, n_cols, rows.size).astype(np.int64)
-    return rows, cols
+    rows, cols, tiles = [], [], []
+    tn = (n_cols + tile - 1) // tile
+    tid = 0
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 <= r0:
+            continue
+        for m0 in range(r0, r1, tile):
+            m1 = min(m0 + tile, r1)
+            for tj in range(tn):
+                n0, n1 = tj * tile, min((tj + 1) * tile, n_cols)
+                rows.append(rng.integers(m0, m1, per_tile))
+                cols.append(rng.integers(n0, n1, per_tile))
+                tiles.append(np.full(per_tile, tid))
+                tid += 1
+        rows.append(np.array([r0, r1 - 1]))
+        cols.append(rng.integers(0, n_cols, 2))
+        tiles.append(np.array([tid - 1, tid - 1]))
+    return (np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64),
+            np.concatenate(tiles).astype(np.int64))
 
 
 def test_moe_full_size_sampled(bbs):
@@ -322,10 +350,11 @@ def test_moe_full_size_sampled(bbs):
     bbs.grouped_nvfp4_gemm(upload_nvfp4(ox, bbs), to_dev(ri), to_dev(off), E, R,
                            upload_nvfp4(B, bbs, n_scales=sdec), F, c, bbs.OUT_BF16)
     torch.cuda.synchronize()
-    rows, cols = _moe_samples(off, F, 11)
+    rows, cols, tiles = _moe_samples(off, F, 11)
     y = bf16_bits_to_f64(host(c[to_dev(rows), to_dev(cols)]).view(np.uint16))
     del c
-    _check(y, _moe_sampled_ref(ox, ri, ws, off, rows, cols), True, "moe-up")
+    ref, ab = _moe_sampled_ref(ox, ri, ws, off, rows, cols)
+    check_bounded_outputs(y, ref, accumulation_bound(ab, H), True, "moe-up", tiles)
     del ws, B
     # down-projection: synthetic stand-in for the routed hidden rows
     oh = O.nvfp4_quantize(synth.normal(R, F, 600, 1.0))
@@ -334,10 +363,11 @@ def test_moe_full_size_sampled(bbs):
     bbs.grouped_nvfp4_gemm(upload_nvfp4(oh, bbs), None, to_dev(off), E, R,
                            upload_nvfp4(B, bbs, n_scales=sdec), H, c, bbs.OUT_BF16)
     torch.cuda.synchronize()
-    rows, cols = _moe_samples(off, H, 12)
+    rows, cols, tiles = _moe_samples(off, H, 12)
     y = bf16_bits_to_f64(host(c[to_dev(rows), to_dev(cols)]).view(np.uint16))
     del c
-    _check(y, _moe_sampled_ref(oh, np.arange(R), ws, off, rows, cols), True, "moe-down")
+    ref, ab = _moe_sampled_ref(oh, np.arange(R), ws, off, rows, cols)
+    check_bounded_outputs(y, ref, accumulation_bound(ab, F), True, "moe-down", tiles)
 
 
 # ---------------------------------------------------------------------------
@@ -397,3 +427,42 @@ def test_grouped_per_token_A(bbs):
         if off[g + 1] > off[g]:
             ref[off[g]:off[g + 1]] = O.gemm_f64(A64[ri[off[g]:off[g + 1]]], ws[g].dequant_f64())
     _check(host(c).astype(np.float64), ref, False, "grouped per-token")
+
+
+@pytest.mark.parametrize("K,bf16", [(256, True), (256, False), (272, True)])
+def test_grouped_dropped_slots(bbs, K, bf16):
+    """row_index entries that are negative or >= A.rows (dropped MoE slots)
+    give +0 output rows, on the large-tile kernel (K % 128 == 0) and the
+    small-tile one (K = 272); the other rows are unaffected.  Unit scales
+    make every product exact, so the comparison is bit for bit."""
+    announce(f"grouped GEMM with dropped slots K={K} bf16={bf16}")
+    G, N, T = 3, 144, 64
+    a = _unit(T, K, 70, False)
+    counts = np.array([50, 0, 90])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = int(off[-1])
+    rng = np.random.default_rng(71)
+    ri = rng.integers(0, T, rows).astype(np.int32)
+    dropped = rng.choice(rows, 24, replace=False)
+    ri[dropped[:12]] = -1
+    ri[dropped[12:18]] = T
+    ri[dropped[18:]] = T + 1000
+    ws = [_unit(N, K, 80 + g, True) for g in range(G)]
+    B = O.NVFP4(np.concatenate([w.codes for w in ws]), np.concatenate([w.scales for w in ws]),
+                np.float32(1), G * N, K, True)
+    c = torch.full((rows, N), 7, dtype=torch.int16 if bf16 else torch.float32, device=dev())
+    bbs.grouped_nvfp4_gemm(upload_nvfp4(a, bbs), to_dev(ri), to_dev(off), G, rows,
+                           upload_nvfp4(B, bbs, n_scales=np.ones(G, np.float32)), N, c,
+                           bbs.OUT_BF16 if bf16 else bbs.OUT_F32)
+    torch.cuda.synchronize()
+    y = host(c)
+    A64 = a.dequant_f64()
+    ref = np.zeros((rows, N))
+    for g in range(G):
+        for i in range(off[g], off[g + 1]):
+            if 0 <= ri[i] < T:
+                ref[i] = A64[ri[i]] @ ws[g].dequant_f64().T
+    if bf16:
+        assert np.array_equal(y.view(np.uint16), (O.bf16_rne(ref).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    else:
+        assert np.array_equal(y.view(np.uint32), ref.astype(np.float32).view(np.uint32))

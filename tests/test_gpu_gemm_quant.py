@@ -7,16 +7,19 @@ FP32 products are exact (integer-valued codes with unit block scales and
 power-of-two decode scales) the codes, scales, decode scale and output amax
 must equal the oracle's encode of the exact product (rounded to BF16) bit for
 bit, with and without GELU.  Elsewhere the FP32 sum order is free, so a
-value lying at a rounding boundary may round either way: there the test
-bounds the fraction of code and scale bytes that differ from the oracle's
-encode of the FP64 product, and checks at full size that the fused kernel
-equals the library's own unfused GEMM + quantize bit for bit.
+value near a rounding boundary may round either way (two correct results,
+4bit.vizuara.ai section 13).  There every block that differs from the
+oracle's encode of the FP64 product must be the oracle's encode of a BF16
+row the FP32 accumulation could have produced: each value inside the BF16
+rounding of [y - E, y + E], E the accumulation bound (K + 4) 2^-24 sum |a b|
+(gpu_util.accumulation_bound).  No block may be left unexplained.
 """
 import numpy as np
 import pytest
 
 import oracle as O
-from gpu_util import announce, dev, host, to_dev, upload_nvfp4
+from gpu_util import (accumulation_bound, announce, bf16_from_key, bf16_window, dev, host,
+                      to_dev, upload_nvfp4)
 from workloads import synth
 
 pytestmark = pytest.mark.gpu
@@ -108,8 +111,67 @@ def test_saturating_scale(bbs):
     assert np.array_equal(host(Y.codes), o.codes)
 
 
-def _mismatch(g, o):
-    return float(np.mean(g != o))
+def _explain_blocks(codes, scales, y64, E, s_enc, gelu):
+    """Blocks of the GPU's 1x16 NVFP4 output (codes, scales: rows x N/2,
+    rows x N/16) against the oracle: returns (differing blocks, unexplained
+    blocks).  A differing block is explained when some admissible BF16 row
+    (each value within the BF16 rounding of [y64 - E, y64 + E], GELU of it
+    with `gelu`) encodes to exactly the GPU's scale code and 16 codes: every
+    code must be the nearest-even E2M1 code of an admissible value times the
+    block's encode scale, and the scale code must be that of a block maximum
+    the admissible values can reach."""
+    f_ref = O.bf16_rne(y64).astype(np.float32)
+    if gelu:
+        f_ref = O.gelu_f32(f_ref)
+    o = O.nvfp4_encode_f32(f_ref, s_enc)
+    R, N = y64.shape
+    nb = N // 16
+    diff = (scales != o.scales) | (codes.reshape(R, nb, 8) != o.codes.reshape(R, nb, 8)).any(axis=2)
+    s_dec = np.float32(1.0) / np.float32(s_enc)
+    unexplained = 0
+    for m, b in zip(*np.nonzero(diff)):
+        lo, hi = bf16_window(y64[m, 16 * b:16 * b + 16], E[m, 16 * b:16 * b + 16])
+        sc = int(scales[m, b])
+        s_b = np.float32(1.0) / (np.float32(O.e4m3_value(sc)) * s_dec)
+        cb = codes[m, 8 * b:8 * b + 8]
+        want = np.stack([cb & 0xF, cb >> 4], axis=1).reshape(16)
+        allowed = []
+        for i in range(16):
+            h = bf16_from_key(np.arange(lo[i], hi[i] + 1))
+            v = (h.astype(np.uint32) << 16).view(np.float32)
+            if gelu:
+                v = O.gelu_f32(v)
+            c = O.e2m1_code(O.round_to(v * s_b, O.E2M1, O.RTN))
+            allowed.append(np.abs(v[c == want[i]]))
+        if any(a.size == 0 for a in allowed):
+            unexplained += 1
+            continue
+        floor = max(float(a.min()) for a in allowed)
+        maxima = np.unique(np.concatenate([a[a >= floor] for a in allowed]))
+        if not any(O.block_scale_code(float(mx), float(s_enc)) == sc for mx in maxima):
+            unexplained += 1
+    return int(diff.sum()), unexplained
+
+
+def _amax_window(y64, E, gelu):
+    """Bounds on the max |value| an admissible BF16 output (GELU of it with
+    `gelu`) can have, from each window's end points: a window holding 0 can
+    give 0; GELU is non-decreasing for x >= 0 and below 0.171875 in
+    magnitude for x < 0 (the oracle's GELU pins), so a window reaching below
+    0 can give at most 0.171875 there and, wholly below 0, is bounded below
+    by 0 only."""
+    lo, hi = bf16_window(y64.ravel(), E.ravel())
+    a = (bf16_from_key(lo).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    b = (bf16_from_key(hi).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if not gelu:
+        small = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(a), np.abs(b)))
+        big = np.maximum(np.abs(a), np.abs(b))
+    else:
+        ga, gb = O.gelu_f32(a.astype(np.float32)), O.gelu_f32(b.astype(np.float32))
+        small = np.where(lo > 0, np.abs(ga), 0.0)
+        big = np.where(hi > 0, np.abs(gb), 0.0)
+        big = np.where(lo < 0, np.maximum(big, 0.171875), big)
+    return float(small.max()), float(big.max())
 
 
 @pytest.mark.parametrize("gelu", [False, True])
@@ -121,10 +183,14 @@ def test_general_operands(bbs, gelu):
     y = _ref(ox, ow, gelu)
     s_enc = O.tensor_s_enc(float(np.abs(y).max()))
     Y, got_amax = _run(bbs, upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs), s_enc, gelu, 256, 384)
-    o = O.nvfp4_encode_f32(y, s_enc)
-    assert _mismatch(host(Y.scales), o.scales) < 2e-3
-    assert _mismatch(host(Y.codes), o.codes) < 2e-3
-    assert abs(got_amax - float(np.abs(y).max())) <= 1e-5 * float(np.abs(y).max())
+    A64, B64 = ox.dequant_f64(), ow.dequant_f64()
+    y64 = O.gemm_f64(A64, B64)
+    E = accumulation_bound(O.gemm_f64(np.abs(A64), np.abs(B64)), 1024)
+    n_diff, n_bad = _explain_blocks(host(Y.codes), host(Y.scales), y64, E, s_enc, gelu)
+    print(f"  {n_diff} of {256 * 24} blocks differ from the encode of RN(y), {n_bad} unexplained")
+    assert n_bad == 0
+    lo, hi = _amax_window(y64, E, gelu)
+    assert lo <= got_amax <= hi, (lo, got_amax, hi)
 
 
 def test_grouped_exact_case(bbs):
@@ -174,17 +240,21 @@ def test_full_size_sampled(bbs):
     rows[-1] = 8191
     sub = O.NVFP4(np.ascontiguousarray(ox.codes[rows]), np.ascontiguousarray(ox.scales[rows]),
                   ox.s_dec, len(rows), 4096, False)
-    y = O.gelu_f32(O.bf16_rne(O.gemm_f64(sub.dequant_f64(), ow.dequant_f64())).astype(np.float32))
+    A64, B64 = sub.dequant_f64(), ow.dequant_f64()
+    y64 = O.gemm_f64(A64, B64)
+    E = accumulation_bound(O.gemm_f64(np.abs(A64), np.abs(B64)), 4096)
     s_enc = O.tensor_s_enc(40.0)
     xq, wq = upload_nvfp4(ox, bbs), upload_nvfp4(ow, bbs)
     Y, got_amax = _run(bbs, xq, wq, s_enc, True, 8192, 14336)
-    o = O.nvfp4_encode_f32(y, s_enc)
     ridx = torch.from_numpy(rows).to(dev())
-    assert _mismatch(host(Y.scales[ridx]), o.scales) < 2e-3
-    assert _mismatch(host(Y.codes[ridx]), o.codes) < 2e-3
-    assert got_amax >= float(np.abs(y).max()) * (1 - 1e-5)
-    # at full size: the fused kernel equals the BF16 GEMM followed by the
-    # fused GELU quantizer, whose amax pass finds the same amax, bit for bit
+    n_diff, n_bad = _explain_blocks(host(Y.codes[ridx]), host(Y.scales[ridx]), y64, E, s_enc, True)
+    print(f"  {n_diff} of {len(rows) * 896} sampled blocks differ from the encode of RN(y), "
+          f"{n_bad} unexplained")
+    assert n_bad == 0
+    assert got_amax >= _amax_window(y64, E, True)[0]
+    # at full size, beside the oracle check above: the fused kernel equals the
+    # library's BF16 GEMM followed by its fused GELU quantizer (whose amax
+    # pass finds the same amax) bit for bit, the header's promise
     h = torch.empty((8192, 14336), dtype=torch.int16, device=dev())
     bbs.nvfp4_gemm(bbs.FMT_NVFP4, xq, wq, h, bbs.OUT_BF16)
     U = bbs.NVFP4Tensor.empty(8192, 14336, device=dev())
@@ -195,3 +265,43 @@ def test_full_size_sampled(bbs):
     assert torch.equal(U.s_dec, Y2.s_dec)
     assert torch.equal(U.scales, Y2.scales)
     assert torch.equal(U.codes, Y2.codes)
+
+
+def test_grouped_dropped_slots(bbs):
+    """Dropped slots (row_index < 0 or >= A.rows) of the quantizing grouped
+    GEMM are encoded as zero rows and leave the reported amax unchanged."""
+    announce("quantizing grouped GEMM with dropped slots, GELU")
+    G, N, K, T = 3, 128, 256, 64
+    a = _unit_scale_operand(T, K, 42, 0.5)
+    counts = np.array([40, 0, 72])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = int(offsets[-1])
+    rng = np.random.default_rng(43)
+    row_index = rng.integers(0, T, rows).astype(np.int32)
+    drop = rng.choice(rows, 20, replace=False)
+    row_index[drop[:10]] = -3
+    row_index[drop[10:]] = T + 7
+    ws = [_unit_scale_operand(N, K, 55 + g, 2.0 ** -(g + 1), True) for g in range(G)]
+    y = np.zeros((rows, N), np.float32)
+    A64 = a.dequant_f64()
+    for g in range(G):
+        for i in range(offsets[g], offsets[g + 1]):
+            if 0 <= row_index[i] < T:
+                y[i] = O.bf16_rne(A64[row_index[i]] @ ws[g].dequant_f64().T)
+    y = O.gelu_f32(y)
+    s_enc = O.tensor_s_enc(float(np.abs(y).max()))
+    B = bbs.NVFP4Tensor.empty(G * N, K, tile2d=True, n_scales=G, device=dev())
+    for g in range(G):
+        B.codes[g * N:(g + 1) * N] = to_dev(ws[g].codes)
+        B.scales[g * N // 16:(g + 1) * N // 16] = to_dev(ws[g].scales)
+        B.s_dec[g] = float(ws[g].s_dec)
+    Y = bbs.NVFP4Tensor.empty(rows, N, device=dev())
+    se = torch.tensor([s_enc], dtype=torch.float32, device=dev())
+    amax = torch.zeros(1, dtype=torch.float32, device=dev())
+    bbs.grouped_nvfp4_gemm_quant(upload_nvfp4(a, bbs), to_dev(row_index), to_dev(offsets), G, rows,
+                                 B, N, se, Y, gelu=True, amax=amax)
+    torch.cuda.synchronize()
+    o = O.nvfp4_encode_f32(y, s_enc)
+    assert np.array_equal(host(Y.scales), o.scales)
+    assert np.array_equal(host(Y.codes), o.codes)
+    assert float(host(amax)[0]) == float(np.abs(y).max())

@@ -148,3 +148,36 @@ def test_full_moe_down_projection(bbs):
         o = O.s2f6_encode_f32(y, rht=True, signs=SIGNS)
         assert np.array_equal(host(Y.scales[ridx]), o.scales), f"expert {g}: scales differ"
         assert np.array_equal(host(Y.codes[ridx]), o.codes), f"expert {g}: codes differ"
+
+
+def test_grouped_dropped_slots(bbs):
+    """Dropped slots of the encoding grouped GEMM come out as the encode of
+    a zero row (scale byte 0, codes 0)."""
+    announce("encoding grouped GEMM with dropped slots")
+    G, N, K, T = 3, 96, 256, 48
+    a = _unit_scale_operand(T, K, 62, 0.25)
+    counts = np.array([30, 50, 0])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows = int(offsets[-1])
+    rng = np.random.default_rng(63)
+    row_index = rng.integers(0, T, rows).astype(np.int32)
+    drop = rng.choice(rows, 16, replace=False)
+    row_index[drop[:8]] = -1
+    row_index[drop[8:]] = T
+    ws = [_unit_scale_operand(N, K, 72 + g, 2.0 ** -(g + 2), True) for g in range(G)]
+    A64 = a.dequant_f64()
+    y = np.zeros((rows, N), np.float32)
+    for g in range(G):
+        for i in range(offsets[g], offsets[g + 1]):
+            if 0 <= row_index[i] < T:
+                y[i] = O.bf16_rne(A64[row_index[i]] @ ws[g].dequant_f64().T)
+    B = bbs.NVFP4Tensor.empty(G * N, K, tile2d=True, n_scales=G, device=dev())
+    for g in range(G):
+        B.codes[g * N:(g + 1) * N] = to_dev(ws[g].codes)
+        B.scales[g * N // 16:(g + 1) * N // 16] = to_dev(ws[g].scales)
+        B.s_dec[g] = float(ws[g].s_dec)
+    Y = bbs.S2F6Tensor.empty(rows, N, device=dev())
+    bbs.grouped_nvfp4_gemm_s2f6(upload_nvfp4(a, bbs), to_dev(row_index), to_dev(offsets), G, rows,
+                                B, N, Y, rht=True, signs=SIGNS)
+    torch.cuda.synchronize()
+    _same(Y, O.s2f6_encode_f32(y, rht=True, signs=SIGNS), "grouped dropped slots")
