@@ -572,6 +572,192 @@ __global__ __launch_bounds__(kQT, MINW) void quant_kernel(QuantParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-wise copies only (no column copy): the NVFP4 row copy (1x16 or 16x16
+// tiles) and / or the MXFP8 row copy.  A wave step covers 16 rows x 512
+// columns, lane l holding columns 8l .. 8l + 7 of each row, so each row's
+// codes go out as one 256-byte (NVFP4) or 512-byte (MXFP8) store of the wave
+// and its block scales as 4-byte words gathered across lanes.  Waves walk
+// the steps with a stride of the whole grid, loading the next step while
+// they encode the current one.
+// ---------------------------------------------------------------------------
+struct RowsLds {
+    float tab[128];
+    float fold[kQT / 64];
+};
+
+// Scale bytes of lanes l, l + d, l + 2d, l + 3d as one little-endian word (in
+// lane l).
+__device__ __forceinline__ uint32_t gather4(uint32_t b, int d) {
+    const uint32_t b1 = __shfl_down(b, d, 64), b2 = __shfl_down(b, 2 * d, 64),
+                   b3 = __shfl_down(b, 3 * d, 64);
+    return (b & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | ((b3 & 0xFFu) << 24);
+}
+
+// Store the scale bytes of `per` consecutive lanes' blocks (one byte per d
+// lanes, starting at lane l0 of a group of 4d lanes) at dst[0..3]: one word
+// when the group is inside the row and 4-byte aligned, else byte stores.
+__device__ __forceinline__ void put_scales4(uint8_t *dst, uint32_t word, int64_t nvalid) {
+    if (nvalid >= 4 && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+        *reinterpret_cast<uint32_t *>(dst) = word;
+    } else {
+        for (int64_t i = 0; i < nvalid && i < 4; ++i) dst[i] = (uint8_t)(word >> (8 * i));
+    }
+}
+
+template <bool HAS_ROW, bool HAS_MX, bool TILE2D, bool GELU, bool SR, int MINW>
+__global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p) {
+    __shared__ __align__(16) RowsLds L;
+    __shared__ __align__(16) float s_gelu[GELU ? kGeluTabSize : 1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t steps_c = (p.C + kAmaxStepC - 1) / kAmaxStepC;
+    const int64_t T = (p.R / 16) * steps_c;
+    const int64_t stride = (int64_t)gridDim.x * (kQT / 64);
+    auto load = [&](int64_t t, uint4 d[16], int64_t &r0, int64_t &c0) {
+        r0 = (t / steps_c) * 16;
+        c0 = (t - (r0 / 16) * steps_c) * kAmaxStepC + lane * 8;
+        const uint16_t *src = p.x + r0 * p.ld + (c0 < p.C ? c0 : p.C - 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * p.ld);
+    };
+    int64_t t = (int64_t)blockIdx.x * (kQT / 64) + w;
+    uint4 v[16];
+    int64_t r0 = 0, c0 = 0;
+    if (t < T) load(t, v, r0, c0);
+
+    // the tensor scale (row copy): partials folded once per workgroup
+    float s_enc = 1.0f;
+    if (HAS_ROW) {
+        float a = 0.0f;
+        for (int i = threadIdx.x; i < p.n_part; i += kQT) a = fmaxf(a, p.part[i]);
+        a = wave_max(a);
+        if (lane == 0) L.fold[w] = a;
+    }
+    if constexpr (GELU) gelu_table_load(s_gelu, p.gelu_tab);
+    __syncthreads();
+    if (HAS_ROW) {
+        s_enc = tensor_s_enc(fmaxf(fmaxf(L.fold[0], L.fold[1]), fmaxf(L.fold[2], L.fold[3])));
+        if (blockIdx.x == 0 && threadIdx.x == 0) p.row_sdec[0] = 1.0f / s_enc;
+        enc_scale_table(L.tab, 1.0f / s_enc);
+    }
+    __syncthreads();
+
+    const int64_t n_step = p.C / 8;
+    while (t < T) {                                   // wave-uniform
+        const int64_t tn = t + stride;
+        uint4 vn[16];
+        int64_t r0n = r0, c0n = c0;
+        if (tn < T) load(tn, vn, r0n, c0n);
+        const bool in = c0 < p.C;
+        auto val = [&](int r, int j) -> float {
+            if constexpr (GELU) return gelu_bf16(elem_bits(v[r], j), s_gelu);
+            else return elem(v[r], j);
+        };
+        uint32_t tsc = 0;
+        float ts = 0.0f;
+        if (HAS_ROW && TILE2D) {
+            float a = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(elem(v[r], j)));
+            tsc = block_scale_code(max_lane_pair(a), s_enc);
+            ts = L.tab[tsc];
+            // one scale byte per 16x16 tile: 32 per wave step, as 8 words
+            const uint32_t word = gather4(tsc, 2);
+            if ((lane & 7) == 0 && in)
+                put_scales4(p.row_scales + (r0 / 16) * (p.C / 16) + c0 / 16, word, (p.C - c0) / 16);
+        }
+        const uint64_t nr0 = (uint64_t)(r0 * p.C + c0) / 8;
+        auto one = [&](auto row_sr, auto mx_sr, int r) {
+            constexpr bool RSR = decltype(row_sr)::value, MSR = decltype(mx_sr)::value;
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[j] = val(r, j);
+            const int64_t row = r0 + r;
+            if (HAS_ROW) {
+                uint32_t sc = tsc;
+                float sv = ts;
+                if (!TILE2D) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
+                    sc = block_scale_code(max_lane_pair(a), s_enc);
+                    sv = L.tab[sc];
+                    const uint32_t word = gather4(sc, 2);
+                    if ((lane & 7) == 0 && in)
+                        put_scales4(p.row_scales + row * (p.C / 16) + c0 / 16, word, (p.C - c0) / 16);
+                }
+                uint32_t packed;
+                if constexpr (RSR) {
+                    uint32_t wd[4];
+                    sr_block(p.row_seed, p.row_stream, nr0 + (uint64_t)r * n_step, wd);
+                    packed = e2m1_sr8(f, sv, wd);
+                } else {
+                    packed = e2m1_rne8(f, sv);
+                }
+                if (in) *reinterpret_cast<uint32_t *>(p.row_codes + row * (p.C / 2) + c0 / 2) = packed;
+            }
+            if (HAS_MX) {
+                float y[8];
+                float a = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    y[j] = f[j];
+                    a = fmaxf(a, fabsf(f[j]));
+                }
+                const uint32_t kb = e8m0_byte(max_lane_quad(a));
+                if (__builtin_amdgcn_ballot_w64(kb == 0)) {   // rare, wave-uniform test
+                    if (kb == 0) {                             // 2^-127: convert 2y at 2^-126
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) y[j] = y[j] * 2.0f;
+                    }
+                }
+                const float cs = e8m0_cvt_scale(kb);
+                uint32_t lo, hi;
+                if constexpr (MSR) {
+                    uint32_t wd[4];
+                    sr_block(p.mx_seed, p.mx_stream, nr0 + (uint64_t)r * n_step, wd);
+                    lo = e4m3_sr4_scaled(y[0], y[1], y[2], y[3], sr_word_lo(wd[0]), sr_word_hi(wd[0]),
+                                         sr_word_lo(wd[1]), sr_word_hi(wd[1]), cs);
+                    hi = e4m3_sr4_scaled(y[4], y[5], y[6], y[7], sr_word_lo(wd[2]), sr_word_hi(wd[2]),
+                                         sr_word_lo(wd[3]), sr_word_hi(wd[3]), cs);
+                } else {
+                    lo = e4m3_rne4_scaled(y[0], y[1], y[2], y[3], cs);
+                    hi = e4m3_rne4_scaled(y[4], y[5], y[6], y[7], cs);
+                }
+                if (in) *reinterpret_cast<uint2 *>(p.mx_codes + row * p.C + c0) = make_uint2(lo, hi);
+                const uint32_t word = gather4(kb, 4);
+                if ((lane & 15) == 0 && in)
+                    put_scales4(p.mx_scales + row * (p.C / 32) + c0 / 32, word, (p.C - c0) / 32);
+            }
+        };
+        auto rows = [&](auto row_sr, auto mx_sr) {
+            // (two loops of 8 rows: each stays under the full-unroll limit)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) one(row_sr, mx_sr, r);
+#pragma unroll
+            for (int r = 8; r < 16; ++r) one(row_sr, mx_sr, r);
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if constexpr (SR) {
+            const bool row_sr = HAS_ROW && p.row_round == 1, mx_sr = HAS_MX && p.mx_round == 1;
+            if (row_sr && mx_sr) rows(T_{}, T_{});
+            else if (row_sr) rows(T_{}, F_{});
+            else if (mx_sr) rows(F_{}, T_{});
+            else rows(F_{}, F_{});
+        } else {
+            rows(F_{}, F_{});
+        }
+        t = tn;
+        r0 = r0n;
+        c0 = c0n;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = vn[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Activation copy: per-token outer scale and / or Four Over Six
 // (4bit.vizuara.ai, section 11; End-to-End 4-Bit Training, recipe details).
 // One wave per row; in chunk k of 512 columns lane l holds columns
@@ -1049,6 +1235,20 @@ static void launch_q(const QuantParams &p, bool sr, hipStream_t s) {
                   quant_min_waves<R_, C_, M_, T_, H_, false>()>(p, s);
 }
 
+// Row-wise copies only: a resident grid of 16 x 512 wave steps.
+template <bool R_, bool M_, bool T_, bool G_, bool SR_>
+static void launch_rows_k(const QuantParams &p, hipStream_t s) {
+    constexpr int MW = 2;                             // (a cap of 4 spills with SR)
+    constexpr auto k = quant_rows_kernel<R_, M_, T_, G_, SR_, MW>;
+    const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC - 1) / kAmaxStepC);
+    hipLaunchKernelGGL(k, dim3(persistent_grid<k>((steps + 3) / 4, s)), dim3(kQT), 0, s, p);
+}
+template <bool R_, bool M_, bool T_, bool G_>
+static void launch_rows(const QuantParams &p, bool sr, hipStream_t s) {
+    (void)sr;                                         // nearest-rounding copies only
+    launch_rows_k<R_, M_, T_, G_, false>(p, s);
+}
+
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
                              bool tile2d, bool rht, hipStream_t s, bool gelu) {
     // the stochastic paths are compiled only into the variant that needs them
@@ -1062,20 +1262,37 @@ hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, b
         else return hipErrorInvalidValue;
         return hipGetLastError();
     }
+    // Row-wise copies only, all rounding to nearest: light ALU work, so the
+    // resident row-step kernel (whole-row stores, next step loaded ahead)
+    // is used; the stochastic ones keep the tile kernel's four waves per SIMD.
+    if (!has_col && !sr) {
+        if (has_row && has_mx) {
+            if (tile2d) launch_rows<1, 1, 1, 0>(p, false, s);
+            else launch_rows<1, 1, 0, 0>(p, false, s);
+        } else if (has_row) {
+            if (tile2d) launch_rows<1, 0, 1, 0>(p, false, s);
+            else launch_rows<1, 0, 0, 0>(p, false, s);
+        } else if (has_mx) {
+            launch_rows<0, 1, 0, 0>(p, false, s);
+        } else {
+            return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     // The combinations the quantizer supports (RHT only on a 1x16 column copy).
     const int key = (has_row << 4) | (has_col << 3) | (has_mx << 2) | (tile2d << 1) | rht;
     switch (key) {
         case 0b10000: launch_q<1, 0, 0, 0, 0>(p, sr, s); break;
         case 0b10010: launch_q<1, 0, 0, 1, 0>(p, sr, s); break;
+        case 0b00100: launch_q<0, 0, 1, 0, 0>(p, sr, s); break;
+        case 0b10100: launch_q<1, 0, 1, 0, 0>(p, sr, s); break;
+        case 0b10110: launch_q<1, 0, 1, 1, 0>(p, sr, s); break;
         case 0b11000: launch_q<1, 1, 0, 0, 0>(p, sr, s); break;
         case 0b11010: launch_q<1, 1, 0, 1, 0>(p, sr, s); break;
         case 0b11001: launch_q<1, 1, 0, 0, 1>(p, sr, s); break;
         case 0b01000: launch_q<0, 1, 0, 0, 0>(p, sr, s); break;
         case 0b01010: launch_q<0, 1, 0, 1, 0>(p, sr, s); break;
         case 0b01001: launch_q<0, 1, 0, 0, 1>(p, sr, s); break;
-        case 0b00100: launch_q<0, 0, 1, 0, 0>(p, sr, s); break;
-        case 0b10100: launch_q<1, 0, 1, 0, 0>(p, sr, s); break;
-        case 0b10110: launch_q<1, 0, 1, 1, 0>(p, sr, s); break;
         case 0b01100: launch_q<0, 1, 1, 0, 0>(p, sr, s); break;
         case 0b01101: launch_q<0, 1, 1, 0, 1>(p, sr, s); break;
         case 0b11100: launch_q<1, 1, 1, 0, 0>(p, sr, s); break;
