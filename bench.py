@@ -11,8 +11,16 @@ X [8192 x 4096] (BF16), W [14336 x 4096] (BF16), dY [8192 x 14336] (BF16):
   7 wgrad        dW = dY^T X        NVFP4 GEMM over the RHT'd copies, FP32 out
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Prints one JSON line (value = whole-step GEMM TFLOP/s including every
-quantize pass), with per-kernel times, a roofline entry for the fprop GEMM
-and the CPU oracle timed on a bounded sample.
+quantize pass), with per-kernel times, a roofline entry for the fprop GEMM,
+the CPU oracle timed on a bounded sample and, from the same oracle, parity
+counts for the outputs of the timed kernels.
+
+Per-kernel times: 10 warm-up calls, then 100 back-to-back calls with a HIP
+event after every 10; "ms" is the median of the ten 10-call means and
+"ms_mean" the mean of a second batch of 100 calls timed by two events only
+(the average launch duration, comparable with a rocprofv3 kernel trace).
+Every timed call, in the step and in the sections after it, cycles through
+ROTATE buffer sets so that its inputs are not resident in the 256 MB MALL.
 """
 import argparse
 import json
@@ -28,7 +36,7 @@ sys.path.insert(0, ROOT)
 M, K, N = 8192, 4096, 14336
 GEMM_FLOP = 2.0 * M * N * K                     # 962.07 GFLOP per GEMM
 PEAK_HBM_GBPS = 8000.0
-PEAK_BF16_TFLOPS = 2500.0                      # MFMA class the NVFP4 GEMM issues
+PEAK_FP16_TFLOPS = 2500.0                      # MFMA class the NVFP4 GEMM issues (fp16)
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
 COPY_BYTES = 1 << 29                            # counter calibration copy (512 MiB)
@@ -54,6 +62,48 @@ def fprop_traffic():
 
 def nvfp4_bytes(r, c):
     return r * c // 2 + r * c // 16
+
+
+def time_calls(torch, calls, n=100, warm=10, group=10):
+    """calls: callables cycled through in order (one per buffer set).  After
+    `warm` calls, n back-to-back calls in groups of `group` with a HIP event
+    between groups (an event between every two calls adds about 3 us to each
+    interval on this GPU).  Returns (median of the group means, mean over a
+    separate batch of n calls between two events)."""
+    k = len(calls)
+    group = max(1, min(group, n))
+    for i in range(warm):
+        calls[i % k]()
+    ng = n // group
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(ng + 1)]
+    ev[0].record()
+    for gi in range(ng):
+        for j in range(group):
+            calls[(warm + gi * group + j) % k]()
+        ev[gi + 1].record()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record()
+    for i in range(n):
+        calls[(warm + n + i) % k]()
+    b1.record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) / group for i in range(ng)]
+    return float(np.median(per)), b0.elapsed_time(b1) / n
+
+
+def gemm_entry(t_med, t_mean, flop, own_peak, own_name, issued_peak=None):
+    tf = flop / (t_med * 1e-3) / 1e12
+    e = {"ms": round(t_med, 4), "ms_mean": round(t_mean, 4), "TFLOP/s": round(tf, 1),
+         f"frac_{own_name}_peak": round(tf / own_peak, 4)}
+    if issued_peak is not None:
+        e["frac_fp16_mfma_peak"] = round(tf / issued_peak, 4)
+    return e
+
+
+def bytes_entry(t_med, t_mean, b):
+    gbps = b / (t_med * 1e-3) / 1e9
+    return {"ms": round(t_med, 4), "ms_mean": round(t_mean, 4), "GB/s": round(gbps, 1),
+            "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4), "bytes": b}
 
 
 def algorithmic_bytes():
@@ -134,6 +184,102 @@ def cpu_baseline():
     }
 
 
+def sample_positions(rows, cols, per_tile, seed, tile=256):
+    """per_tile random outputs inside every tile x tile output tile, plus the
+    last row's first and last 64 columns (the ragged edge of any tiling)."""
+    rng = np.random.default_rng(seed)
+    tm, tn = -(-rows // tile), -(-cols // tile)
+    ti = np.repeat(np.arange(tm), tn * per_tile)
+    tj = np.tile(np.repeat(np.arange(tn), per_tile), tm)
+    r = np.minimum(ti * tile + rng.integers(0, tile, ti.size), rows - 1)
+    c = np.minimum(tj * tile + rng.integers(0, tile, tj.size), cols - 1)
+    edge = np.concatenate([np.arange(64), np.arange(cols - 64, cols)])
+    r = np.concatenate([r, np.full(edge.size, rows - 1)])
+    c = np.concatenate([c, edge])
+    return r.astype(np.int64), c.astype(np.int64)
+
+
+GEMM_SAMPLES = {"fprop": (M, N, 1), "dgrad": (M, K, 2), "wgrad": (N, K, 2)}
+
+
+def capture_outputs(torch, b):
+    """Host copies of one step's outputs: every quantized copy whole, the GEMM
+    outputs at sampled positions (2 per 256 x 256 tile of dX and dW, 1 of Y,
+    and the ragged edge)."""
+    def nv(q):
+        return (q.codes.cpu().numpy(), q.scales.cpu().numpy(), float(q.s_dec[0]))
+
+    def mx(q):
+        return (q.codes.cpu().numpy(), q.scales.cpu().numpy())
+
+    cap = {"xq": nv(b["xq"]), "xc": nv(b["xc"]), "wq": nv(b["wq"]), "gc": nv(b["gc"]),
+           "gm": mx(b["gm"]), "wt": mx(b["wt"])}
+    for name, key in (("fprop", "y"), ("dgrad", "dx"), ("wgrad", "dw")):
+        R, Cn, per_tile = GEMM_SAMPLES[name]
+        r, c = sample_positions(R, Cn, per_tile, 900 + len(name))
+        out = b[key]
+        g = out[torch.from_numpy(r).to(out.device), torch.from_numpy(c).to(out.device)].cpu()
+        if key == "dw":
+            v = g.numpy().astype(np.float64)
+        else:
+            v = ((g.numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+                 .astype(np.float64))
+        cap[name] = (r, c, v)
+    return cap
+
+
+def parity(cap, host_in, signs, seeds):
+    """The timed kernels' outputs of one step against the oracle run on the
+    same inputs: equal bytes of every quantized copy (codes, scales and the
+    FP32 decode scale), and for each GEMM the sampled outputs against the
+    FP64 product of the oracle's own copies, with the rigorous FP32
+    accumulation bound (K + 4) 2^-24 sum|a b| plus the output rounding."""
+    import oracle as O
+    t0 = time.perf_counter()
+    x, w, dy = host_in["x"], host_in["w"], host_in["dy"]
+    ref = {
+        "xq": O.nvfp4_quantize(x),
+        "xc": O.nvfp4_quantize(x, transpose=True, rht=True, signs=signs, mode=O.SR,
+                               seed=seeds["x_col"], stream=0),
+        "wq": O.nvfp4_quantize(w, tile2d=True),
+        "gc": O.nvfp4_quantize(dy, transpose=True, rht=True, signs=signs, mode=O.SR,
+                               seed=seeds["dy_col"], stream=0),
+        "gm": O.mxfp8_quantize(dy, mode=O.SR, seed=seeds["dy_mx8"], stream=0),
+    }
+    ref["wt"] = O.mxfp8_requantize_t(ref["wq"], mode=O.SR, seed=seeds["w_req"], stream=0)
+    t_quant = time.perf_counter() - t0
+    res = {}
+    for key in ("xq", "xc", "wq", "gc", "gm", "wt"):
+        o, g = ref[key], cap[key]
+        total = o.codes.size + o.scales.size
+        equal = int((g[0] == o.codes).sum()) + int((g[1] == o.scales).sum())
+        e = {"bytes": total, "equal": equal}
+        if len(g) == 3:
+            e["s_dec_equal"] = bool(np.float32(g[2]) == np.float32(o.s_dec))
+        res[key] = e
+    gemms = {"fprop": (ref["xq"], ref["wq"], K, "bf16"),
+             "dgrad": (ref["gm"], ref["wt"], N, "bf16"),
+             "wgrad": (ref["gc"], ref["xc"], M, "f32")}
+    for name, (qa, qb, kc, out_t) in gemms.items():
+        r, c, v = cap[name]
+        A, B = qa.dequant_f64(), qb.dequant_f64()
+        y = O.gemm_f64_sampled(A, B, r, c)
+        a_abs = O.gemm_f64_sampled(np.abs(A), np.abs(B), r, c)
+        del A, B
+        acc = (kc + 4) * 2.0 ** -24 * a_abs
+        rnd = 2.0 ** -8 if out_t == "bf16" else 2.0 ** -24
+        bound = acc + rnd * (np.abs(y) + acc)
+        err = np.abs(v - y)
+        ratio = err / np.where(bound > 0, bound, np.inf)
+        res[name] = {"samples": int(v.size), "within_bound": int((err <= bound).sum()),
+                     "max_err_over_bound": float(ratio.max()),
+                     "rel_fro": O.rel_fro(v, y),
+                     "max_abs_err": float(err.max())}
+    res["oracle_s"] = round(time.perf_counter() - t0, 2)
+    res["oracle_quantize_full_size_s"] = round(t_quant, 2)
+    return res
+
+
 def moe_bench(torch, bbs, dev, reps):
     """The MoE expert forward (grouped NVFP4 GEMMs) at its full shape: 65536
     tokens x hidden 4096, 64 experts, top-8 Zipf(1.1) routing with 4 empty
@@ -204,25 +350,19 @@ def moe_bench(torch, bbs, dev, reps):
     }
     codec_bytes = {"combine_encode": rows * H_ * 2 + rows * H_ + rows * H_ // 32,
                    "combine_decode": rows * (H_ + H_ // 32) + rows * 8 + T_ * H_ * 2}
+    # The working set (1.6 GB up output, 0.4 GB weights) is far above the
+    # MALL, so the ops run on one buffer set.
     out = {}
+    flop = 2.0 * rows * F_ * H_
+    hq_bytes = rows * F_ * 2 + rows * F_ // 2 + rows * F_ // 16
     for name, f in ops.items():
-        f()
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(reps):
-            f()
-        s1.record()
-        torch.cuda.synchronize()
-        ms = s0.elapsed_time(s1) / reps
-        e = {"ms": round(ms, 4)}
+        t_med, t_mean = time_calls(torch, [f], n=reps, warm=min(10, reps))
         if name in codec_bytes:
-            gbps = codec_bytes[name] / (ms * 1e-3) / 1e9
-            e.update({"GB/s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-                      "bytes": codec_bytes[name]})
-        elif name not in ("moe_quant_h",):
-            tf = 2.0 * rows * F_ * H_ / (ms * 1e-3) / 1e12
-            e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+            e = bytes_entry(t_med, t_mean, codec_bytes[name])
+        elif name == "moe_quant_h":
+            e = bytes_entry(t_med, t_mean, hq_bytes)
+        else:
+            e = gemm_entry(t_med, t_mean, flop, PEAK_FP4_TFLOPS, "fp4", PEAK_FP16_TFLOPS)
         out[name] = e
     out["routed_rows"] = rows
     out["flop_per_projection"] = 2.0 * rows * F_ * H_
@@ -256,11 +396,13 @@ def main():
     fw = synth.dense_forward(M, K, N)
     bw = synth.backward(M, N)
     signs, seeds = bw["rht_signs"], bw["seeds"]
+    want_oracle = not args.no_cpu_baseline
 
     def up(a):
         return torch.from_numpy(a.view(np.int16)).to(dev)
 
     x0, w0, dy0 = up(fw["x"]), up(fw["w"]), up(bw["dy"])
+    host_in = {"x": fw["x"], "w": fw["w"], "dy": bw["dy"]} if want_oracle else None
     del fw, bw
     T = bbs.NVFP4Tensor
     ws = bbs.amax_workspace(dev)
@@ -275,8 +417,8 @@ def main():
         y = torch.empty((M, N), dtype=torch.int16, device=dev)
         dx = torch.empty((M, K), dtype=torch.int16, device=dev)
         dw = torch.empty((N, K), dtype=torch.float32, device=dev)
-        bufs = {"xq": xq, "xc": xc, "wq": wq, "gc": gc, "gm": gm, "wt": wt, "y": y, "dx": dx,
-                "dw": dw}
+        bufs = {"x": x, "w": w, "dy": dy, "xq": xq, "xc": xc, "wq": wq, "gc": gc, "gm": gm,
+                "wt": wt, "y": y, "dx": dx, "dw": dw}
         return bufs, {
             "quant_x": lambda: bbs.nvfp4_quantize(x, xq, xc, col_round=bbs.SR,
                                                   col_rng=(seeds["x_col"], 0), col_rht=True,
@@ -296,16 +438,16 @@ def main():
     # the same values in every set), so no kernel finds its inputs in the
     # 256 MB MALL from the previous launch; --only (the counter runs) uses one.
     n_sets = 1 if args.only else ROTATE
-    bufs, ops = make_set(x0, w0, dy0)
-    sets = [ops]
-    for _ in range(n_sets - 1):
-        sets.append(make_set(x0.clone(), w0.clone(), dy0.clone())[1])
-    # set 0's buffers serve the sections after the step
-    x, w, dy = x0, w0, dy0
-    xq, xc, wq, y = bufs["xq"], bufs["xc"], bufs["wq"], bufs["y"]
+    sets_b, sets_o = [], []
+    for i in range(n_sets):
+        bset, oset = make_set(x0, w0, dy0) if i == 0 else make_set(x0.clone(), w0.clone(),
+                                                                   dy0.clone())
+        sets_b.append(bset)
+        sets_o.append(oset)
+    ops = sets_o[0]
 
     def step(i=0):
-        for f in sets[i % n_sets].values():
+        for f in sets_o[i % n_sets].values():
             f()
 
     if args.only:
@@ -343,58 +485,45 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
-    # per-kernel timing: the same launches back to back on the same stream
-    per = {}
+    # per-kernel timing: each op alone, cycling over the buffer sets
+    per, per_mean = {}, {}
     for name in ops:
-        for st in sets:
-            st[name]()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for i in range(args.steps):
-            sets[i % n_sets][name]()
-        s1.record()
-        torch.cuda.synchronize()
-        per[name] = s0.elapsed_time(s1) / args.steps
+        per[name], per_mean[name] = time_calls(torch, [o[name] for o in sets_o])
     ab = algorithmic_bytes()
     kernels = {}
-    for name, t_ms in per.items():
-        e = {"ms": round(t_ms, 4)}
+    for name in ops:
         if name in ab:
-            gbps = ab[name] / (t_ms * 1e-3) / 1e9
-            e.update({"GB/s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-                      "bytes": ab[name]})
+            kernels[name] = bytes_entry(per[name], per_mean[name], ab[name])
+        elif name == "dgrad":
+            kernels[name] = gemm_entry(per[name], per_mean[name], GEMM_FLOP, PEAK_FP8_TFLOPS,
+                                       "fp8")
         else:
-            tf = GEMM_FLOP / (t_ms * 1e-3) / 1e12
-            peak = PEAK_FP8_TFLOPS if name == "dgrad" else PEAK_BF16_TFLOPS
-            e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / peak, 4),
-                      "fp4_peak_frac": round(tf / PEAK_FP4_TFLOPS, 4)})
-        kernels[name] = e
+            kernels[name] = gemm_entry(per[name], per_mean[name], GEMM_FLOP, PEAK_FP4_TFLOPS,
+                                       "fp4", PEAK_FP16_TFLOPS)
     print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
+
+    # Outputs of one more step on set 0, kept on the host for the oracle
+    # parity check at the end (whole quantized copies; sampled GEMM outputs).
+    captured = None
+    if want_oracle:
+        step(0)
+        torch.cuda.synchronize()
+        captured = capture_outputs(torch, sets_b[0])
 
     # Activation copy of X with a per-token outer scale and Four Over Six
     # (the first NEXT row; not part of the step) and the fprop GEMM over it.
-    xa = T.empty(M, K, device=dev, sdec_per_row=True)
-    extra = {
-        "quant_x_act": lambda: bbs.nvfp4_quantize(x, xa, row_per_token=True, row_four_six=True),
-        "fprop_act": lambda: bbs.nvfp4_gemm(bbs.FMT_NVFP4, xa, wq, y, bbs.OUT_BF16),
-    }
+    xa = [T.empty(M, K, device=dev, sdec_per_row=True) for _ in sets_b]
     act = {}
-    for name, f in extra.items():
-        f()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(args.steps):
-            f()
-        s1.record()
-        torch.cuda.synchronize()
-        t_ms = s0.elapsed_time(s1) / args.steps
-        e = {"ms": round(t_ms, 4)}
-        if name == "quant_x_act":
-            b = 2 * M * K + nvfp4_bytes(M, K) + 4 * M
-            e.update({"GB/s": round(b / (t_ms * 1e-3) / 1e9, 1), "bytes": b})
-        else:
-            e["TFLOP/s"] = round(GEMM_FLOP / (t_ms * 1e-3) / 1e12, 1)
-        act[name] = e
+    t_med, t_mean = time_calls(torch, [
+        (lambda b=b, a=a: bbs.nvfp4_quantize(b["x"], a, row_per_token=True, row_four_six=True))
+        for b, a in zip(sets_b, xa)])
+    act["quant_x_act"] = bytes_entry(t_med, t_mean, 2 * M * K + nvfp4_bytes(M, K) + 4 * M)
+    t_med, t_mean = time_calls(torch, [
+        (lambda b=b, a=a: bbs.nvfp4_gemm(bbs.FMT_NVFP4, a, b["wq"], b["y"], bbs.OUT_BF16))
+        for b, a in zip(sets_b, xa)])
+    act["fprop_act"] = gemm_entry(t_med, t_mean, GEMM_FLOP, PEAK_FP4_TFLOPS, "fp4",
+                                  PEAK_FP16_TFLOPS)
+    del xa
     print(f"[bench] per-token + 4/6 activation path: {json.dumps(act)}", file=sys.stderr, flush=True)
 
     # The activation quantize with both copies stochastic (4096 x 4096
@@ -405,23 +534,16 @@ def main():
     for _ in range(ROTATE - 1):
         x2.append(x2[0].clone())
     R2 = d2["x"].shape[0]
-    r2, c2 = T.empty(R2, R2, device=dev), T.empty(R2, R2, device=dev)
-    q2 = lambda i: bbs.nvfp4_quantize(x2[i % ROTATE], r2, c2, row_round=bbs.SR,
-                                      row_rng=(d2["seed"], d2["row_stream"]), col_round=bbs.SR,
-                                      col_rng=(d2["seed"], d2["col_stream"]), amax_ws=ws)
-    for i in range(ROTATE):
-        q2(i)
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for i in range(args.steps):
-        q2(i)
-    s1.record()
-    torch.cuda.synchronize()
-    t_ms = s0.elapsed_time(s1) / args.steps
-    b2 = 2 * R2 * R2 + 2 * nvfp4_bytes(R2, R2)
-    act_sr = {"ms": round(t_ms, 4), "GB/s": round(b2 / (t_ms * 1e-3) / 1e9, 1),
-              "hbm_frac": round(b2 / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4), "bytes": b2}
-    del x2, r2, c2
+    o2 = [(T.empty(R2, R2, device=dev), T.empty(R2, R2, device=dev)) for _ in range(ROTATE)]
+    t_med, t_mean = time_calls(torch, [
+        (lambda xi=xi, o=o: bbs.nvfp4_quantize(xi, o[0], o[1], row_round=bbs.SR,
+                                               row_rng=(d2["seed"], d2["row_stream"]),
+                                               col_round=bbs.SR,
+                                               col_rng=(d2["seed"], d2["col_stream"]),
+                                               amax_ws=ws))
+        for xi, o in zip(x2, o2)])
+    act_sr = bytes_entry(t_med, t_mean, 2 * R2 * R2 + 2 * nvfp4_bytes(R2, R2))
+    del x2, o2
     print(f"[bench] activation SR row + col 4096x4096: {json.dumps(act_sr)}", file=sys.stderr,
           flush=True)
 
@@ -429,137 +551,116 @@ def main():
     # layer's two projections): the NVFP4 copy of GELU(H) alone, with its
     # MXFP8 SR copy for the backward pass, and as the per-token + 4/6
     # activation copy.  Each op is the amax pass plus the encode pass.
-    h = up(synth.mlp_hidden(M, N)["h"])
-    hq = T.empty(M, N, device=dev)
-    hm = bbs.MXFP8Tensor.empty(M, N, device=dev)
-    ha = T.empty(M, N, device=dev, sdec_per_row=True)
+    hs = [up(synth.mlp_hidden(M, N)["h"])]
+    for _ in range(ROTATE - 1):
+        hs.append(hs[0].clone())
+    hq = [T.empty(M, N, device=dev) for _ in hs]
+    hm = [bbs.MXFP8Tensor.empty(M, N, device=dev) for _ in hs]
+    ha = [T.empty(M, N, device=dev, sdec_per_row=True) for _ in hs]
+    mx_rng = (synth.MLP_SEEDS["mx8"], 0)
     gelu_ops = {
-        "gelu_quant_row": (lambda: bbs.nvfp4_quantize(h, hq, gelu=True, amax_ws=ws),
-                           2 * M * N + nvfp4_bytes(M, N)),
-        "gelu_quant_row_mx8": (lambda: bbs.nvfp4_quantize(h, hq, None, hm, mx8_round=bbs.SR,
-                                                          mx8_rng=(synth.MLP_SEEDS["mx8"], 0),
-                                                          gelu=True, amax_ws=ws),
-                               2 * M * N + nvfp4_bytes(M, N) + M * N + M * N // 32),
-        "gelu_quant_act": (lambda: bbs.nvfp4_quantize(h, ha, row_per_token=True,
-                                                      row_four_six=True, gelu=True, amax_ws=ws),
-                           2 * M * N + nvfp4_bytes(M, N) + 4 * M),
+        "gelu_quant_row": (
+            [(lambda i=i: bbs.nvfp4_quantize(hs[i], hq[i], gelu=True, amax_ws=ws))
+             for i in range(ROTATE)],
+            2 * M * N + nvfp4_bytes(M, N)),
+        "gelu_quant_row_mx8": (
+            [(lambda i=i: bbs.nvfp4_quantize(hs[i], hq[i], None, hm[i], mx8_round=bbs.SR,
+                                             mx8_rng=mx_rng, gelu=True, amax_ws=ws))
+             for i in range(ROTATE)],
+            2 * M * N + nvfp4_bytes(M, N) + M * N + M * N // 32),
+        "gelu_quant_act": (
+            [(lambda i=i: bbs.nvfp4_quantize(hs[i], ha[i], row_per_token=True,
+                                             row_four_six=True, gelu=True, amax_ws=ws))
+             for i in range(ROTATE)],
+            2 * M * N + nvfp4_bytes(M, N) + 4 * M),
     }
     gelu = {}
-    for name, (f, b) in gelu_ops.items():
-        f()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(args.steps):
-            f()
-        s1.record()
-        torch.cuda.synchronize()
-        t_ms = s0.elapsed_time(s1) / args.steps
-        gelu[name] = {"ms": round(t_ms, 4), "GB/s": round(b / (t_ms * 1e-3) / 1e9, 1),
-                      "bytes": b, "Gelem/s": round(M * N / (t_ms * 1e-3) / 1e9, 1)}
+    for name, (fs, b) in gelu_ops.items():
+        t_med, t_mean = time_calls(torch, fs)
+        gelu[name] = bytes_entry(t_med, t_mean, b)
+        gelu[name]["Gelem/s"] = round(M * N / (t_med * 1e-3) / 1e9, 1)
+    del hs, hq, hm, ha
     # The forward GEMM with the quantize (and GELU) in its epilogue, against
     # the same output through BF16 and a separate quantize pass.  The encode
     # scale is 2688 / the output's amax, taken from a first call.
-    yq = T.empty(M, N, device=dev)
+    yq = [T.empty(M, N, device=dev) for _ in sets_b]
     amax_y = torch.zeros(1, dtype=torch.float32, device=dev)
     s_y = torch.ones(1, dtype=torch.float32, device=dev)
     epi = {}
     for g in (False, True):
-        bbs.nvfp4_gemm_quant(xq, wq, s_y, yq, gelu=g, amax=amax_y)
+        bbs.nvfp4_gemm_quant(sets_b[0]["xq"], sets_b[0]["wq"], s_y, yq[0], gelu=g, amax=amax_y)
         torch.cuda.synchronize()
         s_y.fill_(2688.0 / max(float(amax_y[0]), 1e-30))
         name = "fprop_gelu_quant" if g else "fprop_quant"
-        f = (lambda g=g: bbs.nvfp4_gemm_quant(xq, wq, s_y, yq, gelu=g, amax=amax_y))
-        f()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(args.steps):
-            f()
-        s1.record()
-        torch.cuda.synchronize()
-        t_ms = s0.elapsed_time(s1) / args.steps
-        epi[name] = {"ms": round(t_ms, 4), "TFLOP/s": round(GEMM_FLOP / (t_ms * 1e-3) / 1e12, 1)}
-    f = lambda: bbs.nvfp4_quantize(y, hq, amax_ws=ws)
-    f()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(args.steps):
-        f()
-    s1.record()
-    torch.cuda.synchronize()
-    q_ms = s0.elapsed_time(s1) / args.steps
-    epi["unfused_fprop_bf16_then_quant"] = {"ms": round(per["fprop"] + q_ms, 4)}
+        t_med, t_mean = time_calls(torch, [
+            (lambda b=b, o=o, g=g: bbs.nvfp4_gemm_quant(b["xq"], b["wq"], s_y, o, gelu=g,
+                                                        amax=amax_y))
+            for b, o in zip(sets_b, yq)])
+        epi[name] = gemm_entry(t_med, t_mean, GEMM_FLOP, PEAK_FP4_TFLOPS, "fp4", PEAK_FP16_TFLOPS)
+    q_med, _ = time_calls(torch, [(lambda b=b, o=o: bbs.nvfp4_quantize(b["y"], o, amax_ws=ws))
+                                  for b, o in zip(sets_b, yq)])
+    epi["unfused_fprop_bf16_then_quant"] = {"ms": round(per["fprop"] + q_med, 4)}
     epi["unfused_fprop_bf16_then_gelu_quant"] = {
         "ms": round(per["fprop"] + gelu["gelu_quant_row"]["ms"], 4)}
-    del h, hq, hm, ha, yq
+    del yq
     print(f"[bench] fused GELU + quantize of H {M}x{N}: {json.dumps(gelu)}", file=sys.stderr,
           flush=True)
     print(f"[bench] quantize in the GEMM epilogue: {json.dumps(epi)}", file=sys.stderr, flush=True)
 
     # The layer as a user calls it: the autograd function over the C ABI,
-    # forward alone and forward + backward (allocations and dispatch included).
+    # forward alone and forward + backward (allocations and dispatch
+    # included), one layer (own weight) per buffer set.
     from bit_block_scaled_amd.layer import QLinear
-    layer = QLinear(K, N, seed=seeds["x_col"], rht_signs=signs, device=dev)
-    with torch.no_grad():
-        layer.weight.copy_(w.view(torch.bfloat16))
-    xin = x.view(torch.bfloat16).detach().requires_grad_(True)
-    gin = dy.view(torch.bfloat16)
+    layers = []
+    for b in sets_b:
+        lay = QLinear(K, N, seed=seeds["x_col"], rht_signs=signs, device=dev)
+        with torch.no_grad():
+            lay.weight.copy_(b["w"].view(torch.bfloat16))
+        xin = b["x"].view(torch.bfloat16).detach().requires_grad_(True)
+        layers.append((lay, xin, b["dy"].view(torch.bfloat16)))
 
-    def layer_fwd():
-        layer(xin)
+    def layer_fwd(i):
+        lay, xin, _ = layers[i]
+        lay(xin)
 
-    def layer_fwd_bwd():
-        layer(xin).backward(gin)
+    def layer_fwd_bwd(i):
+        lay, xin, gin = layers[i]
+        lay(xin).backward(gin)
         xin.grad = None
-        layer.weight.grad = None
+        lay.weight.grad = None
 
     layer_t = {}
     for name, f in (("forward", layer_fwd), ("forward_backward", layer_fwd_bwd)):
-        f()
-        torch.cuda.synchronize()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(args.steps):
-            f()
-        s1.record()
-        torch.cuda.synchronize()
-        t_ms = s0.elapsed_time(s1) / args.steps
+        t_med, t_mean = time_calls(torch, [(lambda i=i: f(i)) for i in range(len(layers))])
         flop = GEMM_FLOP * (1 if name == "forward" else 3)
-        layer_t[name] = {"ms": round(t_ms, 4), "TFLOP/s": round(flop / (t_ms * 1e-3) / 1e12, 1)}
-    del layer, xin
+        layer_t[name] = {"ms": round(t_med, 4), "ms_mean": round(t_mean, 4),
+                         "TFLOP/s": round(flop / (t_med * 1e-3) / 1e12, 1)}
+    del layers
     print(f"[bench] QLinear layer (autograd): {json.dumps(layer_t)}", file=sys.stderr, flush=True)
 
     # The MXFP4 comparison format: X and W as MXFP4 (E2M1, E8M0 per 32; RTN)
     # and the same forward GEMM on the block-scaled MFMA with E2M1 operands.
-    x4, w4 = bbs.MXFP4Tensor.empty(M, K, device=dev), bbs.MXFP4Tensor.empty(N, K, device=dev)
-    mx4_ops = {
-        "mxfp4_quant_x": (lambda: bbs.mxfp4_quantize(x, x4), 2 * M * K + M * K // 2 + M * K // 32),
-        "mxfp4_quant_w": (lambda: bbs.mxfp4_quantize(w, w4), 2 * N * K + N * K // 2 + N * K // 32),
-        "mxfp4_fprop": (lambda: bbs.nvfp4_gemm(bbs.FMT_MXFP4, x4, w4, y, bbs.OUT_BF16), None),
-    }
+    x4 = [bbs.MXFP4Tensor.empty(M, K, device=dev) for _ in sets_b]
+    w4 = [bbs.MXFP4Tensor.empty(N, K, device=dev) for _ in sets_b]
     mx4 = {}
-    for name, (f, b) in mx4_ops.items():
-        f()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(args.steps):
-            f()
-        s1.record()
-        torch.cuda.synchronize()
-        t_ms = s0.elapsed_time(s1) / args.steps
-        e = {"ms": round(t_ms, 4)}
-        if b is None:
-            tf = GEMM_FLOP / (t_ms * 1e-3) / 1e12
-            e.update({"TFLOP/s": round(tf, 1), "fp4_peak_frac": round(tf / PEAK_FP4_TFLOPS, 4)})
-        else:
-            e.update({"GB/s": round(b / (t_ms * 1e-3) / 1e9, 1), "bytes": b})
-        mx4[name] = e
+    t_med, t_mean = time_calls(torch, [(lambda b=b, o=o: bbs.mxfp4_quantize(b["x"], o))
+                                       for b, o in zip(sets_b, x4)])
+    mx4["mxfp4_quant_x"] = bytes_entry(t_med, t_mean, 2 * M * K + M * K // 2 + M * K // 32)
+    t_med, t_mean = time_calls(torch, [(lambda b=b, o=o: bbs.mxfp4_quantize(b["w"], o))
+                                       for b, o in zip(sets_b, w4)])
+    mx4["mxfp4_quant_w"] = bytes_entry(t_med, t_mean, 2 * N * K + N * K // 2 + N * K // 32)
+    t_med, t_mean = time_calls(torch, [
+        (lambda b=b, a=a, c=c: bbs.nvfp4_gemm(bbs.FMT_MXFP4, a, c, b["y"], bbs.OUT_BF16))
+        for b, a, c in zip(sets_b, x4, w4)])
+    mx4["mxfp4_fprop"] = gemm_entry(t_med, t_mean, GEMM_FLOP, PEAK_FP4_TFLOPS, "fp4")
     del x4, w4
     print(f"[bench] MXFP4 forward: {json.dumps(mx4)}", file=sys.stderr, flush=True)
 
-    fprop_ms = per["fprop"]
-    fprop_tf = GEMM_FLOP / (fprop_ms * 1e-3) / 1e12
+    fprop_tf = GEMM_FLOP / (per["fprop"] * 1e-3) / 1e12
+    fprop_tf_avg = GEMM_FLOP / (per_mean["fprop"] * 1e-3) / 1e12
     qbytes = ab["quant_x"] + ab["quant_w"]
     q_gbps = qbytes / ((per["quant_x"] + per["quant_w"]) * 1e-3) / 1e9
+    q_all = sum(ab.values()) / (sum(per[k] for k in ab) * 1e-3) / 1e9
     value = 3 * GEMM_FLOP / (ms_per_step * 1e-3) / 1e12
     out = {
         "metric": "NVFP4 quantize GB/s + NVFP4 GEMM TFLOPS (8192x4096x14336), % of roofline",
@@ -572,20 +673,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4/mxfp8 operands, bf16+fp8 MFMA, fp32 accumulate",
+        "dtype": "nvfp4/mxfp8 operands, fp16+fp8 MFMA, fp32 accumulate",
         "data": "synthetic (seeded)",
         "config": {"workload": "dense NVFP4 linear fwd+bwd, X 8192x4096, W 14336x4096, "
                                "dY 8192x14336", "M": M, "K": K, "N": N,
                    "step_gemm_flop": 3 * GEMM_FLOP},
         "quantize_GBps": round(q_gbps, 1),
+        "quantize_GBps_all_passes": round(q_all, 1),
         "gemm_TFLOPs": round(fprop_tf, 1),
         "kernels": kernels,
-        "roofline": {"bound": "mfma", "achieved": round(fprop_tf, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fprop_tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(fprop_tf_avg, 1),
+                     "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fprop_tf_avg / PEAK_FP4_TFLOPS, 4),
                      "traffic": fprop_traffic(), "traffic_unit": "bytes per launch",
                      "kernel": "nvfp4_gemm_big_kernel<true> (fprop, 8192x14336x4096, BF16 out)",
-                     "peak_fp4": PEAK_FP4_TFLOPS,
-                     "frac_fp4": round(fprop_tf / PEAK_FP4_TFLOPS, 4)},
+                     "peak_dtype": "fp4 (the operands' own format)",
+                     "issued_mfma": "v_mfma_f32_32x32x16_f16",
+                     "peak_issued_class": PEAK_FP16_TFLOPS,
+                     "frac_issued_class": round(fprop_tf_avg / PEAK_FP16_TFLOPS, 4)},
         "activation_per_token_4over6": act,
         "activation_sr_row_col_4096x4096": act_sr,
         "gelu_quantize_mlp_hidden_8192x14336": gelu,
@@ -595,15 +700,18 @@ def main():
         "wall_s_timed": round(wall_s, 3),
     }
     if not args.no_moe:
-        del x, w, dy, x0, w0, dy0, xq, xc, wq, y, bufs, ops, sets
+        del x0, w0, dy0, sets_b, sets_o, ops
         torch.cuda.empty_cache()
         print("[bench] MoE grouped GEMMs (65536 tokens, 64 experts, top-8)", file=sys.stderr,
               flush=True)
-        out["moe"] = moe_bench(torch, bbs, dev, max(3, args.steps // 4))
+        out["moe"] = moe_bench(torch, bbs, dev, 100)
         print(f"[bench] moe: {json.dumps(out['moe'])}", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
+    if want_oracle:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()
+        print("[bench] parity of the timed kernels' outputs against the oracle", file=sys.stderr,
+              flush=True)
+        out["parity"] = parity(captured, host_in, signs, seeds)
     print(json.dumps(out), flush=True)
 
 

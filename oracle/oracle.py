@@ -1,8 +1,11 @@
 """Python face of the C oracle (TEST INFRASTRUCTURE; see oracle/nvfp4_oracle.c).
 
 Thin ctypes marshalling over liboracle.so plus plain numpy bookkeeping
-(allocation, reshapes).  Every arithmetic step of the method happens in the C
-file; the only numpy arithmetic here is the error norm used by the checks.
+(allocation, reshapes).  The method's arithmetic happens in the C file, with
+three small exceptions done here in numpy: the maximum of |GELU(x)| taken by
+gelu_quantize (a max, so exact), the FP32 reciprocal 1 / s_enc that
+nvfp4_encode_f32 stores as the decode scale (one IEEE division), and the
+error norms (rel_fro) used by the checks.
 
 Parity note: every function below is pinned by a CPU test in tests/ that
 checks it against what the pages or the mathematics fix (worked examples,
