@@ -102,6 +102,10 @@ __device__ __forceinline__ ARows a_rows(int64_t m0, int64_t m_end, RowMap a_row)
     return ar;
 }
 
+// NJ: 32-column blocks per wave (4: a 256 x 256 tile; 2: a 256 x 128 half
+// tile, whose B side is 128 rows: NJ code copies and NJ / 2 scale copies
+// per wave).
+template <int NJ>
 __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, int64_t K,
                                           const ARows &ar, int64_t n0, int64_t n_end) {
     Plan pl;
@@ -113,19 +117,26 @@ __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, in
     for (int q = 0; q < 4; ++q) {
         const int r = (w * 4 + q) * 16 + (lane >> 2);
         pl.a[q] = A.codes + (int64_t)ar.c[q] * kb + 16 * pos;
+    }
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+        const int r = (w * NJ + q) * 16 + (lane >> 2);
         pl.b[q] = B.codes + brow(r) * kb + 16 * pos;
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int r = (w * 2 + q) * 32 + (lane >> 1);
         const int64_t sa_row = A.tile2d ? ar.s[q] / 16 : ar.s[q];
         pl.sa[q] = A.scales + sa_row * ks + 4 * (lane & 1);
-        if (B.tile2d) {
-            // 16 tile rows: lanes 0..31 (the upper lanes repeat them)
-            const int tr = (lane >> 1) & 15;
-            const int64_t n = min(n0 / 16 + tr, (n_end - 1) / 16);
-            pl.sb[q] = B.scales + n * ks + 4 * (lane & 1);
-        } else {
+    }
+    if (B.tile2d) {
+        // 16 tile rows: lanes 0..31 (the upper lanes repeat them)
+        const int tr = (lane >> 1) & 15;
+        const int64_t n = min(n0 / 16 + tr, (n_end - 1) / 16);
+        pl.sb[0] = pl.sb[1] = B.scales + n * ks + 4 * (lane & 1);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NJ / 2; ++q) {
+            const int r = (w * (NJ / 2) + q) * 32 + (lane >> 1);
             pl.sb[q] = B.scales + brow(r) * ks + 4 * (lane & 1);
         }
     }
@@ -135,7 +146,7 @@ __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, in
 // The copies of one slab, in three parts that the main loop spreads over
 // MFMA steps: 0 = A codes (4 instructions per wave), 1 = B codes (4),
 // 2 = scales (2 + 2, or 2 + 1 when B has 16x16 tiles).
-template <int PART, bool BT>
+template <int PART, bool BT, int NJ>
 __device__ __forceinline__ void issue_part(Stage &st, const Plan &pl, int64_t k0) {
     const int w = threadIdx.x >> 6;
     const int64_t cb = k0 / 2, sk = k0 / 16;
@@ -145,16 +156,16 @@ __device__ __forceinline__ void issue_part(Stage &st, const Plan &pl, int64_t k0
             copy_lds16(pl.a[q] + cb, st.a + (w * 4 + q) * 1024);
     } else if (PART == 1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            copy_lds16(pl.b[q] + cb, st.b + (w * 4 + q) * 1024);
+        for (int q = 0; q < NJ; ++q)
+            copy_lds16(pl.b[q] + cb, st.b + (w * NJ + q) * 1024);
     } else {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
             copy_lds4(pl.sa[q] + sk, st.as + (w * 2 + q) * 256);
         if (!BT) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q)
-                copy_lds4(pl.sb[q] + sk, st.bs + (w * 2 + q) * 256);
+            for (int q = 0; q < NJ / 2; ++q)
+                copy_lds4(pl.sb[q] + sk, st.bs + (w * (NJ / 2) + q) * 256);
         } else {
             // the 16 tile rows (128 bytes); every wave writes the same bytes
             copy_lds4(pl.sb[0] + sk, st.bs);
@@ -162,11 +173,11 @@ __device__ __forceinline__ void issue_part(Stage &st, const Plan &pl, int64_t k0
     }
 }
 
-template <bool BT>
+template <bool BT, int NJ>
 __device__ __forceinline__ void issue(Stage &st, const Plan &pl, int64_t k0) {
-    issue_part<0, BT>(st, pl, k0);
-    issue_part<1, BT>(st, pl, k0);
-    issue_part<2, BT>(st, pl, k0);
+    issue_part<0, BT, NJ>(st, pl, k0);
+    issue_part<1, BT, NJ>(st, pl, k0);
+    issue_part<2, BT, NJ>(st, pl, k0);
 }
 
 // Code words of one 32-byte chunk of a slab for the wave's 4 + 4 fragment
@@ -183,6 +194,7 @@ struct Pairs {
     f16x2 pa[4], pb[4];
 };
 
+template <int NJ>
 __device__ __forceinline__ void load_chunk(Chunk &c, const Stage &st, int chunk, int wm, int wn,
                                            int lane) {
     const int h = lane >> 5, rl = lane & 31;
@@ -192,13 +204,13 @@ __device__ __forceinline__ void load_chunk(Chunk &c, const Stage &st, int chunk,
         c.ca[i] = *reinterpret_cast<const uint4 *>(st.a + r * RB + 16 * swz(r, 2 * chunk + h));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + j * 32 + rl;
+    for (int j = 0; j < NJ; ++j) {
+        const int r = wn * NJ * 32 + j * 32 + rl;
         c.cb[j] = *reinterpret_cast<const uint4 *>(st.b + r * RB + 16 * swz(r, 2 * chunk + h));
     }
 }
 
-template <bool BT>
+template <bool BT, int NJ>
 __device__ __forceinline__ void load_scales(uint2 (&sca)[4], uint2 (&scb)[4], const Stage &st,
                                             int wm, int wn, int lane) {
     const int rl = lane & 31;
@@ -206,12 +218,13 @@ __device__ __forceinline__ void load_scales(uint2 (&sca)[4], uint2 (&scb)[4], co
     for (int i = 0; i < 4; ++i)
         sca[i] = *reinterpret_cast<const uint2 *>(st.as + (wm * 128 + i * 32 + rl) * SB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + j * 32 + rl;
+    for (int j = 0; j < NJ; ++j) {
+        const int r = wn * NJ * 32 + j * 32 + rl;
         scb[j] = *reinterpret_cast<const uint2 *>(st.bs + (BT ? (r >> 4) : r) * SB);
     }
 }
 
+template <int NJ>
 __device__ __forceinline__ void load_pairs(Pairs &p, const uint2 (&sca)[4], const uint2 (&scb)[4],
                                            int chunk, int lane) {
     const int sh = 16 * (lane >> 5);
@@ -219,7 +232,7 @@ __device__ __forceinline__ void load_pairs(Pairs &p, const uint2 (&sca)[4], cons
     for (int i = 0; i < 4; ++i)
         p.pa[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((chunk ? sca[i].y : sca[i].x) >> sh, 1.0f, false);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
         p.pb[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((chunk ? scb[j].y : scb[j].x) >> sh, 1.0f, false);
 }
 
@@ -228,20 +241,22 @@ __device__ __forceinline__ uint32_t word(const uint4 &v, int s) {
 }
 
 // Expanded operands of MFMA step s (0..3) of a chunk.
+template <int NJ>
 __device__ __forceinline__ void expand_step(f16x8 (&af)[4], f16x8 (&bf)[4], const Chunk &c,
                                             const Pairs &p, int s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[i] = expand8_f16(word(c.ca[i], s), p.pa[i][s >> 1]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = expand8_f16(word(c.cb[j], s), p.pb[j][s >> 1]);
+    for (int j = 0; j < NJ; ++j) bf[j] = expand8_f16(word(c.cb[j], s), p.pb[j][s >> 1]);
 }
 
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const f16x8 (&af)[4],
+template <int NJ>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][NJ], const f16x8 (&af)[4],
                                           const f16x8 (&bf)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
@@ -278,26 +293,36 @@ __device__ __forceinline__ void interleave_1_ds_4() {
 }
 
 // One MFMA step in four quarters, fenced from each other: quarter q expands
-// operand pair q of the next step (16 VALU), issues the 4 MFMAs of row block
-// q of this step (interleaved 1:4 with that expansion) and then copy(q), a
-// slab copy or nothing.  The fences keep each copy between MFMAs instead of
-// letting the scheduler gather them into one burst that stalls the wave.
-template <typename Copy>
-__device__ __forceinline__ void step_q(f32x16 (&acc)[4][4], const f16x8 (&af)[4],
+// operand pair q of the next step (A row block q, and B column block q when
+// q < NJ: 16 or 8 VALU), issues the NJ MFMAs of row block q of this step
+// (interleaved with that expansion) and then copy(q), a slab copy or
+// nothing.  The fences keep each copy between MFMAs instead of letting the
+// scheduler gather them into one burst that stalls the wave.
+template <int NJ, typename Copy>
+__device__ __forceinline__ void step_q(f32x16 (&acc)[4][NJ], const f16x8 (&af)[4],
                                        const f16x8 (&bf)[4], f16x8 (&an)[4], f16x8 (&bn)[4],
                                        const Chunk &c, const Pairs &p, int s, Copy copy) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         an[q] = expand8_f16(word(c.ca[q], s), p.pa[q][s >> 1]);
-        bn[q] = expand8_f16(word(c.cb[q], s), p.pb[q][s >> 1]);
+        if (q < NJ) bn[q] = expand8_f16(word(c.cb[q], s), p.pb[q][s >> 1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[q], acc[q][j], 0, 0, 0);
         copy(q);
+        // VALU after each MFMA: the quarter's 16 (q < NJ) or 8 spread evenly
+        if (q < NJ) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            for (int k = 0; k < NJ; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 16 / NJ, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NJ; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8 / NJ, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -349,20 +374,24 @@ __device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)
 // DROP: output rows may be dropped slots of a grouped GEMM, whose scale is
 // 0; adding +0 turns their -0 products into +0, so they come out as the
 // zero rows (and zero blocks) the header promises.
-template <int OUT, bool DROP, typename ScaleFn>
+// NJ: the wave's 32-column blocks (4, or 2 in a 256 x 128 half tile of the
+// plain output modes).
+template <int OUT, bool DROP, int NJ, typename ScaleFn>
 __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
-                                         const f32x16 (&acc)[4][4], int64_t m0, int64_t m_end,
+                                         const f32x16 (&acc)[4][NJ], int64_t m0, int64_t m_end,
                                          int64_t n0, int64_t n_end, ScaleFn scale_of, void *C,
                                          int64_t ldc, int wm, int wn, int lane,
                                          const QuantOut &qo) {
     constexpr bool NVQ = OUT == OUT_Q || OUT == OUT_QG;   // NVFP4 encode
     constexpr bool S2 = OUT == OUT_S2F6;                   // combine wire format
     constexpr bool QUANT = NVQ || S2;
+    static_assert(NJ == 4 || !QUANT, "the encoding epilogues take whole 256-column tiles");
     constexpr bool BF16_OUT = OUT == OUT_BF16 || QUANT;    // BF16 staging
+    constexpr int WC = NJ * 32;                       // the wave's output columns
     constexpr int ES = BF16_OUT ? 2 : 4;              // bytes per element
-    constexpr int RS = 128 * ES + 16;                 // staging row stride
+    constexpr int RS = WC * ES + 16;                  // staging row stride
     constexpr int PR = BF16_OUT ? 32 : 16;            // rows per piece
-    constexpr int LPR = 128 * ES / 16;                // lanes per row on read-back
+    constexpr int LPR = WC * ES / 16;                 // lanes per row on read-back
     constexpr int RPI = 64 / LPR;                     // rows per read-back instruction
     // plain output: pieces alternate between the stage and a second buffer
     // past the ring (where the GELU modes keep their table), so a piece's
@@ -370,7 +399,7 @@ __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
     uint8_t *const buf0 = stage + (threadIdx.x >> 6) * (PR * RS);
     uint8_t *const buf1 = reinterpret_cast<uint8_t *>(const_cast<float *>(tab)) +
                           (threadIdx.x >> 6) * (PR * RS);
-    const int64_t mw = m0 + wm * 128, nw = n0 + wn * 128;
+    const int64_t mw = m0 + wm * 128, nw = n0 + wn * WC;
     const int lr = lane & 31;                          // the lane's row in a 32-row block
     float s_enc = 1.0f, s_dec = 1.0f, amax = 0.0f;
     if (NVQ) {
@@ -388,7 +417,7 @@ __device__ __forceinline__ void epilogue(uint8_t *stage, const float *tab,
             if (lr / PR == piece) {
                 uint8_t *row = buf + (lr - piece * PR) * RS;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int c = j * 32 + 8 * g + 4 * (lane >> 5);
@@ -523,7 +552,8 @@ struct TileRef {
 //   b_view(g)              group g's B operand
 //   a_row(m)               source row of A for output row m (< 0: none)
 //   scale_of(m, g)         output scale of row m in group g's tile
-template <int OUT, bool BT, bool DROP, typename Next, typename BView, typename RowMap, typename ScaleFn>
+template <int OUT, bool BT, bool DROP, int NJ, typename Next, typename BView, typename RowMap,
+          typename ScaleFn>
 __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams &p,
                                           Next next_tile, BView b_view, RowMap a_row,
                                           ScaleFn scale_of) {
@@ -531,16 +561,16 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t K = p.K, N = p.N;
     // global_load_lds instructions one wave issues per slab
-    constexpr int kIssued = 4 + 4 + 2 + (BT ? 1 : 2);
+    constexpr int kIssued = 4 + NJ + 2 + (BT ? 1 : NJ / 2);
     const int64_t nslab = K / BK;
 
     TileRef cur;
     if (!next_tile(cur)) return;
     if (OUT == OUT_QG) gelu_table_load(tab, p.q.gelu_tab);   // ordered by the first barrier
-    Plan pl = make_plan(p.a, b_view(cur.g), K, a_rows(cur.m0, cur.m_end, a_row), cur.n0, N);
+    Plan pl = make_plan<NJ>(p.a, b_view(cur.g), K, a_rows(cur.m0, cur.m_end, a_row), cur.n0, N);
     int cs = 0;                                   // stage holding the current slab
-    issue<BT>(sm.st[0], pl, 0);
-    if (nslab > 1) issue<BT>(sm.st[1], pl, BK);
+    issue<BT, NJ>(sm.st[0], pl, 0);
+    if (nslab > 1) issue<BT, NJ>(sm.st[1], pl, BK);
 
     for (;;) {
         // the next tile (the last tile repeats itself: its copies land in
@@ -554,20 +584,20 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
         wait_vmcnt<0>();
         __syncthreads();
 
-        f32x16 acc[4][4];
+        f32x16 acc[4][NJ];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{0};
+            for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{0};
 
         uint2 sca[4], scb[4];
         Chunk c0, c1;
         Pairs p0, p1;
         f16x8 af[4], bf[4], an[4], bn[4];
-        load_scales<BT>(sca, scb, sm.st[cs], wm, wn, lane);
-        load_chunk(c0, sm.st[cs], 0, wm, wn, lane);
-        load_pairs(p0, sca, scb, 0, lane);
-        expand_step(af, bf, c0, p0, 0);
+        load_scales<BT, NJ>(sca, scb, sm.st[cs], wm, wn, lane);
+        load_chunk<NJ>(c0, sm.st[cs], 0, wm, wn, lane);
+        load_pairs<NJ>(p0, sca, scb, 0, lane);
+        expand_step<NJ>(af, bf, c0, p0, 0);
 
         // The 8 MFMA steps of the current slab, with the expansion of step
         // k + 1 under the MFMAs of step k, and the copies of the slab at
@@ -582,15 +612,17 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
                 copy_lds16(pl.a[q] + kn / 2, dst.a + (wave * 4 + q) * 1024);
             };
             auto copy_b = [&](int q) {
-                copy_lds16(pl.b[q] + kn / 2, dst.b + (wave * 4 + q) * 1024);
+                if (q < NJ) copy_lds16(pl.b[q] + kn / 2, dst.b + (wave * NJ + q) * 1024);
             };
             auto copy_s = [&](int q) {
                 if (q < 2) copy_lds4(pl.sa[q] + kn / 16, dst.as + (wave * 2 + q) * 256);
-                else if (!BT) copy_lds4(pl.sb[q - 2] + kn / 16, dst.bs + (wave * 2 + q - 2) * 256);
-                else if (q == 2) copy_lds4(pl.sb[0] + kn / 16, dst.bs);
+                else if (!BT) {
+                    if (q - 2 < NJ / 2)
+                        copy_lds4(pl.sb[q - 2] + kn / 16, dst.bs + (wave * (NJ / 2) + q - 2) * 256);
+                } else if (q == 2) copy_lds4(pl.sb[0] + kn / 16, dst.bs);
             };
-            load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
-            load_pairs(p1, sca, scb, 1, lane);
+            load_chunk<NJ>(c1, sm.st[cs], 1, wm, wn, lane);
+            load_pairs<NJ>(p1, sca, scb, 1, lane);
             step_q(acc, af, bf, an, bn, c0, p0, 1, copy_a);
             step_q(acc, an, bn, af, bf, c0, p0, 2, copy_b);
             step_q(acc, af, bf, an, bn, c0, p0, 3, copy_s);
@@ -599,11 +631,11 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
             // the next slab is complete once every wave has seen its own copies land
             wait_vmcnt<kIssued>();
             __syncthreads();
-            load_scales<BT>(sca, scb, sm.st[ns], wm, wn, lane);
-            load_chunk(c0, sm.st[ns], 0, wm, wn, lane);
+            load_scales<BT, NJ>(sca, scb, sm.st[ns], wm, wn, lane);
+            load_chunk<NJ>(c0, sm.st[ns], 0, wm, wn, lane);
             step_q(acc, an, bn, af, bf, c1, p1, 2, none);
             step_q(acc, af, bf, an, bn, c1, p1, 3, none);
-            load_pairs(p0, sca, scb, 0, lane);
+            load_pairs<NJ>(p0, sca, scb, 0, lane);
             step_q(acc, an, bn, af, bf, c0, p0, 0, none);
             cs = ns;
         };
@@ -614,7 +646,7 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
         for (int64_t s = 0; s + 2 < nslab; ++s) slab((s + 2) * BK, two_ahead());
         if (nslab > 1) {
             // the second-to-last slab: its look-ahead copy is the next tile's slab 0
-            pl = make_plan(p.a, b_view(nxt.g), K, nar, nxt.n0, N);
+            pl = make_plan<NJ>(p.a, b_view(nxt.g), K, nar, nxt.n0, N);
             slab(0, two_ahead());
         }
         // The last slab, copying the next tile's slab 1 into the stage the
@@ -622,7 +654,7 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
         // the free stage).
         {
             const int c1s = cs == 2 ? 0 : cs + 1, c2s = c1s == 2 ? 0 : c1s + 1;
-            if (nslab == 1) pl = make_plan(p.a, b_view(nxt.g), K, nar, nxt.n0, N);
+            if (nslab == 1) pl = make_plan<NJ>(p.a, b_view(nxt.g), K, nar, nxt.n0, N);
             const int64_t kl = nslab > 1 ? BK : 0;
             Stage &dst = sm.st[nslab > 1 ? c2s : c1s];
             auto none = [](int) {};
@@ -630,15 +662,17 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
                 copy_lds16(pl.a[q] + kl / 2, dst.a + (wave * 4 + q) * 1024);
             };
             auto copy_b = [&](int q) {
-                copy_lds16(pl.b[q] + kl / 2, dst.b + (wave * 4 + q) * 1024);
+                if (q < NJ) copy_lds16(pl.b[q] + kl / 2, dst.b + (wave * NJ + q) * 1024);
             };
             auto copy_s = [&](int q) {
                 if (q < 2) copy_lds4(pl.sa[q] + kl / 16, dst.as + (wave * 2 + q) * 256);
-                else if (!BT) copy_lds4(pl.sb[q - 2] + kl / 16, dst.bs + (wave * 2 + q - 2) * 256);
-                else if (q == 2) copy_lds4(pl.sb[0] + kl / 16, dst.bs);
+                else if (!BT) {
+                    if (q - 2 < NJ / 2)
+                        copy_lds4(pl.sb[q - 2] + kl / 16, dst.bs + (wave * (NJ / 2) + q - 2) * 256);
+                } else if (q == 2) copy_lds4(pl.sb[0] + kl / 16, dst.bs);
             };
-            load_chunk(c1, sm.st[cs], 1, wm, wn, lane);
-            load_pairs(p1, sca, scb, 1, lane);
+            load_chunk<NJ>(c1, sm.st[cs], 1, wm, wn, lane);
+            load_pairs<NJ>(p1, sca, scb, 1, lane);
             step_q(acc, af, bf, an, bn, c0, p0, 1, copy_a);
             step_q(acc, an, bn, af, bf, c0, p0, 2, copy_b);
             step_q(acc, af, bf, an, bn, c0, p0, 3, copy_s);
@@ -651,7 +685,7 @@ __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams
         // every wave is done reading stage cs: it becomes the staging area
         __syncthreads();
         const int g = cur.g;
-        epilogue<OUT, DROP>(reinterpret_cast<uint8_t *>(&sm.st[cs]), tab, acc, cur.m0, cur.m_end,
+        epilogue<OUT, DROP, NJ>(reinterpret_cast<uint8_t *>(&sm.st[cs]), tab, acc, cur.m0, cur.m_end,
                       cur.n0, N, [&](int64_t m) { return scale_of(m, g); }, p.c, p.ldc, wm, wn,
                       lane, p.q);
         if (!more) break;
@@ -693,11 +727,17 @@ __device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_ra
     if ((OUT == big::OUT_Q || OUT == big::OUT_QG) && blockIdx.x == 0 && threadIdx.x == 0)
         p.q.s_dec[0] = 1.0f / p.q.s_enc[0];
     const int64_t tm = (p.M + big::BM - 1) / big::BM, tn = (p.N + big::BN - 1) / big::BN;
-    TileWalk walk(tm * tn);
+    const int64_t total = tm * tn, grid = gridDim.x;
+    // A last round of whole tiles that would leave more than half the
+    // workgroups idle is run as twice as many 256 x 128 half tiles (plain
+    // output modes): every workgroup then takes one half, and the round
+    // costs about half a tile instead of a whole one.
+    constexpr bool kHalves = OUT == big::OUT_F32 || OUT == big::OUT_BF16;
+    const int64_t rem = total % grid;
+    const bool split = kHalves && rem > 0 && 2 * rem <= grid;
+    const int64_t n_whole = split ? total - rem : total;
     const int64_t M = p.M;
-    auto next_tile = [&](big::TileRef &r) -> bool {
-        int64_t tid;
-        if (!walk.take(tid)) return false;
+    auto tile_at = [&](int64_t tid, big::TileRef &r) {
         // grouped order: GROUP_M tiles down M, then along N
         const int64_t gsize = big::GROUP_M * tn;
         const int64_t g = tid / gsize, in = tid - g * gsize;
@@ -706,6 +746,22 @@ __device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_ra
         r.m_end = M;
         r.n0 = (in / gm) * big::BN;
         r.g = 0;
+    };
+    TileWalk walk(n_whole);
+    auto next_tile = [&](big::TileRef &r) -> bool {
+        int64_t tid;
+        if (!walk.take(tid)) return false;
+        tile_at(tid, r);
+        return true;
+    };
+    // half h: tile n_whole + h / 2, columns 128 * (h % 2) onwards (both
+    // halves of a tile fall in one XCD's contiguous share)
+    TileWalk half_walk(split ? 2 * rem : 0);
+    auto next_half = [&](big::TileRef &r) -> bool {
+        int64_t h;
+        if (!half_walk.take(h)) return false;
+        tile_at(n_whole + (h >> 1), r);
+        r.n0 += (h & 1) * (big::BN / 2);
         return true;
     };
     const Fp4View B = p.b;
@@ -714,9 +770,22 @@ __device__ __forceinline__ void dense_body(const GemmParams &p, uint8_t *smem_ra
     const float sb = p.b.s_dec[0];
     auto run = [&](auto scale_of) {
         if (p.b.tile2d)
-            big::run_tiles<OUT, true, false>(sm, tab, p, next_tile, b_view, ident, scale_of);
+            big::run_tiles<OUT, true, false, 4>(sm, tab, p, next_tile, b_view, ident, scale_of);
         else
-            big::run_tiles<OUT, false, false>(sm, tab, p, next_tile, b_view, ident, scale_of);
+            big::run_tiles<OUT, false, false, 4>(sm, tab, p, next_tile, b_view, ident, scale_of);
+        if constexpr (kHalves) {
+            if (split) {
+                // the last whole tile's epilogue has read its staging rows
+                // before the ring is refilled
+                __syncthreads();
+                if (p.b.tile2d)
+                    big::run_tiles<OUT, true, false, 2>(sm, tab, p, next_half, b_view, ident,
+                                                        scale_of);
+                else
+                    big::run_tiles<OUT, false, false, 2>(sm, tab, p, next_half, b_view, ident,
+                                                         scale_of);
+            }
+        }
     };
     if (p.a.sdec_rows) {
         const float *sa = p.a.s_dec;
@@ -799,9 +868,9 @@ __device__ __forceinline__ void grouped_body(const GemmParams &p, uint8_t *smem_
     const float *sdb = p.b.s_dec;
     auto run = [&](auto scale_of) {
         if (B0.tile2d)
-            big::run_tiles<OUT, true, true>(sm, tab, p, next_tile, b_view, gather, scale_of);
+            big::run_tiles<OUT, true, true, 4>(sm, tab, p, next_tile, b_view, gather, scale_of);
         else
-            big::run_tiles<OUT, false, true>(sm, tab, p, next_tile, b_view, gather, scale_of);
+            big::run_tiles<OUT, false, true, 4>(sm, tab, p, next_tile, b_view, gather, scale_of);
     };
     // the output scale of row m: the decode scale of the A row it was
     // computed from times the expert's; 0 for a dropped slot (its copies
@@ -911,7 +980,9 @@ hipError_t launch_grouped_nvfp4_gemm_s2f6(const GemmParams &p, hipStream_t s) {
 }
 
 hipError_t launch_nvfp4_gemm_big(const GemmParams &p, bool bf16_out, hipStream_t s) {
-    const int64_t grid = persistent_grid(dense_tiles(p), s);
+    // up to two workgroups per tile, so that fewer tiles than CUs run as
+    // half tiles
+    const int64_t grid = persistent_grid(2 * dense_tiles(p), s);
     if (bf16_out) launch_with_smem<nvfp4_gemm_big_kernel<true>>(grid, kSmemPlain, p, s);
     else launch_with_smem<nvfp4_gemm_big_kernel<false>>(grid, kSmemPlain, p, s);
     return hipGetLastError();
