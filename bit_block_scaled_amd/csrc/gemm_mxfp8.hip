@@ -154,9 +154,9 @@ constexpr int kIssued8 = 18;
 // The MFMAs of one FP8 slab with all of the wave's fragments read into
 // registers at its start (8 A + 8 B, 128 VGPRs).  After row block 1 every
 // wave has its fragments, so after one barrier the stage is free and the
-// copies of slab sn (two slabs ahead) go into it during row blocks 2-5:
-// they get most of two slabs to land, where copying into the other stage of
-// a two-stage ring gives them one.
+// copies of slab sn (two slabs ahead) go into it during row blocks 2-5, one
+// between every second pair of MFMAs: they get most of two slabs to land,
+// where copying into the other stage of a two-stage ring gives them one.
 __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8], int wm,
                                              int wn, int lane, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
@@ -187,23 +187,25 @@ __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 8; ++j) {
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0,
                                                                          bsc[j], 0, asc[i]);
+            // row blocks 2-5: one copy after every second MFMA (A and B in
+            // turn), the scale copies after row block 5
+            if (i >= 2 && i < 6 && (j & 1)) {
+                const int c = (i - 2) * 4 + (j >> 1), q = c >> 1;
+                if (c & 1) copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
+                else copy_lds16(pl.a_base + kn + pl.a_off[q], st.a + (w * 8 + q) * 1024);
+            }
+            if (i == 6 && j == 0) issue_scales(st, pl, sn);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (i == 1) {
             // this wave's fragment reads are complete; once every wave's are,
             // nobody reads the stage again in this slab
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();
         }
-        if (i >= 2 && i < 6) {
-#pragma unroll
-            for (int q = 2 * (i - 2); q < 2 * (i - 2) + 2; ++q) {
-                copy_lds16(pl.a_base + kn + pl.a_off[q], st.a + (w * 8 + q) * 1024);
-                copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
-            }
-        }
-        if (i == 5) issue_scales(st, pl, sn);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
