@@ -44,9 +44,9 @@ COPY_BYTES = 1 << 29                            # counter calibration copy (512 
 ROTATE = 8                                     # buffer sets the timed runs cycle through
 # HBM bytes per launch of the fprop GEMM, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
-# (profiles/hbm_traffic_step_moe_codec_counters.md), valid only for the kernel
+# (profiles/sq_hbm_counters_step_kernels_8192x4096x14336.md), valid only for the kernel
 # sources they were taken on: reported as null once those sources change.
-FPROP_TRAFFIC = {"bytes": 630826517, "sources_sha256_16": "a9c3771744defed3"}
+FPROP_TRAFFIC = {"bytes": 631962779, "sources_sha256_16": "89157230cacb19d0"}
 FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
                  "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
 
