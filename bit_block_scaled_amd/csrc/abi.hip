@@ -429,10 +429,23 @@ int quantize_impl(const bbs_quant_args *a, float *ws_in, hipStream_t s) {
     }
     const bool rht = a->col && a->col_rht;
     const bool plain = a->row || (a->col && !rht);
+    // An MXFP8 row copy needs no tensor scale: when an amax pass runs anyway
+    // (and no GELU), that pass writes it from the same read.
+    const bool mx_in_amax = a->row_mx8 && !gelu && (plain || rht);
+    p.rht_signs = a->rht_signs;
+    if (a->row_mx8) {
+        p.mx_codes = a->row_mx8->codes;
+        p.mx_scales = a->row_mx8->scales;
+        p.mx_round = a->mx8_round;
+        p.mx_seed = a->mx8_rng.seed;
+        p.mx_stream = a->mx8_rng.stream;
+    }
     if (plain || rht) {
         float *ws = ws_in;
-        hipError_t e = bbs::launch_amax(a->x, a->rows, a->cols, a->ld, plain, rht, a->rht_signs,
-                                        ws, ws + bbs::kAmaxPartials, &p.n_part, s, gelu_tab);
+        hipError_t e =
+            mx_in_amax ? bbs::launch_amax_mx(p, plain, rht, ws, ws + bbs::kAmaxPartials, &p.n_part, s)
+                       : bbs::launch_amax(a->x, a->rows, a->cols, a->ld, plain, rht, a->rht_signs,
+                                          ws, ws + bbs::kAmaxPartials, &p.n_part, s, gelu_tab);
         if ((st = hip_status(e, "amax launch"))) return st;
         p.part = ws;
         p.part_rht = ws + bbs::kAmaxPartials;
@@ -457,15 +470,9 @@ int quantize_impl(const bbs_quant_args *a, float *ws_in, hipStream_t s) {
         p.col_stream = a->col_rng.stream;
         p.rht_signs = a->rht_signs;
     }
-    if (a->row_mx8) {
-        p.mx_codes = a->row_mx8->codes;
-        p.mx_scales = a->row_mx8->scales;
-        p.mx_round = a->mx8_round;
-        p.mx_seed = a->mx8_rng.seed;
-        p.mx_stream = a->mx8_rng.stream;
-    }
     hipError_t e = bbs::launch_quant_tile(p, a->row != nullptr, a->col != nullptr,
-                                          a->row_mx8 != nullptr, a->tile2d != 0, rht, s, gelu);
+                                          a->row_mx8 != nullptr && !mx_in_amax, a->tile2d != 0,
+                                          rht, s, gelu);
     return hip_status(e, "quantize launch");
 }
 

@@ -131,6 +131,10 @@ hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool
 hipError_t launch_gelu_table(float *gelu_tab, hipStream_t s);
 // gelu: the row-wise copies (NVFP4 and / or MXFP8, no column copy, 1x16) are
 // of GELU(x).
+// The amax pass (plain and / or RHT partials) fused with the MXFP8 row copy
+// described by p (p.rht_signs for the RHT); *n_part = the partials written.
+hipError_t launch_amax_mx(const QuantParams &p, bool plain, bool rht, float *part, float *part_rht,
+                          int *n_part, hipStream_t s);
 hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, bool has_mx,
                              bool tile2d, bool rht, hipStream_t s, bool gelu = false);
 hipError_t launch_requant(const RequantParams &p, bool sr, hipStream_t s);

@@ -604,8 +604,15 @@ __device__ __forceinline__ void put_scales4(uint8_t *dst, uint32_t word, int64_t
     }
 }
 
-template <bool HAS_ROW, bool HAS_MX, bool TILE2D, bool GELU, bool SR, int MINW>
-__global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p) {
+// AP / AR: the kernel is also the amax pass of a quantize whose other copies
+// need the tensor scale: it writes the MXFP8 copy (which needs none) and the
+// per-workgroup partials of |x| (AP) and of |RHT(column chunks)| (AR), as
+// amax_kernel does, from the same read.
+template <bool HAS_ROW, bool HAS_MX, bool TILE2D, bool GELU, bool SR, int MINW, bool AP = false,
+          bool AR = false>
+__global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, float *amax_part,
+                                                               float *amax_part_rht) {
+    static_assert(!(AP || AR) || (!HAS_ROW && !GELU), "the amax pass feeds the later copies");
     __shared__ __align__(16) RowsLds L;
     __shared__ __align__(16) float s_gelu[GELU ? kGeluTabSize : 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -642,12 +649,30 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p) {
     __syncthreads();
 
     const int64_t n_step = p.C / 8;
+    float am = 0.0f, amr = 0.0f;                      // amax partials (AP, AR)
     while (t < T) {                                   // wave-uniform
         const int64_t tn = t + stride;
         uint4 vn[16];
         int64_t r0n = r0, c0n = c0;
         if (tn < T) load(tn, vn, r0n, c0n);
         const bool in = c0 < p.C;
+        if (AP && in) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(elem(v[r], j)));
+        }
+        if (AR && in) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float y[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
+                rht16_butterflies(y, p.rht_signs);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) amr = fmaxf(amr, fabsf(y[r]));
+            }
+        }
         auto val = [&](int r, int j) -> float {
             if constexpr (GELU) return gelu_bf16(elem_bits(v[r], j), s_gelu);
             else return elem(v[r], j);
@@ -754,6 +779,27 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p) {
         c0 = c0n;
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = vn[i];
+    }
+    if constexpr (AP || AR) {
+        // the workgroup's partials (the RHT's final multiply by 1/4 is
+        // monotonic, so it is applied to the maximum)
+        am = wave_max(am);
+        amr = wave_max(amr * 0.25f);
+        __shared__ float red[2][kQT / 64];
+        if (lane == 0) {
+            red[0][w] = am;
+            red[1][w] = amr;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float a = red[0][0], b = red[1][0];
+            for (int i = 1; i < kQT / 64; ++i) {
+                a = fmaxf(a, red[0][i]);
+                b = fmaxf(b, red[1][i]);
+            }
+            if (AP) amax_part[blockIdx.x] = a;
+            if (AR) amax_part_rht[blockIdx.x] = b;
+        }
     }
 }
 
@@ -1241,7 +1287,37 @@ static void launch_rows_k(const QuantParams &p, hipStream_t s) {
     constexpr int MW = 2;                             // (a cap of 4 spills with SR)
     constexpr auto k = quant_rows_kernel<R_, M_, T_, G_, SR_, MW>;
     const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC - 1) / kAmaxStepC);
-    hipLaunchKernelGGL(k, dim3(persistent_grid<k>((steps + 3) / 4, s)), dim3(kQT), 0, s, p);
+    hipLaunchKernelGGL(k, dim3(persistent_grid<k>((steps + 3) / 4, s)), dim3(kQT), 0, s, p,
+                       nullptr, nullptr);
+}
+
+// The amax pass of a quantize with an MXFP8 row copy (no GELU): the row-step
+// kernel writes that copy, which needs no tensor scale, and the partials the
+// encode of the other copies folds, from one read of x.
+template <bool SR_, bool AP_, bool AR_>
+static int launch_amax_mx_k(const QuantParams &p, float *part, float *part_rht, hipStream_t s) {
+    constexpr int MW = 2;
+    constexpr auto k = quant_rows_kernel<false, true, false, false, SR_, MW, AP_, AR_>;
+    const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC - 1) / kAmaxStepC);
+    int64_t grid = persistent_grid<k>((steps + 3) / 4, s);
+    if (grid > kAmaxPartials) grid = kAmaxPartials;
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kQT), 0, s, p, part, part_rht);
+    return (int)grid;
+}
+
+hipError_t launch_amax_mx(const QuantParams &p, bool plain, bool rht, float *part, float *part_rht,
+                          int *n_part, hipStream_t s) {
+    const bool sr = p.mx_round == 1;
+    int n = 0;
+    if (plain && rht) n = sr ? launch_amax_mx_k<true, true, true>(p, part, part_rht, s)
+                             : launch_amax_mx_k<false, true, true>(p, part, part_rht, s);
+    else if (plain) n = sr ? launch_amax_mx_k<true, true, false>(p, part, part_rht, s)
+                           : launch_amax_mx_k<false, true, false>(p, part, part_rht, s);
+    else if (rht) n = sr ? launch_amax_mx_k<true, false, true>(p, part, part_rht, s)
+                         : launch_amax_mx_k<false, false, true>(p, part, part_rht, s);
+    else return hipErrorInvalidValue;
+    *n_part = n;
+    return hipGetLastError();
 }
 template <bool R_, bool M_, bool T_, bool G_>
 static void launch_rows(const QuantParams &p, bool sr, hipStream_t s) {
