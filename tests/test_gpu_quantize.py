@@ -136,6 +136,37 @@ def test_backward_pass_combination(bbs):
     _same_mx8(mq, O.mxfp8_quantize(x, mode=O.SR, seed=1, stream=3), "all: MXFP8")
 
 
+MX_COMBOS = [
+    # (row, col, tile2d, rht): the MXFP8 row copy beside copies that need the
+    # tensor amax, which the amax pass then writes from its own read
+    (False, True, False, True),     # dY: columns RHT + MXFP8
+    (True, False, False, False),    # rows 1x16 + MXFP8
+    (True, False, True, False),     # rows 16x16 + MXFP8
+    (True, True, False, False),     # rows + columns + MXFP8
+    (True, True, False, True),      # rows + RHT'd columns + MXFP8
+]
+
+
+@pytest.mark.parametrize("shape", [(32, 96), (64, 1056), (144, 544), (272, 1600)])
+@pytest.mark.parametrize("combo", MX_COMBOS, ids=["colrht", "row", "row2d", "rowcol", "rowcolrht"])
+@pytest.mark.parametrize("mode", [O.RTN, O.SR], ids=["rtn", "sr"])
+def test_mxfp8_beside_amax_copies(bbs, shape, combo, mode):
+    row, col, tile2d, rht = combo
+    R, C = shape
+    announce(f"MXFP8 + copies {combo} {shape} mode={mode}")
+    x = synth.laplace(R, C, 7000 + R + 3 * C, 1e-3)
+    s = synth.rht_signs(402) if rht else 0
+    rq, cq, mq = _gpu_quantize(bbs, x, row=row, col=col, mx=True, tile2d=tile2d, rht=rht, signs=s,
+                               row_round=mode, col_round=mode, mx_round=mode,
+                               row_rng=(11, 1), col_rng=(11, 2), mx_rng=(11, 3))
+    _same_mx8(mq, O.mxfp8_quantize(x, mode=mode, seed=11, stream=3), "MXFP8")
+    if row:
+        _same_fp4(rq, O.nvfp4_quantize(x, tile2d=tile2d, mode=mode, seed=11, stream=1), "row")
+    if col:
+        _same_fp4(cq, O.nvfp4_quantize(x, transpose=True, tile2d=tile2d, rht=rht, signs=s,
+                                       mode=mode, seed=11, stream=2), "col")
+
+
 def test_degenerate_inputs(bbs):
     announce("zero / negative-zero / single-outlier tensors")
     z = np.zeros((32, 64), np.uint16)
