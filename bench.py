@@ -133,9 +133,11 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline():
-    """The oracle, as it stands, on a bounded slice of the same step; each
-    component's time is scaled to the full size by the share of work sampled."""
+def cpu_baseline(full_quant=None):
+    """The oracle, as it stands, on a bounded sample of the same step: the
+    quantize parts at full size when the parity leg has timed them
+    (full_quant), else on the slices below; the FP64 GEMMs on slices, each
+    scaled to the full size by the share of work sampled."""
     import oracle as O
     from workloads import synth
     ms, ns = 512, 2048                    # sampled token rows / weight rows
@@ -158,6 +160,8 @@ def cpu_baseline():
     t0 = time.perf_counter()
     wt = O.mxfp8_requantize_t(wq, mode=O.SR, seed=406)
     t["requant_w"] = (time.perf_counter() - t0) * (N / ns)
+    if full_quant:
+        t.update(full_quant)
     # GEMMs: FP64 over dequantized operands, on ms x ns outputs
     t0 = time.perf_counter()
     O.gemm_f64(xq.dequant_f64(), wq.dequant_f64())
@@ -175,10 +179,12 @@ def cpu_baseline():
         "unit": "TFLOP/s",
         "cores": O.num_threads(),
         "kind": "oracle",
-        "sample": (f"X/dY slices of {ms} token rows, W slice of {ns} rows; fprop on {ms}x{ns} "
-                   f"outputs, dgrad on {ms}x{K} outputs over {ns} of N, wgrad on {ns}x{ns} "
-                   f"outputs over {ms} tokens; each part's time scaled to the full step by "
-                   f"its work ratio"),
+        "sample": ((("quantize passes (X, W, dY, W requantize) at full size; " if full_quant else
+                     f"quantize passes on X/dY slices of {ms} token rows and a W slice of {ns} "
+                     f"rows; ") +
+                    f"FP64 GEMMs on slices: fprop on {ms}x{ns} outputs, dgrad on {ms}x{K} outputs "
+                    f"over {ns} of N, wgrad on {ns}x{ns} outputs over {ms} tokens; each sliced "
+                    f"part's time scaled to the full step by its work ratio")),
         "extrapolated_step_s": round(total, 2),
         "parts_s": {k: round(v, 2) for k, v in t.items()},
     }
@@ -237,16 +243,24 @@ def parity(cap, host_in, signs, seeds):
     import oracle as O
     t0 = time.perf_counter()
     x, w, dy = host_in["x"], host_in["w"], host_in["dy"]
-    ref = {
-        "xq": O.nvfp4_quantize(x),
-        "xc": O.nvfp4_quantize(x, transpose=True, rht=True, signs=signs, mode=O.SR,
-                               seed=seeds["x_col"], stream=0),
-        "wq": O.nvfp4_quantize(w, tile2d=True),
-        "gc": O.nvfp4_quantize(dy, transpose=True, rht=True, signs=signs, mode=O.SR,
-                               seed=seeds["dy_col"], stream=0),
-        "gm": O.mxfp8_quantize(dy, mode=O.SR, seed=seeds["dy_mx8"], stream=0),
-    }
-    ref["wt"] = O.mxfp8_requantize_t(ref["wq"], mode=O.SR, seed=seeds["w_req"], stream=0)
+    ref, op_s = {}, {}
+
+    def timed(op, fn):
+        t1 = time.perf_counter()
+        fn()
+        op_s[op] = time.perf_counter() - t1
+
+    timed("quant_x", lambda: ref.update(
+        xq=O.nvfp4_quantize(x),
+        xc=O.nvfp4_quantize(x, transpose=True, rht=True, signs=signs, mode=O.SR,
+                            seed=seeds["x_col"], stream=0)))
+    timed("quant_w", lambda: ref.update(wq=O.nvfp4_quantize(w, tile2d=True)))
+    timed("quant_dy", lambda: ref.update(
+        gc=O.nvfp4_quantize(dy, transpose=True, rht=True, signs=signs, mode=O.SR,
+                            seed=seeds["dy_col"], stream=0),
+        gm=O.mxfp8_quantize(dy, mode=O.SR, seed=seeds["dy_mx8"], stream=0)))
+    timed("requant_w", lambda: ref.update(
+        wt=O.mxfp8_requantize_t(ref["wq"], mode=O.SR, seed=seeds["w_req"], stream=0)))
     t_quant = time.perf_counter() - t0
     res = {}
     for key in ("xq", "xc", "wq", "gc", "gm", "wt"):
@@ -277,7 +291,7 @@ def parity(cap, host_in, signs, seeds):
                      "max_abs_err": float(err.max())}
     res["oracle_s"] = round(time.perf_counter() - t0, 2)
     res["oracle_quantize_full_size_s"] = round(t_quant, 2)
-    return res
+    return res, op_s
 
 
 def moe_bench(torch, bbs, dev, reps):
@@ -707,11 +721,11 @@ def main():
         out["moe"] = moe_bench(torch, bbs, dev, 100)
         print(f"[bench] moe: {json.dumps(out['moe'])}", file=sys.stderr, flush=True)
     if want_oracle:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline()
         print("[bench] parity of the timed kernels' outputs against the oracle", file=sys.stderr,
               flush=True)
-        out["parity"] = parity(captured, host_in, signs, seeds)
+        out["parity"], full_quant = parity(captured, host_in, signs, seeds)
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(full_quant)
     print(json.dumps(out), flush=True)
 
 
