@@ -650,11 +650,18 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
 
     const int64_t n_step = p.C / 8;
     float am = 0.0f, amr = 0.0f;                      // amax partials (AP, AR)
+    // The next step is loaded while this one is encoded, except in the amax
+    // pass variants: their RHT and stochastic MXFP8 work needs the registers,
+    // and without the look-ahead they run three waves per SIMD instead of
+    // two (measured faster).
+    constexpr bool kAhead = !(AP || AR);
     while (t < T) {                                   // wave-uniform
         const int64_t tn = t + stride;
-        uint4 vn[16];
+        uint4 vn[kAhead ? 16 : 1];
         int64_t r0n = r0, c0n = c0;
-        if (tn < T) load(tn, vn, r0n, c0n);
+        if constexpr (kAhead) {
+            if (tn < T) load(tn, vn, r0n, c0n);
+        }
         const bool in = c0 < p.C;
         if (AP && in) {
 #pragma unroll
@@ -775,10 +782,14 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
             rows(F_{}, F_{});
         }
         t = tn;
-        r0 = r0n;
-        c0 = c0n;
+        if constexpr (kAhead) {
+            r0 = r0n;
+            c0 = c0n;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = vn[i];
+            for (int i = 0; i < 16; ++i) v[i] = vn[i];
+        } else if (t < T) {
+            load(t, v, r0, c0);
+        }
     }
     if constexpr (AP || AR) {
         // the workgroup's partials (the RHT's final multiply by 1/4 is
@@ -1296,7 +1307,9 @@ static void launch_rows_k(const QuantParams &p, hipStream_t s) {
 // encode of the other copies folds, from one read of x.
 template <bool SR_, bool AP_, bool AR_>
 static int launch_amax_mx_k(const QuantParams &p, float *part, float *part_rht, hipStream_t s) {
-    constexpr int MW = 2;
+    // three waves per SIMD for the RHT partials alone (153 VGPRs); with the
+    // plain partials a cap of three spills, so two
+    constexpr int MW = AP_ ? 2 : 3;
     constexpr auto k = quant_rows_kernel<false, true, false, false, SR_, MW, AP_, AR_>;
     const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC - 1) / kAmaxStepC);
     int64_t grid = persistent_grid<k>((steps + 3) / 4, s);
