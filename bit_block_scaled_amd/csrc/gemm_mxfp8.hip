@@ -152,11 +152,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr int kIssued8 = 18;
 
 // The MFMAs of one FP8 slab with all of the wave's fragments read into
-// registers at its start (8 A + 8 B, 128 VGPRs).  After row block 1 every
-// wave has its fragments, so after one barrier the stage is free and the
-// copies of slab sn (two slabs ahead) go into it during row blocks 2-5, one
-// between every second pair of MFMAs: they get most of two slabs to land,
-// where copying into the other stage of a two-stage ring gives them one.
+// registers at its start (8 A + 8 B, 128 VGPRs), in the order the MFMAs use
+// them: the MFMAs run in growing squares (shell k = the blocks that need
+// fragments k and below), so the first waits for two reads instead of nine.
+// After shell 4 every wave has its fragments, so after one barrier the stage
+// is free and the copies of slab sn (two slabs ahead) go into it during
+// shells 5-7, one after every second MFMA: they get most of two slabs to
+// land, where copying into the other stage of a two-stage ring gives them one.
 __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8], int wm,
                                              int wn, int lane, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
@@ -164,49 +166,46 @@ __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8
     const int64_t kn = sn * BK;
     i32x8 af[8], bf[8];
     int asc[8], bsc[8];
-    // A fragment 0 and the B fragments first: LDS returns in order, so the
-    // first row block's MFMAs wait only for the reads they use
-    {
-        const int r = wm * 128 + rl;
-        af[0] = frag(st.a, r, g);
-        asc[0] = (int)((st.as[0][r] >> (8 * g)) & 0xFFu);
-    }
+    // fragments in the order the MFMAs need them: A0, B0, A1, B1, ...
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = wn * 128 + j * 16 + rl;
-        bf[j] = frag(st.b, r, g);
-        bsc[j] = (int)((st.bs[0][r] >> (8 * g)) & 0xFFu);
-    }
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {
-        const int r = wm * 128 + i * 16 + rl;
-        af[i] = frag(st.a, r, g);
-        asc[i] = (int)((st.as[0][r] >> (8 * g)) & 0xFFu);
+    for (int k = 0; k < 8; ++k) {
+        const int ra = wm * 128 + k * 16 + rl, rb = wn * 128 + k * 16 + rl;
+        af[k] = frag(st.a, ra, g);
+        asc[k] = (int)((st.as[0][ra] >> (8 * g)) & 0xFFu);
+        bf[k] = frag(st.b, rb, g);
+        bsc[k] = (int)((st.bs[0][rb] >> (8 * g)) & 0xFFu);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // MFMAs in growing squares: shell k adds (i, k) for i < k and (k, j) for
+    // j <= k, so it needs only fragments 0..k
+    int c = 0;                                         // copies issued
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int k = 0; k < 8; ++k) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int e = 0; e < 2 * k + 1; ++e) {
+            const int i = e < k ? e : k, j = e < k ? k : e - k;
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0,
                                                                          bsc[j], 0, asc[i]);
-            // row blocks 2-5: one copy after every second MFMA (A and B in
-            // turn), the scale copies after row block 5
-            if (i >= 2 && i < 6 && (j & 1)) {
-                const int c = (i - 2) * 4 + (j >> 1), q = c >> 1;
-                if (c & 1) copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
-                else copy_lds16(pl.a_base + kn + pl.a_off[q], st.a + (w * 8 + q) * 1024);
+            // shells 5-7: one copy after every second MFMA (A and B in turn),
+            // then the scale copies
+            if (k >= 5 && (e & 1)) {
+                if (c < 16) {
+                    const int q = c >> 1;
+                    if (c & 1) copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
+                    else copy_lds16(pl.a_base + kn + pl.a_off[q], st.a + (w * 8 + q) * 1024);
+                } else if (c == 16) {
+                    issue_scales(st, pl, sn);
+                }
+                ++c;
             }
-            if (i == 6 && j == 0) issue_scales(st, pl, sn);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (i == 1) {
+        if (k == 4) {
             // this wave's fragment reads are complete; once every wave's are,
             // nobody reads the stage again in this slab
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
