@@ -651,10 +651,10 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
     const int64_t n_step = p.C / 8;
     float am = 0.0f, amr = 0.0f;                      // amax partials (AP, AR)
     // The next step is loaded while this one is encoded, except in the amax
-    // pass variants: their RHT and stochastic MXFP8 work needs the registers,
-    // and without the look-ahead they run three waves per SIMD instead of
-    // two (measured faster).
-    constexpr bool kAhead = !(AP || AR);
+    // pass variants and the GELU copy: their RHT, stochastic MXFP8 or GELU
+    // work needs the registers, and without the look-ahead they run three or
+    // four waves per SIMD instead of two (measured faster).
+    constexpr bool kAhead = !(AP || AR) && !GELU;
     while (t < T) {                                   // wave-uniform
         const int64_t tn = t + stride;
         uint4 vn[kAhead ? 16 : 1];
@@ -1295,7 +1295,9 @@ static void launch_q(const QuantParams &p, bool sr, hipStream_t s) {
 // Row-wise copies only: a resident grid of 16 x 512 wave steps.
 template <bool R_, bool M_, bool T_, bool G_, bool SR_>
 static void launch_rows_k(const QuantParams &p, hipStream_t s) {
-    constexpr int MW = 2;                             // (a cap of 4 spills with SR)
+    // (GELU, no look-ahead: 104 VGPRs; the others keep two steps in
+    // registers, and a cap of four spills with SR)
+    constexpr int MW = G_ ? 4 : 2;
     constexpr auto k = quant_rows_kernel<R_, M_, T_, G_, SR_, MW>;
     const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC - 1) / kAmaxStepC);
     hipLaunchKernelGGL(k, dim3(persistent_grid<k>((steps + 3) / 4, s)), dim3(kQT), 0, s, p,
@@ -1346,6 +1348,7 @@ hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, b
     if (gelu) {
         if (has_col || tile2d || rht) return hipErrorInvalidValue;
         if (has_row && has_mx) launch_q<1, 0, 1, 0, 0, 1>(p, sr, s);
+        else if (has_row && !sr) launch_rows_k<1, 0, 0, 1, false>(p, s);
         else if (has_row) launch_q<1, 0, 0, 0, 0, 1>(p, sr, s);
         else if (has_mx) launch_q<0, 0, 1, 0, 0, 1>(p, sr, s);
         else return hipErrorInvalidValue;
