@@ -1334,9 +1334,9 @@ hipError_t launch_amax_mx(const QuantParams &p, bool plain, bool rht, float *par
     *n_part = n;
     return hipGetLastError();
 }
+// nearest-rounding row copies
 template <bool R_, bool M_, bool T_, bool G_>
-static void launch_rows(const QuantParams &p, bool sr, hipStream_t s) {
-    (void)sr;                                         // nearest-rounding copies only
+static void launch_rows(const QuantParams &p, hipStream_t s) {
     launch_rows_k<R_, M_, T_, G_, false>(p, s);
 }
 
@@ -1356,16 +1356,18 @@ hipError_t launch_quant_tile(const QuantParams &p, bool has_row, bool has_col, b
     }
     // Row-wise copies only, all rounding to nearest: light ALU work, so the
     // resident row-step kernel (whole-row stores, next step loaded ahead)
-    // is used; the stochastic ones keep the tile kernel's four waves per SIMD.
+    // is used; the stochastic ones keep the tile kernel's four waves per SIMD
+    // (GELU rows to nearest take the row-step kernel above, without the
+    // look-ahead).
     if (!has_col && !sr) {
         if (has_row && has_mx) {
-            if (tile2d) launch_rows<1, 1, 1, 0>(p, false, s);
-            else launch_rows<1, 1, 0, 0>(p, false, s);
+            if (tile2d) launch_rows<1, 1, 1, 0>(p, s);
+            else launch_rows<1, 1, 0, 0>(p, s);
         } else if (has_row) {
-            if (tile2d) launch_rows<1, 0, 1, 0>(p, false, s);
-            else launch_rows<1, 0, 0, 0>(p, false, s);
+            if (tile2d) launch_rows<1, 0, 1, 0>(p, s);
+            else launch_rows<1, 0, 0, 0>(p, s);
         } else if (has_mx) {
-            launch_rows<0, 1, 0, 0>(p, false, s);
+            launch_rows<0, 1, 0, 0>(p, s);
         } else {
             return hipErrorInvalidValue;
         }
