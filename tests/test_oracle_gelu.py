@@ -49,6 +49,28 @@ def test_gelu_close_to_x_phi_x():
     assert np.argmax(dev) != 0
 
 
+def test_gelu_matches_fp64_tanh_form_on_every_bf16():
+    """The oracle's FP32 GELU against the same tanh form evaluated in FP64
+    with libm's tanh, on every finite BF16 input: within 2 x (ulp of the
+    result + 2^-24 |x|) (the second term covers the cancellation in
+    1 + tanh for large negative x; the largest ratio seen is 1.42).  A
+    cubic coefficient off in its fourth digit (0.04472) is 26 times the
+    unit away, a wrong sqrt(2/pi) or a dropped half further still."""
+    b = np.arange(65536, dtype=np.uint32)
+    b = b[(b & 0x7F80) != 0x7F80]
+    x = (b << 16).view(np.float32)
+    xd = x.astype(np.float64)
+    a = math.sqrt(2.0 / math.pi) * (xd + 0.044715 * xd ** 3)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = 0.5 * xd * (1.0 + np.tanh(a))
+    ok = np.isfinite(ref)
+    g = O.gelu_f32(x).astype(np.float64)
+    unit = np.spacing(np.abs(ref[ok]).astype(np.float32)).astype(np.float64) + \
+        2.0 ** -24 * np.abs(xd[ok])
+    ratio = np.abs(g[ok] - ref[ok]) / unit
+    assert ratio.max() <= 2.0, (ratio.max(), xd[ok][np.argmax(ratio)])
+
+
 def test_gelu_special_values():
     x = np.float32([0.0, 10.0, 37.5, 1e4, -6.0, -10.0, -1e4])
     g = O.gelu_f32(x)
