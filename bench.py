@@ -106,6 +106,15 @@ def bytes_entry(t_med, t_mean, b):
             "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4), "bytes": b}
 
 
+def two_pass_bytes():
+    """Bytes each quantize op moves through HBM: the amax pass's read of the
+    source, then the encode's read and its outputs (the requantize is one
+    pass)."""
+    ab = algorithmic_bytes()
+    return {"quant_x": ab["quant_x"] + 2 * M * K, "quant_w": ab["quant_w"] + 2 * N * K,
+            "quant_dy": ab["quant_dy"] + 2 * M * N, "requant_w": ab["requant_w"]}
+
+
 def algorithmic_bytes():
     """Bytes each memory-bound pass must move (one read of its input + its outputs)."""
     x_in, w_in, dy_in = 2 * M * K, 2 * N * K, 2 * M * N
@@ -516,6 +525,22 @@ def main():
                                        "fp4", PEAK_FP16_TFLOPS)
     print(f"[bench] per-kernel: {json.dumps(kernels)}", file=sys.stderr, flush=True)
 
+    # The streaming ceiling on this GPU: a plain 512 MiB device copy (read +
+    # write), against which the bytes each quantize op moves are set.
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    c_med, c_mean = time_calls(torch, [lambda: dst.copy_(src)], n=20, warm=3)
+    copy_gbps = 2 * COPY_BYTES / (c_med * 1e-3) / 1e9
+    del src, dst
+    moved = two_pass_bytes()
+    vs_copy = {"copy_GBps": round(copy_gbps, 1)}
+    for name, b in moved.items():
+        gbps = b / (per[name] * 1e-3) / 1e9
+        vs_copy[name] = {"moved_bytes": b, "moved_GBps": round(gbps, 1),
+                         "frac_of_copy": round(gbps / copy_gbps, 4)}
+    print(f"[bench] quantize ops against a device copy: {json.dumps(vs_copy)}", file=sys.stderr,
+          flush=True)
+
     # Outputs of one more step on set 0, kept on the host for the oracle
     # parity check at the end (whole quantized copies; sampled GEMM outputs).
     captured = None
@@ -694,6 +719,7 @@ def main():
                    "step_gemm_flop": 3 * GEMM_FLOP},
         "quantize_GBps": round(q_gbps, 1),
         "quantize_GBps_all_passes": round(q_all, 1),
+        "quantize_vs_copy": vs_copy,
         "gemm_TFLOPs": round(fprop_tf, 1),
         "kernels": kernels,
         "roofline": {"bound": "mfma", "achieved": round(fprop_tf_avg, 1),
