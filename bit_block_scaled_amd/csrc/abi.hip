@@ -350,7 +350,9 @@ namespace {
 
 // The quantizer behind nvfp4_quantize and nvfp4_quantize_noalloc: ws is the
 // amax workspace (BBS_AMAX_WS_FLOATS floats, 16-byte aligned) or nullptr.
-int quantize_impl(const bbs_quant_args *a, float *ws_in, hipStream_t s) {
+// Validates every argument and, unless check_only, enqueues the passes.
+// ws_in: the amax workspace (the caller's or the library's scratch).
+int quantize_impl(const bbs_quant_args *a, float *ws_in, hipStream_t s, bool check_only = false) {
     if (!a) return fail(BBS_EINVAL, "null args");
     if (!a->x) return fail(BBS_EINVAL, "null x");
     if (!a->row && !a->col && !a->row_mx8) return fail(BBS_EINVAL, "no output copy requested");
@@ -402,6 +404,7 @@ int quantize_impl(const bbs_quant_args *a, float *ws_in, hipStream_t s) {
             return fail(BBS_EINVAL, "row_mx8 copy must be rows x cols");
         if (!round_ok(a->mx8_round)) return fail(BBS_EINVAL, "bad mx8_round");
     }
+    if (check_only) return BBS_OK;
 
     bbs::QuantParams p{};
     p.x = a->x;
@@ -518,9 +521,12 @@ int nvfp4_quantize_noalloc(const bbs_quant_args *a, void *stream) {
     if (a->amax_ws)
         return fail(BBS_EINVAL, "nvfp4_quantize_noalloc uses its own scratch: amax_ws must be NULL");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    float *ws = nullptr;
-    int st = scratch_of(s, &ws);
+    // arguments first (the scratch stands in by any aligned address), so a
+    // bad call fails the same way with or without a device
+    int st = quantize_impl(a, reinterpret_cast<float *>(static_cast<uintptr_t>(256)), s, true);
     if (st) return st;
+    float *ws = nullptr;
+    if ((st = scratch_of(s, &ws))) return st;
     return quantize_impl(a, ws, s);
 }
 

@@ -56,7 +56,8 @@ enum bbs_fmt { BBS_FMT_NVFP4 = 0, BBS_FMT_MXFP8 = 1, BBS_FMT_MXFP4 = 2 };
  * FP32 decode scale (G scales for the stacked weights of grouped_nvfp4_gemm),
  * or, with sdec_per_row = 1, to one per row (an activation copy with a
  * per-token outer scale, 4bit.vizuara.ai section 11; 1x16 blocks only).
- * codes must be 16-byte aligned; rows and cols must be multiples of 16. */
+ * codes must be 16-byte aligned; rows and cols must be positive multiples of
+ * 16 (an empty tensor is BBS_EINVAL). */
 typedef struct {
     uint8_t *codes;
     uint8_t *scales;
@@ -101,7 +102,8 @@ typedef struct {
  * (that copy is skipped); at least one must be given. */
 typedef struct {
     const uint16_t *x; /* BF16 source, rows x cols, row stride ld elements   */
-    int64_t rows, cols, ld; /* rows, cols % 16 == 0; ld % 8 == 0; x 16B aligned */
+    int64_t rows, cols, ld; /* rows, cols > 0 and % 16 == 0; ld % 8 == 0;
+                               x 16B aligned */
 
     bbs_fp4 *row;      /* NVFP4 copy of x (blocks along cols), shape rows x cols */
     int32_t row_round; /* BBS_RTN or BBS_SR */

@@ -102,6 +102,31 @@ def test_error_paths_return_status(lib):
     assert L.bbs_strerror(bbs.BBS_EINVAL) == b"invalid argument"
 
 
+def test_empty_tensors_are_rejected(lib):
+    """Zero rows or columns are invalid shapes (BBS_EINVAL, nothing
+    launched), for the quantizer, the requantizer and the GEMMs."""
+    import bit_block_scaled_amd as bbs
+    L = bbs.lib
+    for rows, cols in ((0, 32), (32, 0), (0, 0)):
+        a = bbs.QuantArgs()
+        a.x, a.rows, a.cols, a.ld, a.amax_ws = 0x1000, rows, cols, max(cols, 16), 0x4000
+        d = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, rows, cols, 0)
+        a.row = C.pointer(d)
+        assert L.nvfp4_quantize(C.byref(a), None) == bbs.BBS_EINVAL, (rows, cols)
+        a.amax_ws = None
+        assert L.nvfp4_quantize_noalloc(C.byref(a), None) == bbs.BBS_EINVAL, (rows, cols)
+        assert b"amax_ws" not in L.bbs_last_error()
+        src = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, rows, cols, 0)
+        dst = bbs.Mx8Desc(0x1000, 0x2000, cols, rows)
+        assert L.mxfp8_requantize_t(C.byref(src), C.byref(dst), 0, bbs.Rng(0, 0), None) == \
+            bbs.BBS_EINVAL
+    A = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 0, 64, 0)
+    B = bbs.Fp4Desc(0x1000, 0x2000, 0x3000, 48, 64, 0)
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 48, None) == bbs.BBS_EINVAL
+    A.rows, B.rows = 32, 0
+    assert L.nvfp4_gemm(0, C.byref(A), C.byref(B), C.c_void_p(0x5000), 0, 48, None) == bbs.BBS_EINVAL
+
+
 def test_activation_option_errors(lib):
     """Per-token / Four Over Six: only on a lone 1x16 RTN row copy whose
     descriptor carries per-row decode scales exactly when per-token."""
