@@ -9,12 +9,15 @@
 //   pass 2  quant_kernel: every workgroup folds the partials into the tensor
 //           amax (bit-identical everywhere) and walks a run of 256-row x
 //           128-column tiles of x, loading the next tile while it encodes
-//           this one.  A thread owns a 16 x 8 piece of a tile, loaded as 16
-//           rows of 16 bytes.  From that one read it writes any of: the
-//           row-wise NVFP4 copy (a 1x16 block is two neighbouring lanes), the
-//           column-wise NVFP4 copy of x^T (eight full column blocks per
-//           thread, optional RHT), and the row-wise MXFP8 copy (a block of 32
-//           is four lanes).  The column copy's codes and every copy's block
+//           this one.  A workgroup has 512 threads and a thread owns an
+//           8 x 8 piece of a tile, loaded as 8 rows of 16 bytes.  From that
+//           one read it writes any of: the row-wise NVFP4 copy (a 1x16 block
+//           is two neighbouring lanes), the column-wise NVFP4 copy of x^T
+//           (lanes l and l ^ 16 hold the two halves of a 16 x 8 block and
+//           trade halves, after which each encodes four full column blocks,
+//           optional RHT; without row-wise copies a thread loads a 16 x 4
+//           piece instead and needs no exchange), and the row-wise MXFP8
+//           copy (a block of 32 is four lanes).  The column copy's codes and every copy's block
 //           scales are gathered in LDS and written as whole runs: each
 //           transposed row's 128 code bytes of a tile are one store of eight
 //           lanes.  Block encode scales 1 / (E4M3 x s_dec) come from a table
@@ -35,6 +38,7 @@
 namespace bbs {
 
 constexpr int kQT = 256;                       // threads per workgroup
+constexpr int kET = 512;                       // threads of the tile encode kernel
 constexpr int kTileR = 256, kTileC = 128;      // quantizer tile of x
 constexpr int kReqR = 128, kReqC = 512;        // requantizer tile of the source
 
@@ -66,14 +70,23 @@ __device__ __forceinline__ TileWalk xcd_walk(int64_t T) {
     return {lo + j, hi, gx};
 }
 
-// A thread's 16 x 8 piece of a quantizer tile.
+// A thread's piece of a quantizer tile; wave w holds the 16-row bands 2w
+// and 2w + 1 (lanes 0-31 and 32-63).
+//   with row-wise copies: the 8 x 8 piece half `half` of band `band`,
+//     columns 8 cg .. 8 cg + 7 (v[i] = row i); the two halves of a band's
+//     16 x 8 block are lanes l and l ^ 16.
+//   column copy only (CO): the 16 x 4 piece of band `band`, columns
+//     4 cg .. 4 cg + 3 (words 0-1 of v[i] = row i, words 2-3 = row i + 8).
+// col0 is the first of the four columns whose 16-row blocks the lane
+// encodes for the column copy.
 struct Piece {
     int64_t R0, C0;   // the tile's first row / column
     int64_t r0, c0;   // the piece's first row / column
-    int band, cg;     // 16-row band and 8-column group inside the tile
+    int band, half, cg, col0;
     bool in;          // the piece lies inside x (R, C are multiples of 16)
 };
 
+template <bool CO>
 __device__ __forceinline__ Piece piece_of(int64_t tile, int64_t R, int64_t C) {
     const int64_t tiles_c = (C + kTileC - 1) / kTileC;
     const int64_t tr = tile / tiles_c;
@@ -81,29 +94,81 @@ __device__ __forceinline__ Piece piece_of(int64_t tile, int64_t R, int64_t C) {
     q.R0 = tr * kTileR;
     q.C0 = (tile - tr * tiles_c) * kTileC;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    q.band = w * 4 + (lane >> 4);
-    q.cg = lane & 15;
-    q.r0 = q.R0 + q.band * 16;
-    q.c0 = q.C0 + q.cg * 8;
-    q.in = q.r0 < R && q.c0 < C;
+    q.band = w * 2 + (lane >> 5);
+    if (CO) {
+        q.half = 0;
+        q.cg = lane & 31;
+        q.r0 = q.R0 + q.band * 16;
+        q.c0 = q.C0 + q.cg * 4;
+        q.col0 = q.cg * 4;
+    } else {
+        q.half = (lane >> 4) & 1;
+        q.cg = lane & 15;
+        q.r0 = q.R0 + q.band * 16 + q.half * 8;
+        q.c0 = q.C0 + q.cg * 8;
+        q.col0 = q.cg * 8 + q.half * 4;
+    }
+    q.in = q.R0 + q.band * 16 < R && q.c0 < C;
     return q;
 }
 
-// 16 rows of 16 bytes.  A piece outside x reads a valid piece instead (its
-// results are never stored), so the loads need no branches.
+// 8 rows of 16 bytes, or (CO) 16 rows of 8 bytes.  A piece outside x reads a
+// valid piece instead (its results are never stored), so the loads need no
+// branches.
+template <bool CO>
 __device__ __forceinline__ void load_piece(const uint16_t *x, int64_t R, int64_t C, int64_t ld,
-                                           const Piece &q, uint4 v[16]) {
-    const int64_t r = q.r0 < R ? q.r0 : R - 16;
-    const int64_t c = q.c0 < C ? q.c0 : C - 8;
-    const uint16_t *src = x + r * ld + c;
+                                           const Piece &q, uint4 v[8]) {
+    if (CO) {
+        const int64_t r = q.r0 < R ? q.r0 : R - 16;
+        const int64_t c = q.c0 < C ? q.c0 : C - 4;
+        const uint16_t *src = x + r * ld + c;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + i * ld);
+        for (int i = 0; i < 8; ++i) {
+            const uint2 a = *reinterpret_cast<const uint2 *>(src + i * ld);
+            const uint2 b = *reinterpret_cast<const uint2 *>(src + (i + 8) * ld);
+            v[i] = make_uint4(a.x, a.y, b.x, b.y);
+        }
+    } else {
+        const int64_t r = q.r0 < R ? q.r0 : R - 8;
+        const int64_t c = q.c0 < C ? q.c0 : C - 8;
+        const uint16_t *src = x + r * ld + c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4 *>(src + i * ld);
+    }
+}
+
+// v_permlane16_swap: in each 32-lane group, lanes 16-31 of a trade places
+// with lanes 0-15 of b.  Lanes l and l ^ 16 hold the two halves of a 16-row
+// block, so this is how they exchange data.
+__device__ __forceinline__ void swap_halves(uint32_t &a, uint32_t &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+
+// max(v of lane l, v of lane l ^ 16)
+__device__ __forceinline__ float max_half_pair(float v) {
+    uint32_t a = __float_as_uint(v), b = a;
+    swap_halves(a, b);
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
 
 // Element j (compile-time) of a row of 8 BF16 values, as FP32.
 __device__ __forceinline__ float elem(const uint4 &row, int j) {
     const uint32_t w = j < 2 ? row.x : (j < 4 ? row.y : (j < 6 ? row.z : row.w));
     return (j & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+}
+
+// The same with the sign flipped when sg (0 or 0x80000000) is set, as one
+// integer operation (for an even j, adding sg to w << 16 flips bit 31 alone).
+// The RHT's sign flips are applied here, and its butterflies then called
+// with no signs.
+__device__ __forceinline__ float elem_flip(const uint4 &row, int j, uint32_t sg) {
+    const uint32_t w = j < 2 ? row.x : (j < 4 ? row.y : (j < 6 ? row.z : row.w));
+    return __uint_as_float((j & 1) ? ((w & 0xFFFF0000u) ^ sg) : ((w << 16) + sg));
+}
+__device__ __forceinline__ uint32_t sign_bit(uint32_t signs, int i) {
+    return ((signs >> i) & 1u) << 31;
 }
 
 // Element j (compile-time) of a row of 8 BF16 values, as BF16 bits.
@@ -180,8 +245,8 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
             for (int j = 0; j < 8; ++j) {
                 float y[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
-                rht16_butterflies(y, signs);
+                for (int r = 0; r < 16; ++r) y[r] = elem_flip(v[r], j, sign_bit(signs, r));
+                rht16_butterflies(y, 0u);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mr = fmaxf(mr, fabsf(y[r]));
             }
@@ -265,7 +330,7 @@ struct QuantLds {
     uint8_t mx[kTileR * 4];            // MXFP8 scales
     uint8_t colc[kTileC * 128];        // column copy codes
     float tab[2][128];                 // encode scale per E4M3 code: row, column copy
-    float fold[2][kQT / 64];           // per-wave maxima of the amax partials
+    float fold[2][kET / 64];           // per-wave maxima of the amax partials
     float gelu[GELU ? kGeluTabSize : 1];
 };
 __device__ __forceinline__ int colc_off(int row, int group) {
@@ -273,14 +338,16 @@ __device__ __forceinline__ int colc_off(int row, int group) {
 }
 
 // Encode one tile (piece q, values v) into every requested copy.  Every
-// thread of the workgroup calls it (two barriers inside).
+// thread of the workgroup calls it (two barriers inside).  The column copy
+// rearranges v.
 // SR: some copy rounds stochastically (else every copy rounds to nearest and
 // the stochastic paths are not compiled).
 template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT, bool GELU, bool SR>
 __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q,
-                                            const uint4 (&v)[16], float s_enc_row,
+                                            uint4 (&v)[8], float s_enc_row,
                                             float s_enc_col, QuantLds<GELU> &L) {
     const int lane = threadIdx.x & 63;
+    constexpr bool CO = !HAS_ROW && !HAS_MX;
     // Element j of row r of the piece, as the row-wise copies see it (GELU:
     // looked up where it is used, so the piece stays in its BF16 registers).
     auto val = [&](int r, int j) -> float {
@@ -288,15 +355,17 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
         else return elem(v[r], j);
     };
 
-    // 16x16 tile amax (two lanes hold one tile; TILE2D excludes RHT).
+    // 16x16 tile amax (lanes l, l ^ 1, l ^ 16, l ^ 17 hold one tile; CO: four
+    // neighbouring lanes; TILE2D excludes RHT).
     float tile_amax = 0.0f;
     if (TILE2D) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
             for (int j = 0; j < 8; ++j) tile_amax = fmaxf(tile_amax, fabsf(elem(v[r], j)));
-        tile_amax = max_lane_pair(tile_amax);
+        tile_amax = CO ? max_lane_quad(tile_amax) : max_half_pair(max_lane_pair(tile_amax));
     }
+    const int prow = q.band * 16 + q.half * 8;       // the piece's first row in the tile
 
     // ---- row-wise copies (NVFP4 and MXFP8), one row of the piece at a time ----
     uint32_t tsc = 0;
@@ -319,7 +388,7 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
             for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
             sc = block_scale_code(max_lane_pair(a), s_enc_row);
             s = L.tab[0][sc];
-            if ((lane & 1) == 0) L.row[(q.band * 16 + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
+            if ((lane & 1) == 0) L.row[(prow + r) * 8 + (q.cg >> 1)] = (uint8_t)sc;
         }
         uint32_t packed;
         if constexpr (RSR) {
@@ -364,22 +433,17 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
             hi = e4m3_rne4_scaled(y[4], y[5], y[6], y[7], cs);
         }
         if (q.in) *reinterpret_cast<uint2 *>(p.mx_codes + (q.r0 + r) * p.C + q.c0) = make_uint2(lo, hi);
-        if ((lane & 3) == 0) L.mx[(q.band * 16 + r) * 4 + (q.cg >> 2)] = (uint8_t)kb;
+        if ((lane & 3) == 0) L.mx[(prow + r) * 4 + (q.cg >> 2)] = (uint8_t)kb;
     };
-    // (two loops of 8 rows: each stays under the compiler's full-unroll
-    // limit, so the piece's registers are never indexed at run time)
     auto rows = [&](auto row_sr, auto mx_sr) {
-        auto one = [&](int r) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
             float f[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) f[j] = val(r, j);
             if (HAS_ROW) row_copy(row_sr, r, f);
             if (HAS_MX) mx_copy(mx_sr, r, f);
-        };
-#pragma unroll
-        for (int r = 0; r < 8; ++r) one(r);
-#pragma unroll
-        for (int r = 8; r < 16; ++r) one(r);
+        }
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -394,7 +458,7 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
             rows(F_{}, F_{});
         }
     }
-    if (HAS_ROW && TILE2D && (lane & 1) == 0) L.row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
+    if (HAS_ROW && TILE2D && (lane & 17) == 0) L.row[q.band * 8 + (q.cg >> 1)] = (uint8_t)tsc;
 
     // ---- column-wise NVFP4 copy (of x^T) ---------------------------------------
     if (HAS_COL) {
@@ -404,27 +468,63 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
             csc = block_scale_code(tile_amax, s_enc_col);
             cts = L.tab[1][csc];
         }
-        auto cols = [&](auto sr_tag) {
+        // Lanes l and l ^ 16 hold rows 0-7 and 8-15 of one 16 x 8 block; after
+        // one exchange lane l (half 0) holds columns 0-3 of all 16 rows and
+        // lane l ^ 16 columns 4-7: words 0-1 of v[i] are row i, words 2-3 row
+        // i + 8, of the lane's four columns (the layout CO pieces load).
+        if (!CO) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                swap_halves(v[i].x, v[i].z);
+                swap_halves(v[i].y, v[i].w);
+            }
+        }
+        const int col0 = q.col0;
+        // FUSE: the RHT's 1/4 rides in the block's encode scale.  The block
+        // amax is max |y| / 4 either way (rounding is monotonic), and
+        // (y / 4) s = y (s / 4) is one rounding of the same product while y / 4
+        // and s / 4 are exact; the caller takes the separate multiply unless
+        // the tensor scale bounds every s to [2^-109, 2^89], where an inexact
+        // y / 4 (|y| < 2^-124) gives a product far below any code's threshold.
+        auto cols = [&](auto sr_tag, auto fuse_tag) {
             constexpr bool CSR = decltype(sr_tag)::value;
-            // counter of the first block of column q.c0's chunk; column j adds R / 8
-            const uint64_t n0 = (uint64_t)(q.c0 * p.R + q.r0) / 8;
+            constexpr bool FUSE = decltype(fuse_tag)::value;
+            // counter of the first block of the lane's first column in this
+            // band; each further column adds R / 8
+            const uint64_t n0 = (uint64_t)((q.C0 + col0) * p.R + q.R0 + q.band * 16) / 8;
             const uint64_t nstep = (uint64_t)p.R / 8;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 float y[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
-                if (RHT) rht16(y, p.rht_signs);
+                for (int r = 0; r < 8; ++r) {
+                    if (RHT) {
+                        y[r] = elem_flip(v[r], j, sign_bit(p.rht_signs, r));
+                        y[r + 8] = elem_flip(v[r], 4 + j, sign_bit(p.rht_signs, r + 8));
+                    } else {
+                        y[r] = elem(v[r], j);
+                        y[r + 8] = elem(v[r], 4 + j);
+                    }
+                }
+                if (RHT) {
+                    rht16_butterflies(y, 0u);
+                    if (!FUSE) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) y[r] = y[r] * 0.25f;
+                    }
+                }
                 uint32_t sc = csc;
                 float s = cts;
                 if (!TILE2D) {
                     float a = 0.0f;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(y[r]));
+                    if (FUSE) a = a * 0.25f;
                     sc = block_scale_code(a, s_enc_col);
                     s = L.tab[1][sc];
-                    L.col[(q.cg * 8 + j) * 16 + q.band] = (uint8_t)sc;
+                    L.col[(col0 + j) * 16 + q.band] = (uint8_t)sc;
                 }
+                if (FUSE) s = s * 0.25f;
                 uint32_t w0, w1;
                 if constexpr (CSR) {
                     const uint64_t n = n0 + (uint64_t)j * nstep;
@@ -437,19 +537,29 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
                     w0 = e2m1_rne8(y, s);
                     w1 = e2m1_rne8(y + 8, s);
                 }
-                // transposed row q.cg * 8 + j of the tile, bytes band * 8 .. + 7
-                const int trow = q.cg * 8 + j;
+                // transposed row col0 + j of the tile, bytes band * 8 .. + 7
+                const int trow = col0 + j;
                 *reinterpret_cast<uint2 *>(L.colc + colc_off(trow, q.band >> 1) + (q.band & 1) * 8) =
                     make_uint2(w0, w1);
             }
         };
+        const bool fuse = RHT && !TILE2D && s_enc_col >= 0x1p-100f && s_enc_col <= 0x1p80f;
+        auto cols_r = [&](auto sr_tag) {
+            if constexpr (RHT && !TILE2D) {
+                if (fuse) cols(sr_tag, T_{});
+                else cols(sr_tag, F_{});
+            } else {
+                cols(sr_tag, F_{});
+            }
+        };
         if constexpr (SR) {
-            if (p.col_round == 1) cols(T_{});
-            else cols(F_{});
+            if (p.col_round == 1) cols_r(T_{});
+            else cols_r(F_{});
         } else {
-            cols(F_{});
+            cols_r(F_{});
         }
-        if (TILE2D && (lane & 1) == 0) L.col[(q.cg >> 1) * 16 + q.band] = (uint8_t)csc;
+        if (TILE2D && (CO ? (lane & 3) == 0 : (lane & 17) == 0))
+            L.col[(col0 >> 4) * 16 + q.band] = (uint8_t)csc;
     }
 
     // ---- column codes and block scales, as whole runs -------------------------
@@ -458,12 +568,12 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
     const int64_t nb_row = (p.C - q.C0) / 16, nb_col = (p.R - q.R0) / 16;
     if (HAS_COL) {
         // 128 transposed rows x 16 halves of 8 bytes (16 source rows each):
-        // 8 passes of 256 threads, 16 lanes per 128-byte row
+        // 4 passes of 512 threads, 16 lanes per 128-byte row
         const int64_t rows_in = p.C - q.C0 < kTileC ? p.C - q.C0 : kTileC;
         const int64_t halves_in = (p.R - q.R0) / 16;              // bands inside x
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int idx = i * kQT + t, trow = idx >> 4, h = idx & 15;
+        for (int i = 0; i < kTileC * 16 / kET; ++i) {
+            const int idx = i * kET + t, trow = idx >> 4, h = idx & 15;
             if (trow < rows_in && h < halves_in)
                 *reinterpret_cast<uint2 *>(p.col_codes + (q.C0 + trow) * (p.R / 2) + q.R0 / 2 + h * 8) =
                     *reinterpret_cast<const uint2 *>(L.colc + colc_off(trow, h >> 1) + (h & 1) * 8);
@@ -471,7 +581,7 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
     }
     if (HAS_ROW) {
         if (!TILE2D) {
-            if (q.R0 + t < p.R)
+            if (t < kTileR && q.R0 + t < p.R)
                 put_run<8>(p.row_scales + (q.R0 + t) * (p.C / 16) + q.C0 / 16, L.row + t * 8,
                            nb_row < 8 ? nb_row : 8);
         } else if (t < 16 && q.R0 / 16 + t < p.R / 16) {
@@ -479,7 +589,7 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
                        nb_row < 8 ? nb_row : 8);
         }
     }
-    if (HAS_MX && q.R0 + t < p.R) {
+    if (HAS_MX && t < kTileR && q.R0 + t < p.R) {
         const int64_t nb = (p.C - q.C0) / 32;
         put_run<4>(p.mx_scales + (q.R0 + t) * (p.C / 32) + q.C0 / 32, L.mx + t * 4,
                    nb < 4 ? nb : 4);
@@ -505,25 +615,26 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
 // of tiles, loading the next tile while it encodes the current one.
 template <bool HAS_ROW, bool HAS_COL, bool HAS_MX, bool TILE2D, bool RHT, bool GELU, bool SR,
           bool WALK, int MINW>
-__global__ __launch_bounds__(kQT, MINW) void quant_kernel(QuantParams p) {
+__global__ __launch_bounds__(kET, MINW) void quant_kernel(QuantParams p) {
     static_assert(!GELU || (!HAS_COL && !TILE2D && !RHT), "GELU feeds the row-wise copies");
     __shared__ __align__(16) QuantLds<GELU> L;
     const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
     const TileWalk walk = WALK ? xcd_walk(T) : TileWalk{xcd_tile(blockIdx.x, T), 0, 1};
     // the first tile's piece is in flight while the scales are set up
-    uint4 v[16];
-    Piece q = piece_of(!WALK || walk.first < walk.end ? walk.first : 0, p.R, p.C);
-    if (!WALK || walk.first < walk.end) load_piece(p.x, p.R, p.C, p.ld, q, v);
+    uint4 v[8];
+    constexpr bool CO = !HAS_ROW && !HAS_MX;
+    Piece q = piece_of<CO>(!WALK || walk.first < walk.end ? walk.first : 0, p.R, p.C);
+    if (!WALK || walk.first < walk.end) load_piece<CO>(p.x, p.R, p.C, p.ld, q, v);
 
     // Tensor scales, identical in every wave: the partials are folded once
-    // per workgroup (each thread a strided share, then the four waves).
+    // per workgroup (each thread a strided share, then the eight waves).
     const bool plain_amax = HAS_ROW || (HAS_COL && !RHT);
     {
         float a = 0.0f, b = 0.0f;
         if (plain_amax)
-            for (int i = threadIdx.x; i < p.n_part; i += kQT) a = fmaxf(a, p.part[i]);
+            for (int i = threadIdx.x; i < p.n_part; i += kET) a = fmaxf(a, p.part[i]);
         if (HAS_COL && RHT)
-            for (int i = threadIdx.x; i < p.n_part_rht; i += kQT) b = fmaxf(b, p.part_rht[i]);
+            for (int i = threadIdx.x; i < p.n_part_rht; i += kET) b = fmaxf(b, p.part_rht[i]);
         a = wave_max(a);
         b = wave_max(b);
         if ((threadIdx.x & 63) == 0) {
@@ -532,13 +643,15 @@ __global__ __launch_bounds__(kQT, MINW) void quant_kernel(QuantParams p) {
         }
     }
     __syncthreads();
+    float fa = L.fold[0][0], fb = L.fold[1][0];
+#pragma unroll
+    for (int i = 1; i < kET / 64; ++i) {
+        fa = fmaxf(fa, L.fold[0][i]);
+        fb = fmaxf(fb, L.fold[1][i]);
+    }
     float s_enc_row = 1.0f, s_enc_col = 1.0f;
-    if (plain_amax)
-        s_enc_row = tensor_s_enc(fmaxf(fmaxf(L.fold[0][0], L.fold[0][1]), fmaxf(L.fold[0][2], L.fold[0][3])));
-    if (HAS_COL)
-        s_enc_col = RHT ? tensor_s_enc(fmaxf(fmaxf(L.fold[1][0], L.fold[1][1]),
-                                             fmaxf(L.fold[1][2], L.fold[1][3])))
-                        : s_enc_row;
+    if (plain_amax) s_enc_row = tensor_s_enc(fa);
+    if (HAS_COL) s_enc_col = RHT ? tensor_s_enc(fb) : s_enc_row;
     const float s_dec_row = 1.0f / s_enc_row;
     const float s_dec_col = 1.0f / s_enc_col;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -556,17 +669,17 @@ __global__ __launch_bounds__(kQT, MINW) void quant_kernel(QuantParams p) {
     } else {
         for (int64_t t = walk.first; t < walk.end; t += walk.step) {     // workgroup-uniform
             const int64_t tn = t + walk.step;
-            uint4 vn[16];
+            uint4 vn[8];
             Piece qn = q;
             if (tn < walk.end) {
-                qn = piece_of(tn, p.R, p.C);
-                load_piece(p.x, p.R, p.C, p.ld, qn, vn);
+                qn = piece_of<CO>(tn, p.R, p.C);
+                load_piece<CO>(p.x, p.R, p.C, p.ld, qn, vn);
             }
             encode_tile<HAS_ROW, HAS_COL, HAS_MX, TILE2D, RHT, GELU, SR>(p, q, v, s_enc_row,
                                                                          s_enc_col, L);
             q = qn;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = vn[i];
+            for (int i = 0; i < 8; ++i) v[i] = vn[i];
         }
     }
 }
@@ -674,8 +787,8 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
             for (int j = 0; j < 8; ++j) {
                 float y[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] = elem(v[r], j);
-                rht16_butterflies(y, p.rht_signs);
+                for (int r = 0; r < 16; ++r) y[r] = elem_flip(v[r], j, sign_bit(p.rht_signs, r));
+                rht16_butterflies(y, 0u);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) amr = fmaxf(amr, fabsf(y[r]));
             }
@@ -1206,15 +1319,16 @@ __global__ __launch_bounds__(kQT) void mx4_quant_kernel(const uint16_t *__restri
 // Host-side launchers (called by the C ABI after argument checks).
 // ---------------------------------------------------------------------------
 
-// Workgroups of a persistent launch of `kernel` (kQT threads): as many as
+// Workgroups of a persistent launch of `kernel` (THREADS each): as many as
 // are resident on the stream's device at once, at most `tiles`, at least 1.
 // The occupancy per CU is the kernel's and is looked up once (thread-safe
 // static initialisation).
-template <auto Kernel>
+template <auto Kernel, int THREADS = kQT>
 static int persistent_grid(int64_t tiles, hipStream_t s) {
     static const int per_cu = [] {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, kQT, 0) != hipSuccess || n < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel, THREADS, 0) != hipSuccess ||
+            n < 1)
             n = 1;
         return n;
     }();
@@ -1259,18 +1373,19 @@ hipError_t launch_gelu_table(float *gelu_tab, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The encode kernel variants the library launches (timed per variant):
-// copies rounding to nearest with 16x16 tiles (weights) are light on ALU
-// work and walk runs of tiles at two waves per SIMD, loading ahead; the
-// others take one tile per workgroup with registers capped for four waves
-// per SIMD (three where four would spill: row + column copies without the
-// RHT).
+// The encode kernel variants the library launches (timed per variant; a
+// workgroup of 512 threads is two waves per SIMD): copies with 16x16 tiles
+// (weights) run one workgroup per CU, those rounding to nearest walking runs
+// of tiles and loading ahead; the others take one tile per workgroup with
+// registers capped for four waves per SIMD, or six for the row copy + RHT'd
+// stochastic column copy (activations for wgrad), whose row copy keeps the
+// VALU light enough for the extra waves to pay.
 template <bool T_, bool SR_>
 constexpr bool quant_walk() { return T_ && !SR_; }
 template <bool R_, bool C_, bool M_, bool T_, bool H_, bool SR_>
 constexpr int quant_min_waves() {
-    if (T_) return SR_ ? 3 : 2;
-    if (R_ && C_ && !H_ && SR_) return 3;
+    if (T_) return 2;
+    if (R_ && C_ && H_ && SR_) return 6;
     return 4;
 }
 
@@ -1278,8 +1393,8 @@ template <bool R_, bool C_, bool M_, bool T_, bool H_, bool G_, bool SR_, bool W
 static void launch_qk(const QuantParams &p, hipStream_t s) {
     const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
     constexpr auto k = quant_kernel<R_, C_, M_, T_, H_, G_, SR_, W_, MW_>;
-    const int grid = W_ ? persistent_grid<k>(T, s) : (int)T;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kQT), 0, s, p);
+    const int grid = W_ ? persistent_grid<k, kET>(T, s) : (int)T;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kET), 0, s, p);
 }
 
 template <bool R_, bool C_, bool M_, bool T_, bool H_, bool G_ = false>
