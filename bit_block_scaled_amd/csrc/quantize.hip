@@ -23,10 +23,10 @@
 //           lanes.  Block encode scales 1 / (E4M3 x s_dec) come from a table
 //           of the 127 E4M3 codes built once per workgroup.
 // Requantize (4bit.vizuara.ai sections 9-10): requant_kernel dequantizes a
-// 32-row x 8-column piece of an NVFP4 matrix in FP32 per lane and encodes
-// its 8 transposed rows of 32 as MXFP8 (E8M0 per 32, E4M3 elements, RTN or
-// SR); a workgroup's 512 destination rows x 128 bytes are gathered in LDS and
-// stored as whole rows.  It also walks a run of tiles, loading ahead.
+// 16-row x 8-column piece of an NVFP4 matrix in FP32 per lane and encodes
+// its half of 8 transposed rows of 32 as MXFP8 (E8M0 per 32 shared by a lane
+// pair, E4M3 elements, RTN or SR); a workgroup's 256 destination rows x 128
+// bytes are gathered in LDS and stored as whole rows.
 //
 // Workgroups are mapped to tiles so that each of the 8 XCDs works through a
 // contiguous run of tiles (neighbouring tiles share output lines in L2).
@@ -40,7 +40,8 @@ namespace bbs {
 constexpr int kQT = 256;                       // threads per workgroup
 constexpr int kET = 512;                       // threads of the tile encode kernel
 constexpr int kTileR = 256, kTileC = 128;      // quantizer tile of x
-constexpr int kReqR = 128, kReqC = 512;        // requantizer tile of the source
+constexpr int kReqR = 128, kReqC = 256;        // requantizer tile of the source
+static_assert(kReqC == kQT, "one scale row per thread");
 
 static_assert(kGeluTabOffset + kGeluTabSize <= kWorkspaceFloats, "GELU table exceeds the workspace");
 static_assert(kQT == 256, "the partial fold assumes four waves");
@@ -1094,12 +1095,14 @@ __global__ __launch_bounds__(kQT) void quant_act_kernel(QuantParams p) {
 
 // ---------------------------------------------------------------------------
 // Requantize: NVFP4 [R x C] -> MXFP8 of the transpose [C x R].
-// A tile is 128 source rows (a 32-row band per wave) x 512 source columns (8
-// per lane); each lane turns its 32 rows x 8 columns into 8 destination rows
-// of 32.  The tile's 512 destination rows x 128 code bytes are gathered in
-// LDS (16-byte groups swizzled by (row >> 3) & 7) and stored as whole rows,
-// its 512 x 4 scale bytes as 4-byte runs.  Workgroups walk XCD-contiguous
-// runs of tiles, loading the next tile's codes while encoding this one.
+// A tile is 128 source rows x 256 source columns.  Wave w holds the rows
+// 32w .. 32w + 31 and lane l the 16 rows 32w + 16 (l & 1) .. + 15 of the
+// columns 8 (l >> 1) .. + 7, so a destination row's block of 32 (one wave's
+// rows) is two neighbouring lanes: they share the block maximum and each
+// encodes its 16 values.  The tile's 256 destination rows x 128 code bytes
+// are gathered in LDS (16-byte groups swizzled by (row >> 3) & 7) and stored
+// as whole rows, its 256 x 4 scale bytes as 4-byte runs; the 33 KB of LDS
+// and the 16-row pieces leave room for four workgroups per CU.
 // ---------------------------------------------------------------------------
 struct RequantLds {
     uint8_t codes[kReqC * 128];
@@ -1117,76 +1120,78 @@ __global__ __launch_bounds__(kQT, MINW) void requant_kernel(RequantParams p) {
     __shared__ __align__(16) RequantLds L;
     const int64_t tiles_c = (p.C + kReqC - 1) / kReqC;
     const int64_t T = ((p.R + kReqR - 1) / kReqR) * tiles_c;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane & 1, cg = lane >> 1;
     const float s_dec = p.s_dec[0];
     const int64_t nsb = p.C / 16;                    // scale bytes per scale row
-    constexpr int NB = TILE2D ? 2 : 32;              // block scales per lane
+    constexpr int NB = TILE2D ? 1 : 16;              // block scales per lane
 
-    // Source of tile t for this lane: 32 rows x 8 columns (invalid pieces
-    // read a valid piece and store nothing).
+    // Source of tile t for this lane: 16 rows x 8 columns (invalid pieces
+    // read a valid piece and store nothing; R is a multiple of 32).
     struct Src {
-        int64_t r0, c0;
+        int64_t band, r0, c0;   // the wave's first row, the lane's first row and column
         bool in;
     };
     auto src_of = [&](int64_t tile) -> Src {
         const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
         Src s;
-        s.r0 = tr * kReqR + w * 32;
-        s.c0 = tc * kReqC + lane * 8;
-        s.in = s.r0 < p.R && s.c0 < p.C;
+        s.band = tr * kReqR + w * 32;
+        s.r0 = s.band + h * 16;
+        s.c0 = tc * kReqC + cg * 8;
+        s.in = s.band < p.R && s.c0 < p.C;
         return s;
     };
-    auto load = [&](const Src &s, uint32_t (&cw)[32], uint32_t (&sb)[NB]) {
-        const int64_t r0 = s.r0 < p.R ? s.r0 : p.R - 32;
+    auto load = [&](const Src &s, uint32_t (&cw)[16], uint32_t (&sb)[NB]) {
+        const int64_t r0 = s.r0 < p.R ? s.r0 : p.R - 16;
         const int64_t c0 = s.c0 < p.C ? s.c0 : p.C - 8;
 #pragma unroll
-        for (int r = 0; r < 32; ++r)
+        for (int r = 0; r < 16; ++r)
             cw[r] = *reinterpret_cast<const uint32_t *>(p.codes + (r0 + r) * (p.C / 2) + c0 / 2);
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int64_t srow = TILE2D ? r0 / 16 + i : r0 + i;
+            const int64_t srow = TILE2D ? r0 / 16 : r0 + i;
             sb[i] = p.scales[srow * nsb + c0 / 16];
         }
     };
 
     const TileWalk walk = WALK ? xcd_walk(T) : TileWalk{xcd_tile(blockIdx.x, T), xcd_tile(blockIdx.x, T) + 1, 1};
-    uint32_t cw[32], sb[NB];
+    uint32_t cw[16], sb[NB];
     Src s = src_of(walk.first < walk.end ? walk.first : 0);
     if (walk.first < walk.end) load(s, cw, sb);
     for (int64_t t = walk.first; t < walk.end; t += walk.step) {    // workgroup-uniform
         const int64_t tn = t + walk.step;
-        uint32_t cwn[WALK ? 32 : 1], sbn[WALK ? NB : 1];
+        uint32_t cwn[WALK ? 16 : 1], sbn[WALK ? NB : 1];
         Src sn = s;
         if (WALK && tn < walk.end) {
             sn = src_of(tn);
-            load(sn, *reinterpret_cast<uint32_t(*)[32]>(cwn), *reinterpret_cast<uint32_t(*)[NB]>(sbn));
+            load(sn, *reinterpret_cast<uint32_t(*)[16]>(cwn), *reinterpret_cast<uint32_t(*)[NB]>(sbn));
         }
         float bs[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) bs[i] = __builtin_amdgcn_cvt_scalef32_f32_fp8((int)sb[i], 1.0f, 0);
-        // destination row (in the tile) lane * 8 + j, bytes w * 32 .. + 31
-        auto emit = [&](const float (&x)[32], int j) {
+        // destination row (in the tile) cg * 8 + j, bytes w * 32 + h * 16 .. + 15
+        auto emit = [&](const float (&x)[16], int j) {
             float a = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 32; ++r) a = fmaxf(a, fabsf(x[r]));
-            const uint32_t kb = e8m0_byte(a);
-            float y[32];
+            for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(x[r]));
+            const uint32_t kb = e8m0_byte(max_lane_pair(a));
+            float y[16];
 #pragma unroll
-            for (int r = 0; r < 32; ++r) y[r] = x[r];
+            for (int r = 0; r < 16; ++r) y[r] = x[r];
             if (__builtin_amdgcn_ballot_w64(kb == 0)) {   // rare, wave-uniform test
                 if (kb == 0) {                             // 2^-127: convert 2y at 2^-126
 #pragma unroll
-                    for (int r = 0; r < 32; ++r) y[r] = y[r] * 2.0f;
+                    for (int r = 0; r < 16; ++r) y[r] = y[r] * 2.0f;
                 }
             }
             const float cs = e8m0_cvt_scale(kb);
             const int64_t c = s.c0 + j;                  // destination row
-            uint32_t out[8];
+            uint32_t out[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int g = 0; g < 2; ++g) {
                 if constexpr (SR) {
+                    // Philox block 2h + g of the destination row's 32-block
                     uint32_t wd[4];
-                    sr_block(p.seed, p.stream, (uint64_t)(c * p.R + s.r0) / 8 + g, wd);
+                    sr_block(p.seed, p.stream, (uint64_t)(c * p.R + s.band) / 8 + 2 * h + g, wd);
                     out[2 * g] = e4m3_sr4_scaled(y[8 * g], y[8 * g + 1], y[8 * g + 2], y[8 * g + 3],
                                                  sr_word_lo(wd[0]), sr_word_hi(wd[0]),
                                                  sr_word_lo(wd[1]), sr_word_hi(wd[1]), cs);
@@ -1200,20 +1205,18 @@ __global__ __launch_bounds__(kQT, MINW) void requant_kernel(RequantParams p) {
                                                       y[8 * g + 7], cs);
                 }
             }
-            const int drow = lane * 8 + j;
-            *reinterpret_cast<uint4 *>(L.codes + req_off(drow, 2 * w)) =
+            const int drow = cg * 8 + j;
+            *reinterpret_cast<uint4 *>(L.codes + req_off(drow, 2 * w + h)) =
                 make_uint4(out[0], out[1], out[2], out[3]);
-            *reinterpret_cast<uint4 *>(L.codes + req_off(drow, 2 * w + 1)) =
-                make_uint4(out[4], out[5], out[6], out[7]);
-            L.scales[drow * 4 + w] = (uint8_t)kb;
+            if (h == 0) L.scales[drow * 4 + w] = (uint8_t)kb;
         };
         auto pair = [&](auto jp_tag) {                   // source columns 2jp, 2jp + 1
             constexpr int jp = decltype(jp_tag)::value;
-            float xe[32], xo[32];
+            float xe[16], xo[16];
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
+            for (int r = 0; r < 16; ++r) {
                 const f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[r], 1.0f, jp);
-                const float b = bs[TILE2D ? r / 16 : r];
+                const float b = bs[TILE2D ? 0 : r];
                 // (E2M1 x E4M3) is exact; the multiply by s_dec is one FP32 rounding.
                 xe[r] = (e[0] * b) * s_dec;
                 xo[r] = (e[1] * b) * s_dec;
@@ -1226,34 +1229,31 @@ __global__ __launch_bounds__(kQT, MINW) void requant_kernel(RequantParams p) {
         pair(std::integral_constant<int, 2>{});
         pair(std::integral_constant<int, 3>{});
         __syncthreads();
-        // 512 destination rows x 8 groups of 16 bytes: 16 passes of 256 threads;
-        // then 512 x 4 scale bytes
+        // 256 destination rows x 8 groups of 16 bytes: 8 passes of 256 threads;
+        // then 256 x 4 scale bytes
         {
             const int64_t tr = t / tiles_c, tc = t - tr * tiles_c;
             const int64_t R0 = tr * kReqR, C0 = tc * kReqC;
             const int64_t drows = p.C - C0 < kReqC ? p.C - C0 : kReqC;
             const int64_t groups = (p.R - R0) / 16 < 8 ? (p.R - R0) / 16 : 8;   // R % 32 == 0
 #pragma unroll 4
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < kReqC * 8 / kQT; ++i) {
                 const int idx = i * kQT + threadIdx.x, drow = idx >> 3, g = idx & 7;
                 if (drow < drows && g < groups)
                     *reinterpret_cast<uint4 *>(p.out_codes + (C0 + drow) * p.R + R0 + g * 16) =
                         *reinterpret_cast<const uint4 *>(L.codes + req_off(drow, g));
             }
             const int64_t nsc = (p.R - R0) / 32 < 4 ? (p.R - R0) / 32 : 4;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int drow = i * kQT + threadIdx.x;
-                if (drow < drows)
-                    put_run<4>(p.out_scales + (C0 + drow) * (p.R / 32) + R0 / 32, L.scales + drow * 4,
-                               nsc);
-            }
+            const int drow = threadIdx.x;               // kReqC == kQT
+            if (drow < drows)
+                put_run<4>(p.out_scales + (C0 + drow) * (p.R / 32) + R0 / 32, L.scales + drow * 4,
+                           nsc);
         }
         __syncthreads();
         if constexpr (WALK) {
             s = sn;
 #pragma unroll
-            for (int r = 0; r < 32; ++r) cw[r] = cwn[r];
+            for (int r = 0; r < 16; ++r) cw[r] = cwn[r];
 #pragma unroll
             for (int i = 0; i < NB; ++i) sb[i] = sbn[i];
         }
