@@ -148,7 +148,7 @@ __device__ __forceinline__ Plan make_plan(const Fp4View &A, const Fp4View &B, in
 // 2 = scales (2 + 2, or 2 + 1 when B has 16x16 tiles).
 template <int PART, bool BT, int NJ>
 __device__ __forceinline__ void issue_part(Stage &st, const Plan &pl, int64_t k0) {
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // LDS offsets in SGPRs
     const int64_t cb = k0 / 2, sk = k0 / 16;
     if (PART == 0) {
 #pragma unroll
@@ -557,7 +557,8 @@ template <int OUT, bool BT, bool DROP, int NJ, typename Next, typename BView, ty
 __device__ __forceinline__ void run_tiles(Smem &sm, float *tab, const GemmParams &p,
                                           Next next_tile, BView b_view, RowMap a_row,
                                           ScaleFn scale_of) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    // the wave index is uniform: the copies' LDS offsets live in scalar registers
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t K = p.K, N = p.N;
     // global_load_lds instructions one wave issues per slab
