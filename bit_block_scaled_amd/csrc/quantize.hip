@@ -722,26 +722,36 @@ __device__ __forceinline__ void put_scales4(uint8_t *dst, uint32_t word, int64_t
 // need the tensor scale: it writes the MXFP8 copy (which needs none) and the
 // per-workgroup partials of |x| (AP) and of |RHT(column chunks)| (AR), as
 // amax_kernel does, from the same read.
+// HALF (the amax pass variants): a wave step is 16 rows x 256 columns, lane
+// l holding 8 columns of rows 8 (l >> 5) .. + 7, so the step takes half the
+// registers; for the RHT partials lanes l and l ^ 32 trade halves
+// (v_permlane32_swap) after the MXFP8 copy, each then holding four whole
+// 16-row column blocks.
 template <bool HAS_ROW, bool HAS_MX, bool TILE2D, bool GELU, bool SR, int MINW, bool AP = false,
-          bool AR = false>
+          bool AR = false, bool HALF = false>
 __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, float *amax_part,
                                                                float *amax_part_rht) {
     static_assert(!(AP || AR) || (!HAS_ROW && !GELU), "the amax pass feeds the later copies");
+    static_assert(!HALF || (!HAS_ROW && !GELU), "half steps serve the amax pass variants");
+    constexpr int PR = HALF ? 8 : 16;                        // rows per lane
+    constexpr int SC = HALF ? kAmaxStepC / 2 : kAmaxStepC;   // columns per wave step
     __shared__ __align__(16) RowsLds L;
     __shared__ __align__(16) float s_gelu[GELU ? kGeluTabSize : 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t steps_c = (p.C + kAmaxStepC - 1) / kAmaxStepC;
+    const int hf = HALF ? lane >> 5 : 0, cl = HALF ? lane & 31 : lane;
+    const int64_t steps_c = (p.C + SC - 1) / SC;
     const int64_t T = (p.R / 16) * steps_c;
     const int64_t stride = (int64_t)gridDim.x * (kQT / 64);
-    auto load = [&](int64_t t, uint4 d[16], int64_t &r0, int64_t &c0) {
-        r0 = (t / steps_c) * 16;
-        c0 = (t - (r0 / 16) * steps_c) * kAmaxStepC + lane * 8;
+    auto load = [&](int64_t t, uint4 d[PR], int64_t &r0, int64_t &c0) {
+        const int64_t tr = t / steps_c;
+        r0 = tr * 16 + hf * 8;
+        c0 = (t - tr * steps_c) * SC + cl * 8;
         const uint16_t *src = p.x + r0 * p.ld + (c0 < p.C ? c0 : p.C - 8);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * p.ld);
+        for (int i = 0; i < PR; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * p.ld);
     };
     int64_t t = (int64_t)blockIdx.x * (kQT / 64) + w;
-    uint4 v[16];
+    uint4 v[PR];
     int64_t r0 = 0, c0 = 0;
     if (t < T) load(t, v, r0, c0);
 
@@ -771,7 +781,7 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
     constexpr bool kAhead = !(AP || AR) && !GELU;
     while (t < T) {                                   // wave-uniform
         const int64_t tn = t + stride;
-        uint4 vn[kAhead ? 16 : 1];
+        uint4 vn[kAhead ? PR : 1];
         int64_t r0n = r0, c0n = c0;
         if constexpr (kAhead) {
             if (tn < T) load(tn, vn, r0n, c0n);
@@ -779,11 +789,11 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
         const bool in = c0 < p.C;
         if (AP && in) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < PR; ++r)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(elem(v[r], j)));
         }
-        if (AR && in) {
+        if (AR && !HALF && in) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float y[16];
@@ -878,11 +888,11 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
             }
         };
         auto rows = [&](auto row_sr, auto mx_sr) {
-            // (two loops of 8 rows: each stays under the full-unroll limit)
+            // (loops of 8 rows: each stays under the full-unroll limit)
 #pragma unroll
             for (int r = 0; r < 8; ++r) one(row_sr, mx_sr, r);
 #pragma unroll
-            for (int r = 8; r < 16; ++r) one(row_sr, mx_sr, r);
+            for (int r = 8; r < PR; ++r) one(row_sr, mx_sr, r);
         };
         using T_ = std::true_type;
         using F_ = std::false_type;
@@ -895,12 +905,35 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
         } else {
             rows(F_{}, F_{});
         }
+        if (AR && HALF && in) {
+            // lanes l and l ^ 32 (same columns, the same in-flag) trade
+            // halves: words 0-1 of v[i] then hold row i, words 2-3 row
+            // i + 8, of the lane's four columns 4 (l >> 5) .. + 3
+#pragma unroll
+            for (int i = 0; i < PR; ++i) {
+                const auto a = __builtin_amdgcn_permlane32_swap(v[i].x, v[i].z, false, false);
+                const auto b = __builtin_amdgcn_permlane32_swap(v[i].y, v[i].w, false, false);
+                v[i] = make_uint4(a[0], b[0], a[1], b[1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float y[16];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    y[r] = elem_flip(v[r], j, sign_bit(p.rht_signs, r));
+                    y[r + 8] = elem_flip(v[r], 4 + j, sign_bit(p.rht_signs, r + 8));
+                }
+                rht16_butterflies(y, 0u);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) amr = fmaxf(amr, fabsf(y[r]));
+            }
+        }
         t = tn;
         if constexpr (kAhead) {
             r0 = r0n;
             c0 = c0n;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = vn[i];
+            for (int i = 0; i < PR; ++i) v[i] = vn[i];
         } else if (t < T) {
             load(t, v, r0, c0);
         }
@@ -1424,11 +1457,11 @@ static void launch_rows_k(const QuantParams &p, hipStream_t s) {
 // encode of the other copies folds, from one read of x.
 template <bool SR_, bool AP_, bool AR_>
 static int launch_amax_mx_k(const QuantParams &p, float *part, float *part_rht, hipStream_t s) {
-    // three waves per SIMD for the RHT partials alone (153 VGPRs); with the
-    // plain partials a cap of three spills, so two
-    constexpr int MW = AP_ ? 2 : 3;
-    constexpr auto k = quant_rows_kernel<false, true, false, false, SR_, MW, AP_, AR_>;
-    const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC - 1) / kAmaxStepC);
+    // half steps (8 rows per lane): four waves per SIMD (three with the plain
+    // partials and stochastic rounding, where four would spill)
+    constexpr int MW = AP_ && SR_ ? 3 : 4;
+    constexpr auto k = quant_rows_kernel<false, true, false, false, SR_, MW, AP_, AR_, true>;
+    const int64_t steps = (p.R / 16) * ((p.C + kAmaxStepC / 2 - 1) / (kAmaxStepC / 2));
     int64_t grid = persistent_grid<k>((steps + 3) / 4, s);
     if (grid > kAmaxPartials) grid = kAmaxPartials;
     hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kQT), 0, s, p, part, part_rht);
