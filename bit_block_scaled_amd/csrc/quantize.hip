@@ -4,8 +4,9 @@
 // Procedure", steps 1-4; 4bit.vizuara.ai sections 5-6, 13):
 //   pass 1  amax_kernel: per-workgroup maxima of |x| and / or of the RHT'd
 //           16-row column chunks, from one read of x; no atomics, no zeroing.
-//           A wave reads 16 rows x 512 columns per step (each load a 1 KB
-//           run of one row) and loads its next step while reducing this one.
+//           A wave reads 16 rows x 256 columns per step (each load two
+//           512-byte runs of two rows) and loads its next step while
+//           reducing this one.
 //   pass 2  quant_kernel: every workgroup folds the partials into the tensor
 //           amax (bit-identical everywhere) and walks a run of 256-row x
 //           128-column tiles of x, loading the next tile while it encodes
@@ -211,42 +212,59 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
         for (int i = blockIdx.x * kQT + threadIdx.x; i < kGeluTabSize; i += gridDim.x * kQT)
             gelu_tab[i] = gelu_table_entry(i);
     __shared__ float red[2][kQT / 64];
+    // a wave step is 16 rows x 256 columns: lane l holds 8 columns of rows
+    // 8 (l >> 5) .. + 7; for the RHT maxima lanes l and l ^ 32 trade halves.
+    // (GELU: 16 rows x 512 columns, lane l all 16 rows of its 8 columns.)
+    constexpr int SC = GELU ? kAmaxStepC : kAmaxStepC / 2, PR = GELU ? 16 : 8;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t steps_c = (C + kAmaxStepC - 1) / kAmaxStepC;
+    const int hf = GELU ? 0 : lane >> 5, cl = GELU ? lane : lane & 31;
+    const int64_t steps_c = (C + SC - 1) / SC;
     const int64_t T = (R / 16) * steps_c;
     const int64_t stride = (int64_t)gridDim.x * (kQT / 64);
     float m = 0.0f, mr = 0.0f;
     float mx = 0.0f;     // GELU: largest element seen (0 if none is positive)
-    auto load = [&](int64_t t, uint4 d[16]) -> bool __attribute__((always_inline)) {
+    auto load = [&](int64_t t, uint4 d[PR]) -> bool __attribute__((always_inline)) {
         const int64_t tr = t / steps_c;
-        int64_t c = (t - tr * steps_c) * kAmaxStepC + lane * 8;
+        int64_t c = (t - tr * steps_c) * SC + cl * 8;
         const bool ok = c < C;
         if (!ok) c = C - 8;
-        const uint16_t *src = x + tr * 16 * ld + c;
+        const uint16_t *src = x + (tr * 16 + hf * 8) * ld + c;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * ld);
+        for (int i = 0; i < PR; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * ld);
         return ok;
     };
     int64_t t = (int64_t)blockIdx.x * (kQT / 64) + w;
-    uint4 v[16];
+    uint4 v[PR];
     bool ok = t < T ? load(t, v) : false;
     while (t < T) {                                   // wave-uniform
         const int64_t tn = t + stride;
-        uint4 vn[16];
+        uint4 vn[PR];
         const bool okn = tn < T ? load(tn, vn) : false;
         if (ok) {
         if (PLAIN) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < 8; ++r)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(elem(v[r], j)));
         }
         if (RHT) {
+            // (the partner lane has the same columns, so the same ok):
+            // words 0-1 of v[i] then hold row i, words 2-3 row i + 8, of the
+            // lane's four columns 4 hf .. + 3
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int i = 0; i < 8; ++i) {
+                const auto a = __builtin_amdgcn_permlane32_swap(v[i].x, v[i].z, false, false);
+                const auto b = __builtin_amdgcn_permlane32_swap(v[i].y, v[i].w, false, false);
+                v[i] = make_uint4(a[0], b[0], a[1], b[1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
                 float y[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] = elem_flip(v[r], j, sign_bit(signs, r));
+                for (int r = 0; r < 8; ++r) {
+                    y[r] = elem_flip(v[r], j, sign_bit(signs, r));
+                    y[r + 8] = elem_flip(v[r], 4 + j, sign_bit(signs, r + 8));
+                }
                 rht16_butterflies(y, 0u);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mr = fmaxf(mr, fabsf(y[r]));
@@ -257,14 +275,14 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
             float pm = 0.0f;
             if (ok) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
+                for (int r = 0; r < PR; ++r)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) pm = fmaxf(pm, elem(v[r], j));
             }
             mx = fmaxf(mx, pm);
             if (gelu_tanh(wave_max(pm)) < kGeluNegBound && ok) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
+                for (int r = 0; r < PR; ++r)
 #pragma unroll
                     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(gelu_tanh(elem(v[r], j))));
             }
@@ -272,7 +290,7 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
         t = tn;
         ok = okn;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = vn[i];
+        for (int i = 0; i < PR; ++i) v[i] = vn[i];
     }
     // The transform's final multiply by 1/4 is monotonic, so the maximum of
     // the scaled values is the scaled maximum (bit for bit).
@@ -1372,9 +1390,11 @@ static int persistent_grid(int64_t tiles, hipStream_t s) {
 hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
                        uint32_t signs, float *part, float *part_rht, int *n_part,
                        hipStream_t s, float *gelu_tab) {
-    // one wave per 16 x 512 step; up to 1024 workgroups (2048 with the RHT
-    // maximum alone, whose butterflies make the read slower per byte)
-    const int64_t steps = (R / 16) * ((C + kAmaxStepC - 1) / kAmaxStepC);
+    // one wave per 16 x 256 step (16 x 512 for GELU); up to 1024 workgroups
+    // (2048 with the RHT maximum alone, whose butterflies make the read
+    // slower per byte)
+    const int64_t sc = gelu_tab ? kAmaxStepC : kAmaxStepC / 2;
+    const int64_t steps = (R / 16) * ((C + sc - 1) / sc);
     const int64_t cap = (rht && !plain) ? kAmaxPartials : kAmaxPartials / 2;
     const int64_t want = (steps + kQT / 64 - 1) / (kQT / 64);
     const int grid = (int)(want < cap ? want : cap);
