@@ -93,6 +93,23 @@ def test_col_rht(bbs, shape):
 
 
 @pytest.mark.parametrize("shape", SHAPES)
+def test_col_copy_alone(bbs, shape):
+    """The column copy without row-wise copies (a 16 x 4 piece per thread):
+    1x16 without the RHT and 16x16 tiles, each to nearest and stochastic."""
+    R, C = shape
+    announce(f"col alone 1x16 / 16x16, RTN+SR {shape}")
+    x = synth.student_t(R, C, 5000 + R + C)
+    for tile2d in (False, True):
+        tag = "16x16" if tile2d else "1x16"
+        _, cq, _ = _gpu_quantize(bbs, x, col=True, tile2d=tile2d)
+        _same_fp4(cq, O.nvfp4_quantize(x, transpose=True, tile2d=tile2d), f"col {tag} RTN")
+        _, cq, _ = _gpu_quantize(bbs, x, col=True, tile2d=tile2d, col_round=O.SR,
+                                 col_rng=(31, 3))
+        _same_fp4(cq, O.nvfp4_quantize(x, transpose=True, tile2d=tile2d, mode=O.SR, seed=31,
+                                       stream=3), f"col {tag} SR")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
 def test_tile2d_row_and_col(bbs, shape):
     R, C = shape
     announce(f"16x16 row+col RTN {shape}")
