@@ -18,11 +18,12 @@
 //           trade halves, after which each encodes four full column blocks,
 //           optional RHT; without row-wise copies a thread loads a 16 x 4
 //           piece instead and needs no exchange), and the row-wise MXFP8
-//           copy (a block of 32 is four lanes).  The column copy's codes and every copy's block
-//           scales are gathered in LDS and written as whole runs: each
-//           transposed row's 128 code bytes of a tile are one store of eight
-//           lanes.  Block encode scales 1 / (E4M3 x s_dec) come from a table
-//           of the 127 E4M3 codes built once per workgroup.
+//           copy (a block of 32 is four lanes).  The column copy's codes and
+//           every copy's block scales are gathered in LDS and written as
+//           whole runs: each transposed row's 128 code bytes of a tile are
+//           one store of eight lanes.  Block encode scales 1 / (E4M3 x
+//           s_dec) come from a table of the 127 E4M3 codes built once per
+//           workgroup.
 // Requantize (4bit.vizuara.ai sections 9-10): requant_kernel dequantizes a
 // 16-row x 8-column piece of an NVFP4 matrix in FP32 per lane and encodes
 // its half of 8 transposed rows of 32 as MXFP8 (E8M0 per 32 shared by a lane
