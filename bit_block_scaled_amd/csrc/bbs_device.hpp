@@ -86,27 +86,30 @@ __device__ __forceinline__ uint32_t pack_bytes4(uint32_t b0, uint32_t b1, uint32
 }
 
 // The conversions below only write part of their destination word; the
-// rest comes from their first operand, whose bits are never used here, so
-// a dead input is passed there (no register needs clearing first).
+// rest comes from their first operand.  The first write into a word passes a
+// dead input there (no register needs clearing first), later ones the word
+// built so far, until the writes cover it.
 
-// E2M1 round-to-nearest-even of (a, b): byte with a in bits 3:0 (upper bits
-// of the returned word are unspecified).
-__device__ __forceinline__ uint32_t e2m1_rne_pair(float a, float b) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(__float_as_uint(a), a, b, 1.0f, 0);
-}
-
-// Eight values times s, rounded to nearest, packed little-endian.
+// Eight values times s, rounded to nearest, packed little-endian: pair k is
+// written into byte k of one word (the four byte writes cover it).
 __device__ __forceinline__ uint32_t e2m1_rne8(const float *f, float s) {
-    return pack_bytes4(e2m1_rne_pair(f[0] * s, f[1] * s), e2m1_rne_pair(f[2] * s, f[3] * s),
-                       e2m1_rne_pair(f[4] * s, f[5] * s), e2m1_rne_pair(f[6] * s, f[7] * s));
+    uint32_t w = __float_as_uint(f[0]);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0] * s, f[1] * s, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2] * s, f[3] * s, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4] * s, f[5] * s, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6] * s, f[7] * s, 1.0f, 3);
+    return w;
 }
 
 // Random operand for a 16-bit uniform held in the low / high half of w.
 __device__ __forceinline__ uint32_t sr_word_lo(uint32_t w) { return (w << 16) | 0x8000u; }
-__device__ __forceinline__ uint32_t sr_word_hi(uint32_t w) { return (w & 0xFFFF0000u) | 0x8000u; }
+__device__ __forceinline__ uint32_t sr_word_hi(uint32_t w) {
+    return __builtin_amdgcn_bitop3_b32(w, 0xFFFF0000u, 0x8000u, 0xEA);   // (w & b) | c
+}
 
-// Stochastic E2M1 code of one value (nibble in bits 3:0, bits 7:4 zero,
-// upper bytes unspecified).
+// Stochastic E2M1 code of one value (nibble in bits 3:0, bits 7:4 zero from
+// the +0 in the second slot, upper bytes unspecified: the compiler does not
+// carry the first operand of this conversion into its destination).
 __device__ __forceinline__ uint32_t e2m1_sr1(float v, uint32_t r) {
     f32x2_t p = {v, 0.0f};
     return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(__float_as_uint(v), p, r, 1.0f, 0);
@@ -114,13 +117,14 @@ __device__ __forceinline__ uint32_t e2m1_sr1(float v, uint32_t r) {
 
 // Eight values times s, stochastically rounded with the eight 16-bit
 // uniforms of one Philox block (value j uses half j & 1 of word j >> 1).
+// Byte 0 of (hi << 4) | lo is the code pair, as bits 7:4 of lo are zero.
 __device__ __forceinline__ uint32_t e2m1_sr8(const float *f, float s, const uint32_t w[4]) {
     uint32_t b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t lo = e2m1_sr1(f[2 * i] * s, sr_word_lo(w[i]));
         const uint32_t hi = e2m1_sr1(f[2 * i + 1] * s, sr_word_hi(w[i]));
-        b[i] = (hi << 4) | (lo & 0xFu);
+        b[i] = (hi << 4) | lo;
     }
     return pack_bytes4(b[0], b[1], b[2], b[3]);
 }
@@ -136,10 +140,9 @@ __device__ __forceinline__ uint32_t e4m3_rne_code(float t) {
 
 // Four values (|y| <= 448) rounded to nearest E4M3, bytes little-endian.
 __device__ __forceinline__ uint32_t e4m3_rne4(float y0, float y1, float y2, float y3) {
-    i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y0), y0, y1, 1.0f, false);
-    i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y2), y2, y3, 1.0f, false);
-    return __builtin_amdgcn_perm((uint32_t)(uint16_t)hi[0], (uint32_t)(uint16_t)lo[0],
-                                 0x05040100u);
+    i16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y0), y0, y1, 1.0f, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, y2, y3, 1.0f, true);
+    return __builtin_bit_cast(uint32_t, w);
 }
 
 // Four values (|y| <= 448) stochastically rounded to E4M3 with random
@@ -237,10 +240,9 @@ __device__ __forceinline__ float e8m0_cvt_scale(uint32_t byte) {
 // bytes little-endian.
 __device__ __forceinline__ uint32_t e4m3_rne4_scaled(float y0, float y1, float y2, float y3,
                                                      float scale) {
-    i16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y0), y0, y1, scale, false);
-    i16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y2), y2, y3, scale, false);
-    return __builtin_amdgcn_perm((uint32_t)(uint16_t)hi[0], (uint32_t)(uint16_t)lo[0],
-                                 0x05040100u);
+    i16x2_t w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(as_i16x2(y0), y0, y1, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, y2, y3, scale, true);
+    return __builtin_bit_cast(uint32_t, w);
 }
 
 // Four values stochastically rounded to E4M3 after division by the scale.
