@@ -10,12 +10,12 @@
 // A workgroup (4 waves, 2 x 2) owns a 256 x 256 tile of C; a wave owns
 // 128 x 128 = 8 x 8 MFMAs (256 FP32 accumulators per lane).  K advances in
 // slabs of 128 (one MFMA deep) through two LDS stages (a slab is 66 KB, so
-// no third fits); each wave reads all of a slab's fragments into registers
-// at its start, which frees the stage after one barrier and lets the copies
-// of the slab two ahead go into it.  Slabs are copied
-// global -> LDS with global_load_lds_dwordx4 (no staging registers): each
-// instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so a wave
-// writes 8 rows of 128 bytes per instruction.  Within a row the 16-byte chunk
+// no third fits); each wave holds all of a slab's fragments in registers,
+// read two MFMA shells ahead of their use, which frees the stage after one
+// barrier and lets the copies of the slab two ahead go into it.  Slabs are
+// copied global -> LDS with global_load_lds_dwordx4 (no staging registers):
+// each instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so a
+// wave writes 8 rows of 128 bytes per instruction.  Within a row the 16-byte chunk
 // c is stored at position c ^ ((row >> 1) & 7): the 16 rows that one fragment
 // read touches then fall on 16 distinct bank groups.
 //
@@ -96,8 +96,14 @@ __device__ __forceinline__ Plan make_plan(const Mx8GemmParams &p, int64_t m0, in
     const int64_t nkb = p.K / 32;
     pl.sa_base = p.a_scales + m0 * nkb;
     pl.sb_base = p.b_scales + n0 * nkb;
-    pl.sa_off = (uint32_t)((min(m0 + t, p.M - 1) - m0) * nkb);
-    pl.sb_off = (uint32_t)((min(n0 + t, p.N - 1) - n0) * nkb);
+    // FP8: LDS word t holds the scales of row 128 (t / 128) + 16 k + rl with
+    // rl = (t / 8) % 16 and k = (t % 8) ^ (4 (rl / 8)), so the eight rows
+    // rl + 16 k of a lane's half are adjacent, their halves swapped for
+    // rl >= 8 (lanes rl and rl + 8 then read different banks)
+    const int s_rl = (t >> 3) & 15;
+    const int srow = FP4 ? t : (t >> 7) * 128 + ((t & 7) ^ ((s_rl >> 3) << 2)) * 16 + s_rl;
+    pl.sa_off = (uint32_t)((min(m0 + srow, p.M - 1) - m0) * nkb);
+    pl.sb_off = (uint32_t)((min(n0 + srow, p.N - 1) - n0) * nkb);
     return pl;
 }
 
@@ -151,44 +157,59 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Copies one wave issues per FP8 slab: 8 + 8 code copies, 2 scale copies.
 constexpr int kIssued8 = 18;
 
-// The MFMAs of one FP8 slab with all of the wave's fragments read into
-// registers at its start (8 A + 8 B, 128 VGPRs), in the order the MFMAs use
-// them: the MFMAs run in growing squares (shell k = the blocks that need
-// fragments k and below), so the first waits for two reads instead of nine.
-// After shell 4 every wave has its fragments, so after one barrier the stage
-// is free and the copies of slab sn (two slabs ahead) go into it during
-// shells 5-7, one after every second MFMA: they get most of two slabs to
-// land, where copying into the other stage of a two-stage ring gives them one.
+// The MFMAs of one FP8 slab (8 A + 8 B fragments, 128 VGPRs).  The MFMAs
+// run in growing squares (shell k = the blocks that need fragments k and
+// below), and the fragment reads go two shells ahead of the MFMAs that use
+// them, so a shell waits only for reads issued two shells before and at most
+// 12 LDS reads are in flight (the wait counter holds 15).  After shell 5 the
+// wave's reads are all issued; after one barrier at shell 6 the stage is free
+// and the copies of slab sn (two slabs ahead) go into it during shells 6-7:
+// they get most of two slabs to land, where copying into the other stage of a
+// two-stage ring gives them one.
 __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8], int wm,
                                              int wn, int lane, const Plan &pl, int64_t sn) {
     const int w = threadIdx.x >> 6;
     const int g = lane >> 4, rl = lane & 15;
     const int64_t kn = sn * BK;
     i32x8 af[8], bf[8];
-    int asc[8], bsc[8];
-    // fragments in the order the MFMAs need them: A0, B0, A1, B1, ...
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int ra = wm * 128 + k * 16 + rl, rb = wn * 128 + k * 16 + rl;
-        af[k] = frag(st.a, ra, g);
-        asc[k] = (int)((st.as[0][ra] >> (8 * g)) & 0xFFu);
-        bf[k] = frag(st.b, rb, g);
-        bsc[k] = (int)((st.bs[0][rb] >> (8 * g)) & 0xFFu);
-    }
+    // the lane's eight scale words per operand, adjacent in the stage (rows
+    // rl + 16 k for k = 0-3 in one half, 4-7 in the other: swapped for rl >= 8)
+    const int h0 = rl * 8 + ((rl >> 3) << 2), h1 = rl * 8 + 4 - ((rl >> 3) << 2);
+    const uint4 sa0 = *reinterpret_cast<const uint4 *>(&st.as[0][wm * 128 + h0]);
+    const uint4 sa1 = *reinterpret_cast<const uint4 *>(&st.as[0][wm * 128 + h1]);
+    const uint4 sb0 = *reinterpret_cast<const uint4 *>(&st.bs[0][wn * 128 + h0]);
+    const uint4 sb1 = *reinterpret_cast<const uint4 *>(&st.bs[0][wn * 128 + h1]);
+    auto read = [&](int k) {
+        af[k] = frag(st.a, wm * 128 + k * 16 + rl, g);
+        bf[k] = frag(st.b, wn * 128 + k * 16 + rl, g);
+    };
+    read(0);
+    read(1);
     __builtin_amdgcn_sched_barrier(0);
-    // MFMAs in growing squares: shell k adds (i, k) for i < k and (k, j) for
-    // j <= k, so it needs only fragments 0..k
+    const uint32_t saw[8] = {sa0.x, sa0.y, sa0.z, sa0.w, sa1.x, sa1.y, sa1.z, sa1.w};
+    const uint32_t sbw[8] = {sb0.x, sb0.y, sb0.z, sb0.w, sb1.x, sb1.y, sb1.z, sb1.w};
+    auto byte_of = [&](uint32_t v) { return (int)((v >> (8 * g)) & 0xFFu); };
     int c = 0;                                         // copies issued
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+        if (k + 2 < 8) {
+            read(k + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (k == 6) {
+            // every read of this wave is complete; once every wave's are,
+            // nobody reads the stage again in this slab
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
 #pragma unroll
         for (int e = 0; e < 2 * k + 1; ++e) {
             const int i = e < k ? e : k, j = e < k ? k : e - k;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0, 0, 0,
-                                                                         bsc[j], 0, asc[i]);
-            // shells 5-7: one copy after every second MFMA (A and B in turn),
-            // then the scale copies
-            if (k >= 5 && (e & 1)) {
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bf[j], af[i], acc[i][j], 0, 0, 0, byte_of(sbw[j]), 0, byte_of(saw[i]));
+            // shell 6: a copy after every MFMA, shell 7 after every second
+            // (A and B in turn), then the scale copies
+            if (k == 6 || (k == 7 && (e & 1))) {
                 if (c < 16) {
                     const int q = c >> 1;
                     if (c & 1) copy_lds16(pl.b_base + kn + pl.b_off[q], st.b + (w * 8 + q) * 1024);
@@ -199,12 +220,6 @@ __device__ __forceinline__ void compute_held(Stage<false> &st, f32x4 (&acc)[8][8
                 ++c;
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
-        if (k == 4) {
-            // this wave's fragment reads are complete; once every wave's are,
-            // nobody reads the stage again in this slab
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __syncthreads();
         }
     }
 }
@@ -340,6 +355,11 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
         mx::issue(sm.st[1], pl, nslab > 1 ? 1 : 0);
         mx::wait_vmcnt<mx::kIssued8>();                // slab 0 has landed
         __syncthreads();
+        // no scalar load in flight into the loop: with one pending the LDS
+        // counter is out of order and every fragment wait becomes lgkmcnt(0)
+        // (the epilogue's arguments are loaded here, not under the loop)
+        asm volatile("" ::"s"(p.c), "s"(p.ldc), "s"(p.M), "s"(p.N));
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         for (int64_t s = 0; s < nslab; ++s) {
             const int64_t sn = s + 2 < nslab ? s + 2 : nslab - 1;
             mx::compute_held(sm.st[s & 1], acc, wm, wn, lane, pl, sn);
