@@ -413,19 +413,33 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
     } else {
     // The MFMAs take the B fragment first, so block (i, jj) holds the
     // transposed 16 x 16 product: lane l has output row l % 16 and columns
-    // 4 * (l / 16) + v, four consecutive columns stored at once.
+    // 4 * (l / 16) + v, four consecutive columns stored at once.  A tile
+    // wholly inside C stores without bounds tests, each row block from one
+    // address (the column blocks at immediate offsets).
+    const int64_t nl = n0 + wn * 128 + 4 * (lane >> 4);       // column of block 0
+    auto row_blocks = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 16 + (lane & 15);
-        if (m >= p.M) continue;
+        for (int i = 0; i < 8; ++i) {
+            const int64_t m = m0 + wm * 128 + i * 16 + (lane & 15);
+            if (!FULL && m >= p.M) continue;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int64_t n = n0 + wn * 128 + jj * 16 + 4 * (lane >> 4);
-            if (n >= p.N) continue;
-            const f32x4 y = acc[i][jj];
-            store4(m, n, y[0], y[1], y[2], y[3]);
+            for (int jj = 0; jj < 8; ++jj) {
+                if (!FULL && nl + jj * 16 >= p.N) continue;
+                const f32x4 y = acc[i][jj];
+                if (BF16_OUT) {
+                    uint16_t *row = reinterpret_cast<uint16_t *>(p.c) + m * p.ldc + nl;
+                    *reinterpret_cast<uint2 *>(row + jj * 16) =
+                        make_uint2(pk_bf16(y[0], y[1]), pk_bf16(y[2], y[3]));
+                } else {
+                    float *row = reinterpret_cast<float *>(p.c) + m * p.ldc + nl;
+                    *reinterpret_cast<float4 *>(row + jj * 16) = make_float4(y[0], y[1], y[2], y[3]);
+                }
+            }
         }
-    }
+    };
+    if (m0 + mx::BM <= p.M && n0 + mx::BN <= p.N) row_blocks(std::true_type{});
+    else row_blocks(std::false_type{});
     }
 }
 
