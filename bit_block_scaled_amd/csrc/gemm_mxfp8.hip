@@ -258,6 +258,9 @@ __device__ __forceinline__ void compute4_held(Stage<true> &st, f32x16 (&acc)[4][
         bs0[j] = st.bs[0][r];
         bs1[j] = st.bs[1][r];
     }
+    // the chunks in step order (each step's MFMAs then wait only for their
+    // own reads and those before)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int c = 2 * ks + h;
@@ -271,8 +274,8 @@ __device__ __forceinline__ void compute4_held(Stage<true> &st, f32x16 (&acc)[4][
             const int r = wm * 128 + i * 32 + rl;
             ad[ks][i] = *reinterpret_cast<const uint4 *>(st.a + r * BK + 16 * swz(r, c));
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int c = 2 * ks + h;                      // the lane's 16-byte chunk
@@ -374,6 +377,8 @@ __device__ __forceinline__ void mx_gemm_big(const Mx8GemmParams &p, uint8_t *sme
         mx::issue(sm.st[1], pl, nslab > 1 ? 1 : 0);
         mx::wait_vmcnt<mx::kIssued4>();                // slab 0 has landed
         __syncthreads();
+        asm volatile("" ::"s"(p.c), "s"(p.ldc), "s"(p.M), "s"(p.N));
+        __builtin_amdgcn_s_waitcnt(0xC07F);           // as for FP8
         for (int64_t s = 0; s < nslab; ++s) {
             const int64_t sn = s + 2 < nslab ? s + 2 : nslab - 1;
             mx::compute4_held(sm.st[s & 1], acc, wm, wn, lane, pl, sn);

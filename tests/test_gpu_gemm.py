@@ -135,7 +135,9 @@ def test_full_wgrad(bbs):
 
 @pytest.mark.parametrize("M,N,K", [(32, 32, 32), (144, 80, 96), (256, 256, 512), (80, 272, 1056),
                                    # large-tile kernel: one, two and three slabs, ragged tiles
-                                   (256, 256, 128), (272, 400, 256), (528, 272, 384)])
+                                   # (M = 300: a row group of the last tile only partly in A)
+                                   (256, 256, 128), (272, 400, 256), (528, 272, 384),
+                                   (300, 208, 256)])
 def test_mxfp8_small(bbs, M, N, K):
     announce(f"MXFP8 GEMM M={M} N={N} K={K}")
     a = O.mxfp8_quantize(synth.laplace(M, K, M + K, 1e-3), mode=O.SR, seed=1)
