@@ -178,8 +178,12 @@ __device__ __forceinline__ float div6(float a) {
     constexpr float kInv6 = 0x1.555556p-3f;             // RN(1/6)
     float q = a * kInv6;
     q = __builtin_fmaf(__builtin_fmaf(-q, 6.0f, a), kInv6, q);
-    if (__builtin_amdgcn_ballot_w64(a < 0x1p-124f))       // rare: wave-uniform branch
+    if (__builtin_amdgcn_ballot_w64(a < 0x1p-124f)) {     // rare: wave-uniform branch
+        // (an empty volatile statement keeps the compiler from hoisting the
+        // division out of the branch into every call)
+        asm volatile("");
         if (a < 0x1p-124f) q = a / 6.0f;
+    }
     return q;
 }
 

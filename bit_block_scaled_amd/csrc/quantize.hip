@@ -515,6 +515,17 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
             const uint64_t nstep = (uint64_t)p.R / 8;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                // column copy alone (registers to spare): the column's random
+                // words first, which do not depend on the values, so they
+                // overlap the transform and the scale (which ends in a rarely
+                // taken branch)
+                constexpr bool EARLY = CSR && !HAS_ROW && !HAS_MX;
+                uint32_t wr0[4], wr1[4];
+                const uint64_t n = n0 + (uint64_t)j * nstep;
+                if constexpr (EARLY) {
+                    sr_block(p.col_seed, p.col_stream, n, wr0);
+                    sr_block(p.col_seed, p.col_stream, n + 1, wr1);
+                }
                 float y[16];
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
@@ -547,12 +558,10 @@ __device__ __forceinline__ void encode_tile(const QuantParams &p, const Piece &q
                 if (FUSE) s = s * 0.25f;
                 uint32_t w0, w1;
                 if constexpr (CSR) {
-                    const uint64_t n = n0 + (uint64_t)j * nstep;
-                    uint32_t w[4];
-                    sr_block(p.col_seed, p.col_stream, n, w);
-                    w0 = e2m1_sr8(y, s, w);
-                    sr_block(p.col_seed, p.col_stream, n + 1, w);
-                    w1 = e2m1_sr8(y + 8, s, w);
+                    if constexpr (!EARLY) sr_block(p.col_seed, p.col_stream, n, wr0);
+                    w0 = e2m1_sr8(y, s, wr0);
+                    if constexpr (!EARLY) sr_block(p.col_seed, p.col_stream, n + 1, wr1);
+                    w1 = e2m1_sr8(y + 8, s, wr1);
                 } else {
                     w0 = e2m1_rne8(y, s);
                     w1 = e2m1_rne8(y + 8, s);
