@@ -46,7 +46,7 @@ ROTATE = 8                                     # buffer sets the timed runs cycl
 # WRITE_SIZE runs scaled by what the same counters read for the 512 MiB copy
 # (profiles/sq_hbm_counters_step_kernels_8192x4096x14336.md), valid only for the kernel
 # sources they were taken on: reported as null once those sources change.
-FPROP_TRAFFIC = {"bytes": 626605598, "sources_sha256_16": "a1e6566283563662"}
+FPROP_TRAFFIC = {"bytes": 626723567, "sources_sha256_16": "9210d85e89b17c03"}
 FPROP_SOURCES = ["bit_block_scaled_amd/csrc/gemm_nvfp4.hip", "bit_block_scaled_amd/csrc/bbs_device.hpp",
                  "bit_block_scaled_amd/csrc/bbs_kernels.hpp", "bit_block_scaled_amd/build.py"]
 
