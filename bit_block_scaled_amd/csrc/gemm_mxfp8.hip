@@ -160,8 +160,9 @@ constexpr int kIssued8 = 18;
 // The MFMAs of one FP8 slab (8 A + 8 B fragments, 128 VGPRs).  The MFMAs
 // run in growing squares (shell k = the blocks that need fragments k and
 // below), and the fragment reads go two shells ahead of the MFMAs that use
-// them, so a shell waits only for reads issued two shells before and at most
-// 12 LDS reads are in flight (the wait counter holds 15).  After shell 5 the
+// them, so a shell waits only for the reads issued before the previous
+// shell's, not for all 20 of the slab (the LDS wait counter tracks at most
+// 15, and with more in flight the compiler waits for all).  After shell 5 the
 // wave's reads are all issued; after one barrier at shell 6 the stage is free
 // and the copies of slab sn (two slabs ahead) go into it during shells 6-7:
 // they get most of two slabs to land, where copying into the other stage of a
