@@ -319,10 +319,39 @@ __global__ __launch_bounds__(kQT) void amax_kernel(const uint16_t *__restrict__ 
 // Pass 2: encode.
 // ---------------------------------------------------------------------------
 
-// The tensor amax: the maximum of n <= kAmaxPartials partials, in every lane.
+// A thread's share of n <= kAmaxPartials amax partials, NT threads taking
+// every NT-th: all its loads are issued before any value is used, so they
+// cost one memory round trip, and, issued ahead of a tile's loads, they are
+// waited on without waiting for the tile (the memory counter drains in
+// order of issue).
+template <int NT>
+struct PartShare {
+    static constexpr int K = kAmaxPartials / NT;
+    float v[K];
+    __device__ __forceinline__ void load(const float *part, int n) {
+        const int t = (int)threadIdx.x % NT;
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = t + k * NT < n ? part[t + k * NT] : 0.0f;
+    }
+    __device__ __forceinline__ float max() const {
+        float m = v[0];
+#pragma unroll
+        for (int k = 1; k < K; ++k) m = fmaxf(m, v[k]);
+        return m;
+    }
+};
+
+// The tensor amax: the maximum of n <= kAmaxPartials partials, in every lane
+// (the first 256 in one round trip, any others in a loop).
 __device__ __forceinline__ float fold_partials(const float *part, int n) {
-    float m = 0.0f;
-    for (int i = threadIdx.x & 63; i < n; i += 64) m = fmaxf(m, part[i]);
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = (threadIdx.x & 63) + 64 * k;
+        v[k] = i < n ? part[i] : 0.0f;
+    }
+    float m = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    for (int i = (threadIdx.x & 63) + 256; i < n; i += 64) m = fmaxf(m, part[i]);
     return wave_max(m);
 }
 
@@ -649,21 +678,23 @@ __global__ __launch_bounds__(kET, MINW) void quant_kernel(QuantParams p) {
     __shared__ __align__(16) QuantLds<GELU> L;
     const int64_t T = ((p.R + kTileR - 1) / kTileR) * ((p.C + kTileC - 1) / kTileC);
     const TileWalk walk = WALK ? xcd_walk(T) : TileWalk{xcd_tile(blockIdx.x, T), 0, 1};
-    // the first tile's piece is in flight while the scales are set up
+    // Tensor scales, identical in every wave: the partials are folded once
+    // per workgroup (each thread a strided share, then the eight waves),
+    // while the first tile's piece, loaded after them, is in flight.
+    constexpr bool plain_amax = HAS_ROW || (HAS_COL && !RHT);
+    // (the tile's arguments are read with the partials', not a round trip
+    // after them)
+    asm volatile("" ::"s"(p.x), "s"(p.R), "s"(p.C), "s"(p.ld), "s"(p.part), "s"(p.n_part));
+    PartShare<kET> pa, pb;
+    if (plain_amax) pa.load(p.part, p.n_part);
+    if (HAS_COL && RHT) pb.load(p.part_rht, p.n_part_rht);
     uint4 v[8];
     constexpr bool CO = !HAS_ROW && !HAS_MX;
     Piece q = piece_of<CO>(!WALK || walk.first < walk.end ? walk.first : 0, p.R, p.C);
     if (!WALK || walk.first < walk.end) load_piece<CO>(p.x, p.R, p.C, p.ld, q, v);
-
-    // Tensor scales, identical in every wave: the partials are folded once
-    // per workgroup (each thread a strided share, then the eight waves).
-    const bool plain_amax = HAS_ROW || (HAS_COL && !RHT);
+    __builtin_amdgcn_sched_barrier(0);      // every load issued before the fold waits
     {
-        float a = 0.0f, b = 0.0f;
-        if (plain_amax)
-            for (int i = threadIdx.x; i < p.n_part; i += kET) a = fmaxf(a, p.part[i]);
-        if (HAS_COL && RHT)
-            for (int i = threadIdx.x; i < p.n_part_rht; i += kET) b = fmaxf(b, p.part_rht[i]);
+        float a = plain_amax ? pa.max() : 0.0f, b = HAS_COL && RHT ? pb.max() : 0.0f;
         a = wave_max(a);
         b = wave_max(b);
         if ((threadIdx.x & 63) == 0) {
@@ -778,17 +809,19 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
 #pragma unroll
         for (int i = 0; i < PR; ++i) d[i] = *reinterpret_cast<const uint4 *>(src + i * p.ld);
     };
+    // the tensor scale (row copy): partials folded once per workgroup while
+    // the first step, loaded after them, is in flight
+    asm volatile("" ::"s"(p.x), "s"(p.R), "s"(p.C), "s"(p.ld), "s"(p.part), "s"(p.n_part));
+    PartShare<kQT> pa;
+    if (HAS_ROW) pa.load(p.part, p.n_part);
     int64_t t = (int64_t)blockIdx.x * (kQT / 64) + w;
     uint4 v[PR];
     int64_t r0 = 0, c0 = 0;
     if (t < T) load(t, v, r0, c0);
-
-    // the tensor scale (row copy): partials folded once per workgroup
+    __builtin_amdgcn_sched_barrier(0);
     float s_enc = 1.0f;
     if (HAS_ROW) {
-        float a = 0.0f;
-        for (int i = threadIdx.x; i < p.n_part; i += kQT) a = fmaxf(a, p.part[i]);
-        a = wave_max(a);
+        float a = wave_max(pa.max());
         if (lane == 0) L.fold[w] = a;
     }
     if constexpr (GELU) gelu_table_load(s_gelu, p.gelu_tab);
@@ -1400,12 +1433,11 @@ static int persistent_grid(int64_t tiles, hipStream_t s) {
 hipError_t launch_amax(const uint16_t *x, int64_t R, int64_t C, int64_t ld, bool plain, bool rht,
                        uint32_t signs, float *part, float *part_rht, int *n_part,
                        hipStream_t s, float *gelu_tab) {
-    // one wave per 16 x 256 step (16 x 512 for GELU); up to 1024 workgroups
-    // (2048 with the RHT maximum alone, whose butterflies make the read
-    // slower per byte)
+    // one wave per 16 x 256 step (16 x 512 for GELU); up to 256 workgroups
+    // (1024 for GELU, whose tanh makes the pass slower per byte)
     const int64_t sc = gelu_tab ? kAmaxStepC : kAmaxStepC / 2;
     const int64_t steps = (R / 16) * ((C + sc - 1) / sc);
-    const int64_t cap = (rht && !plain) ? kAmaxPartials : kAmaxPartials / 2;
+    const int64_t cap = gelu_tab ? kAmaxPartials / 2 : kAmaxPartials / 8;
     const int64_t want = (steps + kQT / 64 - 1) / (kQT / 64);
     const int grid = (int)(want < cap ? want : cap);
     *n_part = grid;
