@@ -341,6 +341,23 @@ struct PartShare {
     }
 };
 
+// The GELU table, workspace -> LDS, by asynchronous LDS copies (no
+// registers, no wait per load): wave w of the NT threads copies the 1 KB
+// chunks w, w + NT / 64, ...  The caller waits for the vector memory counter
+// to drain, then synchronises, before the first lookup.
+template <int NT>
+__device__ __forceinline__ void gelu_table_copy(float *lds, const float *tab) {
+    constexpr int kChunks = kGeluTabSize * 4 / 1024, kWaves = NT / 64;
+    static_assert(kGeluTabSize % 256 == 0, "whole 1 KB chunks");
+    const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < (kChunks + kWaves - 1) / kWaves; ++k) {
+        const int c = w + k * kWaves;
+        if (c < kChunks) copy_lds16(tab + c * 256 + lane * 4, lds + c * 256);
+    }
+}
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
 // The tensor amax: the maximum of n <= kAmaxPartials partials, in every lane
 // (the first 256 in one round trip, any others in a loop).
 __device__ __forceinline__ float fold_partials(const float *part, int n) {
@@ -720,7 +737,10 @@ __global__ __launch_bounds__(kET, MINW) void quant_kernel(QuantParams p) {
     }
     if (HAS_ROW) enc_scale_table(L.tab[0], s_dec_row);
     if (HAS_COL) enc_scale_table(L.tab[1], s_dec_col);
-    if constexpr (GELU) gelu_table_load(L.gelu, p.gelu_tab);
+    if constexpr (GELU) {
+        gelu_table_copy<kET>(L.gelu, p.gelu_tab);
+        wait_vmem();
+    }
     __syncthreads();
 
     if constexpr (!WALK) {
@@ -824,7 +844,10 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
         float a = wave_max(pa.max());
         if (lane == 0) L.fold[w] = a;
     }
-    if constexpr (GELU) gelu_table_load(s_gelu, p.gelu_tab);
+    if constexpr (GELU) {
+        gelu_table_copy<kQT>(s_gelu, p.gelu_tab);
+        wait_vmem();
+    }
     __syncthreads();
     if (HAS_ROW) {
         s_enc = tensor_s_enc(fmaxf(fmaxf(L.fold[0], L.fold[1]), fmaxf(L.fold[2], L.fold[3])));
@@ -1117,7 +1140,8 @@ __global__ __launch_bounds__(kQT) void quant_act_kernel(QuantParams p) {
     for (int k = 0; k < kActChunks; ++k)
         if (k < nch) load_chunk8(row, p.C, k, lane, v[k]);
     if constexpr (GELU) {
-        gelu_table_load(s_gelu, p.gelu_tab);        // while the row is in flight
+        gelu_table_copy<kQT>(s_gelu, p.gelu_tab);   // while the row is in flight
+        wait_vmem();
         __syncthreads();
     }
     if (!live) return;                                // whole waves leave together
