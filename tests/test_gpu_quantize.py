@@ -184,6 +184,25 @@ def test_mxfp8_beside_amax_copies(bbs, shape, combo, mode):
                                        mode=mode, seed=11, stream=2), "col")
 
 
+@pytest.mark.parametrize("combo", [MX_COMBOS[1], MX_COMBOS[4]], ids=["row", "rowcolrht"])
+def test_mxfp8_beside_amax_copies_many_partials(bbs, combo):
+    # 2048 x 4096: the amax pass with the MXFP8 copy runs 512 workgroups, so
+    # the encode folds 512 partials (more than one per thread of its share)
+    row, col, tile2d, rht = combo
+    R, C = 2048, 4096
+    announce(f"MXFP8 + copies {combo} {(R, C)} mode=SR, many partials")
+    x = synth.laplace(R, C, 7100, 1e-3)
+    s = synth.rht_signs(403) if rht else 0
+    rq, cq, mq = _gpu_quantize(bbs, x, row=row, col=col, mx=True, tile2d=tile2d, rht=rht, signs=s,
+                               row_round=O.SR, col_round=O.SR, mx_round=O.SR,
+                               row_rng=(12, 1), col_rng=(12, 2), mx_rng=(12, 3))
+    _same_mx8(mq, O.mxfp8_quantize(x, mode=O.SR, seed=12, stream=3), "MXFP8")
+    _same_fp4(rq, O.nvfp4_quantize(x, tile2d=tile2d, mode=O.SR, seed=12, stream=1), "row")
+    if col:
+        _same_fp4(cq, O.nvfp4_quantize(x, transpose=True, tile2d=tile2d, rht=rht, signs=s,
+                                       mode=O.SR, seed=12, stream=2), "col")
+
+
 def test_degenerate_inputs(bbs):
     announce("zero / negative-zero / single-outlier tensors")
     z = np.zeros((32, 64), np.uint16)
