@@ -708,7 +708,10 @@ __global__ __launch_bounds__(kET, MINW) void quant_kernel(QuantParams p) {
     uint4 v[8];
     constexpr bool CO = !HAS_ROW && !HAS_MX;
     Piece q = piece_of<CO>(!WALK || walk.first < walk.end ? walk.first : 0, p.R, p.C);
-    if (!WALK || walk.first < walk.end) load_piece<CO>(p.x, p.R, p.C, p.ld, q, v);
+    // (unconditional, so that the fold's wait can leave these loads in flight
+    // on every path: a workgroup without tiles loads tile 0, which always
+    // exists, and never uses it)
+    load_piece<CO>(p.x, p.R, p.C, p.ld, q, v);
     __builtin_amdgcn_sched_barrier(0);      // every load issued before the fold waits
     {
         float a = plain_amax ? pa.max() : 0.0f, b = HAS_COL && RHT ? pb.max() : 0.0f;
@@ -837,7 +840,8 @@ __global__ __launch_bounds__(kQT, MINW) void quant_rows_kernel(QuantParams p, fl
     int64_t t = (int64_t)blockIdx.x * (kQT / 64) + w;
     uint4 v[PR];
     int64_t r0 = 0, c0 = 0;
-    if (t < T) load(t, v, r0, c0);
+    if (HAS_ROW) load(t < T ? t : 0, v, r0, c0);     // (step 0 always exists; see quant_kernel)
+    else if (t < T) load(t, v, r0, c0);
     __builtin_amdgcn_sched_barrier(0);
     float s_enc = 1.0f;
     if (HAS_ROW) {
